@@ -1,0 +1,346 @@
+"""Plain CPU oracle for KIVI-style quantized KV-cache append and decode attention.
+
+TEST INFRASTRUCTURE. Only tests/, __graft_entry__.smoke() and the cpu_baseline
+leg of bench.py may import this module. The product path (the HIP library and
+its Python binding) never imports it, and this module imports nothing from the
+product path: it works on plain numpy arrays.
+
+Written slowly and directly so that a reader can check it against the pages:
+
+  [P2] zubnet.ai -- "KV cache compression techniques for LLM inference
+       (H2O, KIVI, MLA, StreamingLLM)", paragraph on the quantization family.
+  [P3] encorp.ai -- "La compression du cache KV est une décision
+       d'infrastructure, pas un débat sur les modèles", section on HBM, not
+       FLOPs, being the ceiling.
+  [P4] patricehuetz.fr -- "Quantification du KV-Cache : TurboQuant et l'état de
+       l'art en 2026": section "Le problème : le KV-cache, gouffre silencieux"
+       (memory formula), section "KIVI (2024) — la quantification asymétrique
+       par canal", innovation 3 "Bit-packing dense : INT4 et INT2 en mémoire
+       GPU" and innovation 4 "Fenêtre résiduelle".
+  [P1] ai-automate.fr -- "KV-cache compressé et modèles 4-bit ...", section on
+       Minima-KV (partial attention states merged by an online softmax).
+
+What the pages fix: keys are quantized per channel, values per token [P2; P4
+KIVI]; each channel carries its own min/max parameters [P4 KIVI]; codes are
+INT2 (or INT4) packed 16 (or 8) to a 32-bit word [P4 innovation 3]; the most
+recent tokens stay in full precision [P4 KIVI; P4 innovation 4]; the cache size
+is 2*L*H*d*S*bytes [P4 "Le problème"].
+
+What the pages leave open is taken here as follows (each reading is one line
+of the readings list kept with the design notes):
+  * the quantizer is asymmetric uniform min/max: scale = (max-min)/(2^b-1),
+    zero-point = min, x_hat = code*scale + zero; scale and zero are stored as
+    fp16;
+  * formula F fixes every rounding in fp32: see quantize_groups();
+  * a constant group (scale rounds to 0) gets all-zero codes;
+  * LSB-first packing: slot i of a word sits at bits [i*b, (i+1)*b);
+  * keys are grouped over G consecutive tokens (one block), values over G_V
+    consecutive channels of one token;
+  * the residual window keeps R <= r < R+G tokens: after a flush, the oldest
+    complete G-token blocks beyond R are quantized, so Q = G*floor(max(S-R,0)/G);
+  * attention uses softmax scale 1/sqrt(d) by default, query head h' reads kv
+    head floor(h'/n_g), and is evaluated in fp64 on the dequantized cache.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass
+
+import numpy as np
+
+F32 = np.float32
+
+
+# ---------------------------------------------------------------------------
+# Configuration of one cache layer (plain data; mirrors the C struct fields).
+# ---------------------------------------------------------------------------
+@dataclass(frozen=True)
+class CacheSpec:
+    batch: int
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    k_bits: int
+    v_bits: int
+    k_group: int          # G: tokens per key group (= tokens per block)
+    v_group: int          # G_V: channels per value group
+    residual: int         # R
+    res_capacity: int     # ring slots per (sequence, kv head)
+    dtype: str            # "f16" or "bf16"
+
+    @property
+    def n_g(self) -> int:
+        return self.num_q_heads // self.num_kv_heads
+
+
+# ---------------------------------------------------------------------------
+# Formula F: asymmetric min/max quantization of one group, fixed in fp32.
+# [P4, section "KIVI (2024)"]: every channel (keys) or token (values) has its
+# own min/max parameters; the rounding steps are this oracle's reading.
+# ---------------------------------------------------------------------------
+def quantize_groups(x: np.ndarray, bits: int, axis: int):
+    """Quantize groups of a float32 array that lie along `axis`.
+
+    Steps, each an IEEE fp32 operation rounded to nearest-even (no fused
+    multiply-add anywhere):
+      mn, mx = min, max of the group
+      z16 = fp16(mn)                                  (round to nearest even)
+      s16 = fp16( fp32(mx - mn) / fp32(2^b - 1) )
+      if s16 == 0: every code is 0
+      else: inv = fp32(1 / fp32(s16))
+            t = fp32( fp32(x - fp32(z16)) * inv )
+            code = clamp(round_half_even(t), 0, 2^b - 1)
+
+    Returns (s16, z16, codes) with s16/z16 float16 arrays of the reduced shape
+    and codes uint8 of x's shape.
+    """
+    x = np.asarray(x, dtype=F32)
+    qmax = F32(2 ** bits - 1)
+    mn = x.min(axis=axis, keepdims=True)
+    mx = x.max(axis=axis, keepdims=True)
+    z16 = mn.astype(np.float16)
+    s16 = ((mx - mn) / qmax).astype(np.float16)
+    s32 = s16.astype(F32)
+    z32 = z16.astype(F32)
+    with np.errstate(divide="ignore", invalid="ignore", over="ignore"):
+        inv = F32(1.0) / s32
+        t = (x - z32) * inv
+        codes = np.clip(np.rint(t), F32(0.0), qmax)
+    codes = np.where(s32 == 0, F32(0.0), codes).astype(np.uint8)
+    return np.squeeze(s16, axis=axis), np.squeeze(z16, axis=axis), codes
+
+
+def dequantize(codes: np.ndarray, s16: np.ndarray, z16: np.ndarray) -> np.ndarray:
+    """x_hat = code * scale + zero, in fp64 (exact for these operands)."""
+    return codes.astype(np.float64) * s16.astype(np.float64) + z16.astype(np.float64)
+
+
+# ---------------------------------------------------------------------------
+# Dense bit-packing [P4, innovation 3]: 32/b codes per uint32, LSB first.
+# ---------------------------------------------------------------------------
+def pack_lsb_first(codes: np.ndarray, bits: int) -> np.ndarray:
+    """Pack the last axis of `codes` into uint32 words, slot i at bits [i*b, (i+1)*b)."""
+    per = 32 // bits
+    c = np.asarray(codes, dtype=np.uint32)
+    n = c.shape[-1]
+    if n % per:
+        raise ValueError(f"last axis {n} is not a multiple of {per}")
+    c = c.reshape(c.shape[:-1] + (n // per, per))
+    words = np.zeros(c.shape[:-1], dtype=np.uint32)
+    for i in range(per):
+        words |= (c[..., i] & np.uint32(2 ** bits - 1)) << np.uint32(i * bits)
+    return words
+
+
+def unpack_lsb_first(words: np.ndarray, bits: int) -> np.ndarray:
+    """Inverse of pack_lsb_first: uint32 words -> codes along a longer last axis."""
+    per = 32 // bits
+    w = np.asarray(words, dtype=np.uint32)
+    out = np.empty(w.shape + (per,), dtype=np.uint8)
+    for i in range(per):
+        out[..., i] = (w >> np.uint32(i * bits)) & np.uint32(2 ** bits - 1)
+    return out.reshape(w.shape[:-1] + (w.shape[-1] * per,))
+
+
+# ---------------------------------------------------------------------------
+# One quantized block: G tokens of one (sequence, kv head).
+#
+# Record layout (little-endian bytes, sections in this order):
+#   K codes  uint32 [G][d*b_K/32]      token-major: word w of token t holds
+#                                      channels w*32/b_K ... (LSB first)
+#   K scale  fp16   [d]                per channel, over the G tokens
+#   K zero   fp16   [d]
+#   V codes  uint32 [d][G*b_V/32]      channel-major: word w of channel c holds
+#                                      tokens w*32/b_V ... of the block
+#   V scale  fp16   [d/G_V][G]         per (channel group, token)
+#   V zero   fp16   [d/G_V][G]
+# ---------------------------------------------------------------------------
+def record_sections(spec: CacheSpec):
+    G, d = spec.k_group, spec.head_dim
+    kc = G * d * spec.k_bits // 8
+    ks = 2 * d
+    vc = d * G * spec.v_bits // 8
+    vs = 2 * (d // spec.v_group) * G
+    return {"k_codes": kc, "k_scale": ks, "k_zero": ks,
+            "v_codes": vc, "v_scale": vs, "v_zero": vs}
+
+
+def record_bytes(spec: CacheSpec) -> int:
+    return sum(record_sections(spec).values())
+
+
+def quantize_block(spec: CacheSpec, kblk: np.ndarray, vblk: np.ndarray):
+    """Quantize one block. kblk, vblk: float32 [G][d] (exact input values).
+
+    Keys: one group per channel over the G tokens [P4 KIVI: keys per channel].
+    Values: one group per (token, G_V consecutive channels) [P4 KIVI: values
+    per token].
+    Returns a dict of the section arrays.
+    """
+    G, d, gv = spec.k_group, spec.head_dim, spec.v_group
+    assert kblk.shape == (G, d) and vblk.shape == (G, d)
+    ks, kz, kcodes = quantize_groups(kblk, spec.k_bits, axis=0)          # [d], [d], [G][d]
+    vs, vz, vcodes = quantize_groups(vblk.reshape(G, d // gv, gv), spec.v_bits, axis=2)
+    vcodes = vcodes.reshape(G, d)                                         # [G][d]
+    return {
+        "k_codes": pack_lsb_first(kcodes, spec.k_bits),                   # [G][d*bK/32]
+        "k_scale": ks, "k_zero": kz,                                      # [d]
+        "v_codes": pack_lsb_first(vcodes.T, spec.v_bits),                 # [d][G*bV/32]
+        "v_scale": np.ascontiguousarray(vs.T),                            # [d/G_V][G]
+        "v_zero": np.ascontiguousarray(vz.T),
+    }
+
+
+def block_to_bytes(sec) -> np.ndarray:
+    parts = [np.ascontiguousarray(sec[k]).view(np.uint8).ravel()
+             for k in ("k_codes", "k_scale", "k_zero", "v_codes", "v_scale", "v_zero")]
+    return np.concatenate(parts)
+
+
+def bytes_to_block(spec: CacheSpec, rec: np.ndarray):
+    """Parse record bytes back into section arrays (inverse of block_to_bytes)."""
+    sizes = record_sections(spec)
+    G, d, gv = spec.k_group, spec.head_dim, spec.v_group
+    out, off = {}, 0
+    shapes = {
+        "k_codes": ((G, d * spec.k_bits // 32), np.uint32),
+        "k_scale": ((d,), np.float16), "k_zero": ((d,), np.float16),
+        "v_codes": ((d, G * spec.v_bits // 32), np.uint32),
+        "v_scale": ((d // gv, G), np.float16), "v_zero": ((d // gv, G), np.float16),
+    }
+    rec = np.ascontiguousarray(rec, dtype=np.uint8)
+    for name in ("k_codes", "k_scale", "k_zero", "v_codes", "v_scale", "v_zero"):
+        n = sizes[name]
+        shp, dt = shapes[name]
+        out[name] = rec[off:off + n].view(dt).reshape(shp)
+        off += n
+    return out
+
+
+def dequantize_block(spec: CacheSpec, sec):
+    """fp64 [G][d] key and value reconstructions of one block."""
+    G, d, gv = spec.k_group, spec.head_dim, spec.v_group
+    kcodes = unpack_lsb_first(sec["k_codes"], spec.k_bits)               # [G][d]
+    khat = dequantize(kcodes, sec["k_scale"][None, :], sec["k_zero"][None, :])
+    vcodes = unpack_lsb_first(sec["v_codes"], spec.v_bits).T            # [G][d]
+    vs = np.repeat(sec["v_scale"].T, gv, axis=1)                          # [G][d]
+    vz = np.repeat(sec["v_zero"].T, gv, axis=1)
+    vhat = dequantize(vcodes, vs, vz)
+    return khat, vhat
+
+
+# ---------------------------------------------------------------------------
+# Residual window policy [P4 KIVI: recent tokens stay fp16; P4 innovation 4:
+# the last R tokens stay in full precision and the switch is invisible to the
+# attention kernel].  Reading: after a flush R <= r < R+G.
+# ---------------------------------------------------------------------------
+def quantized_prefix(S: int, R: int, G: int) -> int:
+    """Q = number of leading tokens held quantized once the window is flushed."""
+    return G * (max(S - R, 0) // G)
+
+
+# ---------------------------------------------------------------------------
+# Expected cache state after appending S_b tokens per sequence and flushing.
+# ---------------------------------------------------------------------------
+def expected_blocks(spec: CacheSpec, K: np.ndarray, V: np.ndarray, S_b: int):
+    """Records of every quantized block of one (sequence, kv head).
+
+    K, V: float32 [>=S_b][d] input values of that pair. Returns uint8
+    [Q/G][record_bytes].
+    """
+    G = spec.k_group
+    Q = quantized_prefix(S_b, spec.residual, G)
+    recs = [block_to_bytes(quantize_block(spec, K[j * G:(j + 1) * G], V[j * G:(j + 1) * G]))
+            for j in range(Q // G)]
+    if not recs:
+        return np.zeros((0, record_bytes(spec)), np.uint8)
+    return np.stack(recs)
+
+
+def ring_slots(Q: int, S: int, capacity: int) -> np.ndarray:
+    """Ring-buffer slots holding residual tokens Q..S-1 (token t lives at t mod C)."""
+    return np.arange(Q, S) % capacity
+
+
+# ---------------------------------------------------------------------------
+# Attention in fp64 [P4 "Le problème": queries read back the stored keys and
+# values of every earlier token].
+# ---------------------------------------------------------------------------
+def attention_fp64(q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float) -> np.ndarray:
+    """Softmax attention of queries q [n][d] over keys/values K, V [T][d], fp64."""
+    q = np.asarray(q, np.float64)
+    K = np.asarray(K, np.float64)
+    V = np.asarray(V, np.float64)
+    s = float(scale) * (q @ K.T)                      # [n][T]
+    m = s.max(axis=1, keepdims=True)
+    p = np.exp(s - m)
+    return (p @ V) / p.sum(axis=1, keepdims=True)
+
+
+def pair_cache_fp64(spec: CacheSpec, K: np.ndarray, V: np.ndarray, S_b: int):
+    """The attention inputs of one (sequence, kv head): dequantized blocks then
+    the exact residual tokens, in token order. Returns (Khat, Vhat) [S_b][d]."""
+    G = spec.k_group
+    Q = quantized_prefix(S_b, spec.residual, G)
+    ks, vs = [], []
+    for j in range(Q // G):
+        kh, vh = dequantize_block(spec, quantize_block(spec, K[j * G:(j + 1) * G], V[j * G:(j + 1) * G]))
+        ks.append(kh)
+        vs.append(vh)
+    ks.append(np.asarray(K[Q:S_b], np.float64))
+    vs.append(np.asarray(V[Q:S_b], np.float64))
+    return np.concatenate(ks, axis=0), np.concatenate(vs, axis=0)
+
+
+def decode_attention(spec: CacheSpec, q: np.ndarray, K: np.ndarray, V: np.ndarray,
+                     lengths, scale: float | None = None, pairs=None) -> np.ndarray:
+    """Single-token decode attention over the quantized cache, fp64.
+
+    q: [B][H_q][d]; K, V: [B][H_kv][>=max S][d] float32 input values;
+    lengths: S_b per sequence. Query head h' reads kv head h'//n_g.
+    `pairs` limits the work to a list of (b, h_kv); other outputs are NaN.
+    Returns out [B][H_q][d] float64.
+    """
+    B, Hq, d = q.shape
+    n_g = spec.n_g
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    out = np.full((B, Hq, d), np.nan)
+    if pairs is None:
+        pairs = [(b, h) for b in range(B) for h in range(spec.num_kv_heads)]
+    for b, h in pairs:
+        S_b = int(lengths[b])
+        if S_b == 0:
+            out[b, h * n_g:(h + 1) * n_g] = 0.0
+            continue
+        Kh, Vh = pair_cache_fp64(spec, K[b, h], V[b, h], S_b)
+        out[b, h * n_g:(h + 1) * n_g] = attention_fp64(q[b, h * n_g:(h + 1) * n_g], Kh, Vh, scale)
+    return out
+
+
+def exact_attention(spec: CacheSpec, q, K, V, lengths, scale=None, pairs=None):
+    """Attention on the unquantized inputs (for the fidelity report only)."""
+    B, Hq, d = q.shape
+    n_g = spec.n_g
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    out = np.full((B, Hq, d), np.nan)
+    if pairs is None:
+        pairs = [(b, h) for b in range(B) for h in range(spec.num_kv_heads)]
+    for b, h in pairs:
+        S_b = int(lengths[b])
+        out[b, h * n_g:(h + 1) * n_g] = attention_fp64(
+            q[b, h * n_g:(h + 1) * n_g], K[b, h, :S_b], V[b, h, :S_b], scale)
+    return out
+
+
+# ---------------------------------------------------------------------------
+# KV-cache memory [P4 "Le problème"]: 2 * L * H * d * S * bytes per element.
+# ---------------------------------------------------------------------------
+def kv_cache_bytes(layers: int, heads: int, head_dim: int, tokens: int, bytes_per_elt: float) -> float:
+    return 2 * layers * heads * head_dim * tokens * bytes_per_elt
+
+
+def quantized_bytes_per_token(spec: CacheSpec) -> float:
+    """Bytes one quantized token occupies per kv head (codes + scale/zero)."""
+    return record_bytes(spec) / spec.k_group
