@@ -1,0 +1,184 @@
+/*
+ * kvq.h -- C ABI of libkvq: KIVI-style asymmetric low-bit KV-cache append,
+ * residual flush (quantize + pack) and single-token decode attention over the
+ * packed cache, for AMD Instinct MI355X (gfx950).
+ *
+ * Sources (cited by page title and section):
+ *   [P2] zubnet.ai, survey of KV-cache compression techniques (H2O, KIVI, MLA,
+ *        StreamingLLM): quantization family -- keep every token, lower the bits;
+ *        KIVI quantizes keys per channel and values per token.
+ *   [P3] encorp.ai, "La compression du cache KV est une décision
+ *        d'infrastructure, pas un débat sur les modèles": decode is bound by
+ *        HBM traffic, not FLOPs.
+ *   [P4] patricehuetz.fr, "Quantification du KV-Cache : TurboQuant et l'état de
+ *        l'art en 2026": section "Le problème" (cache bytes = 2*L*H*d*S*bytes),
+ *        section "KIVI (2024)" (per-channel keys, per-token values, own min/max
+ *        parameters, INT2 with a full-precision residual of recent tokens),
+ *        innovation 3 (16 INT2 or 8 INT4 codes per 32-bit word; 16-token blocks
+ *        for paged attention), innovation 4 (the most recent tokens stay in
+ *        full precision and attention reads both parts transparently).
+ *   [P1] ai-automate.fr, "KV-cache compressé et modèles 4-bit ...", section on
+ *        Minima-KV: partial attention states merged by a globally normalised
+ *        online softmax.
+ *
+ * Memory model. The caller owns every buffer (sized with kvq_get_layout and
+ * kvq_workspace_size). The library allocates nothing, keeps no global state,
+ * borrows the pointers for the duration of a call and enqueues its kernels on
+ * the caller's HIP stream (passed as void*; NULL is the default stream). All
+ * pointers in kvq_cache and every tensor argument are DEVICE pointers.
+ *
+ * One kvq_cache is one layer. For each (sequence b, kv head h):
+ *   - tokens [0, Q_b) are quantized, in blocks of G tokens (a "record" each);
+ *   - tokens [Q_b, S_b) sit in a full-precision ring buffer of res_capacity
+ *     slots; token t lives in slot t mod res_capacity;
+ *   - after kvq_flush_residual, R <= S_b - Q_b < R + G whenever S_b >= R,
+ *     i.e. Q_b = G * floor(max(S_b - R, 0) / G).
+ *
+ * Record of one block (little-endian, sections in this order, no padding):
+ *   K codes  uint32 [G][d*k_bits/32]   token-major; word w of token t holds
+ *                                       channels w*32/k_bits.. , LSB first
+ *                                       (slot i at bits [i*b, (i+1)*b))
+ *   K scale  fp16   [d]                 per channel over the block's G tokens
+ *   K zero   fp16   [d]
+ *   V codes  uint32 [d][G*v_bits/32]   channel-major; word w of channel c holds
+ *                                       tokens w*32/v_bits.. of the block
+ *   V scale  fp16   [d/G_V][G]          per (channel group, token)
+ *   V zero   fp16   [d/G_V][G]
+ * Dense store: records at [B][H_kv][max_blocks]. Paged store: one page holds
+ * the records of one block for all H_kv heads, records at [num_pages][H_kv],
+ * and block_table[b][j] names the page of block j of sequence b.
+ *
+ * Quantizer (formula F, every step an fp32 IEEE operation rounded to nearest
+ * even, no fused multiply-add), per group x_1..x_n (a key channel over G
+ * tokens, or G_V channels of one value token):
+ *   z = fp16(min x);  s = fp16(fp32(max x - min x) / (2^b - 1));
+ *   s == 0 -> all codes 0;  else inv = fp32(1/s),
+ *   code_i = clamp(round_half_even(fp32(fp32(x_i - z) * inv)), 0, 2^b - 1);
+ *   x_hat = code*s + z.
+ * Input values whose group minimum lies outside the fp16 normal range are
+ * outside the supported domain (results stay deterministic).
+ *
+ * Errors. Argument errors are reported synchronously, before any launch.
+ * Conditions only the device can see (ring full, flush past max_blocks, page
+ * index out of range) skip the affected work and OR a KVQ_DEV_* bit into the
+ * cache's sticky error word (read it with kvq_read_device_error). No call
+ * aborts or throws.
+ */
+#ifndef KVQ_H
+#define KVQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  KVQ_OK = 0,
+  KVQ_ERR_INVALID_ARG = 1,   /* null pointer, non-positive or inconsistent size */
+  KVQ_ERR_UNSUPPORTED = 2,   /* a well-formed configuration with no kernel in this build */
+  KVQ_ERR_WORKSPACE = 3,     /* workspace smaller than kvq_workspace_size() */
+  KVQ_ERR_LAUNCH = 4,        /* the HIP runtime rejected a launch or a copy */
+} kvq_status;
+
+enum { KVQ_F16 = 0, KVQ_BF16 = 1 };
+
+/* Bits of the device-side sticky error word. */
+enum {
+  KVQ_DEV_RESIDUAL_FULL = 1, /* an append would overflow the ring: that sequence's tokens were not taken */
+  KVQ_DEV_BLOCKS_FULL = 2,   /* a flush needed a block index >= max_blocks: it stopped there */
+  KVQ_DEV_BAD_PAGE = 4,      /* a block_table entry was outside [0, num_pages): that block was skipped */
+  KVQ_DEV_BAD_COUNT = 8,     /* an n_new[b] outside [0, n_max]: that sequence took nothing */
+  KVQ_DEV_TOO_LONG = 16,     /* decode met S_b > max_seq_tokens: tokens past the bound were ignored */
+};
+
+typedef struct {
+  int32_t batch;          /* B, sequences in this cache                                   */
+  int32_t num_q_heads;    /* H_q                                                          */
+  int32_t num_kv_heads;   /* H_kv; H_q % H_kv == 0; query head h' reads kv head h'/(H_q/H_kv) */
+  int32_t head_dim;       /* d: 64 or 128                                                  */
+  int32_t k_bits;         /* 2 or 4                                                       */
+  int32_t v_bits;         /* 2 or 4                                                       */
+  int32_t k_group;        /* G: tokens per key group = tokens per block (16, 32 or 64)    */
+  int32_t v_group;        /* G_V: channels per value group (16, 32 or 64; divides d)      */
+  int32_t residual;       /* R >= 0: tokens kept in full precision                         */
+  int32_t res_capacity;   /* ring slots per (sequence, kv head); >= R + G                 */
+  int32_t max_blocks;     /* dense: blocks per (sequence, kv head); paged: block_table width */
+  int32_t num_pages;      /* 0: dense store; > 0: paged store with this many pages         */
+  int32_t dtype;          /* KVQ_F16 or KVQ_BF16: K, V, q and the ring                     */
+} kvq_config;
+
+typedef struct {
+  size_t record;          /* bytes of one block of one kv head                              */
+  size_t blocks;          /* bytes of the block store (dense records or page pool)           */
+  size_t block_table;     /* bytes of the page table (int32 [B][max_blocks]); 0 if dense     */
+  size_t ring;            /* bytes of EACH of k_ring and v_ring: [B][H_kv][res_capacity][d]  */
+  size_t state;           /* bytes of the state words; must be zeroed before first use       */
+} kvq_layout;
+
+typedef struct {
+  void* blocks;                /* block store, 16-byte aligned                                */
+  const int32_t* block_table;  /* paged: [B][max_blocks] page of each block; NULL if dense    */
+  void* k_ring;                /* [B][H_kv][res_capacity][d] of dtype                          */
+  void* v_ring;
+  int32_t* state;              /* [B][4] {Q_b, S_b, internal, internal} then the error word;
+                                  zero-filled by the caller for an empty cache                 */
+} kvq_cache;
+
+/* Host only. Validates cfg and fills the byte sizes of every cache buffer.
+ * Returns KVQ_ERR_INVALID_ARG / KVQ_ERR_UNSUPPORTED for a rejected config. */
+kvq_status kvq_get_layout(const kvq_config* cfg, kvq_layout* out);
+
+/* Host only. Bytes of the decode workspace for sequences of at most
+ * max_seq_tokens tokens (partial softmax states of the sequence splits). */
+kvq_status kvq_workspace_size(const kvq_config* cfg, int32_t max_seq_tokens, size_t* bytes);
+
+/* Append new key/value rows to the full-precision ring ([P4] KIVI: recent
+ * tokens stay in full precision).
+ *   k_new, v_new: [B][H_kv][n_max][d] of dtype (device);
+ *   n_new: device int32 [B], tokens to take from each sequence's first rows
+ *          (0 <= n_new[b] <= n_max), or NULL to take n_max from every sequence.
+ * S_b grows by n_new[b]. A sequence whose ring would overflow
+ * (S_b - Q_b + n_new[b] > res_capacity) takes nothing and sets
+ * KVQ_DEV_RESIDUAL_FULL; call kvq_flush_residual between large chunks. */
+kvq_status kvq_append(const kvq_config* cfg, const kvq_cache* cache,
+                      const void* k_new, const void* v_new,
+                      const int32_t* n_new, int32_t n_max, void* stream);
+
+/* Quantize and pack the oldest complete G-token blocks of every ring so that
+ * R <= S_b - Q_b < R + G afterwards ([P4] KIVI per-channel keys / per-token
+ * values; [P4] innovation 3 dense packing; innovation 4 residual window).
+ * Does nothing for sequences whose ring holds fewer than R + G tokens. */
+kvq_status kvq_flush_residual(const kvq_config* cfg, const kvq_cache* cache, void* stream);
+
+/* One decode step of attention for every (sequence, query head): the quantized
+ * blocks are dequantized on the fly and the ring tokens read as they are;
+ * sequence splits are merged by an online softmax ([P1] Minima-KV).
+ *   q:   [B][H_q][d] of dtype (device), one query token per sequence;
+ *   out: [B][H_q][d] fp32 (device);
+ *   softmax_scale: multiplies q.k; <= 0 selects 1/sqrt(d);
+ *   max_seq_tokens: an upper bound on every S_b (sizes the grid; the exact
+ *                   lengths are read on the device);
+ *   workspace: device scratch of at least kvq_workspace_size(cfg, max_seq_tokens)
+ *              bytes; its contents need no initialisation.
+ * A sequence with S_b == 0 gets a zero output. Calls that share a workspace
+ * must be ordered on one stream. */
+kvq_status kvq_decode_attention(const kvq_config* cfg, const kvq_cache* cache,
+                                const void* q, float* out, float softmax_scale,
+                                int32_t max_seq_tokens, void* workspace,
+                                size_t workspace_bytes, void* stream);
+
+/* Copies the cache's sticky error word (an OR of KVQ_DEV_* bits; 0 = nothing
+ * so far) into *err after the stream's earlier work, waiting for the stream. */
+kvq_status kvq_read_device_error(const kvq_config* cfg, const kvq_cache* cache, void* stream,
+                                 int32_t* err);
+
+/* Static string naming a status code. */
+const char* kvq_status_string(kvq_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVQ_H */

@@ -1,0 +1,147 @@
+// Host side of the C ABI declared in include/kvq.h: argument validation, byte
+// layout arithmetic and kernel launches on the caller's stream. No allocation,
+// no global state.
+//
+// Sources:
+//   [P4] patricehuetz.fr, "Quantification du KV-Cache : TurboQuant et l'état de
+//        l'art en 2026": section "Le problème" gives the dense cache size
+//        2*L*H*d*S*bytes that the packed layout shrinks; innovation 3 fixes the
+//        packing density (16 INT2 / 8 INT4 per 32-bit word) and 16-token blocks
+//        for paged caches.
+#include <cmath>
+#include <cstring>
+
+#include "common.h"
+
+using kvq::Geom;
+
+namespace {
+
+constexpr int kMaxBatch = 4096;
+
+bool pow2_in(int v, int lo, int hi) { return v >= lo && v <= hi && (v & (v - 1)) == 0; }
+
+kvq_status validate(const kvq_config* c) {
+  if (c == nullptr) return KVQ_ERR_INVALID_ARG;
+  if (c->batch <= 0 || c->num_q_heads <= 0 || c->num_kv_heads <= 0 || c->head_dim <= 0 ||
+      c->k_group <= 0 || c->v_group <= 0 || c->residual < 0 || c->res_capacity <= 0 || c->max_blocks < 0 ||
+      c->num_pages < 0)
+    return KVQ_ERR_INVALID_ARG;
+  if (c->num_q_heads % c->num_kv_heads != 0) return KVQ_ERR_INVALID_ARG;
+  if (c->dtype != KVQ_F16 && c->dtype != KVQ_BF16) return KVQ_ERR_INVALID_ARG;
+  if ((c->k_bits != 2 && c->k_bits != 4) || (c->v_bits != 2 && c->v_bits != 4)) return KVQ_ERR_UNSUPPORTED;
+  if (c->head_dim % c->v_group != 0) return KVQ_ERR_INVALID_ARG;
+  if (c->res_capacity < c->residual + c->k_group) return KVQ_ERR_INVALID_ARG;
+  if (c->head_dim != 64 && c->head_dim != 128) return KVQ_ERR_UNSUPPORTED;
+  if (!pow2_in(c->k_group, 16, 64) || !pow2_in(c->v_group, 16, 64)) return KVQ_ERR_UNSUPPORTED;
+  if (c->num_q_heads / c->num_kv_heads > 8) return KVQ_ERR_UNSUPPORTED;
+  if (c->batch > kMaxBatch) return KVQ_ERR_UNSUPPORTED;
+  if ((long long)c->k_group * c->v_bits < 32) return KVQ_ERR_UNSUPPORTED;
+  return KVQ_OK;
+}
+
+kvq_status validate_cache(const kvq_config* c, const kvq_cache* k) {
+  if (k == nullptr || k->blocks == nullptr || k->k_ring == nullptr || k->v_ring == nullptr ||
+      k->state == nullptr)
+    return KVQ_ERR_INVALID_ARG;
+  if ((c->num_pages > 0) != (k->block_table != nullptr)) return KVQ_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(k->blocks) | reinterpret_cast<uintptr_t>(k->k_ring) |
+       reinterpret_cast<uintptr_t>(k->v_ring)) & 15)
+    return KVQ_ERR_INVALID_ARG;
+  return KVQ_OK;
+}
+
+kvq_status launched(hipError_t e) { return e == hipSuccess ? KVQ_OK : KVQ_ERR_LAUNCH; }
+
+}  // namespace
+
+extern "C" {
+
+kvq_status kvq_get_layout(const kvq_config* cfg, kvq_layout* out) {
+  const kvq_status st = validate(cfg);
+  if (st != KVQ_OK) return st;
+  if (out == nullptr) return KVQ_ERR_INVALID_ARG;
+  const Geom g = kvq::make_geom(*cfg);
+  out->record = (size_t)g.rec_bytes;
+  if (cfg->num_pages > 0) {
+    out->blocks = (size_t)cfg->num_pages * g.Hkv * g.rec_bytes;
+    out->block_table = (size_t)g.B * cfg->max_blocks * sizeof(int32_t);
+  } else {
+    out->blocks = (size_t)g.B * g.Hkv * (size_t)cfg->max_blocks * g.rec_bytes;
+    out->block_table = 0;
+  }
+  out->ring = (size_t)g.B * g.Hkv * (size_t)g.C * g.d * 2;
+  out->state = (size_t)kvq::state_words(g.B) * sizeof(int32_t);
+  return KVQ_OK;
+}
+
+kvq_status kvq_workspace_size(const kvq_config* cfg, int32_t max_seq_tokens, size_t* bytes) {
+  const kvq_status st = validate(cfg);
+  if (st != KVQ_OK) return st;
+  if (bytes == nullptr || max_seq_tokens < 0) return KVQ_ERR_INVALID_ARG;
+  *bytes = kvq::plan_decode(kvq::make_geom(*cfg), max_seq_tokens).ws_bytes;
+  return KVQ_OK;
+}
+
+kvq_status kvq_append(const kvq_config* cfg, const kvq_cache* cache, const void* k_new, const void* v_new,
+                      const int32_t* n_new, int32_t n_max, void* stream) {
+  kvq_status st = validate(cfg);
+  if (st != KVQ_OK) return st;
+  if ((st = validate_cache(cfg, cache)) != KVQ_OK) return st;
+  if (k_new == nullptr || v_new == nullptr || n_max < 0) return KVQ_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(k_new) | reinterpret_cast<uintptr_t>(v_new)) & 15) return KVQ_ERR_INVALID_ARG;
+  if (n_max == 0) return KVQ_OK;
+  return launched(kvq::launch_append(kvq::make_geom(*cfg), *cache, k_new, v_new, n_new, n_max,
+                                     static_cast<hipStream_t>(stream)));
+}
+
+kvq_status kvq_flush_residual(const kvq_config* cfg, const kvq_cache* cache, void* stream) {
+  kvq_status st = validate(cfg);
+  if (st != KVQ_OK) return st;
+  if ((st = validate_cache(cfg, cache)) != KVQ_OK) return st;
+  return launched(kvq::launch_flush(kvq::make_geom(*cfg), *cache, static_cast<hipStream_t>(stream)));
+}
+
+kvq_status kvq_decode_attention(const kvq_config* cfg, const kvq_cache* cache, const void* q, float* out,
+                                float softmax_scale, int32_t max_seq_tokens, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  kvq_status st = validate(cfg);
+  if (st != KVQ_OK) return st;
+  if ((st = validate_cache(cfg, cache)) != KVQ_OK) return st;
+  if (q == nullptr || out == nullptr || max_seq_tokens < 0 || !std::isfinite(softmax_scale))
+    return KVQ_ERR_INVALID_ARG;
+  const Geom g = kvq::make_geom(*cfg);
+  const kvq::DecodePlan plan = kvq::plan_decode(g, max_seq_tokens);
+  if (workspace == nullptr || workspace_bytes < plan.ws_bytes) return KVQ_ERR_WORKSPACE;
+  const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt((float)g.d);
+  return launched(kvq::launch_decode(g, *cache, q, out, scale, max_seq_tokens, workspace,
+                                     static_cast<hipStream_t>(stream)));
+}
+
+kvq_status kvq_read_device_error(const kvq_config* cfg, const kvq_cache* cache, void* stream,
+                                 int32_t* err) {
+  const kvq_status st = validate(cfg);
+  if (st != KVQ_OK) return st;
+  if (cache == nullptr || cache->state == nullptr || err == nullptr) return KVQ_ERR_INVALID_ARG;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  int32_t word = 0;
+  if (hipMemcpyAsync(&word, cache->state + 4 * cfg->batch, sizeof(word), hipMemcpyDeviceToHost, s) !=
+          hipSuccess ||
+      hipStreamSynchronize(s) != hipSuccess)
+    return KVQ_ERR_LAUNCH;
+  *err = word;
+  return KVQ_OK;
+}
+
+const char* kvq_status_string(kvq_status s) {
+  switch (s) {
+    case KVQ_OK: return "ok";
+    case KVQ_ERR_INVALID_ARG: return "invalid argument";
+    case KVQ_ERR_UNSUPPORTED: return "unsupported configuration";
+    case KVQ_ERR_WORKSPACE: return "workspace too small";
+    case KVQ_ERR_LAUNCH: return "kernel launch failed";
+  }
+  return "unknown status";
+}
+
+}  // extern "C"

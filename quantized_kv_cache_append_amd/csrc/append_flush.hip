@@ -1,0 +1,240 @@
+// Append into the full-precision ring, and flush = quantize + pack the oldest
+// complete blocks (gfx950).
+//
+// Sources:
+//   [P4] patricehuetz.fr, "Quantification du KV-Cache : TurboQuant et l'état de
+//        l'art en 2026": section "KIVI (2024)" -- keys are quantized per channel
+//        and values per token, each group with its own min/max parameters, and
+//        the most recent tokens stay in full precision; innovation 3 -- 16 INT2
+//        or 8 INT4 codes per 32-bit word; innovation 4 -- a window of the most
+//        recent tokens in full precision next to the low-bit history.
+//   [P2] zubnet.ai survey, quantization family: keep every token, lower the bits.
+//
+// Flush is bandwidth-light (it touches each token once, when it leaves the
+// window) so one workgroup quantizes one G-token block of one kv head: the
+// tile is staged in LDS with 16-byte loads, column (key) and row-group (value)
+// min/max are taken from LDS, codes go to LDS, and the packed words are written
+// with consecutive lanes on consecutive words.
+#include "common.h"
+
+namespace kvq {
+
+namespace {
+
+constexpr int kAppendTokensPerWG = 64;
+constexpr int kFlushThreads = 256;
+constexpr int kMaxG = 64, kMaxD = 128;
+
+__global__ __launch_bounds__(256) void append_kernel(Geom g, const uint16_t* __restrict__ k_new,
+                                                     const uint16_t* __restrict__ v_new,
+                                                     const int32_t* __restrict__ n_new, int n_max,
+                                                     uint16_t* __restrict__ k_ring,
+                                                     uint16_t* __restrict__ v_ring,
+                                                     int32_t* __restrict__ state) {
+  const int pair = blockIdx.x;
+  const int b = pair / g.Hkv;
+  __shared__ int s_S, s_n, s_ok;
+  if (threadIdx.x == 0) {
+    const int Q = state[4 * b + kStateQ];
+    const int S = state[4 * b + kStateS];
+    const int n = n_new ? n_new[b] : n_max;
+    const bool count_ok = n >= 0 && n <= n_max;
+    s_S = S;
+    s_n = n;
+    s_ok = count_ok ? ((S - Q) + n <= g.C ? 1 : 2) : 0;   // 1 ok, 2 ring full, 0 bad count
+  }
+  __syncthreads();
+  if (s_ok == 1) {
+    const int t0 = blockIdx.y * kAppendTokensPerWG;
+    const int nt = min(kAppendTokensPerWG, s_n - t0);
+    const int vec_per_tok = g.d / 8;   // 16-byte vectors per token row
+    for (int idx = threadIdx.x; idx < nt * vec_per_tok; idx += blockDim.x) {
+      const int i = t0 + idx / vec_per_tok;
+      const int v = idx % vec_per_tok;
+      const int slot = (s_S + i) % g.C;
+      const size_t src = ((size_t)pair * n_max + i) * g.d + (size_t)v * 8;
+      const size_t dst = ((size_t)pair * g.C + slot) * g.d + (size_t)v * 8;
+      *reinterpret_cast<uint4*>(k_ring + dst) = *reinterpret_cast<const uint4*>(k_new + src);
+      *reinterpret_cast<uint4*>(v_ring + dst) = *reinterpret_cast<const uint4*>(v_new + src);
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x == 0 && last_arrival(&state[4 * b + kStateAppendCnt], g.Hkv * gridDim.y)) {
+    if (s_ok == 1)
+      state[4 * b + kStateS] = s_S + s_n;
+    else
+      atomicOr(&state[4 * g.B], s_ok == 0 ? KVQ_DEV_BAD_COUNT : KVQ_DEV_RESIDUAL_FULL);
+  }
+}
+
+// Formula F on one group whose min and max are known (fp32 IEEE steps, round to
+// nearest even, no fused multiply-add). Returns the fp16 bits of scale and
+// zero and the reciprocal used for the codes (0 for a constant group).
+struct GroupParams {
+  uint16_t s16, z16;
+  float zf, inv;
+};
+__device__ __forceinline__ GroupParams group_params(float mn, float mx, int bits) {
+  GroupParams p;
+  p.z16 = f32_to_f16_bits(mn);
+  const float qmax = (float)((1 << bits) - 1);
+  const float range = __fsub_rn(mx, mn);
+  p.s16 = f32_to_f16_bits(__fdiv_rn(range, qmax));
+  const float sf = f16_to_f32(p.s16);
+  p.zf = f16_to_f32(p.z16);
+  p.inv = (sf == 0.0f) ? 0.0f : __fdiv_rn(1.0f, sf);
+  return p;
+}
+__device__ __forceinline__ uint32_t group_code(float x, const GroupParams& p, int bits) {
+  if (p.inv == 0.0f) return 0u;
+  const float t = __fmul_rn(__fsub_rn(x, p.zf), p.inv);
+  const float qmax = (float)((1 << bits) - 1);
+  const float r = fminf(fmaxf(rintf(t), 0.0f), qmax);
+  return (uint32_t)r;
+}
+
+template <bool BF16>
+__global__ __launch_bounds__(kFlushThreads) void flush_kernel(Geom g, uint8_t* __restrict__ blocks,
+                                                              const int32_t* __restrict__ table,
+                                                              const uint16_t* __restrict__ k_ring,
+                                                              const uint16_t* __restrict__ v_ring,
+                                                              int32_t* __restrict__ state) {
+  const int pair = blockIdx.x;
+  const int b = pair / g.Hkv, h = pair % g.Hkv;
+  const int k = blockIdx.y;
+  const int tid = threadIdx.x;
+
+  __shared__ uint16_t s_k[kMaxG * kMaxD];      // [G][d] input bits
+  __shared__ uint16_t s_v[kMaxG * kMaxD];
+  __shared__ uint8_t s_kc[kMaxG * kMaxD];      // [G][d] key codes
+  __shared__ uint8_t s_vc[kMaxD * kMaxG];      // [d][G] value codes (channel-major)
+  __shared__ int s_Q, s_nfl, s_nok, s_bad;
+
+  if (tid == 0) {
+    const int Q = state[4 * b + kStateQ];
+    const int S = state[4 * b + kStateS];
+    const int r = S - Q;
+    const int nfl = (r >= g.R + g.G) ? (r - g.R) / g.G : 0;
+    const int room = g.max_blocks - Q / g.G;
+    s_Q = Q;
+    s_nfl = nfl;
+    s_nok = min(nfl, max(room, 0));
+    s_bad = 0;
+  }
+  __syncthreads();
+
+  if (k < s_nok) {
+    const int blk = s_Q / g.G + k;
+    uint8_t* rec = const_cast<uint8_t*>(block_record(g, blocks, table, b, h, blk));
+    if (rec == nullptr) {
+      if (tid == 0) s_bad = 1;
+    } else {
+      const int G = g.G, d = g.d;
+      // stage the G x d tile of keys and values (tokens blk*G .. blk*G+G-1)
+      const int vec_per_tok = d / 8;
+      for (int idx = tid; idx < G * vec_per_tok; idx += kFlushThreads) {
+        const int t = idx / vec_per_tok, v = idx % vec_per_tok;
+        const int slot = (blk * G + t) % g.C;
+        const size_t src = ((size_t)pair * g.C + slot) * d + (size_t)v * 8;
+        *reinterpret_cast<uint4*>(&s_k[t * d + v * 8]) = *reinterpret_cast<const uint4*>(k_ring + src);
+        *reinterpret_cast<uint4*>(&s_v[t * d + v * 8]) = *reinterpret_cast<const uint4*>(v_ring + src);
+      }
+      __syncthreads();
+
+      uint16_t* ks = reinterpret_cast<uint16_t*>(rec + g.rec_ks);
+      uint16_t* kz = reinterpret_cast<uint16_t*>(rec + g.rec_kz);
+      uint16_t* vs = reinterpret_cast<uint16_t*>(rec + g.rec_vs);
+      uint16_t* vz = reinterpret_cast<uint16_t*>(rec + g.rec_vz);
+
+      // keys: one group per channel over the G tokens
+      for (int c = tid; c < d; c += kFlushThreads) {
+        float mn = in_to_f32<BF16>(s_k[c]), mx = mn;
+        for (int t = 1; t < G; ++t) {
+          const float x = in_to_f32<BF16>(s_k[t * d + c]);
+          mn = fminf(mn, x);
+          mx = fmaxf(mx, x);
+        }
+        const GroupParams p = group_params(mn, mx, g.kb);
+        ks[c] = p.s16;
+        kz[c] = p.z16;
+        for (int t = 0; t < G; ++t)
+          s_kc[t * d + c] = (uint8_t)group_code(in_to_f32<BF16>(s_k[t * d + c]), p, g.kb);
+      }
+      // values: one group per (token, G_V consecutive channels)
+      const int ngr = d / g.GV;
+      for (int idx = tid; idx < G * ngr; idx += kFlushThreads) {
+        const int t = idx / ngr, j = idx % ngr;
+        const uint16_t* row = &s_v[t * d + j * g.GV];
+        float mn = in_to_f32<BF16>(row[0]), mx = mn;
+        for (int c = 1; c < g.GV; ++c) {
+          const float x = in_to_f32<BF16>(row[c]);
+          mn = fminf(mn, x);
+          mx = fmaxf(mx, x);
+        }
+        const GroupParams p = group_params(mn, mx, g.vb);
+        vs[j * G + t] = p.s16;
+        vz[j * G + t] = p.z16;
+        for (int c = 0; c < g.GV; ++c)
+          s_vc[(j * g.GV + c) * G + t] = (uint8_t)group_code(in_to_f32<BF16>(row[c]), p, g.vb);
+      }
+      __syncthreads();
+
+      // pack keys: word w of token t holds channels w*P .. w*P+P-1, LSB first
+      uint32_t* kc = reinterpret_cast<uint32_t*>(rec + g.rec_kc);
+      const int kP = 32 / g.kb;
+      for (int idx = tid; idx < G * g.k_words; idx += kFlushThreads) {
+        const int t = idx / g.k_words, w = idx % g.k_words;
+        const uint8_t* src = &s_kc[t * d + w * kP];
+        uint32_t word = 0;
+        for (int i = 0; i < kP; ++i) word |= (uint32_t)src[i] << (i * g.kb);
+        kc[idx] = word;
+      }
+      // pack values: word w of channel c holds tokens w*P .. w*P+P-1, LSB first
+      uint32_t* vc = reinterpret_cast<uint32_t*>(rec + g.rec_vc);
+      const int vP = 32 / g.vb;
+      for (int idx = tid; idx < d * g.v_words; idx += kFlushThreads) {
+        const int c = idx / g.v_words, w = idx % g.v_words;
+        const uint8_t* src = &s_vc[c * G + w * vP];
+        uint32_t word = 0;
+        for (int i = 0; i < vP; ++i) word |= (uint32_t)src[i] << (i * g.vb);
+        vc[idx] = word;
+      }
+    }
+  }
+  __syncthreads();
+  if (tid == 0) {
+    if (s_bad) atomicOr(&state[4 * g.B], KVQ_DEV_BAD_PAGE);
+    if (last_arrival(&state[4 * b + kStateFlushCnt], g.Hkv * gridDim.y)) {
+      state[4 * b + kStateQ] = s_Q + s_nok * g.G;
+      if (s_nok < s_nfl) atomicOr(&state[4 * g.B], KVQ_DEV_BLOCKS_FULL);
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_append(const Geom& g, const kvq_cache& c, const void* k_new, const void* v_new,
+                         const int32_t* n_new, int n_max, hipStream_t s) {
+  const int chunks = (n_max + kAppendTokensPerWG - 1) / kAppendTokensPerWG;
+  dim3 grid(g.B * g.Hkv, chunks > 0 ? chunks : 1);
+  hipLaunchKernelGGL(append_kernel, grid, dim3(256), 0, s, g,
+                     static_cast<const uint16_t*>(k_new), static_cast<const uint16_t*>(v_new), n_new,
+                     n_max, static_cast<uint16_t*>(c.k_ring), static_cast<uint16_t*>(c.v_ring), c.state);
+  return hipGetLastError();
+}
+
+hipError_t launch_flush(const Geom& g, const kvq_cache& c, hipStream_t s) {
+  const int max_fl = (g.C - g.R) / g.G;   // r <= C bounds the blocks one flush can take
+  dim3 grid(g.B * g.Hkv, max_fl);
+  if (g.dtype == KVQ_BF16)
+    hipLaunchKernelGGL(flush_kernel<true>, grid, dim3(kFlushThreads), 0, s, g,
+                       static_cast<uint8_t*>(c.blocks), c.block_table,
+                       static_cast<const uint16_t*>(c.k_ring), static_cast<const uint16_t*>(c.v_ring), c.state);
+  else
+    hipLaunchKernelGGL(flush_kernel<false>, grid, dim3(kFlushThreads), 0, s, g,
+                       static_cast<uint8_t*>(c.blocks), c.block_table,
+                       static_cast<const uint16_t*>(c.k_ring), static_cast<const uint16_t*>(c.v_ring), c.state);
+  return hipGetLastError();
+}
+
+}  // namespace kvq

@@ -1,0 +1,132 @@
+// Shared device/host definitions of libkvq (gfx950).
+//
+// Sources:
+//   [P4] patricehuetz.fr, "Quantification du KV-Cache : TurboQuant et l'état de
+//        l'art en 2026" -- section "KIVI (2024)" (per-channel keys, per-token
+//        values, own min/max parameters, full-precision recent tokens),
+//        innovation 3 (dense INT2/INT4 packing into 32-bit words, 16-token
+//        blocks for paged attention), innovation 4 (residual window).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kvq.h"
+
+namespace kvq {
+
+// Everything a kernel needs to know about one cache layer. Plain data, passed
+// by value as a kernel argument.
+struct Geom {
+  int B, Hq, Hkv, d, ng;
+  int kb, vb, G, GV, R, C;
+  int max_blocks, num_pages, dtype;
+  // record section offsets (bytes) and sizes
+  int rec_kc, rec_ks, rec_kz, rec_vc, rec_vs, rec_vz, rec_bytes;
+  int k_words;   // uint32 words of K codes per token: d*kb/32
+  int v_words;   // uint32 words of V codes per channel: G*vb/32
+};
+
+// Fill the derived fields of a Geom from a validated config.
+inline Geom make_geom(const kvq_config& c) {
+  Geom g{};
+  g.B = c.batch; g.Hq = c.num_q_heads; g.Hkv = c.num_kv_heads; g.d = c.head_dim;
+  g.ng = c.num_q_heads / c.num_kv_heads;
+  g.kb = c.k_bits; g.vb = c.v_bits; g.G = c.k_group; g.GV = c.v_group;
+  g.R = c.residual; g.C = c.res_capacity;
+  g.max_blocks = c.max_blocks; g.num_pages = c.num_pages; g.dtype = c.dtype;
+  g.k_words = g.d * g.kb / 32;
+  g.v_words = g.G * g.vb / 32;
+  g.rec_kc = 0;
+  g.rec_ks = g.G * g.k_words * 4;
+  g.rec_kz = g.rec_ks + 2 * g.d;
+  g.rec_vc = g.rec_kz + 2 * g.d;
+  g.rec_vs = g.rec_vc + g.d * g.v_words * 4;
+  g.rec_vz = g.rec_vs + 2 * (g.d / g.GV) * g.G;
+  g.rec_bytes = g.rec_vz + 2 * (g.d / g.GV) * g.G;
+  return g;
+}
+
+// State words per sequence: {Q_b, S_b, flush arrivals, append arrivals};
+// the sticky error word follows the B entries.
+constexpr int kStateQ = 0, kStateS = 1, kStateFlushCnt = 2, kStateAppendCnt = 3;
+__host__ __device__ inline int state_words(int B) { return 4 * B + 4; }
+
+#ifdef __HIPCC__
+// ---- conversions --------------------------------------------------------------
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
+  return __uint_as_float(bits16 << 16);
+}
+__device__ __forceinline__ float f16_to_f32(uint32_t bits16) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)bits16);
+}
+template <bool BF16>
+__device__ __forceinline__ float in_to_f32(uint32_t bits16) {
+  return BF16 ? bf16_to_f32(bits16) : f16_to_f32(bits16);
+}
+// fp32 -> fp16 bits, round to nearest even.
+__device__ __forceinline__ uint16_t f32_to_f16_bits(float x) {
+  return __builtin_bit_cast(uint16_t, (_Float16)x);
+}
+
+// ---- addressing ---------------------------------------------------------------
+// Record of block `blk` of (sequence b, kv head h); nullptr for a page index
+// outside the pool.
+__device__ __forceinline__ const uint8_t* block_record(const Geom& g, const uint8_t* blocks,
+                                                       const int32_t* table, int b, int h, int blk) {
+  if (table == nullptr)
+    return blocks + (((size_t)b * g.Hkv + h) * g.max_blocks + blk) * (size_t)g.rec_bytes;
+  const int page = table[(size_t)b * g.max_blocks + blk];
+  if (page < 0 || page >= g.num_pages) return nullptr;
+  return blocks + ((size_t)page * g.Hkv + h) * (size_t)g.rec_bytes;
+}
+
+// ---- wave helpers (wave64) ----------------------------------------------------
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+// Orders this wave's LDS writes before its later LDS reads of other lanes' data.
+__device__ __forceinline__ void wave_lds_fence() {
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+  __builtin_amdgcn_wave_barrier();
+}
+
+// One thread per workgroup calls this after the workgroup's work is done.
+// Returns true for exactly one caller among `total` arrivals on `counter`,
+// after every other arrival; that caller also re-arms the counter to 0.
+__device__ __forceinline__ bool last_arrival(int* counter, int total) {
+  __threadfence();
+  const int old = atomicAdd(counter, 1);
+  if (old == total - 1) {
+    atomicExch(counter, 0);
+    __threadfence();
+    return true;
+  }
+  return false;
+}
+#endif
+
+// Launch wrappers (defined in the .hip files). Return hipSuccess or the error.
+hipError_t launch_append(const Geom& g, const kvq_cache& c, const void* k_new, const void* v_new,
+                         const int32_t* n_new, int n_max, hipStream_t s);
+hipError_t launch_flush(const Geom& g, const kvq_cache& c, hipStream_t s);
+hipError_t launch_decode(const Geom& g, const kvq_cache& c, const void* q, float* out, float scale,
+                         int max_seq_tokens, void* ws, hipStream_t s);
+
+// Decode work decomposition shared by the workspace sizing and the kernels.
+struct DecodePlan {
+  int bps;            // quantized blocks per split
+  int nq_max;         // upper bound on quantized splits per (sequence, kv head)
+  size_t items_max;   // upper bound on work items (splits incl. the ring split)
+  size_t ws_bytes;    // workspace bytes
+};
+DecodePlan plan_decode(const Geom& g, int max_seq_tokens);
+
+}  // namespace kvq

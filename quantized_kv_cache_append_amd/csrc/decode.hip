@@ -1,0 +1,323 @@
+// Split-sequence decode attention over the packed cache, and the combine of the
+// split partial states (gfx950).
+//
+// Sources:
+//   [P4] patricehuetz.fr, "Quantification du KV-Cache : TurboQuant et l'état de
+//        l'art en 2026": section "KIVI (2024)" (dequantization with per-channel
+//        key and per-token value parameters), innovation 3 (codes unpacked from
+//        32-bit words in registers), innovation 4 (the full-precision window is
+//        read by the same attention pass as the low-bit history).
+//   [P3] encorp.ai, "La compression du cache KV est une décision
+//        d'infrastructure ...": every decoded token streams the cache from HBM,
+//        so the kernel is organised around that stream.
+//   [P1] ai-automate.fr, "KV-cache compressé et modèles 4-bit ...", Minima-KV:
+//        partial attention states combined by a globally normalised online
+//        softmax -- the split/combine used here.
+//
+// Work decomposition. For each (sequence b, kv head h) the quantized blocks are
+// cut into splits of `bps` blocks, plus one split for the ring tokens. A work
+// item is one split; each wavefront of a persistent grid walks the item list
+// with a grid stride. The per-sequence item counts come from the device-side
+// lengths, so ragged batches need no host synchronisation. Each item leaves a
+// partial state (running max m, sum l, unnormalised o[d]) per query head of
+// the group; the combine kernel merges them.
+//
+// This file holds the generic VALU path (any head_dim 64/128, any group size,
+// n_g <= 8): scores lane-per-token with the key scale folded into the query
+// (q~ = q * s_K) and the zero-point term added once per block, values
+// lane-per-channel.
+#include "common.h"
+
+namespace kvq {
+
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kNgMax = 8;
+
+__device__ __forceinline__ int items_of(int Q, int G, int bps, int nq_max, bool* too_long) {
+  const int nblk = Q / G;
+  int nq = (nblk + bps - 1) / bps;
+  if (nq > nq_max) {
+    nq = nq_max;
+    *too_long = true;
+  }
+  return nq + 1;
+}
+
+template <int D, bool BF16>
+__global__ __launch_bounds__(256) void decode_generic_kernel(
+    Geom g, const uint8_t* __restrict__ blocks, const int32_t* __restrict__ table,
+    const uint16_t* __restrict__ k_ring, const uint16_t* __restrict__ v_ring, int32_t* __restrict__ state,
+    const uint16_t* __restrict__ q, float scale, int bps, int nq_max, float* __restrict__ ws) {
+  constexpr int CPL = D / 64;   // channels per lane
+  extern __shared__ int smem[];
+  int* prefix = smem;   // [B + 1] exclusive prefix of items per sequence
+  float* scratch = reinterpret_cast<float*>(smem + ((g.B + 4) & ~3));
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  float* qt = scratch + wave * (kNgMax * D + kNgMax * 64);   // [8][D]
+  float* pb = qt + kNgMax * D;                               // [8][64]
+
+  bool too_long = false;
+  for (int b = threadIdx.x; b < g.B; b += blockDim.x)
+    prefix[b + 1] = items_of(state[4 * b + kStateQ], g.G, bps, nq_max, &too_long);
+  if (too_long && blockIdx.x == 0) atomicOr(&state[4 * g.B], KVQ_DEV_TOO_LONG);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    prefix[0] = 0;
+    for (int b = 0; b < g.B; ++b) prefix[b + 1] += prefix[b];
+  }
+  __syncthreads();
+
+  const int W = g.Hkv * prefix[g.B];
+  const int ng = g.ng;
+  for (int w = blockIdx.x * kWaves + wave; w < W; w += gridDim.x * kWaves) {
+    int lo = 0, hi = g.B - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (g.Hkv * prefix[mid] <= w) lo = mid; else hi = mid - 1;
+    }
+    const int b = lo;
+    const int cb = prefix[b + 1] - prefix[b];
+    const int rem = w - g.Hkv * prefix[b];
+    const int h = rem / cb, item = rem % cb;
+    const int pair = b * g.Hkv + h;
+    const int Q = state[4 * b + kStateQ];
+    const int S = state[4 * b + kStateS];
+
+    float qv[kNgMax][CPL], o[kNgMax][CPL], m[kNgMax], l[kNgMax];
+#pragma unroll
+    for (int j = 0; j < kNgMax; ++j) {
+      m[j] = -INFINITY;
+      l[j] = 0.f;
+#pragma unroll
+      for (int k = 0; k < CPL; ++k) {
+        o[j][k] = 0.f;
+        qv[j][k] = (j < ng) ? in_to_f32<BF16>(q[((size_t)b * g.Hq + h * ng + j) * D + lane + 64 * k]) : 0.f;
+      }
+    }
+
+    // online softmax update for one tile of up to 64 tokens (lane = token)
+    auto softmax_tile = [&](float (&sc)[kNgMax], bool valid) {
+#pragma unroll
+      for (int j = 0; j < kNgMax; ++j) {
+        if (j >= ng) break;
+        const float s = valid ? sc[j] : -INFINITY;
+        const float bm = wave_max(s);
+        const float mn = fmaxf(m[j], bm);
+        const float alpha = (m[j] == -INFINITY) ? 0.f : __expf(m[j] - mn);
+        const float p = valid ? __expf(s - mn) : 0.f;
+        l[j] = l[j] * alpha + wave_sum(p);
+        m[j] = mn;
+#pragma unroll
+        for (int k = 0; k < CPL; ++k) o[j][k] *= alpha;
+        pb[j * 64 + lane] = p;
+      }
+      wave_lds_fence();
+    };
+
+    if (item < cb - 1) {
+      // ---- quantized blocks [item*bps, ...) ----
+      const int nblk = Q / g.G;
+      const int blk0 = item * bps, blk1 = min(blk0 + bps, nblk);
+      const int kP = 32 / g.kb, vP = 32 / g.vb;
+      const uint32_t kmask = (1u << g.kb) - 1, vmask = (1u << g.vb) - 1;
+      for (int blk = blk0; blk < blk1; ++blk) {
+        const uint8_t* rec = block_record(g, blocks, table, b, h, blk);
+        if (rec == nullptr) continue;
+        const uint16_t* ks = reinterpret_cast<const uint16_t*>(rec + g.rec_ks);
+        const uint16_t* kz = reinterpret_cast<const uint16_t*>(rec + g.rec_kz);
+        float kap[kNgMax];
+#pragma unroll
+        for (int j = 0; j < kNgMax; ++j) kap[j] = 0.f;
+#pragma unroll
+        for (int k = 0; k < CPL; ++k) {
+          const int c = lane + 64 * k;
+          const float s = f16_to_f32(ks[c]), z = f16_to_f32(kz[c]);
+#pragma unroll
+          for (int j = 0; j < kNgMax; ++j) {
+            if (j >= ng) break;
+            qt[j * D + c] = qv[j][k] * s;
+            kap[j] += qv[j][k] * z;
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < kNgMax; ++j)
+          if (j < ng) kap[j] = wave_sum(kap[j]);
+        wave_lds_fence();
+
+        // scores, lane = token of the block
+        const bool valid = lane < g.G;
+        float sc[kNgMax];
+#pragma unroll
+        for (int j = 0; j < kNgMax; ++j) sc[j] = 0.f;
+        if (valid) {
+          const uint32_t* kw = reinterpret_cast<const uint32_t*>(rec + g.rec_kc) + (size_t)lane * g.k_words;
+          for (int wd = 0; wd < g.k_words; ++wd) {
+            const uint32_t word = kw[wd];
+            for (int sl = 0; sl < kP; ++sl) {
+              const float code = (float)((word >> (sl * g.kb)) & kmask);
+              const int c = wd * kP + sl;
+#pragma unroll
+              for (int j = 0; j < kNgMax; ++j)
+                if (j < ng) sc[j] += qt[j * D + c] * code;
+            }
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < kNgMax; ++j) sc[j] = scale * (sc[j] + kap[j]);
+        softmax_tile(sc, valid);
+
+        // values, lane = channel
+        const uint16_t* vs = reinterpret_cast<const uint16_t*>(rec + g.rec_vs);
+        const uint16_t* vz = reinterpret_cast<const uint16_t*>(rec + g.rec_vz);
+#pragma unroll
+        for (int k = 0; k < CPL; ++k) {
+          const int c = lane + 64 * k;
+          const int gr = c / g.GV;
+          const uint32_t* vw = reinterpret_cast<const uint32_t*>(rec + g.rec_vc) + (size_t)c * g.v_words;
+          for (int t = 0; t < g.G; ++t) {
+            const uint32_t word = vw[t / vP];
+            const float code = (float)((word >> ((t % vP) * g.vb)) & vmask);
+            const float val = f16_to_f32(vs[gr * g.G + t]) * code + f16_to_f32(vz[gr * g.G + t]);
+#pragma unroll
+            for (int j = 0; j < kNgMax; ++j)
+              if (j < ng) o[j][k] += pb[j * 64 + t] * val;
+          }
+        }
+        wave_lds_fence();
+      }
+    } else {
+      // ---- full-precision ring tokens [Q, S) ----
+#pragma unroll
+      for (int k = 0; k < CPL; ++k)
+#pragma unroll
+        for (int j = 0; j < kNgMax; ++j)
+          if (j < ng) qt[j * D + lane + 64 * k] = qv[j][k];
+      wave_lds_fence();
+      for (int t0 = Q; t0 < S; t0 += 64) {
+        const int t = t0 + lane;
+        const bool valid = t < S;
+        float sc[kNgMax];
+#pragma unroll
+        for (int j = 0; j < kNgMax; ++j) sc[j] = 0.f;
+        if (valid) {
+          const uint16_t* kr = k_ring + ((size_t)pair * g.C + (t % g.C)) * D;
+          for (int c = 0; c < D; ++c) {
+            const float x = in_to_f32<BF16>(kr[c]);
+#pragma unroll
+            for (int j = 0; j < kNgMax; ++j)
+              if (j < ng) sc[j] += qt[j * D + c] * x;
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < kNgMax; ++j) sc[j] *= scale;
+        softmax_tile(sc, valid);
+        const int nt = min(64, S - t0);
+#pragma unroll
+        for (int k = 0; k < CPL; ++k) {
+          const int c = lane + 64 * k;
+          for (int tt = 0; tt < nt; ++tt) {
+            const float x = in_to_f32<BF16>(v_ring[((size_t)pair * g.C + ((t0 + tt) % g.C)) * D + c]);
+#pragma unroll
+            for (int j = 0; j < kNgMax; ++j)
+              if (j < ng) o[j][k] += pb[j * 64 + tt] * x;
+          }
+        }
+        wave_lds_fence();
+      }
+    }
+
+    // partial state of this item, per query head of the group
+#pragma unroll
+    for (int j = 0; j < kNgMax; ++j) {
+      if (j >= ng) break;
+      float* dst = ws + ((size_t)w * ng + j) * (D + 2);
+#pragma unroll
+      for (int k = 0; k < CPL; ++k) dst[lane + 64 * k] = o[j][k];
+      if (lane == 0) {
+        dst[D] = m[j];
+        dst[D + 1] = l[j];
+      }
+    }
+  }
+}
+
+// Merge the partial states of one (sequence, query head): with M = max m_i,
+// o = sum_i e^(m_i - M) o_i / sum_i e^(m_i - M) l_i.
+template <int D>
+__global__ __launch_bounds__(64) void combine_kernel(Geom g, const int32_t* __restrict__ state, int bps,
+                                                     int nq_max, const float* __restrict__ ws,
+                                                     float* __restrict__ out) {
+  constexpr int CPL = D / 64;
+  const int bh = blockIdx.x;
+  const int b = bh / g.Hq, hq = bh % g.Hq;
+  const int h = hq / g.ng, j = hq % g.ng;
+  const int lane = threadIdx.x;
+  bool dummy = false;
+  int part = 0;
+  for (int bb = lane; bb < b; bb += 64) part += items_of(state[4 * bb + kStateQ], g.G, bps, nq_max, &dummy);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) part += __shfl_xor(part, off, 64);
+  const int cb = items_of(state[4 * b + kStateQ], g.G, bps, nq_max, &dummy);
+  const size_t base = (size_t)g.Hkv * part + (size_t)h * cb;
+
+  float M = -INFINITY;
+  for (int i = 0; i < cb; ++i) M = fmaxf(M, ws[((base + i) * g.ng + j) * (D + 2) + D]);
+  float L = 0.f, acc[CPL];
+#pragma unroll
+  for (int k = 0; k < CPL; ++k) acc[k] = 0.f;
+  if (M != -INFINITY) {
+    for (int i = 0; i < cb; ++i) {
+      const float* src = ws + ((base + i) * g.ng + j) * (D + 2);
+      const float e = __expf(src[D] - M);
+      L += e * src[D + 1];
+#pragma unroll
+      for (int k = 0; k < CPL; ++k) acc[k] += e * src[lane + 64 * k];
+    }
+  }
+  const float inv = (L > 0.f) ? 1.f / L : 0.f;
+#pragma unroll
+  for (int k = 0; k < CPL; ++k) out[((size_t)b * g.Hq + hq) * D + lane + 64 * k] = acc[k] * inv;
+}
+
+template <int D, bool BF16>
+hipError_t launch_generic(const Geom& g, const kvq_cache& c, const void* q, float* out, float scale,
+                          const DecodePlan& plan, void* ws, hipStream_t s) {
+  const int wgs = (int)std::min<size_t>((plan.items_max + kWaves - 1) / kWaves, 2048);
+  const size_t lds = (size_t)((g.B + 4) & ~3) * 4 + (size_t)kWaves * (kNgMax * D + kNgMax * 64) * 4;
+  hipLaunchKernelGGL((decode_generic_kernel<D, BF16>), dim3(wgs), dim3(256), lds, s, g,
+                     static_cast<const uint8_t*>(c.blocks), c.block_table,
+                     static_cast<const uint16_t*>(c.k_ring), static_cast<const uint16_t*>(c.v_ring), c.state,
+                     static_cast<const uint16_t*>(q), scale, plan.bps, plan.nq_max, static_cast<float*>(ws));
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((combine_kernel<D>), dim3(g.B * g.Hq), dim3(64), 0, s, g, c.state, plan.bps, plan.nq_max,
+                     static_cast<const float*>(ws), out);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+DecodePlan plan_decode(const Geom& g, int max_seq_tokens) {
+  DecodePlan p{};
+  p.bps = 8;
+  const int maxblk = std::max(max_seq_tokens - g.R, 0) / g.G;
+  p.nq_max = (maxblk + p.bps - 1) / p.bps;
+  p.items_max = (size_t)g.B * g.Hkv * (size_t)(p.nq_max + 1);
+  p.ws_bytes = p.items_max * (size_t)g.ng * (size_t)(g.d + 2) * 4;
+  return p;
+}
+
+hipError_t launch_decode(const Geom& g, const kvq_cache& c, const void* q, float* out, float scale,
+                         int max_seq_tokens, void* ws, hipStream_t s) {
+  const DecodePlan plan = plan_decode(g, max_seq_tokens);
+  const bool bf16 = g.dtype == KVQ_BF16;
+  if (g.d == 128)
+    return bf16 ? launch_generic<128, true>(g, c, q, out, scale, plan, ws, s)
+                : launch_generic<128, false>(g, c, q, out, scale, plan, ws, s);
+  return bf16 ? launch_generic<64, true>(g, c, q, out, scale, plan, ws, s)
+              : launch_generic<64, false>(g, c, q, out, scale, plan, ws, s);
+}
+
+}  // namespace kvq

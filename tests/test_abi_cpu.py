@@ -1,0 +1,125 @@
+"""Host-side checks of the C ABI (no kernel launches): the library loads, exports
+every function include/kvq.h declares, sizes buffers as the layout says and
+rejects bad arguments before touching the device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from oracle import kivi
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _cfg(B, **kw):
+    base = dict(batch=8, num_q_heads=32, num_kv_heads=32, head_dim=128, k_bits=2, v_bits=2, k_group=32,
+                v_group=32, residual=128, res_capacity=160, max_blocks=128, num_pages=0, dtype=0)
+    base.update(kw)
+    return B.kvq_config(**base)
+
+
+def test_library_exports_every_declared_function(kvq_lib):
+    header = open(os.path.join(ROOT, "include", "kvq.h")).read()
+    declared = set(re.findall(r"^(?:kvq_status|const char\*)\s+(kvq_\w+)\(", header, re.M))
+    assert declared, "no declarations parsed"
+    from quantized_kv_cache_append_amd import binding as B
+    assert declared == set(B.EXPORTED)
+    for name in declared:
+        assert hasattr(kvq_lib, name), name
+
+
+@pytest.mark.parametrize("kb,vb,G,GV,d,per_tok", [(2, 2, 32, 32, 128, 96), (4, 4, 32, 32, 128, 160),
+                                                   (2, 2, 64, 64, 128, 80), (4, 2, 16, 32, 128, 144),
+                                                   (2, 2, 32, 32, 64, 48)])
+def test_layout_matches_oracle_record(kvq_lib, kb, vb, G, GV, d, per_tok):
+    from quantized_kv_cache_append_amd import binding as B
+    cfg = _cfg(B, k_bits=kb, v_bits=vb, k_group=G, v_group=GV, head_dim=d, res_capacity=128 + G)
+    lay = B.kvq_get_layout(cfg)
+    spec = kivi.CacheSpec(8, 32, 32, d, kb, vb, G, GV, 128, 128 + G, "f16")
+    assert lay.record == kivi.record_bytes(spec) == per_tok * G
+    assert lay.blocks == 8 * 32 * 128 * lay.record
+    assert lay.ring == 8 * 32 * (128 + G) * d * 2
+    assert lay.block_table == 0
+    assert lay.state == (4 * 8 + 4) * 4
+
+
+def test_paged_layout(kvq_lib):
+    from quantized_kv_cache_append_amd import binding as B
+    cfg = _cfg(B, batch=64, num_q_heads=48, num_kv_heads=8, k_bits=4, v_bits=2, k_group=16, v_group=32,
+               residual=64, res_capacity=80, max_blocks=4096, num_pages=60000, dtype=1)
+    lay = B.kvq_get_layout(cfg)
+    assert lay.record == 2304
+    assert lay.blocks == 60000 * 8 * 2304
+    assert lay.block_table == 64 * 4096 * 4
+
+
+def test_quantized_bytes_shrink_the_closed_form(kvq_lib):
+    # 70B-shaped layer at INT2, G=G_V=64: 80 B per token per kv head against 512 B in bf16
+    from quantized_kv_cache_append_amd import binding as B
+    cfg = _cfg(B, batch=4, num_q_heads=64, num_kv_heads=8, k_group=64, v_group=64, res_capacity=192,
+               max_blocks=2048, dtype=1)
+    lay = B.kvq_get_layout(cfg)
+    dense = kivi.kv_cache_bytes(1, 8, 128, 2048 * 64, 2) * 4
+    assert dense / lay.blocks == pytest.approx(512 / 80)
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("num_kv_heads", 5, 1), ("k_bits", 3, 2), ("v_bits", 8, 2), ("head_dim", 96, 2), ("head_dim", 100, 1), ("head_dim", 256, 2),
+    ("res_capacity", 159, 1), ("k_group", 24, 2), ("k_group", 128, 2), ("v_group", 24, 1), ("num_q_heads", 48, 1),
+    ("dtype", 7, 1), ("batch", 0, 1), ("residual", -1, 1),
+])
+def test_invalid_configs_are_rejected(kvq_lib, field, value, status):
+    from quantized_kv_cache_append_amd import binding as B
+    cfg = _cfg(B, **{field: value})
+    if field == "k_group":
+        cfg.res_capacity = 128 + value
+    lay = B.kvq_layout()
+    assert kvq_lib.kvq_get_layout(ctypes.byref(cfg), ctypes.byref(lay)) == status
+
+
+def test_group_query_ratio_above_eight_is_unsupported(kvq_lib):
+    from quantized_kv_cache_append_amd import binding as B
+    cfg = _cfg(B, num_q_heads=64, num_kv_heads=4)
+    lay = B.kvq_layout()
+    assert kvq_lib.kvq_get_layout(ctypes.byref(cfg), ctypes.byref(lay)) == B.KVQ_ERR_UNSUPPORTED
+
+
+def test_calls_reject_null_and_misaligned_pointers(kvq_lib):
+    from quantized_kv_cache_append_amd import binding as B
+    cfg = _cfg(B)
+    empty = B.kvq_cache()
+    assert kvq_lib.kvq_append(ctypes.byref(cfg), ctypes.byref(empty), None, None, None, 1, None) == 1
+    assert kvq_lib.kvq_flush_residual(ctypes.byref(cfg), None, None) == 1
+    fake = B.kvq_cache(blocks=0x1000, block_table=None, k_ring=0x2008, v_ring=0x3000, state=0x4000)
+    assert kvq_lib.kvq_flush_residual(ctypes.byref(cfg), ctypes.byref(fake), None) == 1
+    ok = B.kvq_cache(blocks=0x1000, block_table=None, k_ring=0x2000, v_ring=0x3000, state=0x4000)
+    # paged config without a table is inconsistent
+    paged = _cfg(B, num_pages=10)
+    assert kvq_lib.kvq_flush_residual(ctypes.byref(paged), ctypes.byref(ok), None) == 1
+    # decode: too small a workspace is reported before any launch
+    need = B.kvq_workspace_size(cfg, 4096)
+    assert need > 0
+    assert kvq_lib.kvq_decode_attention(ctypes.byref(cfg), ctypes.byref(ok), ctypes.c_void_p(0x5000),
+                                        ctypes.c_void_p(0x6000), ctypes.c_float(0.0), 4096,
+                                        ctypes.c_void_p(0x7000), need - 1, None) == B.KVQ_ERR_WORKSPACE
+    assert kvq_lib.kvq_decode_attention(ctypes.byref(cfg), ctypes.byref(ok), None, ctypes.c_void_p(0x6000),
+                                        ctypes.c_float(0.0), 4096, ctypes.c_void_p(0x7000), need, None) == 1
+    assert kvq_lib.kvq_decode_attention(ctypes.byref(cfg), ctypes.byref(ok), ctypes.c_void_p(0x5000),
+                                        ctypes.c_void_p(0x6000), ctypes.c_float(float("nan")), 4096,
+                                        ctypes.c_void_p(0x7000), need, None) == 1
+
+
+def test_workspace_grows_with_sequence_bound(kvq_lib):
+    from quantized_kv_cache_append_amd import binding as B
+    cfg = _cfg(B)
+    a, b = B.kvq_workspace_size(cfg, 1000), B.kvq_workspace_size(cfg, 100000)
+    assert 0 < a < b
+    assert B.kvq_workspace_size(cfg, 0) > 0   # the ring split always exists
+
+
+def test_status_strings(kvq_lib):
+    from quantized_kv_cache_append_amd import binding as B
+    assert B.status_string(0) == "ok"
+    assert "workspace" in B.status_string(3)
+    assert B.status_string(99) == "unknown status"
