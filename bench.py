@@ -124,7 +124,7 @@ def main():
     log(f"[bench] workload {w.name}: {w.description}")
 
     inp = W.make_layer(w, device=dev, lengths=lengths0)
-    chunk = 2048
+    chunk = 512
     probe = cache_for_workload(w, lengths0, chunk, extra_tokens=0, device=dev)
     rec = probe.record_bytes
     per_copy = probe.blocks.numel() + 2 * probe.k_ring.numel() * 2
@@ -156,8 +156,7 @@ def main():
         ci = i % copies
         c = caches[ci]
         kn, vn, q = toks[i % pool]
-        c.append(kn, vn)
-        c.flush()
+        c.append_flush(kn, vn)
         lens[ci] = [s + 1 for s in lens[ci]]
         if ev is not None:
             ev[0].record()

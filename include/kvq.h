@@ -40,8 +40,12 @@
  *                                       (slot i at bits [i*b, (i+1)*b))
  *   K scale  fp16   [d]                 per channel over the block's G tokens
  *   K zero   fp16   [d]
- *   V codes  uint32 [d][G*v_bits/32]   channel-major; word w of channel c holds
- *                                       tokens w*32/v_bits.. of the block
+ *   V codes  G*d*v_bits/8 bytes in 8-token chunks: the code of (token t,
+ *            channel c) is entry pos(t,c) of an LSB-first stream of v_bits-wide
+ *            codes packed into little-endian uint32 words, with
+ *              pos(t,c) = ((t/8 * 16 + c%16) * (d/16) + c/16) * 8 + t%8
+ *            (for each run of 8 tokens, for each c%16, for each c/16: that
+ *            channel's 8 codes in token order)
  *   V scale  fp16   [d/G_V][G]          per (channel group, token)
  *   V zero   fp16   [d/G_V][G]
  * Dense store: records at [B][H_kv][max_blocks]. Paged store: one page holds
@@ -151,6 +155,14 @@ kvq_status kvq_append(const kvq_config* cfg, const kvq_cache* cache,
  * values; [P4] innovation 3 dense packing; innovation 4 residual window).
  * Does nothing for sequences whose ring holds fewer than R + G tokens. */
 kvq_status kvq_flush_residual(const kvq_config* cfg, const kvq_cache* cache, void* stream);
+
+/* kvq_append followed by kvq_flush_residual, as one launch when n_max <= 64
+ * (one workgroup per (sequence, kv head) appends its rows and quantizes the
+ * blocks that leave the window): the decode-step path. Same arguments, result
+ * and device errors as the two calls in sequence. */
+kvq_status kvq_append_flush(const kvq_config* cfg, const kvq_cache* cache,
+                            const void* k_new, const void* v_new,
+                            const int32_t* n_new, int32_t n_max, void* stream);
 
 /* One decode step of attention for every (sequence, query head): the quantized
  * blocks are dequantized on the fly and the ring tokens read as they are;

@@ -150,8 +150,11 @@ def unpack_lsb_first(words: np.ndarray, bits: int) -> np.ndarray:
 #                                      channels w*32/b_K ... (LSB first)
 #   K scale  fp16   [d]                per channel, over the G tokens
 #   K zero   fp16   [d]
-#   V codes  uint32 [d][G*b_V/32]      channel-major: word w of channel c holds
-#                                      tokens w*32/b_V ... of the block
+#   V codes  8-token chunks: the code of (token t, channel c) sits at bit
+#            position pos(t, c) * b_V of the section, with
+#              pos(t, c) = ((t//8 * 16 + c%16) * (d//16) + c//16) * 8 + t%8,
+#            i.e. for each run of 8 tokens, for each c%16, for each c//16, the 8
+#            tokens of that channel LSB first (a little-endian uint32 stream)
 #   V scale  fp16   [d/G_V][G]         per (channel group, token)
 #   V zero   fp16   [d/G_V][G]
 # ---------------------------------------------------------------------------
@@ -167,6 +170,25 @@ def record_sections(spec: CacheSpec):
 
 def record_bytes(spec: CacheSpec) -> int:
     return sum(record_sections(spec).values())
+
+
+def value_code_order(G: int, d: int) -> np.ndarray:
+    """Stream position of every (token, channel) value code, [G][d] -> int."""
+    t = np.arange(G)[:, None]
+    c = np.arange(d)[None, :]
+    return ((t // 8 * 16 + c % 16) * (d // 16) + c // 16) * 8 + t % 8
+
+
+def value_code_stream(vcodes: np.ndarray) -> np.ndarray:
+    """[G][d] codes -> 1-D stream in record order (see the record layout)."""
+    G, d = vcodes.shape
+    out = np.empty(G * d, dtype=vcodes.dtype)
+    out[value_code_order(G, d).ravel()] = vcodes.ravel()
+    return out
+
+
+def value_codes_from_stream(stream: np.ndarray, G: int, d: int) -> np.ndarray:
+    return stream[value_code_order(G, d)]
 
 
 def quantize_block(spec: CacheSpec, kblk: np.ndarray, vblk: np.ndarray):
@@ -185,7 +207,7 @@ def quantize_block(spec: CacheSpec, kblk: np.ndarray, vblk: np.ndarray):
     return {
         "k_codes": pack_lsb_first(kcodes, spec.k_bits),                   # [G][d*bK/32]
         "k_scale": ks, "k_zero": kz,                                      # [d]
-        "v_codes": pack_lsb_first(vcodes.T, spec.v_bits),                 # [d][G*bV/32]
+        "v_codes": pack_lsb_first(value_code_stream(vcodes), spec.v_bits),
         "v_scale": np.ascontiguousarray(vs.T),                            # [d/G_V][G]
         "v_zero": np.ascontiguousarray(vz.T),
     }
@@ -205,7 +227,7 @@ def bytes_to_block(spec: CacheSpec, rec: np.ndarray):
     shapes = {
         "k_codes": ((G, d * spec.k_bits // 32), np.uint32),
         "k_scale": ((d,), np.float16), "k_zero": ((d,), np.float16),
-        "v_codes": ((d, G * spec.v_bits // 32), np.uint32),
+        "v_codes": ((G * d * spec.v_bits // 32,), np.uint32),
         "v_scale": ((d // gv, G), np.float16), "v_zero": ((d // gv, G), np.float16),
     }
     rec = np.ascontiguousarray(rec, dtype=np.uint8)
@@ -222,7 +244,7 @@ def dequantize_block(spec: CacheSpec, sec):
     G, d, gv = spec.k_group, spec.head_dim, spec.v_group
     kcodes = unpack_lsb_first(sec["k_codes"], spec.k_bits)               # [G][d]
     khat = dequantize(kcodes, sec["k_scale"][None, :], sec["k_zero"][None, :])
-    vcodes = unpack_lsb_first(sec["v_codes"], spec.v_bits).T            # [G][d]
+    vcodes = value_codes_from_stream(unpack_lsb_first(sec["v_codes"], spec.v_bits), G, d)  # [G][d]
     vs = np.repeat(sec["v_scale"].T, gv, axis=1)                          # [G][d]
     vz = np.repeat(sec["v_zero"].T, gv, axis=1)
     vhat = dequantize(vcodes, vs, vz)

@@ -18,7 +18,7 @@ KVQ_OK, KVQ_ERR_INVALID_ARG, KVQ_ERR_UNSUPPORTED, KVQ_ERR_WORKSPACE, KVQ_ERR_LAU
 KVQ_F16, KVQ_BF16 = 0, 1
 KVQ_DEV_RESIDUAL_FULL, KVQ_DEV_BLOCKS_FULL, KVQ_DEV_BAD_PAGE, KVQ_DEV_BAD_COUNT, KVQ_DEV_TOO_LONG = 1, 2, 4, 8, 16
 
-EXPORTED = ("kvq_get_layout", "kvq_workspace_size", "kvq_append", "kvq_flush_residual",
+EXPORTED = ("kvq_get_layout", "kvq_workspace_size", "kvq_append", "kvq_append_flush", "kvq_flush_residual",
             "kvq_decode_attention", "kvq_read_device_error", "kvq_status_string")
 
 
@@ -64,6 +64,7 @@ def load():
         "kvq_get_layout": [cfgp, ctypes.POINTER(kvq_layout)],
         "kvq_workspace_size": [cfgp, I32, ctypes.POINTER(SZ)],
         "kvq_append": [cfgp, cachep, P, P, P, I32, P],
+        "kvq_append_flush": [cfgp, cachep, P, P, P, I32, P],
         "kvq_flush_residual": [cfgp, cachep, P],
         "kvq_decode_attention": [cfgp, cachep, P, P, F, I32, P, SZ, P],
         "kvq_read_device_error": [cfgp, cachep, P, ctypes.POINTER(I32)],
@@ -104,6 +105,11 @@ def kvq_workspace_size(cfg: kvq_config, max_seq_tokens: int) -> int:
 def kvq_append(cfg, cache, k_new_ptr, v_new_ptr, n_new_ptr, n_max, stream):
     _check(load().kvq_append(ctypes.byref(cfg), ctypes.byref(cache), k_new_ptr, v_new_ptr,
                              n_new_ptr, int(n_max), stream), "kvq_append")
+
+
+def kvq_append_flush(cfg, cache, k_new_ptr, v_new_ptr, n_new_ptr, n_max, stream):
+    _check(load().kvq_append_flush(ctypes.byref(cfg), ctypes.byref(cache), k_new_ptr, v_new_ptr,
+                                   n_new_ptr, int(n_max), stream), "kvq_append_flush")
 
 
 def kvq_flush_residual(cfg, cache, stream):

@@ -102,6 +102,20 @@ class QuantizedKVCache:
         B.kvq_append(c, self.cache, k_new.data_ptr(), v_new.data_ptr(), n_ptr, n_max, _stream_handle())
         self.max_len_bound += n_max
 
+    def append_flush(self, k_new: torch.Tensor, v_new: torch.Tensor, n_new: torch.Tensor | None = None):
+        """append() then flush(), fused into one launch for small appends."""
+        c = self.cfg
+        n_max = k_new.shape[2] if k_new.dim() == 4 else -1
+        shape = (c.batch, c.num_kv_heads, n_max, c.head_dim)
+        self._check(k_new, shape, self.dtype, "k_new")
+        self._check(v_new, shape, self.dtype, "v_new")
+        n_ptr = None
+        if n_new is not None:
+            self._check(n_new, (c.batch,), torch.int32, "n_new")
+            n_ptr = n_new.data_ptr()
+        B.kvq_append_flush(c, self.cache, k_new.data_ptr(), v_new.data_ptr(), n_ptr, n_max, _stream_handle())
+        self.max_len_bound += n_max
+
     def flush(self):
         B.kvq_flush_residual(self.cfg, self.cache, _stream_handle())
 

@@ -95,6 +95,18 @@ kvq_status kvq_append(const kvq_config* cfg, const kvq_cache* cache, const void*
                                      static_cast<hipStream_t>(stream)));
 }
 
+kvq_status kvq_append_flush(const kvq_config* cfg, const kvq_cache* cache, const void* k_new, const void* v_new,
+                            const int32_t* n_new, int32_t n_max, void* stream) {
+  kvq_status st = validate(cfg);
+  if (st != KVQ_OK) return st;
+  if ((st = validate_cache(cfg, cache)) != KVQ_OK) return st;
+  if (k_new == nullptr || v_new == nullptr || n_max < 0) return KVQ_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(k_new) | reinterpret_cast<uintptr_t>(v_new)) & 15) return KVQ_ERR_INVALID_ARG;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (n_max == 0) return launched(kvq::launch_flush(kvq::make_geom(*cfg), *cache, s));
+  return launched(kvq::launch_append_flush(kvq::make_geom(*cfg), *cache, k_new, v_new, n_new, n_max, s));
+}
+
 kvq_status kvq_flush_residual(const kvq_config* cfg, const kvq_cache* cache, void* stream) {
   kvq_status st = validate(cfg);
   if (st != KVQ_OK) return st;

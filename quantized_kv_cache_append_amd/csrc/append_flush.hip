@@ -10,11 +10,21 @@
 //        recent tokens in full precision next to the low-bit history.
 //   [P2] zubnet.ai survey, quantization family: keep every token, lower the bits.
 //
-// Flush is bandwidth-light (it touches each token once, when it leaves the
-// window) so one workgroup quantizes one G-token block of one kv head: the
-// tile is staged in LDS with 16-byte loads, column (key) and row-group (value)
-// min/max are taken from LDS, codes go to LDS, and the packed words are written
-// with consecutive lanes on consecutive words.
+// Flush is bandwidth-light (each token is quantized once, when it leaves the
+// window), so one workgroup quantizes one G-token block of one kv head at a
+// time: the tile is staged in LDS with 16-byte loads, column (key) and
+// row-group (value) min/max are taken from LDS, codes go to LDS and the packed
+// words are written with consecutive lanes on consecutive words.
+//
+// Three kernels share that block routine:
+//   append_kernel        copies new rows into the ring (grid: pair x 64-token chunk);
+//   flush_kernel         quantizes the complete blocks past the window
+//                        (grid: pair x Y, each workgroup strides over the blocks);
+//   append_flush_kernel  both, one workgroup per pair -- the decode-step path,
+//                        one launch instead of two.
+// Lengths live on the device: the workgroups of one sequence read (Q_b, S_b),
+// and the last of them to finish (an arrival counter in the state words)
+// publishes the new values, so no host synchronisation is needed.
 #include "common.h"
 
 namespace kvq {
@@ -22,50 +32,7 @@ namespace kvq {
 namespace {
 
 constexpr int kAppendTokensPerWG = 64;
-constexpr int kFlushThreads = 256;
-constexpr int kMaxG = 64, kMaxD = 128;
-
-__global__ __launch_bounds__(256) void append_kernel(Geom g, const uint16_t* __restrict__ k_new,
-                                                     const uint16_t* __restrict__ v_new,
-                                                     const int32_t* __restrict__ n_new, int n_max,
-                                                     uint16_t* __restrict__ k_ring,
-                                                     uint16_t* __restrict__ v_ring,
-                                                     int32_t* __restrict__ state) {
-  const int pair = blockIdx.x;
-  const int b = pair / g.Hkv;
-  __shared__ int s_S, s_n, s_ok;
-  if (threadIdx.x == 0) {
-    const int Q = state[4 * b + kStateQ];
-    const int S = state[4 * b + kStateS];
-    const int n = n_new ? n_new[b] : n_max;
-    const bool count_ok = n >= 0 && n <= n_max;
-    s_S = S;
-    s_n = n;
-    s_ok = count_ok ? ((S - Q) + n <= g.C ? 1 : 2) : 0;   // 1 ok, 2 ring full, 0 bad count
-  }
-  __syncthreads();
-  if (s_ok == 1) {
-    const int t0 = blockIdx.y * kAppendTokensPerWG;
-    const int nt = min(kAppendTokensPerWG, s_n - t0);
-    const int vec_per_tok = g.d / 8;   // 16-byte vectors per token row
-    for (int idx = threadIdx.x; idx < nt * vec_per_tok; idx += blockDim.x) {
-      const int i = t0 + idx / vec_per_tok;
-      const int v = idx % vec_per_tok;
-      const int slot = (s_S + i) % g.C;
-      const size_t src = ((size_t)pair * n_max + i) * g.d + (size_t)v * 8;
-      const size_t dst = ((size_t)pair * g.C + slot) * g.d + (size_t)v * 8;
-      *reinterpret_cast<uint4*>(k_ring + dst) = *reinterpret_cast<const uint4*>(k_new + src);
-      *reinterpret_cast<uint4*>(v_ring + dst) = *reinterpret_cast<const uint4*>(v_new + src);
-    }
-  }
-  __syncthreads();
-  if (threadIdx.x == 0 && last_arrival(&state[4 * b + kStateAppendCnt], g.Hkv * gridDim.y)) {
-    if (s_ok == 1)
-      state[4 * b + kStateS] = s_S + s_n;
-    else
-      atomicOr(&state[4 * g.B], s_ok == 0 ? KVQ_DEV_BAD_COUNT : KVQ_DEV_RESIDUAL_FULL);
-  }
-}
+constexpr int kThreads = 256;
 
 // Formula F on one group whose min and max are known (fp32 IEEE steps, round to
 // nearest even, no fused multiply-add). Returns the fp16 bits of scale and
@@ -93,118 +60,248 @@ __device__ __forceinline__ uint32_t group_code(float x, const GroupParams& p, in
   return (uint32_t)r;
 }
 
+// LDS of the block routine: raw tile [G][d] x 2 (16-bit), codes [G][d] x 2 (8-bit).
+__host__ __device__ inline size_t block_lds_bytes(int G, int d) { return (size_t)6 * G * d; }
+
+// Quantize tokens blk*G .. blk*G+G-1 of ring `pair` into record `rec`.
+// Called by all kThreads threads of the workgroup; ends with a barrier.
 template <bool BF16>
-__global__ __launch_bounds__(kFlushThreads) void flush_kernel(Geom g, uint8_t* __restrict__ blocks,
-                                                              const int32_t* __restrict__ table,
-                                                              const uint16_t* __restrict__ k_ring,
-                                                              const uint16_t* __restrict__ v_ring,
-                                                              int32_t* __restrict__ state) {
+__device__ void quantize_block(const Geom& g, uint8_t* __restrict__ rec, const uint16_t* __restrict__ k_ring,
+                               const uint16_t* __restrict__ v_ring, int pair, int blk, uint8_t* smem) {
+  const int G = g.G, d = g.d, tid = threadIdx.x;
+  uint16_t* s_k = reinterpret_cast<uint16_t*>(smem);   // [G][d]
+  uint16_t* s_v = s_k + G * d;                         // [G][d]
+  uint8_t* s_kc = reinterpret_cast<uint8_t*>(s_v + G * d);   // [G][d] key codes
+  uint8_t* s_vc = s_kc + G * d;                              // [d][G] value codes
+
+  const int vec_per_tok = d / 8;
+  for (int idx = tid; idx < G * vec_per_tok; idx += kThreads) {
+    const int t = idx / vec_per_tok, v = idx % vec_per_tok;
+    const int slot = (blk * G + t) % g.C;
+    const size_t src = ((size_t)pair * g.C + slot) * d + (size_t)v * 8;
+    *reinterpret_cast<uint4*>(&s_k[t * d + v * 8]) = *reinterpret_cast<const uint4*>(k_ring + src);
+    *reinterpret_cast<uint4*>(&s_v[t * d + v * 8]) = *reinterpret_cast<const uint4*>(v_ring + src);
+  }
+  __syncthreads();
+
+  uint16_t* ks = reinterpret_cast<uint16_t*>(rec + g.rec_ks);
+  uint16_t* kz = reinterpret_cast<uint16_t*>(rec + g.rec_kz);
+  uint16_t* vs = reinterpret_cast<uint16_t*>(rec + g.rec_vs);
+  uint16_t* vz = reinterpret_cast<uint16_t*>(rec + g.rec_vz);
+
+  // keys: one group per channel over the G tokens
+  for (int c = tid; c < d; c += kThreads) {
+    float mn = in_to_f32<BF16>(s_k[c]), mx = mn;
+    for (int t = 1; t < G; ++t) {
+      const float x = in_to_f32<BF16>(s_k[t * d + c]);
+      mn = fminf(mn, x);
+      mx = fmaxf(mx, x);
+    }
+    const GroupParams p = group_params(mn, mx, g.kb);
+    ks[c] = p.s16;
+    kz[c] = p.z16;
+    for (int t = 0; t < G; ++t) s_kc[t * d + c] = (uint8_t)group_code(in_to_f32<BF16>(s_k[t * d + c]), p, g.kb);
+  }
+  // values: one group per (token, G_V consecutive channels)
+  const int ngr = d / g.GV;
+  for (int idx = tid; idx < G * ngr; idx += kThreads) {
+    const int t = idx / ngr, j = idx % ngr;
+    const uint16_t* row = &s_v[t * d + j * g.GV];
+    float mn = in_to_f32<BF16>(row[0]), mx = mn;
+    for (int c = 1; c < g.GV; ++c) {
+      const float x = in_to_f32<BF16>(row[c]);
+      mn = fminf(mn, x);
+      mx = fmaxf(mx, x);
+    }
+    const GroupParams p = group_params(mn, mx, g.vb);
+    vs[j * G + t] = p.s16;
+    vz[j * G + t] = p.z16;
+    for (int c = 0; c < g.GV; ++c)
+      s_vc[(j * g.GV + c) * G + t] = (uint8_t)group_code(in_to_f32<BF16>(row[c]), p, g.vb);
+  }
+  __syncthreads();
+
+  // keys: word w of token t holds channels w*P .. w*P+P-1, LSB first
+  uint32_t* kc = reinterpret_cast<uint32_t*>(rec + g.rec_kc);
+  const int kP = 32 / g.kb;
+  for (int idx = tid; idx < G * g.k_words; idx += kThreads) {
+    const int t = idx / g.k_words, w = idx % g.k_words;
+    const uint8_t* src = &s_kc[t * d + w * kP];
+    uint32_t word = 0;
+    for (int i = 0; i < kP; ++i) word |= (uint32_t)src[i] << (i * g.kb);
+    kc[idx] = word;
+  }
+  // values in 8-token chunks: code (t, c) at stream position
+  // ((t/8 * 16 + c%16) * (d/16) + c/16) * 8 + t%8, LSB first
+  uint32_t* vc = reinterpret_cast<uint32_t*>(rec + g.rec_vc);
+  const int vP = 32 / g.vb;
+  const int nt_count = d / 16;
+  for (int idx = tid; idx < G * d * g.vb / 32; idx += kThreads) {
+    uint32_t word = 0;
+    for (int i = 0; i < vP; ++i) {
+      const int pos = idx * vP + i;
+      const int rest = pos >> 3;
+      const int nt = rest % nt_count, rest2 = rest / nt_count;
+      const int t = (rest2 >> 4) * 8 + (pos & 7);
+      const int c = nt * 16 + (rest2 & 15);
+      word |= (uint32_t)s_vc[c * G + t] << (i * g.vb);
+    }
+    vc[idx] = word;
+  }
+  __syncthreads();
+}
+
+// Copy tokens i in [t_lo, t_hi) of pair `pair` from the new rows into the ring,
+// starting at absolute position S (16-byte vectors).
+__device__ __forceinline__ void copy_to_ring(const Geom& g, const uint16_t* __restrict__ k_new,
+                                             const uint16_t* __restrict__ v_new, int n_max, uint16_t* k_ring,
+                                             uint16_t* v_ring, int pair, int S, int t_lo, int t_hi) {
+  const int vec_per_tok = g.d / 8;
+  for (int idx = threadIdx.x; idx < (t_hi - t_lo) * vec_per_tok; idx += kThreads) {
+    const int i = t_lo + idx / vec_per_tok;
+    const int v = idx % vec_per_tok;
+    const int slot = (S + i) % g.C;
+    const size_t src = ((size_t)pair * n_max + i) * g.d + (size_t)v * 8;
+    const size_t dst = ((size_t)pair * g.C + slot) * g.d + (size_t)v * 8;
+    *reinterpret_cast<uint4*>(k_ring + dst) = *reinterpret_cast<const uint4*>(k_new + src);
+    *reinterpret_cast<uint4*>(v_ring + dst) = *reinterpret_cast<const uint4*>(v_new + src);
+  }
+}
+
+// Blocks a flush takes for a sequence with Q quantized of S tokens, and how
+// many of those fit under max_blocks.
+struct FlushPlan {
+  int nfl, nok;
+};
+__device__ __forceinline__ FlushPlan flush_plan(const Geom& g, int Q, int S) {
+  const int r = S - Q;
+  FlushPlan f;
+  f.nfl = (r >= g.R + g.G) ? (r - g.R) / g.G : 0;
+  f.nok = min(f.nfl, max(g.max_blocks - Q / g.G, 0));
+  return f;
+}
+
+__global__ __launch_bounds__(kThreads) void append_kernel(Geom g, const uint16_t* __restrict__ k_new,
+                                                          const uint16_t* __restrict__ v_new,
+                                                          const int32_t* __restrict__ n_new, int n_max,
+                                                          uint16_t* __restrict__ k_ring,
+                                                          uint16_t* __restrict__ v_ring, int32_t* __restrict__ state) {
   const int pair = blockIdx.x;
-  const int b = pair / g.Hkv, h = pair % g.Hkv;
-  const int k = blockIdx.y;
-  const int tid = threadIdx.x;
-
-  __shared__ uint16_t s_k[kMaxG * kMaxD];      // [G][d] input bits
-  __shared__ uint16_t s_v[kMaxG * kMaxD];
-  __shared__ uint8_t s_kc[kMaxG * kMaxD];      // [G][d] key codes
-  __shared__ uint8_t s_vc[kMaxD * kMaxG];      // [d][G] value codes (channel-major)
-  __shared__ int s_Q, s_nfl, s_nok, s_bad;
-
-  if (tid == 0) {
+  const int b = pair / g.Hkv;
+  __shared__ int s_S, s_n, s_ok;
+  if (threadIdx.x == 0) {
     const int Q = state[4 * b + kStateQ];
     const int S = state[4 * b + kStateS];
-    const int r = S - Q;
-    const int nfl = (r >= g.R + g.G) ? (r - g.R) / g.G : 0;
-    const int room = g.max_blocks - Q / g.G;
+    const int n = n_new ? n_new[b] : n_max;
+    const bool count_ok = n >= 0 && n <= n_max;
+    s_S = S;
+    s_n = n;
+    s_ok = count_ok ? ((S - Q) + n <= g.C ? 1 : 2) : 0;   // 1 ok, 2 ring full, 0 bad count
+  }
+  __syncthreads();
+  if (s_ok == 1) {
+    const int t0 = blockIdx.y * kAppendTokensPerWG;
+    copy_to_ring(g, k_new, v_new, n_max, k_ring, v_ring, pair, s_S, t0, min(t0 + kAppendTokensPerWG, s_n));
+  }
+  __syncthreads();
+  if (threadIdx.x == 0 && last_arrival(&state[4 * b + kStateAppendCnt], g.Hkv * gridDim.y)) {
+    if (s_ok == 1)
+      state[4 * b + kStateS] = s_S + s_n;
+    else
+      atomicOr(&state[4 * g.B], s_ok == 0 ? KVQ_DEV_BAD_COUNT : KVQ_DEV_RESIDUAL_FULL);
+  }
+}
+
+template <bool BF16>
+__global__ __launch_bounds__(kThreads) void flush_kernel(Geom g, uint8_t* __restrict__ blocks,
+                                                         const int32_t* __restrict__ table,
+                                                         const uint16_t* __restrict__ k_ring,
+                                                         const uint16_t* __restrict__ v_ring,
+                                                         int32_t* __restrict__ state) {
+  extern __shared__ uint8_t smem[];
+  const int pair = blockIdx.x;
+  const int b = pair / g.Hkv, h = pair % g.Hkv;
+  __shared__ int s_Q, s_nfl, s_nok, s_bad;
+  if (threadIdx.x == 0) {
+    const int Q = state[4 * b + kStateQ];
+    const FlushPlan f = flush_plan(g, Q, state[4 * b + kStateS]);
     s_Q = Q;
-    s_nfl = nfl;
-    s_nok = min(nfl, max(room, 0));
+    s_nfl = f.nfl;
+    s_nok = f.nok;
     s_bad = 0;
   }
   __syncthreads();
-
-  if (k < s_nok) {
+  for (int k = blockIdx.y; k < s_nok; k += gridDim.y) {
     const int blk = s_Q / g.G + k;
     uint8_t* rec = const_cast<uint8_t*>(block_record(g, blocks, table, b, h, blk));
     if (rec == nullptr) {
-      if (tid == 0) s_bad = 1;
-    } else {
-      const int G = g.G, d = g.d;
-      // stage the G x d tile of keys and values (tokens blk*G .. blk*G+G-1)
-      const int vec_per_tok = d / 8;
-      for (int idx = tid; idx < G * vec_per_tok; idx += kFlushThreads) {
-        const int t = idx / vec_per_tok, v = idx % vec_per_tok;
-        const int slot = (blk * G + t) % g.C;
-        const size_t src = ((size_t)pair * g.C + slot) * d + (size_t)v * 8;
-        *reinterpret_cast<uint4*>(&s_k[t * d + v * 8]) = *reinterpret_cast<const uint4*>(k_ring + src);
-        *reinterpret_cast<uint4*>(&s_v[t * d + v * 8]) = *reinterpret_cast<const uint4*>(v_ring + src);
-      }
-      __syncthreads();
-
-      uint16_t* ks = reinterpret_cast<uint16_t*>(rec + g.rec_ks);
-      uint16_t* kz = reinterpret_cast<uint16_t*>(rec + g.rec_kz);
-      uint16_t* vs = reinterpret_cast<uint16_t*>(rec + g.rec_vs);
-      uint16_t* vz = reinterpret_cast<uint16_t*>(rec + g.rec_vz);
-
-      // keys: one group per channel over the G tokens
-      for (int c = tid; c < d; c += kFlushThreads) {
-        float mn = in_to_f32<BF16>(s_k[c]), mx = mn;
-        for (int t = 1; t < G; ++t) {
-          const float x = in_to_f32<BF16>(s_k[t * d + c]);
-          mn = fminf(mn, x);
-          mx = fmaxf(mx, x);
-        }
-        const GroupParams p = group_params(mn, mx, g.kb);
-        ks[c] = p.s16;
-        kz[c] = p.z16;
-        for (int t = 0; t < G; ++t)
-          s_kc[t * d + c] = (uint8_t)group_code(in_to_f32<BF16>(s_k[t * d + c]), p, g.kb);
-      }
-      // values: one group per (token, G_V consecutive channels)
-      const int ngr = d / g.GV;
-      for (int idx = tid; idx < G * ngr; idx += kFlushThreads) {
-        const int t = idx / ngr, j = idx % ngr;
-        const uint16_t* row = &s_v[t * d + j * g.GV];
-        float mn = in_to_f32<BF16>(row[0]), mx = mn;
-        for (int c = 1; c < g.GV; ++c) {
-          const float x = in_to_f32<BF16>(row[c]);
-          mn = fminf(mn, x);
-          mx = fmaxf(mx, x);
-        }
-        const GroupParams p = group_params(mn, mx, g.vb);
-        vs[j * G + t] = p.s16;
-        vz[j * G + t] = p.z16;
-        for (int c = 0; c < g.GV; ++c)
-          s_vc[(j * g.GV + c) * G + t] = (uint8_t)group_code(in_to_f32<BF16>(row[c]), p, g.vb);
-      }
-      __syncthreads();
-
-      // pack keys: word w of token t holds channels w*P .. w*P+P-1, LSB first
-      uint32_t* kc = reinterpret_cast<uint32_t*>(rec + g.rec_kc);
-      const int kP = 32 / g.kb;
-      for (int idx = tid; idx < G * g.k_words; idx += kFlushThreads) {
-        const int t = idx / g.k_words, w = idx % g.k_words;
-        const uint8_t* src = &s_kc[t * d + w * kP];
-        uint32_t word = 0;
-        for (int i = 0; i < kP; ++i) word |= (uint32_t)src[i] << (i * g.kb);
-        kc[idx] = word;
-      }
-      // pack values: word w of channel c holds tokens w*P .. w*P+P-1, LSB first
-      uint32_t* vc = reinterpret_cast<uint32_t*>(rec + g.rec_vc);
-      const int vP = 32 / g.vb;
-      for (int idx = tid; idx < d * g.v_words; idx += kFlushThreads) {
-        const int c = idx / g.v_words, w = idx % g.v_words;
-        const uint8_t* src = &s_vc[c * G + w * vP];
-        uint32_t word = 0;
-        for (int i = 0; i < vP; ++i) word |= (uint32_t)src[i] << (i * g.vb);
-        vc[idx] = word;
-      }
+      if (threadIdx.x == 0) s_bad = 1;
+      continue;
     }
+    quantize_block<BF16>(g, rec, k_ring, v_ring, pair, blk, smem);
   }
   __syncthreads();
-  if (tid == 0) {
+  if (threadIdx.x == 0) {
     if (s_bad) atomicOr(&state[4 * g.B], KVQ_DEV_BAD_PAGE);
     if (last_arrival(&state[4 * b + kStateFlushCnt], g.Hkv * gridDim.y)) {
+      state[4 * b + kStateQ] = s_Q + s_nok * g.G;
+      if (s_nok < s_nfl) atomicOr(&state[4 * g.B], KVQ_DEV_BLOCKS_FULL);
+    }
+  }
+}
+
+// Append then flush, one workgroup per (sequence, kv head): the decode-step
+// path. Every workgroup of a sequence derives the same new lengths from the
+// same (Q_b, S_b, n_b); the last to finish publishes them.
+template <bool BF16>
+__global__ __launch_bounds__(kThreads) void append_flush_kernel(Geom g, const uint16_t* __restrict__ k_new,
+                                                                const uint16_t* __restrict__ v_new,
+                                                                const int32_t* __restrict__ n_new, int n_max,
+                                                                uint8_t* __restrict__ blocks,
+                                                                const int32_t* __restrict__ table,
+                                                                uint16_t* __restrict__ k_ring,
+                                                                uint16_t* __restrict__ v_ring,
+                                                                int32_t* __restrict__ state) {
+  extern __shared__ uint8_t smem[];
+  const int pair = blockIdx.x;
+  const int b = pair / g.Hkv, h = pair % g.Hkv;
+  __shared__ int s_Q, s_S, s_n, s_ok, s_nfl, s_nok, s_bad;
+  if (threadIdx.x == 0) {
+    const int Q = state[4 * b + kStateQ];
+    const int S = state[4 * b + kStateS];
+    const int n = n_new ? n_new[b] : n_max;
+    const bool count_ok = n >= 0 && n <= n_max;
+    const int ok = count_ok ? ((S - Q) + n <= g.C ? 1 : 2) : 0;
+    const FlushPlan f = flush_plan(g, Q, ok == 1 ? S + n : S);
+    s_Q = Q;
+    s_S = S;
+    s_n = n;
+    s_ok = ok;
+    s_nfl = f.nfl;
+    s_nok = f.nok;
+    s_bad = 0;
+  }
+  __syncthreads();
+  if (s_ok == 1) copy_to_ring(g, k_new, v_new, n_max, k_ring, v_ring, pair, s_S, 0, s_n);
+  // the block routine reads the ring through plain loads: make this
+  // workgroup's ring writes visible to all of its threads first
+  __threadfence_block();
+  __syncthreads();
+  for (int k = 0; k < s_nok; ++k) {
+    const int blk = s_Q / g.G + k;
+    uint8_t* rec = const_cast<uint8_t*>(block_record(g, blocks, table, b, h, blk));
+    if (rec == nullptr) {
+      if (threadIdx.x == 0) s_bad = 1;
+      continue;
+    }
+    quantize_block<BF16>(g, rec, k_ring, v_ring, pair, blk, smem);
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    if (s_bad) atomicOr(&state[4 * g.B], KVQ_DEV_BAD_PAGE);
+    if (s_ok != 1) atomicOr(&state[4 * g.B], s_ok == 0 ? KVQ_DEV_BAD_COUNT : KVQ_DEV_RESIDUAL_FULL);
+    if (last_arrival(&state[4 * b + kStateAppendCnt], g.Hkv)) {
+      if (s_ok == 1) state[4 * b + kStateS] = s_S + s_n;
       state[4 * b + kStateQ] = s_Q + s_nok * g.G;
       if (s_nok < s_nfl) atomicOr(&state[4 * g.B], KVQ_DEV_BLOCKS_FULL);
     }
@@ -217,23 +314,52 @@ hipError_t launch_append(const Geom& g, const kvq_cache& c, const void* k_new, c
                          const int32_t* n_new, int n_max, hipStream_t s) {
   const int chunks = (n_max + kAppendTokensPerWG - 1) / kAppendTokensPerWG;
   dim3 grid(g.B * g.Hkv, chunks > 0 ? chunks : 1);
-  hipLaunchKernelGGL(append_kernel, grid, dim3(256), 0, s, g,
+  hipLaunchKernelGGL(append_kernel, grid, dim3(kThreads), 0, s, g,
                      static_cast<const uint16_t*>(k_new), static_cast<const uint16_t*>(v_new), n_new,
                      n_max, static_cast<uint16_t*>(c.k_ring), static_cast<uint16_t*>(c.v_ring), c.state);
   return hipGetLastError();
 }
 
 hipError_t launch_flush(const Geom& g, const kvq_cache& c, hipStream_t s) {
-  const int max_fl = (g.C - g.R) / g.G;   // r <= C bounds the blocks one flush can take
-  dim3 grid(g.B * g.Hkv, max_fl);
+  // A ring of C slots holds at most (C - R) / G complete blocks past the
+  // window; spread them over up to Y workgroups per pair, Y chosen so that a
+  // large flush fills the GPU and a decode-sized one launches one per pair.
+  const int max_fl = std::max((g.C - g.R) / g.G, 1);
+  const int pairs = g.B * g.Hkv;
+  const int Y = std::max(1, std::min(max_fl, (2048 + pairs - 1) / pairs));
+  dim3 grid(pairs, Y);
+  const size_t lds = block_lds_bytes(g.G, g.d);
   if (g.dtype == KVQ_BF16)
-    hipLaunchKernelGGL(flush_kernel<true>, grid, dim3(kFlushThreads), 0, s, g,
-                       static_cast<uint8_t*>(c.blocks), c.block_table,
-                       static_cast<const uint16_t*>(c.k_ring), static_cast<const uint16_t*>(c.v_ring), c.state);
+    hipLaunchKernelGGL(flush_kernel<true>, grid, dim3(kThreads), lds, s, g, static_cast<uint8_t*>(c.blocks),
+                       c.block_table, static_cast<const uint16_t*>(c.k_ring),
+                       static_cast<const uint16_t*>(c.v_ring), c.state);
   else
-    hipLaunchKernelGGL(flush_kernel<false>, grid, dim3(kFlushThreads), 0, s, g,
-                       static_cast<uint8_t*>(c.blocks), c.block_table,
-                       static_cast<const uint16_t*>(c.k_ring), static_cast<const uint16_t*>(c.v_ring), c.state);
+    hipLaunchKernelGGL(flush_kernel<false>, grid, dim3(kThreads), lds, s, g, static_cast<uint8_t*>(c.blocks),
+                       c.block_table, static_cast<const uint16_t*>(c.k_ring),
+                       static_cast<const uint16_t*>(c.v_ring), c.state);
+  return hipGetLastError();
+}
+
+hipError_t launch_append_flush(const Geom& g, const kvq_cache& c, const void* k_new, const void* v_new,
+                               const int32_t* n_new, int n_max, hipStream_t s) {
+  if (n_max > kAppendTokensPerWG) {
+    // a large append keeps the parallel copy and the parallel flush
+    hipError_t e = launch_append(g, c, k_new, v_new, n_new, n_max, s);
+    return e != hipSuccess ? e : launch_flush(g, c, s);
+  }
+  const size_t lds = block_lds_bytes(g.G, g.d);
+  dim3 grid(g.B * g.Hkv);
+  const auto* kn = static_cast<const uint16_t*>(k_new);
+  const auto* vn = static_cast<const uint16_t*>(v_new);
+  auto* blocks = static_cast<uint8_t*>(c.blocks);
+  auto* kr = static_cast<uint16_t*>(c.k_ring);
+  auto* vr = static_cast<uint16_t*>(c.v_ring);
+  if (g.dtype == KVQ_BF16)
+    hipLaunchKernelGGL(append_flush_kernel<true>, grid, dim3(kThreads), lds, s, g, kn, vn, n_new, n_max, blocks,
+                       c.block_table, kr, vr, c.state);
+  else
+    hipLaunchKernelGGL(append_flush_kernel<false>, grid, dim3(kThreads), lds, s, g, kn, vn, n_new, n_max, blocks,
+                       c.block_table, kr, vr, c.state);
   return hipGetLastError();
 }
 

@@ -117,16 +117,27 @@ __device__ __forceinline__ bool last_arrival(int* counter, int total) {
 hipError_t launch_append(const Geom& g, const kvq_cache& c, const void* k_new, const void* v_new,
                          const int32_t* n_new, int n_max, hipStream_t s);
 hipError_t launch_flush(const Geom& g, const kvq_cache& c, hipStream_t s);
+hipError_t launch_append_flush(const Geom& g, const kvq_cache& c, const void* k_new, const void* v_new,
+                               const int32_t* n_new, int n_max, hipStream_t s);
 hipError_t launch_decode(const Geom& g, const kvq_cache& c, const void* q, float* out, float scale,
                          int max_seq_tokens, void* ws, hipStream_t s);
 
 // Decode work decomposition shared by the workspace sizing and the kernels.
 struct DecodePlan {
+  bool fast;          // MFMA kernel (else the generic VALU kernel)
   int bps;            // quantized blocks per split
+  int rc;             // ring tokens per ring chunk
   int nq_max;         // upper bound on quantized splits per (sequence, kv head)
-  size_t items_max;   // upper bound on work items (splits incl. the ring split)
+  int nr_max;         // upper bound on ring chunks per (sequence, kv head)
+  size_t items_max;   // upper bound on work items
   size_t ws_bytes;    // workspace bytes
 };
 DecodePlan plan_decode(const Geom& g, int max_seq_tokens);
+
+// MFMA path (decode_fast_dispatch.hip): whether a configuration has an
+// instantiation, its blocks per set, and the launch.
+bool fast_supported(const Geom& g, int* blocks_per_set);
+hipError_t launch_decode_fast(const Geom& g, const kvq_cache& c, const void* q, float scale, const DecodePlan& p,
+                              void* ws, hipStream_t s);
 
 }  // namespace kvq

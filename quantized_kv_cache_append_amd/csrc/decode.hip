@@ -14,19 +14,24 @@
 //        partial attention states combined by a globally normalised online
 //        softmax -- the split/combine used here.
 //
-// Work decomposition. For each (sequence b, kv head h) the quantized blocks are
-// cut into splits of `bps` blocks, plus one split for the ring tokens. A work
-// item is one split; each wavefront of a persistent grid walks the item list
-// with a grid stride. The per-sequence item counts come from the device-side
-// lengths, so ragged batches need no host synchronisation. Each item leaves a
-// partial state (running max m, sum l, unnormalised o[d]) per query head of
-// the group; the combine kernel merges them.
+// Work decomposition (decode_items.h). For each (sequence b, kv head h) the
+// quantized blocks are cut into splits and the ring tokens into chunks; a work
+// item is one split or chunk. The per-sequence item counts come from the
+// device-side lengths, so ragged batches need no host synchronisation. Each
+// item leaves a partial state (running max m, sum l, unnormalised o[d]) per
+// query head of the group, scores in log2 units (the query is pre-multiplied
+// by softmax_scale * log2 e, so exp becomes exp2); the combine kernel merges
+// them.
 //
-// This file holds the generic VALU path (any head_dim 64/128, any group size,
-// n_g <= 8): scores lane-per-token with the key scale folded into the query
-// (q~ = q * s_K) and the zero-point term added once per block, values
-// lane-per-channel.
+// This file holds the plan, the combine and the generic VALU path (head_dim 64
+// or 128, any supported group size, n_g <= 8), used for configurations the
+// MFMA path (decode_fast.h) has no instantiation for: scores lane-per-token
+// with the key scale folded into the query (q~ = q * s_K) and the zero-point
+// term added once per block, values lane-per-channel.
+#include <algorithm>
+
 #include "common.h"
+#include "decode_items.h"
 
 namespace kvq {
 
@@ -35,21 +40,11 @@ namespace {
 constexpr int kWaves = 4;
 constexpr int kNgMax = 8;
 
-__device__ __forceinline__ int items_of(int Q, int G, int bps, int nq_max, bool* too_long) {
-  const int nblk = Q / G;
-  int nq = (nblk + bps - 1) / bps;
-  if (nq > nq_max) {
-    nq = nq_max;
-    *too_long = true;
-  }
-  return nq + 1;
-}
-
 template <int D, bool BF16>
 __global__ __launch_bounds__(256) void decode_generic_kernel(
     Geom g, const uint8_t* __restrict__ blocks, const int32_t* __restrict__ table,
     const uint16_t* __restrict__ k_ring, const uint16_t* __restrict__ v_ring, int32_t* __restrict__ state,
-    const uint16_t* __restrict__ q, float scale, int bps, int nq_max, float* __restrict__ ws) {
+    const uint16_t* __restrict__ q, float qscale, int bps, int rc, int nq_max, int nr_max, float* __restrict__ ws) {
   constexpr int CPL = D / 64;   // channels per lane
   extern __shared__ int smem[];
   int* prefix = smem;   // [B + 1] exclusive prefix of items per sequence
@@ -58,32 +53,18 @@ __global__ __launch_bounds__(256) void decode_generic_kernel(
   float* qt = scratch + wave * (kNgMax * D + kNgMax * 64);   // [8][D]
   float* pb = qt + kNgMax * D;                               // [8][64]
 
-  bool too_long = false;
-  for (int b = threadIdx.x; b < g.B; b += blockDim.x)
-    prefix[b + 1] = items_of(state[4 * b + kStateQ], g.G, bps, nq_max, &too_long);
-  if (too_long && blockIdx.x == 0) atomicOr(&state[4 * g.B], KVQ_DEV_TOO_LONG);
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    prefix[0] = 0;
-    for (int b = 0; b < g.B; ++b) prefix[b + 1] += prefix[b];
-  }
-  __syncthreads();
+  build_prefix(g, state, bps, rc, nq_max, nr_max, prefix, blockIdx.x == 0);
 
   const int W = g.Hkv * prefix[g.B];
   const int ng = g.ng;
   for (int w = blockIdx.x * kWaves + wave; w < W; w += gridDim.x * kWaves) {
-    int lo = 0, hi = g.B - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (g.Hkv * prefix[mid] <= w) lo = mid; else hi = mid - 1;
-    }
-    const int b = lo;
-    const int cb = prefix[b + 1] - prefix[b];
-    const int rem = w - g.Hkv * prefix[b];
-    const int h = rem / cb, item = rem % cb;
+    const ItemRef it = locate_item(g, prefix, w);
+    const int b = it.b, h = it.h, item = it.item;
     const int pair = b * g.Hkv + h;
     const int Q = state[4 * b + kStateQ];
     const int S = state[4 * b + kStateS];
+    bool unused_flag = false;
+    const ItemCounts cnt = items_of(Q, S, g.G, bps, rc, nq_max, nr_max, &unused_flag);
 
     float qv[kNgMax][CPL], o[kNgMax][CPL], m[kNgMax], l[kNgMax];
 #pragma unroll
@@ -93,7 +74,7 @@ __global__ __launch_bounds__(256) void decode_generic_kernel(
 #pragma unroll
       for (int k = 0; k < CPL; ++k) {
         o[j][k] = 0.f;
-        qv[j][k] = (j < ng) ? in_to_f32<BF16>(q[((size_t)b * g.Hq + h * ng + j) * D + lane + 64 * k]) : 0.f;
+        qv[j][k] = (j < ng) ? in_to_f32<BF16>(q[((size_t)b * g.Hq + h * ng + j) * D + lane + 64 * k]) * qscale : 0.f;
       }
     }
 
@@ -105,8 +86,8 @@ __global__ __launch_bounds__(256) void decode_generic_kernel(
         const float s = valid ? sc[j] : -INFINITY;
         const float bm = wave_max(s);
         const float mn = fmaxf(m[j], bm);
-        const float alpha = (m[j] == -INFINITY) ? 0.f : __expf(m[j] - mn);
-        const float p = valid ? __expf(s - mn) : 0.f;
+        const float alpha = (m[j] == -INFINITY) ? 0.f : exp2f(m[j] - mn);
+        const float p = valid ? exp2f(s - mn) : 0.f;
         l[j] = l[j] * alpha + wave_sum(p);
         m[j] = mn;
 #pragma unroll
@@ -116,11 +97,11 @@ __global__ __launch_bounds__(256) void decode_generic_kernel(
       wave_lds_fence();
     };
 
-    if (item < cb - 1) {
+    if (item < cnt.nq) {
       // ---- quantized blocks [item*bps, ...) ----
       const int nblk = Q / g.G;
       const int blk0 = item * bps, blk1 = min(blk0 + bps, nblk);
-      const int kP = 32 / g.kb, vP = 32 / g.vb;
+      const int kP = 32 / g.kb;
       const uint32_t kmask = (1u << g.kb) - 1, vmask = (1u << g.vb) - 1;
       for (int blk = blk0; blk < blk1; ++blk) {
         const uint8_t* rec = block_record(g, blocks, table, b, h, blk);
@@ -165,7 +146,7 @@ __global__ __launch_bounds__(256) void decode_generic_kernel(
           }
         }
 #pragma unroll
-        for (int j = 0; j < kNgMax; ++j) sc[j] = scale * (sc[j] + kap[j]);
+        for (int j = 0; j < kNgMax; ++j) sc[j] = sc[j] + kap[j];
         softmax_tile(sc, valid);
 
         // values, lane = channel
@@ -175,10 +156,11 @@ __global__ __launch_bounds__(256) void decode_generic_kernel(
         for (int k = 0; k < CPL; ++k) {
           const int c = lane + 64 * k;
           const int gr = c / g.GV;
-          const uint32_t* vw = reinterpret_cast<const uint32_t*>(rec + g.rec_vc) + (size_t)c * g.v_words;
+          const uint32_t* vw = reinterpret_cast<const uint32_t*>(rec + g.rec_vc);
+          const int cpos = ((c & 15) * (D / 16) + (c >> 4)) * 8;   // stream position of (t=0, c)
           for (int t = 0; t < g.G; ++t) {
-            const uint32_t word = vw[t / vP];
-            const float code = (float)((word >> ((t % vP) * g.vb)) & vmask);
+            const int bit = (cpos + (t >> 3) * 8 * D + (t & 7)) * g.vb;
+            const float code = (float)((vw[bit >> 5] >> (bit & 31)) & vmask);
             const float val = f16_to_f32(vs[gr * g.G + t]) * code + f16_to_f32(vz[gr * g.G + t]);
 #pragma unroll
             for (int j = 0; j < kNgMax; ++j)
@@ -188,16 +170,17 @@ __global__ __launch_bounds__(256) void decode_generic_kernel(
         wave_lds_fence();
       }
     } else {
-      // ---- full-precision ring tokens [Q, S) ----
+      // ---- full-precision ring tokens of this chunk ----
+      const int r0 = Q + (item - cnt.nq) * rc, r1 = min(S, r0 + rc);
 #pragma unroll
       for (int k = 0; k < CPL; ++k)
 #pragma unroll
         for (int j = 0; j < kNgMax; ++j)
           if (j < ng) qt[j * D + lane + 64 * k] = qv[j][k];
       wave_lds_fence();
-      for (int t0 = Q; t0 < S; t0 += 64) {
+      for (int t0 = r0; t0 < r1; t0 += 64) {
         const int t = t0 + lane;
-        const bool valid = t < S;
+        const bool valid = t < r1;
         float sc[kNgMax];
 #pragma unroll
         for (int j = 0; j < kNgMax; ++j) sc[j] = 0.f;
@@ -210,10 +193,8 @@ __global__ __launch_bounds__(256) void decode_generic_kernel(
               if (j < ng) sc[j] += qt[j * D + c] * x;
           }
         }
-#pragma unroll
-        for (int j = 0; j < kNgMax; ++j) sc[j] *= scale;
         softmax_tile(sc, valid);
-        const int nt = min(64, S - t0);
+        const int nt = min(64, r1 - t0);
 #pragma unroll
         for (int k = 0; k < CPL; ++k) {
           const int c = lane + 64 * k;
@@ -243,37 +224,66 @@ __global__ __launch_bounds__(256) void decode_generic_kernel(
   }
 }
 
-// Merge the partial states of one (sequence, query head): with M = max m_i,
-// o = sum_i e^(m_i - M) o_i / sum_i e^(m_i - M) l_i.
+// Merge the partial states of one (sequence, query head) (scores in log2
+// units): with M = max m_i, o = sum_i 2^(m_i - M) o_i / sum_i 2^(m_i - M) l_i.
 template <int D>
-__global__ __launch_bounds__(64) void combine_kernel(Geom g, const int32_t* __restrict__ state, int bps,
-                                                     int nq_max, const float* __restrict__ ws,
+__global__ __launch_bounds__(64) void combine_kernel(Geom g, const int32_t* __restrict__ state, int bps, int rc,
+                                                     int nq_max, int nr_max, const float* __restrict__ ws,
                                                      float* __restrict__ out) {
   constexpr int CPL = D / 64;
   const int bh = blockIdx.x;
   const int b = bh / g.Hq, hq = bh % g.Hq;
   const int h = hq / g.ng, j = hq % g.ng;
   const int lane = threadIdx.x;
-  bool dummy = false;
+  bool unused_flag = false;
   int part = 0;
-  for (int bb = lane; bb < b; bb += 64) part += items_of(state[4 * bb + kStateQ], g.G, bps, nq_max, &dummy);
+  for (int bb = lane; bb < b; bb += 64) {
+    const ItemCounts c = items_of(state[4 * bb + kStateQ], state[4 * bb + kStateS], g.G, bps, rc, nq_max, nr_max,
+                                  &unused_flag);
+    part += c.nq + c.nr;
+  }
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) part += __shfl_xor(part, off, 64);
-  const int cb = items_of(state[4 * b + kStateQ], g.G, bps, nq_max, &dummy);
+  const ItemCounts cc = items_of(state[4 * b + kStateQ], state[4 * b + kStateS], g.G, bps, rc, nq_max, nr_max,
+                                 &unused_flag);
+  const int cb = cc.nq + cc.nr;
   const size_t base = (size_t)g.Hkv * part + (size_t)h * cb;
+  const size_t stride = (size_t)g.ng * (D + 2);
+  const float* src0 = ws + base * stride + (size_t)j * (D + 2);
 
+  // the item maxima, 64 at a time, then their maximum
   float M = -INFINITY;
-  for (int i = 0; i < cb; ++i) M = fmaxf(M, ws[((base + i) * g.ng + j) * (D + 2) + D]);
+  for (int i = lane; i < cb; i += 64) M = fmaxf(M, src0[i * stride + D]);
+  M = wave_max(M);
   float L = 0.f, acc[CPL];
 #pragma unroll
   for (int k = 0; k < CPL; ++k) acc[k] = 0.f;
   if (M != -INFINITY) {
-    for (int i = 0; i < cb; ++i) {
-      const float* src = ws + ((base + i) * g.ng + j) * (D + 2);
-      const float e = __expf(src[D] - M);
-      L += e * src[D + 1];
+    int i = 0;
+    for (; i + 4 <= cb; i += 4) {   // four independent item loads in flight
+      float e[4], l[4], v[4][CPL];
 #pragma unroll
-      for (int k = 0; k < CPL; ++k) acc[k] += e * src[lane + 64 * k];
+      for (int u = 0; u < 4; ++u) {
+        const float* src = src0 + (i + u) * stride;
+        e[u] = src[D];
+        l[u] = src[D + 1];
+#pragma unroll
+        for (int k = 0; k < CPL; ++k) v[u][k] = src[lane + 64 * k];
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const float wgt = exp2f(e[u] - M);
+        L += wgt * l[u];
+#pragma unroll
+        for (int k = 0; k < CPL; ++k) acc[k] += wgt * v[u][k];
+      }
+    }
+    for (; i < cb; ++i) {
+      const float* src = src0 + i * stride;
+      const float wgt = exp2f(src[D] - M);
+      L += wgt * src[D + 1];
+#pragma unroll
+      for (int k = 0; k < CPL; ++k) acc[k] += wgt * src[lane + 64 * k];
     }
   }
   const float inv = (L > 0.f) ? 1.f / L : 0.f;
@@ -282,18 +292,15 @@ __global__ __launch_bounds__(64) void combine_kernel(Geom g, const int32_t* __re
 }
 
 template <int D, bool BF16>
-hipError_t launch_generic(const Geom& g, const kvq_cache& c, const void* q, float* out, float scale,
-                          const DecodePlan& plan, void* ws, hipStream_t s) {
+hipError_t launch_generic(const Geom& g, const kvq_cache& c, const void* q, float scale, const DecodePlan& plan,
+                          void* ws, hipStream_t s) {
   const int wgs = (int)std::min<size_t>((plan.items_max + kWaves - 1) / kWaves, 2048);
   const size_t lds = (size_t)((g.B + 4) & ~3) * 4 + (size_t)kWaves * (kNgMax * D + kNgMax * 64) * 4;
   hipLaunchKernelGGL((decode_generic_kernel<D, BF16>), dim3(wgs), dim3(256), lds, s, g,
                      static_cast<const uint8_t*>(c.blocks), c.block_table,
                      static_cast<const uint16_t*>(c.k_ring), static_cast<const uint16_t*>(c.v_ring), c.state,
-                     static_cast<const uint16_t*>(q), scale, plan.bps, plan.nq_max, static_cast<float*>(ws));
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((combine_kernel<D>), dim3(g.B * g.Hq), dim3(64), 0, s, g, c.state, plan.bps, plan.nq_max,
-                     static_cast<const float*>(ws), out);
+                     static_cast<const uint16_t*>(q), scale * 1.4426950408889634f, plan.bps, plan.rc, plan.nq_max,
+                     plan.nr_max, static_cast<float*>(ws));
   return hipGetLastError();
 }
 
@@ -301,10 +308,27 @@ hipError_t launch_generic(const Geom& g, const kvq_cache& c, const void* q, floa
 
 DecodePlan plan_decode(const Geom& g, int max_seq_tokens) {
   DecodePlan p{};
-  p.bps = 8;
+  int nb_set = 1;
+  p.fast = fast_supported(g, &nb_set);
   const int maxblk = std::max(max_seq_tokens - g.R, 0) / g.G;
+  if (p.fast) {
+    // About one split per wave slot of the GPU (256 CUs x 8), 512..4096 tokens,
+    // a whole number of sets.
+    const double total = (double)g.B * g.Hkv * std::max(max_seq_tokens, 1);
+    int split = 512;
+    while (split < 4096 && total / split > 2048.0) split *= 2;
+    const int set_tok = nb_set * g.G;
+    split = std::max(set_tok, split / set_tok * set_tok);
+    p.bps = split / g.G;
+    p.rc = 32;
+    p.nr_max = (g.C + p.rc - 1) / p.rc;
+  } else {
+    p.bps = 8;
+    p.rc = g.C;
+    p.nr_max = 1;
+  }
   p.nq_max = (maxblk + p.bps - 1) / p.bps;
-  p.items_max = (size_t)g.B * g.Hkv * (size_t)(p.nq_max + 1);
+  p.items_max = (size_t)g.B * g.Hkv * (size_t)(p.nq_max + p.nr_max);
   p.ws_bytes = p.items_max * (size_t)g.ng * (size_t)(g.d + 2) * 4;
   return p;
 }
@@ -313,11 +337,23 @@ hipError_t launch_decode(const Geom& g, const kvq_cache& c, const void* q, float
                          int max_seq_tokens, void* ws, hipStream_t s) {
   const DecodePlan plan = plan_decode(g, max_seq_tokens);
   const bool bf16 = g.dtype == KVQ_BF16;
+  hipError_t e;
+  if (plan.fast)
+    e = launch_decode_fast(g, c, q, scale, plan, ws, s);
+  else if (g.d == 128)
+    e = bf16 ? launch_generic<128, true>(g, c, q, scale, plan, ws, s)
+             : launch_generic<128, false>(g, c, q, scale, plan, ws, s);
+  else
+    e = bf16 ? launch_generic<64, true>(g, c, q, scale, plan, ws, s)
+             : launch_generic<64, false>(g, c, q, scale, plan, ws, s);
+  if (e != hipSuccess) return e;
   if (g.d == 128)
-    return bf16 ? launch_generic<128, true>(g, c, q, out, scale, plan, ws, s)
-                : launch_generic<128, false>(g, c, q, out, scale, plan, ws, s);
-  return bf16 ? launch_generic<64, true>(g, c, q, out, scale, plan, ws, s)
-              : launch_generic<64, false>(g, c, q, out, scale, plan, ws, s);
+    hipLaunchKernelGGL((combine_kernel<128>), dim3(g.B * g.Hq), dim3(64), 0, s, g, c.state, plan.bps, plan.rc,
+                       plan.nq_max, plan.nr_max, static_cast<const float*>(ws), out);
+  else
+    hipLaunchKernelGGL((combine_kernel<64>), dim3(g.B * g.Hq), dim3(64), 0, s, g, c.state, plan.bps, plan.rc,
+                       plan.nq_max, plan.nr_max, static_cast<const float*>(ws), out);
+  return hipGetLastError();
 }
 
 }  // namespace kvq

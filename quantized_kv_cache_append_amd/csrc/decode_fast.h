@@ -1,0 +1,697 @@
+// MFMA decode path for head_dim 128 (gfx950): kernel template. Instantiated per
+// configuration in decode_fast_*.hip.
+//
+// Sources:
+//   [P4] patricehuetz.fr, "Quantification du KV-Cache : TurboQuant et l'état de
+//        l'art en 2026": section "KIVI (2024)" -- keys quantized per channel,
+//        values per token, each group with its own min/max parameters, recent
+//        tokens in full precision; innovation 3 -- codes packed 16 (INT2) or 8
+//        (INT4) per 32-bit word and unpacked in registers; innovation 4 -- the
+//        window of recent tokens is read by the same attention pass.
+//   [P3] encorp.ai, "La compression du cache KV est une décision
+//        d'infrastructure ...": decode streams the cache from HBM and is bound
+//        by that traffic.
+//   [P1] ai-automate.fr, "KV-cache compressé et modèles 4-bit ...", Minima-KV:
+//        partial attention states merged by an online softmax.
+//
+// Arithmetic. With x_hat = code*s + z, the score of token t for query q is
+//   q . k_hat_t = sum_c (q_c s_c) code_tc + sum_c q_c z_c ,
+// so per block the key scale is folded into the query (q~ = q * s_K) and the
+// zero-point term kappa = q . z_K is one dot product per block; likewise
+//   o_c = sum_t (p_t s_tj) code_tc + sum_t p_t z_tj          (j = group of c).
+// The contractions run on MFMA (v_mfma_f32_16x16x32_bf16): codes 0..15 are
+// exact in bf16 (unpacked with the scaled fp4/fp8 -> bf16 conversions), and the
+// real-valued operand (q~ or p~) is split into a bf16 high part and a bf16
+// remainder, two MFMAs accumulating in fp32 -- about 16 significant bits per
+// product term instead of bf16's 8.
+//
+// Layout of one wave's work item: a run of quantized blocks of one (sequence,
+// kv head), processed in "sets" of NB blocks whose NB*NG (block, head) pairs
+// are the 16 columns of the score MFMA; or a chunk of up to 32 ring tokens.
+// Scores come out as D[token][(block, head)]; after the online-softmax update
+// the probabilities, scaled per value group and split hi/lo, go through LDS
+// into the A operand of the P.V MFMA (rows = head hi / head lo, k = tokens,
+// columns = 16 channels). The value codes are stored in 8-token chunks so that
+// each lane's B operand is one contiguous 16- (INT2) or 32-byte (INT4) load.
+#pragma once
+
+#include "common.h"
+#include "decode_items.h"
+
+namespace kvq {
+namespace fast {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(8 * sizeof(_Float16)))) _Float16 f16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2v __attribute__((ext_vector_type(2)));
+
+constexpr int kWaves = 4;
+constexpr int kRingChunk = 32;
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ f32x4 mfma_bf16(uint4 a, uint4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
+                                                 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma_f16(uint4 a, uint4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0,
+                                                0, 0);
+}
+
+// --- exact code unpacking --------------------------------------------------------
+// 8 codes of one 8-element run (LSB first) -> 4 bf16 pairs in the k order
+// (0,2) (1,3) (4,6) (5,7). INT2: a 2-bit code c placed in a nibble reads as
+// fp4 e2m1 c/2, so a scale of 2 gives c exactly. INT4: a 4-bit code in a byte
+// reads as fp8 e4m3 c*2^-9 (subnormals and the first binade are evenly
+// spaced), so a scale of 2^9 gives c exactly.
+template <int SEL>
+__device__ __forceinline__ uint32_t fp4x2_to_bf16x2(uint32_t src) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(src, 2.0f, SEL));
+}
+template <bool HI>
+__device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t src) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(src, 512.0f, HI));
+}
+// Both 16-bit halves of an INT2 word (two runs of 8 codes).
+__device__ __forceinline__ void unpack_int2_word(uint32_t w, uint4& lo_run, uint4& hi_run) {
+  const uint32_t e0 = w & 0x33333333u, e1 = (w >> 2) & 0x33333333u;
+  lo_run.x = fp4x2_to_bf16x2<0>(e0);
+  lo_run.y = fp4x2_to_bf16x2<0>(e1);
+  lo_run.z = fp4x2_to_bf16x2<1>(e0);
+  lo_run.w = fp4x2_to_bf16x2<1>(e1);
+  hi_run.x = fp4x2_to_bf16x2<2>(e0);
+  hi_run.y = fp4x2_to_bf16x2<2>(e1);
+  hi_run.z = fp4x2_to_bf16x2<3>(e0);
+  hi_run.w = fp4x2_to_bf16x2<3>(e1);
+}
+// One INT4 word (one run of 8 codes).
+__device__ __forceinline__ uint4 unpack_int4_word(uint32_t w) {
+  const uint32_t e0 = w & 0x0F0F0F0Fu, e1 = (w >> 4) & 0x0F0F0F0Fu;
+  uint4 r;
+  r.x = fp8x2_to_bf16x2<false>(e0);
+  r.y = fp8x2_to_bf16x2<false>(e1);
+  r.z = fp8x2_to_bf16x2<true>(e0);
+  r.w = fp8x2_to_bf16x2<true>(e1);
+  return r;
+}
+// k position of element e of a run of 8 (its own inverse).
+__host__ __device__ constexpr int kperm(int e) { return (e & 4) | ((e & 1) << 1) | ((e >> 1) & 1); }
+
+// --- hi/lo splits -------------------------------------------------------------------
+__device__ __forceinline__ void split_bf16(float x0, float x1, uint32_t& hi, uint32_t& lo) {
+  const bf16x2v h = {(__bf16)x0, (__bf16)x1};
+  hi = __builtin_bit_cast(uint32_t, h);
+  const float h0 = __uint_as_float(hi << 16), h1 = __uint_as_float(hi & 0xffff0000u);
+  const bf16x2v l = {(__bf16)(x0 - h0), (__bf16)(x1 - h1)};
+  lo = __builtin_bit_cast(uint32_t, l);
+}
+__device__ __forceinline__ void split_f16(float x0, float x1, uint32_t& hi, uint32_t& lo) {
+  const f16x2v h = {(_Float16)x0, (_Float16)x1};
+  hi = __builtin_bit_cast(uint32_t, h);
+  const float h0 = (float)h[0], h1 = (float)h[1];
+  const f16x2v l = {(_Float16)(x0 - h0), (_Float16)(x1 - h1)};
+  lo = __builtin_bit_cast(uint32_t, l);
+}
+__device__ __forceinline__ float lo_half_f16(uint32_t w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)w); }
+__device__ __forceinline__ float hi_half_f16(uint32_t w) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
+}
+
+// --- cross-lane helpers ---------------------------------------------------------------
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+template <int K>
+__device__ __forceinline__ float ror(float x) { return dpp<0x120 + K>(x); }
+
+struct OpMax {
+  __device__ __forceinline__ float operator()(float a, float b) const { return fmaxf(a, b); }
+};
+struct OpAdd {
+  __device__ __forceinline__ float operator()(float a, float b) const { return a + b; }
+};
+
+// Combine x over the lanes holding the same head: columns n = blk*NG + head
+// of every 16-lane row (unused columns must hold the identity), then the four
+// rows. Every lane of a used column ends with the head's total.
+template <int NG, typename Op>
+__device__ __forceinline__ float reduce_head(float x, int n, Op op) {
+  if constexpr (NG == 6) {
+    const float a = ror<6>(x);    // lane n <- lane n-6
+    const float b = ror<10>(x);   // lane n <- lane n+6
+    x = op(x, n < 6 ? b : a);
+  } else {
+    if constexpr (NG <= 1) x = op(x, ror<1>(x));
+    if constexpr (NG <= 2) x = op(x, ror<2>(x));
+    if constexpr (NG <= 4) x = op(x, ror<4>(x));
+    if constexpr (NG <= 8) x = op(x, ror<8>(x));
+  }
+  auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = op(__uint_as_float(r16[0]), __uint_as_float(r16[1]));
+  auto r32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return op(__uint_as_float(r32[0]), __uint_as_float(r32[1]));
+}
+// Combine over the four rows only (same lane position).
+template <typename Op>
+__device__ __forceinline__ float reduce_rows(float x, Op op) {
+  auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = op(__uint_as_float(r16[0]), __uint_as_float(r16[1]));
+  auto r32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return op(__uint_as_float(r32[0]), __uint_as_float(r32[1]));
+}
+
+template <int NG_, int KB_, int VB_, int G_, int GV_, bool BF16_>
+struct Cfg {
+  static constexpr int NG = NG_, KB = KB_, VB = VB_, G = G_, GV = GV_;
+  static constexpr bool BF16 = BF16_;
+  static constexpr int D = 128;
+  static constexpr int NB = (16 / NG) < 4 ? (16 / NG) : 4;   // blocks per set
+  static constexpr int NCOL = NB * NG;                         // used score columns
+  static constexpr int TPB = G / 16;                           // 16-token tiles per block
+  static constexpr int SET_TOK = NB * G;
+  static constexpr int KS_SET = SET_TOK / 32;                  // P.V k-steps per set
+  static constexpr int NGR = D / GV;                           // value groups
+  static constexpr int KROW = D * KB / 8;                      // key code bytes per token
+  static constexpr int KLANE = KROW / 4;                       // per lane group
+  static constexpr int VLANE = 8 * VB;                         // value code bytes per lane per k-step
+  // record sections
+  static constexpr int REC_KC = 0;
+  static constexpr int REC_KS = G * KROW;
+  static constexpr int REC_KZ = REC_KS + 2 * D;
+  static constexpr int REC_VC = REC_KZ + 2 * D;
+  static constexpr int REC_VS = REC_VC + G * D * VB / 8;
+  static constexpr int REC_VZ = REC_VS + 2 * NGR * G;
+  static constexpr int REC = REC_VZ + 2 * NGR * G;
+  // per-wave LDS (bytes)
+  static constexpr int LDS_Q = NG * D * 4;
+  static constexpr int LDS_A = KS_SET * NGR * 4 * 2 * NG * 16;
+  static constexpr int LDS_O = 2 * NG * D * 4;
+  static constexpr int LDS_P = kRingChunk * NG * 4;
+  static constexpr int LDS_BUF = (LDS_A > LDS_O ? (LDS_A > LDS_P ? LDS_A : LDS_P) : (LDS_O > LDS_P ? LDS_O : LDS_P));
+  static constexpr int LDS_ALPHA = 16 * 4;
+  static constexpr int LDS_LAM = NG * NGR * 4;
+  static constexpr int LDS_ZERO = 16;
+  static constexpr int LDS_WAVE = LDS_Q + LDS_BUF + LDS_ALPHA + LDS_LAM + LDS_ZERO;
+  static_assert(NG == 1 || NG == 2 || NG == 4 || NG == 6 || NG == 8, "column reductions exist for these groups");
+  static_assert(NB >= 2, "query group must fit two blocks in 16 columns");
+  static_assert(G % 16 == 0 && SET_TOK % 32 == 0, "sets must be whole P.V k-steps");
+  static_assert(GV >= 16 && D % GV == 0, "value groups must cover whole 16-channel tiles");
+};
+
+// Pointer to block `blk` of (b, h); nullptr if a paged entry is out of range.
+template <class C>
+__device__ __forceinline__ const uint8_t* rec_ptr(const Geom& g, const uint8_t* blocks, const int32_t* table, int b,
+                                                  int h, int blk) {
+  if (table == nullptr) return blocks + (((size_t)b * g.Hkv + h) * g.max_blocks + blk) * (size_t)C::REC;
+  const int page = table[(size_t)b * g.max_blocks + blk];
+  if (page < 0 || page >= g.num_pages) return nullptr;
+  return blocks + ((size_t)page * g.Hkv + h) * (size_t)C::REC;
+}
+
+template <int NBYTES>
+struct Chunk;
+template <>
+struct Chunk<8> {
+  uint2 v;
+};
+template <>
+struct Chunk<16> {
+  uint4 v;
+};
+template <>
+struct Chunk<32> {
+  uint4 a, b;
+};
+template <int NBYTES>
+__device__ __forceinline__ Chunk<NBYTES> load_chunk(const uint8_t* p) {
+  Chunk<NBYTES> c;
+  if constexpr (NBYTES == 8) {
+    c.v = *reinterpret_cast<const uint2*>(p);
+  } else if constexpr (NBYTES == 16) {
+    c.v = *reinterpret_cast<const uint4*>(p);
+  } else {
+    c.a = *reinterpret_cast<const uint4*>(p);
+    c.b = *reinterpret_cast<const uint4*>(p + 16);
+  }
+  return c;
+}
+
+// Key-code A operand of k-step ks from a lane's chunk of one token row
+// (channels 32g .. 32g+31): k position kperm(e) of k-step ks is channel
+// 32g + 8ks + e.
+template <class C>
+__device__ __forceinline__ void key_operands(const Chunk<C::KLANE>& ch, uint4 (&a)[4]) {
+  if constexpr (C::KB == 2) {
+    unpack_int2_word(ch.v.x, a[0], a[1]);
+    unpack_int2_word(ch.v.y, a[2], a[3]);
+  } else {
+    a[0] = unpack_int4_word(ch.v.x);
+    a[1] = unpack_int4_word(ch.v.y);
+    a[2] = unpack_int4_word(ch.v.z);
+    a[3] = unpack_int4_word(ch.v.w);
+  }
+}
+// Value-code B operands of the 8 column tiles (channel 16nt + n) from a lane's
+// chunk: 8 channels x 8 tokens.
+template <class C>
+__device__ __forceinline__ void value_operands(const Chunk<C::VLANE>& ch, uint4 (&bop)[8]) {
+  if constexpr (C::VB == 2) {
+    unpack_int2_word(ch.v.x, bop[0], bop[1]);
+    unpack_int2_word(ch.v.y, bop[2], bop[3]);
+    unpack_int2_word(ch.v.z, bop[4], bop[5]);
+    unpack_int2_word(ch.v.w, bop[6], bop[7]);
+  } else {
+    bop[0] = unpack_int4_word(ch.a.x);
+    bop[1] = unpack_int4_word(ch.a.y);
+    bop[2] = unpack_int4_word(ch.a.z);
+    bop[3] = unpack_int4_word(ch.a.w);
+    bop[4] = unpack_int4_word(ch.b.x);
+    bop[5] = unpack_int4_word(ch.b.y);
+    bop[6] = unpack_int4_word(ch.b.z);
+    bop[7] = unpack_int4_word(ch.b.w);
+  }
+}
+
+template <class C>
+__device__ __forceinline__ float in_val(uint32_t bits16) {
+  return C::BF16 ? __uint_as_float(bits16 << 16) : (float)__builtin_bit_cast(_Float16, (uint16_t)bits16);
+}
+
+// ------------------------------------------------------------------------------------
+// The kernel. One wave = one work item; 4 waves per workgroup share the item
+// table in LDS and nothing else.
+// ------------------------------------------------------------------------------------
+template <class C>
+__global__ __launch_bounds__(256) void decode_fast_kernel(Geom g, const uint8_t* __restrict__ blocks,
+                                                          const int32_t* __restrict__ table,
+                                                          const uint16_t* __restrict__ k_ring,
+                                                          const uint16_t* __restrict__ v_ring,
+                                                          const int32_t* __restrict__ state,
+                                                          const uint16_t* __restrict__ q, float qscale, int bps,
+                                                          int nq_max, int nr_max, float* __restrict__ ws) {
+  constexpr int NG = C::NG, D = C::D, NB = C::NB, TPB = C::TPB, NGR = C::NGR, KS_SET = C::KS_SET;
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  int* prefix = reinterpret_cast<int*>(smem);
+  const int pre_bytes = ((g.B + 1) * 4 + 15) & ~15;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int gq = lane >> 4, n = lane & 15;   // lane group (k quarter / output row quad), column
+  uint8_t* wl = smem + pre_bytes + wave * C::LDS_WAVE;
+  float* qs = reinterpret_cast<float*>(wl);                                   // [NG][D] scaled query
+  uint8_t* buf = wl + C::LDS_Q;                                               // A operands / outputs / ring p
+  float* alpha_l = reinterpret_cast<float*>(buf + C::LDS_BUF);                // [16]
+  float* lam_l = alpha_l + 16;                                                // [NG][NGR]
+  uint4* zero16 = reinterpret_cast<uint4*>(lam_l + NG * NGR);
+
+  build_prefix(g, state, bps, kRingChunk, nq_max, nr_max, prefix, blockIdx.x == 0);
+  const int w = blockIdx.x * kWaves + wave;
+  if (w >= g.Hkv * prefix[g.B]) return;
+  const ItemRef it = locate_item(g, prefix, w);
+  const int b = it.b, h = it.h;
+  const int Q = state[4 * b + kStateQ], S = state[4 * b + kStateS];
+  const int nblk = Q / g.G;
+  bool unused_flag = false;
+  const ItemCounts cnt = items_of(Q, S, g.G, bps, kRingChunk, nq_max, nr_max, &unused_flag);
+  if (lane == 0) *zero16 = make_uint4(0, 0, 0, 0);
+
+  // scaled query, log2 units: q' = q * softmax_scale * log2(e)
+  for (int idx = lane; idx < NG * D; idx += 64) {
+    const int j = idx / D, c = idx % D;
+    qs[idx] = in_val<C>(q[((size_t)b * g.Hq + h * NG + j) * D + c]) * qscale;
+  }
+  wave_lds_fence();
+
+  float* out_part = ws + (size_t)w * NG * (D + 2);
+
+  if (it.item >= cnt.nq) {
+    // ===================== ring chunk: full-precision tokens =====================
+    const int t0 = Q + (it.item - cnt.nq) * kRingChunk;
+    const int t1 = min(S, t0 + kRingChunk);
+    const int pair = b * g.Hkv + h;
+    // B operand: q' hi/lo, column n = head, k position e of k-step ks = channel 32gq + 8ks + e
+    uint4 bq_hi[4], bq_lo[4];
+    float escale = 1.0f;
+    if constexpr (!C::BF16) {
+      // fp16 operands: bring the largest |q'| near 2^14 (exact power of two)
+      float mx = 0.f;
+      for (int idx = lane; idx < NG * D; idx += 64) mx = fmaxf(mx, fabsf(qs[idx]));
+      mx = wave_max(mx);
+      const int e = mx > 0.f ? 14 - ilogbf(mx) : 0;
+      escale = ldexpf(1.0f, e);
+    }
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      uint32_t hi[4], lo[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int c = 32 * gq + 8 * ks + 2 * r;
+        const float x0 = n < NG ? qs[n * D + c] * escale : 0.f;
+        const float x1 = n < NG ? qs[n * D + c + 1] * escale : 0.f;
+        if constexpr (C::BF16) split_bf16(x0, x1, hi[r], lo[r]);
+        else split_f16(x0, x1, hi[r], lo[r]);
+      }
+      bq_hi[ks] = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+      bq_lo[ks] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+    }
+    float s[2][4];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      const int t = t0 + 16 * tt + n;   // A row = token
+      const bool tv = t < t1;
+      const uint16_t* krow = k_ring + ((size_t)pair * g.C + (tv ? t % g.C : 0)) * D + 32 * gq;
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        uint4 a = tv ? *reinterpret_cast<const uint4*>(krow + 8 * ks) : make_uint4(0, 0, 0, 0);
+        if constexpr (C::BF16) {
+          acc = mfma_bf16(a, bq_hi[ks], acc);
+          acc = mfma_bf16(a, bq_lo[ks], acc);
+        } else {
+          acc = mfma_f16(a, bq_hi[ks], acc);
+          acc = mfma_f16(a, bq_lo[ks], acc);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int tok = t0 + 16 * tt + 4 * gq + i;   // D row = token, column n = head
+        s[tt][i] = (n < NG && tok < t1) ? acc[i] / escale : -INFINITY;
+      }
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[tt][i]);
+    mx = reduce_rows(mx, OpMax{});
+    float lsum = 0.f;
+    float* pl = reinterpret_cast<float*>(buf);   // [32 tokens][NG]
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float p = s[tt][i] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(s[tt][i] - mx);
+        lsum += p;
+        if (n < NG) pl[(16 * tt + 4 * gq + i) * NG + n] = p;
+      }
+    lsum = reduce_rows(lsum, OpAdd{});
+    wave_lds_fence();
+    // P.V on the vector ALUs: lane owns channels 2*lane, 2*lane+1
+    float o0[NG], o1[NG];
+#pragma unroll
+    for (int j = 0; j < NG; ++j) o0[j] = o1[j] = 0.f;
+    for (int t = t0; t < t1; ++t) {
+      const uint32_t vv = *reinterpret_cast<const uint32_t*>(v_ring + ((size_t)pair * g.C + t % g.C) * D + 2 * lane);
+      const float v0 = in_val<C>(vv & 0xffffu), v1 = in_val<C>(vv >> 16);
+      const float* prow = pl + (t - t0) * NG;
+#pragma unroll
+      for (int j = 0; j < NG; ++j) {
+        const float p = prow[j];
+        o0[j] = fmaf(p, v0, o0[j]);
+        o1[j] = fmaf(p, v1, o1[j]);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < NG; ++j) {
+      float* dst = out_part + j * (D + 2);
+      *reinterpret_cast<float2*>(dst + 2 * lane) = make_float2(o0[j], o1[j]);
+    }
+    if (gq == 0 && n < NG) {
+      out_part[n * (D + 2) + D] = mx;
+      out_part[n * (D + 2) + D + 1] = lsum;
+    }
+    return;
+  }
+
+  // ===================== quantized blocks [blk_begin, blk_end) =====================
+  const int blk_begin = it.item * bps;
+  const int blk_end = min(blk_begin + bps, nblk);
+  const int nsets = (blk_end - blk_begin + NB - 1) / NB;
+  const int cbk = n / NG, chd = n % NG;   // column's block within the set, column's head
+  const bool col_used = n < C::NCOL;
+
+  // block record of set `si`, block `bi` (clamped into the item's range)
+  auto rec_at = [&](int si, int bi) -> const uint8_t* {
+    int blk = blk_begin + si * NB + bi;
+    if (blk >= blk_end) blk = blk_end - 1;
+    const uint8_t* p = rec_ptr<C>(g, blocks, table, b, h, blk);
+    return p != nullptr ? p : rec_ptr<C>(g, blocks, table, b, h, blk_begin);
+  };
+  auto blk_ok = [&](int si, int bi) -> bool {
+    const int blk = blk_begin + si * NB + bi;
+    if (blk >= blk_end) return false;
+    return table == nullptr || rec_ptr<C>(g, blocks, table, b, h, blk) != nullptr;
+  };
+
+  // ---- register buffers for one set, refilled right after their last use ----
+  uint4 ksz[8];                          // K scale (4 x 16 B) and zero (4 x 16 B), channels 32gq..+31, column block
+  Chunk<C::KLANE> kc[NB][TPB];           // key code rows
+  uint2 vsz[TPB][NGR][2];                // V scale / zero of the lane's 4 tokens per tile and group
+  Chunk<C::VLANE> vc[KS_SET];            // value code chunks
+
+  auto load_ksz = [&](int si) {
+    const uint8_t* p = rec_at(si, cbk);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      ksz[k] = *reinterpret_cast<const uint4*>(p + C::REC_KS + 64 * gq + 16 * k);
+      ksz[4 + k] = *reinterpret_cast<const uint4*>(p + C::REC_KZ + 64 * gq + 16 * k);
+    }
+  };
+  auto load_kc = [&](int si) {
+#pragma unroll
+    for (int bi = 0; bi < NB; ++bi) {
+      const uint8_t* p = rec_at(si, bi);
+#pragma unroll
+      for (int tt = 0; tt < TPB; ++tt)
+        kc[bi][tt] = load_chunk<C::KLANE>(p + C::REC_KC + (16 * tt + n) * C::KROW + gq * C::KLANE);
+    }
+  };
+  auto load_vsz = [&](int si) {
+    const uint8_t* p = rec_at(si, cbk);
+#pragma unroll
+    for (int tt = 0; tt < TPB; ++tt)
+#pragma unroll
+      for (int j = 0; j < NGR; ++j) {
+        const int off = (j * C::G + 16 * tt + 4 * gq) * 2;
+        vsz[tt][j][0] = *reinterpret_cast<const uint2*>(p + C::REC_VS + off);
+        vsz[tt][j][1] = *reinterpret_cast<const uint2*>(p + C::REC_VZ + off);
+      }
+  };
+  auto load_vc = [&](int si) {
+#pragma unroll
+    for (int ks = 0; ks < KS_SET; ++ks) {
+      const int tok = 32 * ks + 8 * gq;   // set-relative first token of this lane group's run
+      const uint8_t* p = rec_at(si, tok / C::G);
+      const int g8 = (tok % C::G) / 8;
+      vc[ks] = load_chunk<C::VLANE>(p + C::REC_VC + (g8 * 16 + n) * C::VLANE);
+    }
+  };
+
+  if (nsets > 0) {
+    load_ksz(0);
+    load_kc(0);
+    load_vsz(0);
+    load_vc(0);
+  }
+
+  // running state: per lane for its column's head
+  float m_ref = -INFINITY, l_part = 0.f, lam[NGR];
+#pragma unroll
+  for (int j = 0; j < NGR; ++j) lam[j] = 0.f;
+  f32x4 dpv[8];
+#pragma unroll
+  for (int nt = 0; nt < 8; ++nt) dpv[nt] = {0.f, 0.f, 0.f, 0.f};
+
+  for (int si = 0; si < nsets; ++si) {
+    const bool more = si + 1 < nsets;
+    const bool my_blk = col_used && blk_ok(si, cbk);
+
+    // ---- B operand: q~ = q' * s_K (hi/lo) and kappa = q' . z_K for the column ----
+    uint4 bhi[4], blo[4];
+    float kap = 0.f;
+    {
+      const float* qrow = qs + chd * D + 32 * gq;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const uint4 sv = ksz[ks], zv = ksz[4 + ks];   // channels 32gq + 8ks + (0..7) as fp16 pairs
+        const float4 qa = *reinterpret_cast<const float4*>(qrow + 8 * ks);
+        const float4 qb = *reinterpret_cast<const float4*>(qrow + 8 * ks + 4);
+        const float qv[8] = {qa.x, qa.y, qa.z, qa.w, qb.x, qb.y, qb.z, qb.w};
+        const uint32_t s2[4] = {sv.x, sv.y, sv.z, sv.w}, z2[4] = {zv.x, zv.y, zv.z, zv.w};
+        float x[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float se = (e & 1) ? hi_half_f16(s2[e >> 1]) : lo_half_f16(s2[e >> 1]);
+          const float ze = (e & 1) ? hi_half_f16(z2[e >> 1]) : lo_half_f16(z2[e >> 1]);
+          x[e] = qv[e] * se;
+          kap = fmaf(qv[e], ze, kap);
+        }
+        uint32_t hi[4], lo[4];
+        // register r holds k positions 2r, 2r+1 = elements kperm(2r), kperm(2r+1)
+        split_bf16(x[0], x[2], hi[0], lo[0]);
+        split_bf16(x[1], x[3], hi[1], lo[1]);
+        split_bf16(x[4], x[6], hi[2], lo[2]);
+        split_bf16(x[5], x[7], hi[3], lo[3]);
+        bhi[ks] = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+        blo[ks] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+      }
+      kap = reduce_rows(kap, OpAdd{});
+    }
+    if (more) load_ksz(si + 1);
+
+    // ---- scores: D[token][column] for every tile of every block of the set ----
+    float sc[TPB][4];
+#pragma unroll
+    for (int tt = 0; tt < TPB; ++tt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sc[tt][i] = -INFINITY;
+#pragma unroll
+    for (int bi = 0; bi < NB; ++bi) {
+      const bool mine = cbk == bi;
+#pragma unroll
+      for (int tt = 0; tt < TPB; ++tt) {
+        uint4 a[4];
+        key_operands<C>(kc[bi][tt], a);
+        f32x4 acc = {kap, kap, kap, kap};
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+          acc = mfma_bf16(a[ks], bhi[ks], acc);
+          acc = mfma_bf16(a[ks], blo[ks], acc);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sc[tt][i] = mine ? acc[i] : sc[tt][i];
+      }
+    }
+    if (more) load_kc(si + 1);
+    if (!my_blk) {
+#pragma unroll
+      for (int tt = 0; tt < TPB; ++tt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sc[tt][i] = -INFINITY;
+    }
+
+    // ---- online softmax (log2 units) ----
+    float mx = -INFINITY;
+#pragma unroll
+    for (int tt = 0; tt < TPB; ++tt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sc[tt][i]);
+    mx = reduce_head<NG>(mx, n, OpMax{});
+    const float m_new = fmaxf(m_ref, mx);
+    const float alpha = (m_new == -INFINITY || m_ref == -INFINITY) ? (m_new == -INFINITY ? 1.f : 0.f)
+                                                                   : __builtin_amdgcn_exp2f(m_ref - m_new);
+    m_ref = m_new;
+    float p[TPB][4];
+    float psum = 0.f;
+#pragma unroll
+    for (int tt = 0; tt < TPB; ++tt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        p[tt][i] = sc[tt][i] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sc[tt][i] - m_new);
+        psum += p[tt][i];
+      }
+    l_part = l_part * alpha + psum;
+#pragma unroll
+    for (int j = 0; j < NGR; ++j) lam[j] *= alpha;
+    // rescale of the P.V accumulators: row r of D holds head r % NG (hi) or (lo)
+    if (gq == 0) alpha_l[n] = n < 2 * NG ? alpha : 1.f;
+    wave_lds_fence();
+    {
+      const float4 ar = *reinterpret_cast<const float4*>(alpha_l + 4 * gq);
+      const float a4[4] = {ar.x, ar.y, ar.z, ar.w};
+#pragma unroll
+      for (int nt = 0; nt < 8; ++nt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dpv[nt][i] *= a4[i];
+    }
+
+    // ---- p~ = p * s_V per value group, hi/lo, into the P.V A operand in LDS ----
+    // (every used column writes, so the slots of a missing block hold zeros)
+    if (col_used) {
+#pragma unroll
+      for (int tt = 0; tt < TPB; ++tt) {
+        const int T = cbk * C::G + 16 * tt + 4 * gq;   // set-relative token of p[tt][0]
+        const int ks = T >> 5, gp = (T >> 3) & 3, kvb = (T >> 2) & 1;
+#pragma unroll
+        for (int j = 0; j < NGR; ++j) {
+          const uint2 sv = vsz[tt][j][0], zv = vsz[tt][j][1];
+          const float s4[4] = {lo_half_f16(sv.x), hi_half_f16(sv.x), lo_half_f16(sv.y), hi_half_f16(sv.y)};
+          const float z4[4] = {lo_half_f16(zv.x), hi_half_f16(zv.x), lo_half_f16(zv.y), hi_half_f16(zv.y)};
+          float x[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            x[i] = p[tt][i] * s4[i];
+            lam[j] = fmaf(p[tt][i], z4[i], lam[j]);
+          }
+          uint32_t hi02, lo02, hi13, lo13;
+          split_bf16(x[0], x[2], hi02, lo02);
+          split_bf16(x[1], x[3], hi13, lo13);
+          uint8_t* base = buf + (((ks * NGR + j) * 4 + gp) * 2 * NG) * 16 + kvb * 8;
+          *reinterpret_cast<uint2*>(base + chd * 16) = make_uint2(hi02, hi13);
+          *reinterpret_cast<uint2*>(base + (NG + chd) * 16) = make_uint2(lo02, lo13);
+        }
+      }
+    }
+    if (more) load_vsz(si + 1);
+    wave_lds_fence();
+
+    // ---- P.V: D[head hi|lo][channel] += p~ . code ----
+#pragma unroll
+    for (int ks = 0; ks < KS_SET; ++ks) {
+      uint4 av[NGR];
+#pragma unroll
+      for (int j = 0; j < NGR; ++j)
+        av[j] = n < 2 * NG ? *reinterpret_cast<const uint4*>(buf + (((ks * NGR + j) * 4 + gq) * 2 * NG + n) * 16)
+                           : *zero16;
+      uint4 bv[8];
+      value_operands<C>(vc[ks], bv);
+#pragma unroll
+      for (int nt = 0; nt < 8; ++nt) dpv[nt] = mfma_bf16(av[(16 * nt) / C::GV], bv[nt], dpv[nt]);
+    }
+    if (more) load_vc(si + 1);
+    wave_lds_fence();
+  }
+
+  // ---- item result: per head h', o = D[h'] + D[NG+h'] + lam(h', group) ----
+  l_part = reduce_head<NG>(col_used ? l_part : 0.f, n, OpAdd{});
+#pragma unroll
+  for (int j = 0; j < NGR; ++j) lam[j] = reduce_head<NG>(col_used ? lam[j] : 0.f, n, OpAdd{});
+  float* ol = reinterpret_cast<float*>(buf);   // [2NG][D]
+#pragma unroll
+  for (int nt = 0; nt < 8; ++nt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 4 * gq + i;
+      if (r < 2 * NG) ol[r * D + 16 * nt + n] = dpv[nt][i];
+    }
+  if (gq == 0 && n < NG) {
+#pragma unroll
+    for (int j = 0; j < NGR; ++j) lam_l[n * NGR + j] = lam[j];
+    out_part[n * (D + 2) + D] = m_ref;
+    out_part[n * (D + 2) + D + 1] = l_part;
+  }
+  wave_lds_fence();
+#pragma unroll
+  for (int j = 0; j < NG; ++j)
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int c = lane + 64 * k;
+      out_part[j * (D + 2) + c] = ol[j * D + c] + ol[(NG + j) * D + c] + lam_l[j * NGR + c / C::GV];
+    }
+}
+
+template <class C>
+hipError_t launch_fast(const Geom& g, const kvq_cache& c, const void* q, float scale, int bps, int nq_max,
+                       int nr_max, size_t items_max, void* ws, hipStream_t s) {
+  const int wgs = (int)((items_max + kWaves - 1) / kWaves);
+  const size_t lds = (size_t)(((g.B + 1) * 4 + 15) & ~15) + (size_t)kWaves * C::LDS_WAVE;
+  hipLaunchKernelGGL((decode_fast_kernel<C>), dim3(wgs), dim3(256), lds, s, g,
+                     static_cast<const uint8_t*>(c.blocks), c.block_table, static_cast<const uint16_t*>(c.k_ring),
+                     static_cast<const uint16_t*>(c.v_ring), c.state, static_cast<const uint16_t*>(q),
+                     scale * kLog2e, bps, nq_max, nr_max, static_cast<float*>(ws));
+  return hipGetLastError();
+}
+
+}  // namespace fast
+}  // namespace kvq

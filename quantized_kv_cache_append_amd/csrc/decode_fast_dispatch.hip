@@ -1,0 +1,56 @@
+// Instantiations of the MFMA decode path (decode_fast.h) and their dispatch.
+//
+// One instantiation per cache configuration the workloads use (query group,
+// key/value bits, key and value group sizes, input dtype); any other
+// configuration runs the generic kernel in decode.hip.
+#include "decode_fast.h"
+
+namespace kvq {
+
+namespace {
+
+struct FastEntry {
+  int ng, kb, vb, G, GV, dtype;
+  int nb_set;
+  hipError_t (*launch)(const Geom&, const kvq_cache&, const void*, float, int, int, int, size_t, void*,
+                       hipStream_t);
+};
+
+template <int NG, int KB, int VB, int G, int GV, bool BF16>
+constexpr FastEntry entry() {
+  using C = fast::Cfg<NG, KB, VB, G, GV, BF16>;
+  return FastEntry{NG, KB, VB, G, GV, BF16 ? KVQ_BF16 : KVQ_F16, C::NB, &fast::launch_fast<C>};
+}
+
+constexpr FastEntry kFast[] = {
+    entry<1, 2, 2, 32, 32, false>(),   // MHA, INT2, G = G_V = 32, fp16 (a Llama-2-7B-shaped layer)
+    entry<1, 2, 2, 32, 32, true>(),
+    entry<4, 4, 4, 32, 32, true>(),    // GQA 4, INT4 (a Llama-3-8B-shaped layer)
+    entry<4, 2, 2, 32, 32, true>(),    // GQA 4, INT2
+    entry<8, 2, 2, 64, 64, true>(),    // GQA 8, INT2, G = G_V = 64 (a 70B-shaped layer)
+    entry<6, 4, 2, 16, 32, true>(),    // GQA 6, INT4 keys / INT2 values, 16-token pages
+};
+
+const FastEntry* find(const Geom& g) {
+  if (g.d != 128) return nullptr;
+  for (const FastEntry& e : kFast)
+    if (e.ng == g.ng && e.kb == g.kb && e.vb == g.vb && e.G == g.G && e.GV == g.GV && e.dtype == g.dtype) return &e;
+  return nullptr;
+}
+
+}  // namespace
+
+bool fast_supported(const Geom& g, int* blocks_per_set) {
+  const FastEntry* e = find(g);
+  if (e && blocks_per_set) *blocks_per_set = e->nb_set;
+  return e != nullptr;
+}
+
+hipError_t launch_decode_fast(const Geom& g, const kvq_cache& c, const void* q, float scale, const DecodePlan& p,
+                              void* ws, hipStream_t s) {
+  const FastEntry* e = find(g);
+  if (e == nullptr) return hipErrorInvalidValue;
+  return e->launch(g, c, q, scale, p.bps, p.nq_max, p.nr_max, p.items_max, ws, s);
+}
+
+}  // namespace kvq

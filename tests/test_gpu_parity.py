@@ -114,8 +114,9 @@ def test_constant_groups_quantize_exactly():
     check_decode(out, spec, to_np(inp.q), to_np(k), to_np(v), [S], scale=default_scale(w.head_dim))
 
 
+@pytest.mark.parametrize("fused", [False, True])
 @pytest.mark.parametrize("wname", ["llama2-7b-layer", "ragged-paged"])
-def test_decode_steps_across_flush(wname):
+def test_decode_steps_across_flush(wname, fused):
     """Prefill, then decode steps of append(1) -> flush -> attention, across a
     block boundary; every step's output and the final records match."""
     over = dict(batch=2, num_q_heads=4, num_kv_heads=2) if wname == "llama2-7b-layer" else \
@@ -133,8 +134,11 @@ def test_decode_steps_across_flush(wname):
         idx = torch.tensor(lengths) + st
         kn = torch.stack([inp.k[b, :, idx[b]:idx[b] + 1] for b in range(w.batch)]).contiguous()
         vn = torch.stack([inp.v[b, :, idx[b]:idx[b] + 1] for b in range(w.batch)]).contiguous()
-        cache.append(kn.cuda(), vn.cuda())
-        cache.flush()
+        if fused:
+            cache.append_flush(kn.cuda(), vn.cuda())
+        else:
+            cache.append(kn.cuda(), vn.cuda())
+            cache.flush()
         q = W.new_tokens(w, inp, 1, device="cpu", seed=6, step=st)[2]
         out = cache.decode(q.cuda())
         cur = [s + st + 1 for s in lengths]
@@ -152,3 +156,41 @@ def test_ring_overflow_sets_device_error():
     torch.cuda.synchronize()
     assert cache.read_device_error() & 1
     assert cache.lengths() == ([0], [0])
+
+
+def test_fused_append_flush_ragged_counts_match_separate_calls():
+    """Ragged n_new through the fused call gives the same cache bytes as
+    append + flush, and both match the oracle."""
+    w = W.WORKLOADS["ragged-paged"].replace(batch=4, num_q_heads=12, num_kv_heads=2)
+    lengths = [70, 81, 200, 64]
+    full = [s + 40 for s in lengths]
+    inp = W.make_layer(w, device="cpu", seed=8, lengths=full)
+    caches = []
+    for fused in (False, True):
+        cache = make_cache(w, lengths, 64, extra_tokens=40)   # ring R + G - 1 + 64 takes 58 new rows
+        cache.prefill(inp.k.cuda(), inp.v.cuda(), lengths, 64)
+        cur = list(lengths)
+        for step, n in enumerate([1, 3, 0, 7, 29]):
+            counts = torch.tensor([n, max(n - 1, 0), n, 2 * n], dtype=torch.int32)
+            nmax = int(counts.max())
+            kn = torch.zeros(w.batch, w.num_kv_heads, max(nmax, 1), w.head_dim, dtype=w.torch_dtype)
+            vn = torch.zeros_like(kn)
+            for b in range(w.batch):
+                c = int(counts[b])
+                kn[b, :, :c] = inp.k[b, :, cur[b]:cur[b] + c]
+                vn[b, :, :c] = inp.v[b, :, cur[b]:cur[b] + c]
+            if fused:
+                cache.append_flush(kn[:, :, :max(nmax, 1)].contiguous().cuda(),
+                                   vn[:, :, :max(nmax, 1)].contiguous().cuda(), counts.cuda())
+            else:
+                cache.append(kn.cuda(), vn.cuda(), counts.cuda())
+                cache.flush()
+            cur = [cur[b] + int(counts[b]) for b in range(w.batch)]
+        torch.cuda.synchronize()
+        assert cache.read_device_error() == 0
+        caches.append(cache)
+    assert torch.equal(caches[0].blocks, caches[1].blocks)
+    assert caches[0].lengths() == caches[1].lengths()
+    spec = spec_of(w, caches[1].cfg.res_capacity)
+    pairs = [(b, h) for b in range(w.batch) for h in range(w.num_kv_heads)]
+    check_records(caches[1], spec, to_np(inp.k), to_np(inp.v), cur, pairs)

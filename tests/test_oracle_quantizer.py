@@ -184,8 +184,10 @@ def test_record_layout_hand_offsets():
     assert w[0] == 0xC0000000 and w[1] == 0x00000003 and not w[2:].any()
     ks = rec[64:96].view(np.float16)
     assert ks[0] == 1.0 and ks[15] == 1.0 and not ks[1:15].any()
+    # V codes, 8-token chunks: (t=2, c=5) at position ((0*16 + 5)*1 + 0)*8 + 2 = 42
+    # -> bit 84 -> word 2, bit 20
     vw = rec[128:192].view(np.uint32)
-    assert vw[5] == (3 << 4) and not np.delete(vw, 5).any()
+    assert vw[2] == (3 << 20) and not np.delete(vw, 2).any()
     vs = rec[192:224].view(np.float16)
     assert vs[2] == 1.0 and not np.delete(vs, 2).any()
 
@@ -218,9 +220,23 @@ def test_record_layout_value_scales_are_group_major():
     rec = kivi.block_to_bytes(kivi.quantize_block(spec, K, V))
     kc = 16 * 32 * 4 // 8            # 256 B of key codes (4 words per token)
     vc_off = kc + 2 * 64             # after key scale and zero (32 fp16 each)
-    vw = rec[vc_off:vc_off + 32 * 4].view(np.uint32)     # 32 channels x 1 word
-    assert vw[21] == (3 << 4) and not np.delete(vw, 21).any()
+    # (t=2, c=21): position ((0*16 + 5)*2 + 1)*8 + 2 = 90 -> bit 180 -> word 5, bit 20
+    vw = rec[vc_off:vc_off + 32 * 4].view(np.uint32)
+    assert vw[5] == (3 << 20) and not np.delete(vw, 5).any()
     vs = rec[vc_off + 128:vc_off + 128 + 64].view(np.float16).reshape(2, 16)
     assert vs[1, 2] == np.float16(0.5) and np.count_nonzero(vs) == 1
     vz = rec[vc_off + 192:vc_off + 256].view(np.float16)
     assert not vz.any()
+
+
+def test_record_layout_value_codes_second_token_chunk_int4():
+    # G = 16, d = 16, 4-bit values: token 9 (second 8-token chunk), channel 3.
+    spec = _tiny_spec(kb=2, vb=4)
+    K = np.zeros((16, 16), np.float32)
+    V = np.zeros((16, 16), np.float32)
+    V[9, 3] = 15.0                  # group of token 9: range 15 over 15 steps -> code 15
+    rec = kivi.block_to_bytes(kivi.quantize_block(spec, K, V))
+    vc_off = 64 + 32 + 32           # after 16 key words and key scale/zero
+    vw = rec[vc_off:vc_off + 128].view(np.uint32)   # 16 tokens x 16 channels x 4 bits
+    # position ((1*16 + 3)*1 + 0)*8 + 1 = 153 -> bit 612 -> word 19, bit 4
+    assert vw[19] == (15 << 4) and not np.delete(vw, 19).any()
