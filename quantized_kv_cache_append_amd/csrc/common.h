@@ -92,10 +92,12 @@ __device__ __forceinline__ float wave_sum(float v) {
   for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
   return v;
 }
-// Orders this wave's LDS writes before its later LDS reads of other lanes' data.
+// Orders this wave's LDS writes before its later LDS reads of other lanes'
+// data: waits for the wave's outstanding LDS operations only (global loads in
+// flight stay in flight) and keeps the compiler from moving memory accesses
+// across it.
 __device__ __forceinline__ void wave_lds_fence() {
-  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
-  __builtin_amdgcn_wave_barrier();
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 }
 
 // One thread per workgroup calls this after the workgroup's work is done.

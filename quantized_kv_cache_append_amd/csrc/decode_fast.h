@@ -35,6 +35,8 @@
 // each lane's B operand is one contiguous 16- (INT2) or 32-byte (INT4) load.
 #pragma once
 
+#include <type_traits>
+
 #include "common.h"
 #include "decode_items.h"
 
@@ -163,10 +165,10 @@ __device__ __forceinline__ float reduce_rows(float x, Op op) {
   return op(__uint_as_float(r32[0]), __uint_as_float(r32[1]));
 }
 
-template <int NG_, int KB_, int VB_, int G_, int GV_, bool BF16_>
+template <int NG_, int KB_, int VB_, int G_, int GV_, bool BF16_, bool PAGED_>
 struct Cfg {
   static constexpr int NG = NG_, KB = KB_, VB = VB_, G = G_, GV = GV_;
-  static constexpr bool BF16 = BF16_;
+  static constexpr bool BF16 = BF16_, PAGED = PAGED_;
   static constexpr int D = 128;
   static constexpr int NB = (16 / NG) < 4 ? (16 / NG) : 4;   // blocks per set
   static constexpr int NCOL = NB * NG;                         // used score columns
@@ -205,7 +207,7 @@ struct Cfg {
 template <class C>
 __device__ __forceinline__ const uint8_t* rec_ptr(const Geom& g, const uint8_t* blocks, const int32_t* table, int b,
                                                   int h, int blk) {
-  if (table == nullptr) return blocks + (((size_t)b * g.Hkv + h) * g.max_blocks + blk) * (size_t)C::REC;
+  if constexpr (!C::PAGED) return blocks + (((size_t)b * g.Hkv + h) * g.max_blocks + blk) * (size_t)C::REC;
   const int page = table[(size_t)b * g.max_blocks + blk];
   if (page < 0 || page >= g.num_pages) return nullptr;
   return blocks + ((size_t)page * g.Hkv + h) * (size_t)C::REC;
@@ -280,209 +282,207 @@ __device__ __forceinline__ float in_val(uint32_t bits16) {
   return C::BF16 ? __uint_as_float(bits16 << 16) : (float)__builtin_bit_cast(_Float16, (uint16_t)bits16);
 }
 
-// ------------------------------------------------------------------------------------
-// The kernel. One wave = one work item; 4 waves per workgroup share the item
-// table in LDS and nothing else.
-// ------------------------------------------------------------------------------------
+// Scores are in log2 units. The running maximum of a head is only moved (and
+// the accumulated state rescaled) when a new score exceeds it by more than
+// this, so probabilities stay below 2^8 and most sets skip the rescale.
+constexpr float kRescaleLog2 = 8.0f;
+
+// Per-wave LDS regions.
 template <class C>
-__global__ __launch_bounds__(256) void decode_fast_kernel(Geom g, const uint8_t* __restrict__ blocks,
-                                                          const int32_t* __restrict__ table,
-                                                          const uint16_t* __restrict__ k_ring,
-                                                          const uint16_t* __restrict__ v_ring,
-                                                          const int32_t* __restrict__ state,
-                                                          const uint16_t* __restrict__ q, float qscale, int bps,
-                                                          int nq_max, int nr_max, float* __restrict__ ws) {
-  constexpr int NG = C::NG, D = C::D, NB = C::NB, TPB = C::TPB, NGR = C::NGR, KS_SET = C::KS_SET;
-  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  int* prefix = reinterpret_cast<int*>(smem);
-  const int pre_bytes = ((g.B + 1) * 4 + 15) & ~15;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int gq = lane >> 4, n = lane & 15;   // lane group (k quarter / output row quad), column
-  uint8_t* wl = smem + pre_bytes + wave * C::LDS_WAVE;
-  float* qs = reinterpret_cast<float*>(wl);                                   // [NG][D] scaled query
-  uint8_t* buf = wl + C::LDS_Q;                                               // A operands / outputs / ring p
-  float* alpha_l = reinterpret_cast<float*>(buf + C::LDS_BUF);                // [16]
-  float* lam_l = alpha_l + 16;                                                // [NG][NGR]
-  uint4* zero16 = reinterpret_cast<uint4*>(lam_l + NG * NGR);
+struct WaveLds {
+  float* qs;        // [NG][D] query scaled to log2 units
+  uint8_t* buf;     // P.V A operands / item outputs / ring probabilities
+  float* alpha;     // [16] per P.V row
+  float* lam;       // [NG][NGR]
+  uint4* zero16;
+};
 
-  build_prefix(g, state, bps, kRingChunk, nq_max, nr_max, prefix, blockIdx.x == 0);
-  const int w = blockIdx.x * kWaves + wave;
-  if (w >= g.Hkv * prefix[g.B]) return;
-  const ItemRef it = locate_item(g, prefix, w);
-  const int b = it.b, h = it.h;
-  const int Q = state[4 * b + kStateQ], S = state[4 * b + kStateS];
-  const int nblk = Q / g.G;
-  bool unused_flag = false;
-  const ItemCounts cnt = items_of(Q, S, g.G, bps, kRingChunk, nq_max, nr_max, &unused_flag);
-  if (lane == 0) *zero16 = make_uint4(0, 0, 0, 0);
-
-  // scaled query, log2 units: q' = q * softmax_scale * log2(e)
-  for (int idx = lane; idx < NG * D; idx += 64) {
-    const int j = idx / D, c = idx % D;
-    qs[idx] = in_val<C>(q[((size_t)b * g.Hq + h * NG + j) * D + c]) * qscale;
+// ---------------------------------------------------------------------------------
+// A chunk of up to 32 full-precision ring tokens [t0, t1).
+// Scores on MFMA (A = key rows as stored, B = query hi/lo), P.V on the vector ALUs.
+// ---------------------------------------------------------------------------------
+template <class C>
+__device__ __forceinline__ void ring_chunk(const Geom& g, const WaveLds<C>& L, const uint16_t* __restrict__ k_ring,
+                                           const uint16_t* __restrict__ v_ring, int pair, int t0, int t1,
+                                           float* __restrict__ out_part) {
+  constexpr int NG = C::NG, D = C::D;
+  const int lane = threadIdx.x & 63, gq = lane >> 4, n = lane & 15;
+  // B operand: q' hi/lo, column n = head, k position e of k-step ks = channel 32gq + 8ks + e
+  uint4 bq_hi[4], bq_lo[4];
+  float escale = 1.0f;
+  if constexpr (!C::BF16) {
+    // fp16 operands: bring the largest |q'| near 2^14 (an exact power of two)
+    float mx = 0.f;
+    for (int idx = lane; idx < NG * D; idx += 64) mx = fmaxf(mx, fabsf(L.qs[idx]));
+    mx = wave_max(mx);
+    escale = ldexpf(1.0f, mx > 0.f ? 14 - ilogbf(mx) : 0);
   }
-  wave_lds_fence();
-
-  float* out_part = ws + (size_t)w * NG * (D + 2);
-
-  if (it.item >= cnt.nq) {
-    // ===================== ring chunk: full-precision tokens =====================
-    const int t0 = Q + (it.item - cnt.nq) * kRingChunk;
-    const int t1 = min(S, t0 + kRingChunk);
-    const int pair = b * g.Hkv + h;
-    // B operand: q' hi/lo, column n = head, k position e of k-step ks = channel 32gq + 8ks + e
-    uint4 bq_hi[4], bq_lo[4];
-    float escale = 1.0f;
-    if constexpr (!C::BF16) {
-      // fp16 operands: bring the largest |q'| near 2^14 (exact power of two)
-      float mx = 0.f;
-      for (int idx = lane; idx < NG * D; idx += 64) mx = fmaxf(mx, fabsf(qs[idx]));
-      mx = wave_max(mx);
-      const int e = mx > 0.f ? 14 - ilogbf(mx) : 0;
-      escale = ldexpf(1.0f, e);
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    uint32_t hi[4], lo[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int c = 32 * gq + 8 * ks + 2 * r;
+      const float x0 = n < NG ? L.qs[n * D + c] * escale : 0.f;
+      const float x1 = n < NG ? L.qs[n * D + c + 1] * escale : 0.f;
+      if constexpr (C::BF16) split_bf16(x0, x1, hi[r], lo[r]);
+      else split_f16(x0, x1, hi[r], lo[r]);
     }
+    bq_hi[ks] = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+    bq_lo[ks] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+  }
+  float s[2][4];
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt) {
+    const int t = t0 + 16 * tt + n;   // A row = token
+    const bool tv = t < t1;
+    const uint16_t* krow = k_ring + ((size_t)pair * g.C + (tv ? t % g.C : 0)) * D + 32 * gq;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-      uint32_t hi[4], lo[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int c = 32 * gq + 8 * ks + 2 * r;
-        const float x0 = n < NG ? qs[n * D + c] * escale : 0.f;
-        const float x1 = n < NG ? qs[n * D + c + 1] * escale : 0.f;
-        if constexpr (C::BF16) split_bf16(x0, x1, hi[r], lo[r]);
-        else split_f16(x0, x1, hi[r], lo[r]);
-      }
-      bq_hi[ks] = make_uint4(hi[0], hi[1], hi[2], hi[3]);
-      bq_lo[ks] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
-    }
-    float s[2][4];
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-      const int t = t0 + 16 * tt + n;   // A row = token
-      const bool tv = t < t1;
-      const uint16_t* krow = k_ring + ((size_t)pair * g.C + (tv ? t % g.C : 0)) * D + 32 * gq;
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        uint4 a = tv ? *reinterpret_cast<const uint4*>(krow + 8 * ks) : make_uint4(0, 0, 0, 0);
-        if constexpr (C::BF16) {
-          acc = mfma_bf16(a, bq_hi[ks], acc);
-          acc = mfma_bf16(a, bq_lo[ks], acc);
-        } else {
-          acc = mfma_f16(a, bq_hi[ks], acc);
-          acc = mfma_f16(a, bq_lo[ks], acc);
-        }
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int tok = t0 + 16 * tt + 4 * gq + i;   // D row = token, column n = head
-        s[tt][i] = (n < NG && tok < t1) ? acc[i] / escale : -INFINITY;
+      const uint4 a = tv ? *reinterpret_cast<const uint4*>(krow + 8 * ks) : make_uint4(0, 0, 0, 0);
+      if constexpr (C::BF16) {
+        acc = mfma_bf16(a, bq_hi[ks], acc);
+        acc = mfma_bf16(a, bq_lo[ks], acc);
+      } else {
+        acc = mfma_f16(a, bq_hi[ks], acc);
+        acc = mfma_f16(a, bq_lo[ks], acc);
       }
     }
-    float mx = -INFINITY;
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[tt][i]);
-    mx = reduce_rows(mx, OpMax{});
-    float lsum = 0.f;
-    float* pl = reinterpret_cast<float*>(buf);   // [32 tokens][NG]
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float p = s[tt][i] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(s[tt][i] - mx);
-        lsum += p;
-        if (n < NG) pl[(16 * tt + 4 * gq + i) * NG + n] = p;
-      }
-    lsum = reduce_rows(lsum, OpAdd{});
-    wave_lds_fence();
-    // P.V on the vector ALUs: lane owns channels 2*lane, 2*lane+1
-    float o0[NG], o1[NG];
-#pragma unroll
-    for (int j = 0; j < NG; ++j) o0[j] = o1[j] = 0.f;
-    for (int t = t0; t < t1; ++t) {
-      const uint32_t vv = *reinterpret_cast<const uint32_t*>(v_ring + ((size_t)pair * g.C + t % g.C) * D + 2 * lane);
-      const float v0 = in_val<C>(vv & 0xffffu), v1 = in_val<C>(vv >> 16);
-      const float* prow = pl + (t - t0) * NG;
-#pragma unroll
-      for (int j = 0; j < NG; ++j) {
-        const float p = prow[j];
-        o0[j] = fmaf(p, v0, o0[j]);
-        o1[j] = fmaf(p, v1, o1[j]);
-      }
+    for (int i = 0; i < 4; ++i) {
+      const int tok = t0 + 16 * tt + 4 * gq + i;   // D row = token, column n = head
+      s[tt][i] = (n < NG && tok < t1) ? acc[i] / escale : -INFINITY;
     }
+  }
+  float mx = -INFINITY;
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[tt][i]);
+  mx = reduce_rows(mx, OpMax{});
+  float lsum = 0.f;
+  float* pl = reinterpret_cast<float*>(L.buf);   // [32 tokens][NG]
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float p = s[tt][i] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(s[tt][i] - mx);
+      lsum += p;
+      if (n < NG) pl[(16 * tt + 4 * gq + i) * NG + n] = p;
+    }
+  lsum = reduce_rows(lsum, OpAdd{});
+  wave_lds_fence();
+  // P.V on the vector ALUs: lane owns channels 2*lane, 2*lane+1. All the
+  // chunk's value rows are loaded first (independent loads in flight), rows
+  // past t1 read row t0 and get probability 0.
+  uint32_t vv[kRingChunk];
+#pragma unroll
+  for (int u = 0; u < kRingChunk; ++u) {
+    const int t = t0 + u < t1 ? t0 + u : t0;
+    vv[u] = *reinterpret_cast<const uint32_t*>(v_ring + ((size_t)pair * g.C + t % g.C) * D + 2 * lane);
+  }
+  float o0[NG], o1[NG];
+#pragma unroll
+  for (int j = 0; j < NG; ++j) o0[j] = o1[j] = 0.f;
+#pragma unroll
+  for (int u = 0; u < kRingChunk; ++u) {
+    const float v0 = in_val<C>(vv[u] & 0xffffu), v1 = in_val<C>(vv[u] >> 16);
+    const float* prow = pl + u * NG;
 #pragma unroll
     for (int j = 0; j < NG; ++j) {
-      float* dst = out_part + j * (D + 2);
-      *reinterpret_cast<float2*>(dst + 2 * lane) = make_float2(o0[j], o1[j]);
+      const float p = prow[j];   // 0 for rows past t1
+      o0[j] = fmaf(p, v0, o0[j]);
+      o1[j] = fmaf(p, v1, o1[j]);
     }
-    if (gq == 0 && n < NG) {
-      out_part[n * (D + 2) + D] = mx;
-      out_part[n * (D + 2) + D + 1] = lsum;
-    }
-    return;
   }
+#pragma unroll
+  for (int j = 0; j < NG; ++j) {
+    float* dst = out_part + j * (D + 2);
+    *reinterpret_cast<float2*>(dst + 2 * lane) = make_float2(o0[j], o1[j]);
+  }
+  if (gq == 0 && n < NG) {
+    out_part[n * (D + 2) + D] = mx;
+    out_part[n * (D + 2) + D + 1] = lsum;
+  }
+}
 
-  // ===================== quantized blocks [blk_begin, blk_end) =====================
-  const int blk_begin = it.item * bps;
-  const int blk_end = min(blk_begin + bps, nblk);
+// ---------------------------------------------------------------------------------
+// Quantized blocks [blk_begin, blk_end) of one (sequence, kv head), in sets of NB.
+// ---------------------------------------------------------------------------------
+template <class C>
+__device__ __forceinline__ void quant_item(const Geom& g, const WaveLds<C>& L, const uint8_t* __restrict__ blocks,
+                                           const int32_t* __restrict__ table, int b, int h, int blk_begin,
+                                           int blk_end, float* __restrict__ out_part) {
+  constexpr int NG = C::NG, D = C::D, NB = C::NB, TPB = C::TPB, NGR = C::NGR, KS_SET = C::KS_SET;
+  const int lane = threadIdx.x & 63, gq = lane >> 4, n = lane & 15;
   const int nsets = (blk_end - blk_begin + NB - 1) / NB;
   const int cbk = n / NG, chd = n % NG;   // column's block within the set, column's head
   const bool col_used = n < C::NCOL;
 
-  // block record of set `si`, block `bi` (clamped into the item's range)
-  auto rec_at = [&](int si, int bi) -> const uint8_t* {
-    int blk = blk_begin + si * NB + bi;
-    if (blk >= blk_end) blk = blk_end - 1;
-    const uint8_t* p = rec_ptr<C>(g, blocks, table, b, h, blk);
-    return p != nullptr ? p : rec_ptr<C>(g, blocks, table, b, h, blk_begin);
+  // Record of block blk of this pair. The dense store keeps a pair's blocks
+  // contiguous; the paged store looks the page up (an out-of-range page reads
+  // page 0 and the block is masked out). `blk` must lie in [blk_begin, blk_end).
+  const uint8_t* pair_base = blocks + ((size_t)b * g.Hkv + h) * (size_t)g.max_blocks * C::REC;
+  const int32_t* trow = table + (size_t)b * g.max_blocks;
+  auto page_ok = [&](int blk) -> bool {
+    if constexpr (!C::PAGED) return true;
+    const int page = trow[blk];
+    return page >= 0 && page < g.num_pages;
   };
-  auto blk_ok = [&](int si, int bi) -> bool {
-    const int blk = blk_begin + si * NB + bi;
-    if (blk >= blk_end) return false;
-    return table == nullptr || rec_ptr<C>(g, blocks, table, b, h, blk) != nullptr;
+  auto rec_at = [&](int blk) -> const uint8_t* {
+    if constexpr (!C::PAGED) {
+      return pair_base + (size_t)blk * C::REC;
+    } else {
+      int page = trow[blk];
+      page = (page >= 0 && page < g.num_pages) ? page : 0;
+      return blocks + ((size_t)page * g.Hkv + h) * (size_t)C::REC;
+    }
   };
+  const int blk_last = blk_end - 1;
 
   // ---- register buffers for one set, refilled right after their last use ----
-  uint4 ksz[8];                          // K scale (4 x 16 B) and zero (4 x 16 B), channels 32gq..+31, column block
-  Chunk<C::KLANE> kc[NB][TPB];           // key code rows
-  uint2 vsz[TPB][NGR][2];                // V scale / zero of the lane's 4 tokens per tile and group
-  Chunk<C::VLANE> vc[KS_SET];            // value code chunks
+  uint4 ksz[8];                 // K scale (4 x 16 B) and zero (4 x 16 B), channels 32gq..+31, column block
+  Chunk<C::KLANE> kc[NB][TPB];  // key code rows
+  uint2 vsz[TPB][NGR][2];       // V scale / zero of the lane's 4 tokens per tile and group
+  Chunk<C::VLANE> vc[KS_SET];   // value code chunks
 
+  // loaders for set si (blocks clamped into the item)
   auto load_ksz = [&](int si) {
-    const uint8_t* p = rec_at(si, cbk);
+    const uint8_t* p = rec_at(min(blk_begin + si * NB + cbk, blk_last)) + C::REC_KS + 64 * gq;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      ksz[k] = *reinterpret_cast<const uint4*>(p + C::REC_KS + 64 * gq + 16 * k);
-      ksz[4 + k] = *reinterpret_cast<const uint4*>(p + C::REC_KZ + 64 * gq + 16 * k);
+      ksz[k] = *reinterpret_cast<const uint4*>(p + 16 * k);
+      ksz[4 + k] = *reinterpret_cast<const uint4*>(p + (C::REC_KZ - C::REC_KS) + 16 * k);
     }
   };
   auto load_kc = [&](int si) {
+    const int off = C::REC_KC + n * C::KROW + gq * C::KLANE;
 #pragma unroll
     for (int bi = 0; bi < NB; ++bi) {
-      const uint8_t* p = rec_at(si, bi);
+      const uint8_t* p = rec_at(min(blk_begin + si * NB + bi, blk_last)) + off;
 #pragma unroll
-      for (int tt = 0; tt < TPB; ++tt)
-        kc[bi][tt] = load_chunk<C::KLANE>(p + C::REC_KC + (16 * tt + n) * C::KROW + gq * C::KLANE);
+      for (int tt = 0; tt < TPB; ++tt) kc[bi][tt] = load_chunk<C::KLANE>(p + 16 * tt * C::KROW);
     }
   };
   auto load_vsz = [&](int si) {
-    const uint8_t* p = rec_at(si, cbk);
+    const uint8_t* p = rec_at(min(blk_begin + si * NB + cbk, blk_last)) + C::REC_VS + 8 * gq;
 #pragma unroll
     for (int tt = 0; tt < TPB; ++tt)
 #pragma unroll
       for (int j = 0; j < NGR; ++j) {
-        const int off = (j * C::G + 16 * tt + 4 * gq) * 2;
-        vsz[tt][j][0] = *reinterpret_cast<const uint2*>(p + C::REC_VS + off);
-        vsz[tt][j][1] = *reinterpret_cast<const uint2*>(p + C::REC_VZ + off);
+        const int off = (j * C::G + 16 * tt) * 2;
+        vsz[tt][j][0] = *reinterpret_cast<const uint2*>(p + off);
+        vsz[tt][j][1] = *reinterpret_cast<const uint2*>(p + (C::REC_VZ - C::REC_VS) + off);
       }
   };
   auto load_vc = [&](int si) {
 #pragma unroll
     for (int ks = 0; ks < KS_SET; ++ks) {
       const int tok = 32 * ks + 8 * gq;   // set-relative first token of this lane group's run
-      const uint8_t* p = rec_at(si, tok / C::G);
+      // for G >= 32 the k-step lies in one block (wave-uniform); G = 16 spans two
+      const int bi = C::G >= 32 ? (32 * ks) / C::G : tok / C::G;
+      const uint8_t* p = rec_at(min(blk_begin + si * NB + bi, blk_last));
       const int g8 = (tok % C::G) / 8;
       vc[ks] = load_chunk<C::VLANE>(p + C::REC_VC + (g8 * 16 + n) * C::VLANE);
     }
@@ -503,15 +503,19 @@ __global__ __launch_bounds__(256) void decode_fast_kernel(Geom g, const uint8_t*
 #pragma unroll
   for (int nt = 0; nt < 8; ++nt) dpv[nt] = {0.f, 0.f, 0.f, 0.f};
 
-  for (int si = 0; si < nsets; ++si) {
-    const bool more = si + 1 < nsets;
-    const bool my_blk = col_used && blk_ok(si, cbk);
-
+  // One set. With `prefetch`, each register buffer is refilled for the next
+  // set right after its last use here; the last set is peeled off so that the
+  // loads are never under a branch (the compiler then keeps them in flight
+  // across the loop instead of waiting for them).
+  auto run_set = [&](int si, auto prefetch) {
+    constexpr bool PF = decltype(prefetch)::value;
+    const int my_b = blk_begin + si * NB + cbk;
+    const bool my_blk = col_used && my_b < blk_end && page_ok(min(my_b, blk_last));
     // ---- B operand: q~ = q' * s_K (hi/lo) and kappa = q' . z_K for the column ----
     uint4 bhi[4], blo[4];
     float kap = 0.f;
     {
-      const float* qrow = qs + chd * D + 32 * gq;
+      const float* qrow = L.qs + chd * D + 32 * gq;
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
         const uint4 sv = ksz[ks], zv = ksz[4 + ks];   // channels 32gq + 8ks + (0..7) as fp16 pairs
@@ -538,7 +542,7 @@ __global__ __launch_bounds__(256) void decode_fast_kernel(Geom g, const uint8_t*
       }
       kap = reduce_rows(kap, OpAdd{});
     }
-    if (more) load_ksz(si + 1);
+    if constexpr (PF) load_ksz(si + 1);
 
     // ---- scores: D[token][column] for every tile of every block of the set ----
     float sc[TPB][4];
@@ -563,7 +567,7 @@ __global__ __launch_bounds__(256) void decode_fast_kernel(Geom g, const uint8_t*
         for (int i = 0; i < 4; ++i) sc[tt][i] = mine ? acc[i] : sc[tt][i];
       }
     }
-    if (more) load_kc(si + 1);
+    if constexpr (PF) load_kc(si + 1);
     if (!my_blk) {
 #pragma unroll
       for (int tt = 0; tt < TPB; ++tt)
@@ -571,40 +575,41 @@ __global__ __launch_bounds__(256) void decode_fast_kernel(Geom g, const uint8_t*
         for (int i = 0; i < 4; ++i) sc[tt][i] = -INFINITY;
     }
 
-    // ---- online softmax (log2 units) ----
+    // ---- online softmax (log2 units), lazily rescaled ----
     float mx = -INFINITY;
 #pragma unroll
     for (int tt = 0; tt < TPB; ++tt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sc[tt][i]);
     mx = reduce_head<NG>(mx, n, OpMax{});
-    const float m_new = fmaxf(m_ref, mx);
-    const float alpha = (m_new == -INFINITY || m_ref == -INFINITY) ? (m_new == -INFINITY ? 1.f : 0.f)
-                                                                   : __builtin_amdgcn_exp2f(m_ref - m_new);
-    m_ref = m_new;
-    float p[TPB][4];
-    float psum = 0.f;
+    const bool grow = col_used && mx > m_ref + kRescaleLog2;
+    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+      const float m_new = fmaxf(m_ref, mx);
+      const float alpha = (m_ref == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_ref - m_new);
+      m_ref = m_new;
+      l_part *= alpha;
 #pragma unroll
-    for (int tt = 0; tt < TPB; ++tt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        p[tt][i] = sc[tt][i] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sc[tt][i] - m_new);
-        psum += p[tt][i];
-      }
-    l_part = l_part * alpha + psum;
-#pragma unroll
-    for (int j = 0; j < NGR; ++j) lam[j] *= alpha;
-    // rescale of the P.V accumulators: row r of D holds head r % NG (hi) or (lo)
-    if (gq == 0) alpha_l[n] = n < 2 * NG ? alpha : 1.f;
-    wave_lds_fence();
-    {
-      const float4 ar = *reinterpret_cast<const float4*>(alpha_l + 4 * gq);
+      for (int j = 0; j < NGR; ++j) lam[j] *= alpha;
+      // row r of the P.V accumulators holds head r % NG (hi rows, then lo rows)
+      if (gq == 0) L.alpha[n] = n < 2 * NG ? alpha : 1.f;
+      wave_lds_fence();
+      const float4 ar = *reinterpret_cast<const float4*>(L.alpha + 4 * gq);
       const float a4[4] = {ar.x, ar.y, ar.z, ar.w};
 #pragma unroll
       for (int nt = 0; nt < 8; ++nt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) dpv[nt][i] *= a4[i];
     }
+    float p[TPB][4];
+    float psum = 0.f;
+#pragma unroll
+    for (int tt = 0; tt < TPB; ++tt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        p[tt][i] = sc[tt][i] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sc[tt][i] - m_ref);
+        psum += p[tt][i];
+      }
+    l_part += psum;
 
     // ---- p~ = p * s_V per value group, hi/lo, into the P.V A operand in LDS ----
     // (every used column writes, so the slots of a missing block hold zeros)
@@ -627,13 +632,13 @@ __global__ __launch_bounds__(256) void decode_fast_kernel(Geom g, const uint8_t*
           uint32_t hi02, lo02, hi13, lo13;
           split_bf16(x[0], x[2], hi02, lo02);
           split_bf16(x[1], x[3], hi13, lo13);
-          uint8_t* base = buf + (((ks * NGR + j) * 4 + gp) * 2 * NG) * 16 + kvb * 8;
+          uint8_t* base = L.buf + (((ks * NGR + j) * 4 + gp) * 2 * NG) * 16 + kvb * 8;
           *reinterpret_cast<uint2*>(base + chd * 16) = make_uint2(hi02, hi13);
           *reinterpret_cast<uint2*>(base + (NG + chd) * 16) = make_uint2(lo02, lo13);
         }
       }
     }
-    if (more) load_vsz(si + 1);
+    if constexpr (PF) load_vsz(si + 1);
     wave_lds_fence();
 
     // ---- P.V: D[head hi|lo][channel] += p~ . code ----
@@ -642,22 +647,25 @@ __global__ __launch_bounds__(256) void decode_fast_kernel(Geom g, const uint8_t*
       uint4 av[NGR];
 #pragma unroll
       for (int j = 0; j < NGR; ++j)
-        av[j] = n < 2 * NG ? *reinterpret_cast<const uint4*>(buf + (((ks * NGR + j) * 4 + gq) * 2 * NG + n) * 16)
-                           : *zero16;
+        av[j] = *reinterpret_cast<const uint4*>(
+            n < 2 * NG ? L.buf + (((ks * NGR + j) * 4 + gq) * 2 * NG + n) * 16 : reinterpret_cast<uint8_t*>(L.zero16));
       uint4 bv[8];
       value_operands<C>(vc[ks], bv);
 #pragma unroll
       for (int nt = 0; nt < 8; ++nt) dpv[nt] = mfma_bf16(av[(16 * nt) / C::GV], bv[nt], dpv[nt]);
     }
-    if (more) load_vc(si + 1);
+    if constexpr (PF) load_vc(si + 1);
     wave_lds_fence();
-  }
+  };
+
+  for (int si = 0; si + 1 < nsets; ++si) run_set(si, std::true_type{});
+  if (nsets > 0) run_set(nsets - 1, std::false_type{});
 
   // ---- item result: per head h', o = D[h'] + D[NG+h'] + lam(h', group) ----
   l_part = reduce_head<NG>(col_used ? l_part : 0.f, n, OpAdd{});
 #pragma unroll
   for (int j = 0; j < NGR; ++j) lam[j] = reduce_head<NG>(col_used ? lam[j] : 0.f, n, OpAdd{});
-  float* ol = reinterpret_cast<float*>(buf);   // [2NG][D]
+  float* ol = reinterpret_cast<float*>(L.buf);   // [2NG][D]
 #pragma unroll
   for (int nt = 0; nt < 8; ++nt)
 #pragma unroll
@@ -667,7 +675,7 @@ __global__ __launch_bounds__(256) void decode_fast_kernel(Geom g, const uint8_t*
     }
   if (gq == 0 && n < NG) {
 #pragma unroll
-    for (int j = 0; j < NGR; ++j) lam_l[n * NGR + j] = lam[j];
+    for (int j = 0; j < NGR; ++j) L.lam[n * NGR + j] = lam[j];
     out_part[n * (D + 2) + D] = m_ref;
     out_part[n * (D + 2) + D + 1] = l_part;
   }
@@ -677,8 +685,63 @@ __global__ __launch_bounds__(256) void decode_fast_kernel(Geom g, const uint8_t*
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
       const int c = lane + 64 * k;
-      out_part[j * (D + 2) + c] = ol[j * D + c] + ol[(NG + j) * D + c] + lam_l[j * NGR + c / C::GV];
+      out_part[j * (D + 2) + c] = ol[j * D + c] + ol[(NG + j) * D + c] + L.lam[j * NGR + c / C::GV];
     }
+}
+
+// ------------------------------------------------------------------------------------
+// The kernel. One wave = one work item; 4 waves per workgroup share the item
+// table in LDS and nothing else.
+// ------------------------------------------------------------------------------------
+template <class C>
+__global__ __launch_bounds__(256) void decode_fast_kernel(Geom g, const uint8_t* __restrict__ blocks,
+                                                          const int32_t* __restrict__ table,
+                                                          const uint16_t* __restrict__ k_ring,
+                                                          const uint16_t* __restrict__ v_ring,
+                                                          const int32_t* __restrict__ state,
+                                                          const uint16_t* __restrict__ q, float qscale, int bps,
+                                                          int nq_max, int nr_max, float* __restrict__ ws) {
+  constexpr int NG = C::NG, D = C::D;
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  int* prefix = reinterpret_cast<int*>(smem);
+  const int pre_bytes = ((g.B + 1) * 4 + 15) & ~15;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  uint8_t* wl = smem + pre_bytes + wave * C::LDS_WAVE;
+  WaveLds<C> L;
+  L.qs = reinterpret_cast<float*>(wl);
+  L.buf = wl + C::LDS_Q;
+  L.alpha = reinterpret_cast<float*>(L.buf + C::LDS_BUF);
+  L.lam = L.alpha + 16;
+  L.zero16 = reinterpret_cast<uint4*>(L.lam + NG * C::NGR);
+
+  build_prefix(g, state, bps, kRingChunk, nq_max, nr_max, prefix, blockIdx.x == 0);
+  const int w = blockIdx.x * kWaves + wave;
+  if (w >= g.Hkv * prefix[g.B]) return;
+  const ItemRef it = locate_item(g, prefix, w);
+  // the item is the same for every lane of the wave: keep it in scalar registers
+  const int b = __builtin_amdgcn_readfirstlane(it.b);
+  const int h = __builtin_amdgcn_readfirstlane(it.h);
+  const int item = __builtin_amdgcn_readfirstlane(it.item);
+  const int Q = state[4 * b + kStateQ], S = state[4 * b + kStateS];
+  bool unused_flag = false;
+  const ItemCounts cnt = items_of(Q, S, g.G, bps, kRingChunk, nq_max, nr_max, &unused_flag);
+  if (lane == 0) *L.zero16 = make_uint4(0, 0, 0, 0);
+
+  // scaled query, log2 units: q' = q * softmax_scale * log2(e)
+  for (int idx = lane; idx < NG * D; idx += 64) {
+    const int j = idx / D, c = idx % D;
+    L.qs[idx] = in_val<C>(q[((size_t)b * g.Hq + h * NG + j) * D + c]) * qscale;
+  }
+  wave_lds_fence();
+
+  float* out_part = ws + (size_t)w * NG * (D + 2);
+  if (item >= cnt.nq) {
+    const int t0 = Q + (item - cnt.nq) * kRingChunk;
+    ring_chunk<C>(g, L, k_ring, v_ring, b * g.Hkv + h, t0, min(S, t0 + kRingChunk), out_part);
+  } else {
+    const int blk_begin = item * bps;
+    quant_item<C>(g, L, blocks, table, b, h, blk_begin, min(blk_begin + bps, Q / g.G), out_part);
+  }
 }
 
 template <class C>

@@ -11,30 +11,37 @@ namespace {
 
 struct FastEntry {
   int ng, kb, vb, G, GV, dtype;
+  bool paged;
   int nb_set;
   hipError_t (*launch)(const Geom&, const kvq_cache&, const void*, float, int, int, int, size_t, void*,
                        hipStream_t);
 };
 
-template <int NG, int KB, int VB, int G, int GV, bool BF16>
+template <int NG, int KB, int VB, int G, int GV, bool BF16, bool PAGED>
 constexpr FastEntry entry() {
-  using C = fast::Cfg<NG, KB, VB, G, GV, BF16>;
-  return FastEntry{NG, KB, VB, G, GV, BF16 ? KVQ_BF16 : KVQ_F16, C::NB, &fast::launch_fast<C>};
+  using C = fast::Cfg<NG, KB, VB, G, GV, BF16, PAGED>;
+  return FastEntry{NG, KB, VB, G, GV, BF16 ? KVQ_BF16 : KVQ_F16, PAGED, C::NB, &fast::launch_fast<C>};
 }
 
+// dense and paged store of each configuration
+#define KVQ_FAST(NG, KB, VB, G, GV, BF16) entry<NG, KB, VB, G, GV, BF16, false>(), entry<NG, KB, VB, G, GV, BF16, true>()
+
 constexpr FastEntry kFast[] = {
-    entry<1, 2, 2, 32, 32, false>(),   // MHA, INT2, G = G_V = 32, fp16 (a Llama-2-7B-shaped layer)
-    entry<1, 2, 2, 32, 32, true>(),
-    entry<4, 4, 4, 32, 32, true>(),    // GQA 4, INT4 (a Llama-3-8B-shaped layer)
-    entry<4, 2, 2, 32, 32, true>(),    // GQA 4, INT2
-    entry<8, 2, 2, 64, 64, true>(),    // GQA 8, INT2, G = G_V = 64 (a 70B-shaped layer)
-    entry<6, 4, 2, 16, 32, true>(),    // GQA 6, INT4 keys / INT2 values, 16-token pages
+    KVQ_FAST(1, 2, 2, 32, 32, false),   // MHA, INT2, G = G_V = 32, fp16 (a Llama-2-7B-shaped layer)
+    KVQ_FAST(1, 2, 2, 32, 32, true),
+    KVQ_FAST(4, 4, 4, 32, 32, true),    // GQA 4, INT4 (a Llama-3-8B-shaped layer)
+    KVQ_FAST(4, 2, 2, 32, 32, true),    // GQA 4, INT2
+    KVQ_FAST(8, 2, 2, 64, 64, true),    // GQA 8, INT2, G = G_V = 64 (a 70B-shaped layer)
+    KVQ_FAST(6, 4, 2, 16, 32, true),    // GQA 6, INT4 keys / INT2 values, 16-token pages
 };
+#undef KVQ_FAST
 
 const FastEntry* find(const Geom& g) {
   if (g.d != 128) return nullptr;
   for (const FastEntry& e : kFast)
-    if (e.ng == g.ng && e.kb == g.kb && e.vb == g.vb && e.G == g.G && e.GV == g.GV && e.dtype == g.dtype) return &e;
+    if (e.ng == g.ng && e.kb == g.kb && e.vb == g.vb && e.G == g.G && e.GV == g.GV && e.dtype == g.dtype &&
+        e.paged == (g.num_pages > 0))
+      return &e;
   return nullptr;
 }
 
