@@ -126,7 +126,8 @@ typedef struct {
   const int32_t* block_table;  /* paged: [B][max_blocks] page of each block; NULL if dense    */
   void* k_ring;                /* [B][H_kv][res_capacity][d] of dtype                          */
   void* v_ring;
-  int32_t* state;              /* [B][4] {Q_b, S_b, internal, internal} then the error word;
+  int32_t* state;              /* [B][4] {Q_b, S_b, internal, internal}, then the error word
+                                  and internal decode counters (kvq_layout.state bytes in all);
                                   zero-filled by the caller for an empty cache                 */
 } kvq_cache;
 
@@ -174,8 +175,10 @@ kvq_status kvq_append_flush(const kvq_config* cfg, const kvq_cache* cache,
  *                   lengths are read on the device);
  *   workspace: device scratch of at least kvq_workspace_size(cfg, max_seq_tokens)
  *              bytes; its contents need no initialisation.
- * A sequence with S_b == 0 gets a zero output. Calls that share a workspace
- * must be ordered on one stream. */
+ * A sequence with S_b == 0 gets a zero output. The launch hands out its work
+ * through counters in the cache's state words (and re-arms them when it ends),
+ * so decode calls on one cache, like calls that share a workspace, must be
+ * ordered on one stream. */
 kvq_status kvq_decode_attention(const kvq_config* cfg, const kvq_cache* cache,
                                 const void* q, float* out, float softmax_scale,
                                 int32_t max_seq_tokens, void* workspace,

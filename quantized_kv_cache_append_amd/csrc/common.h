@@ -11,6 +11,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 #include "kvq.h"
 
 namespace kvq {
@@ -48,9 +50,15 @@ inline Geom make_geom(const kvq_config& c) {
 }
 
 // State words per sequence: {Q_b, S_b, flush arrivals, append arrivals};
-// the sticky error word follows the B entries.
+// then the sticky error word (4B), the decode's finished-wave counter
+// (4B + 1), and the decode's work-queue counters, one per 128-byte line
+// (4B + kQueueStride * (k + 1), k < kQueues).
 constexpr int kStateQ = 0, kStateS = 1, kStateFlushCnt = 2, kStateAppendCnt = 3;
-__host__ __device__ inline int state_words(int B) { return 4 * B + 4; }
+constexpr int kQueues = 8;        // decode work queues (counters on separate cache lines)
+constexpr int kQueueStride = 32;  // int32 words between queue counters
+__host__ __device__ inline int state_words(int B) { return 4 * B + kQueueStride * (kQueues + 1); }
+__host__ __device__ inline int state_done_word(int B) { return 4 * B + 1; }
+__host__ __device__ inline int state_queue_word(int B, int k) { return 4 * B + kQueueStride * (k + 1); }
 
 #ifdef __HIPCC__
 // ---- conversions --------------------------------------------------------------
@@ -127,18 +135,17 @@ hipError_t launch_decode(const Geom& g, const kvq_cache& c, const void* q, float
 // Decode work decomposition shared by the workspace sizing and the kernels.
 struct DecodePlan {
   bool fast;          // MFMA kernel (else the generic VALU kernel)
-  int bps;            // quantized blocks per split
-  int rc;             // ring tokens per ring chunk
-  int nq_max;         // upper bound on quantized splits per (sequence, kv head)
-  int nr_max;         // upper bound on ring chunks per (sequence, kv head)
-  size_t items_max;   // upper bound on work items
-  size_t ws_bytes;    // workspace bytes
+  int nb_set;         // blocks per set (unit sizes are whole sets)
+  int max_blk;        // quantized blocks per (sequence, kv head) the workspace is sized for
+  size_t units_max;   // upper bound on work units
+  size_t ws_bytes;    // workspace bytes: the unit plan, then the partial states
 };
 DecodePlan plan_decode(const Geom& g, int max_seq_tokens);
 
 // MFMA path (decode_fast_dispatch.hip): whether a configuration has an
 // instantiation, its blocks per set, and the launch.
 bool fast_supported(const Geom& g, int* blocks_per_set);
+int fast_ring_chunk();   // ring tokens per ring unit of the MFMA path
 hipError_t launch_decode_fast(const Geom& g, const kvq_cache& c, const void* q, float scale, const DecodePlan& p,
                               void* ws, hipStream_t s);
 

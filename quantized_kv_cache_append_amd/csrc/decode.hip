@@ -14,14 +14,13 @@
 //        partial attention states combined by a globally normalised online
 //        softmax -- the split/combine used here.
 //
-// Work decomposition (decode_items.h). For each (sequence b, kv head h) the
-// quantized blocks are cut into splits and the ring tokens into chunks; a work
-// item is one split or chunk. The per-sequence item counts come from the
-// device-side lengths, so ragged batches need no host synchronisation. Each
-// item leaves a partial state (running max m, sum l, unnormalised o[d]) per
-// query head of the group, scores in log2 units (the query is pre-multiplied
-// by softmax_scale * log2 e, so exp becomes exp2); the combine kernel merges
-// them.
+// Work decomposition (decode_units.h). Each (sequence b, kv head h) gives one
+// unit for its ring tokens and units of consecutive quantized blocks; the unit
+// counts come from the device-side lengths, so ragged batches need no host
+// synchronisation. Each unit leaves a partial state (running max m, sum l,
+// unnormalised o[d]) per query head of the group, scores in log2 units (the
+// query is pre-multiplied by softmax_scale * log2 e, so exp becomes exp2); the
+// combine kernel merges them.
 //
 // This file holds the plan, the combine and the generic VALU path (head_dim 64
 // or 128, any supported group size, n_g <= 8), used for configurations the
@@ -31,7 +30,7 @@
 #include <algorithm>
 
 #include "common.h"
-#include "decode_items.h"
+#include "decode_units.h"
 
 namespace kvq {
 
@@ -39,32 +38,41 @@ namespace {
 
 constexpr int kWaves = 4;
 constexpr int kNgMax = 8;
+constexpr int kRingAll = 1 << 30;   // ring tokens per ring unit of the generic kernel: all of them
 
 template <int D, bool BF16>
 __global__ __launch_bounds__(256) void decode_generic_kernel(
     Geom g, const uint8_t* __restrict__ blocks, const int32_t* __restrict__ table,
     const uint16_t* __restrict__ k_ring, const uint16_t* __restrict__ v_ring, int32_t* __restrict__ state,
-    const uint16_t* __restrict__ q, float qscale, int bps, int rc, int nq_max, int nr_max, float* __restrict__ ws) {
+    const uint16_t* __restrict__ q, float qscale, int max_blk, int* __restrict__ ws_plan, float* __restrict__ ws) {
   constexpr int CPL = D / 64;   // channels per lane
   extern __shared__ int smem[];
-  int* prefix = smem;   // [B + 1] exclusive prefix of items per sequence
-  float* scratch = reinterpret_cast<float*>(smem + ((g.B + 4) & ~3));
+  int* plan = smem;
+  const int pints = plan_ints(g.B);
+  int* red = plan + pints;
+  float* scratch = reinterpret_cast<float*>(smem + ((pints + 16 * kSections + 3) & ~3));
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   float* qt = scratch + wave * (kNgMax * D + kNgMax * 64);   // [8][D]
   float* pb = qt + kNgMax * D;                               // [8][64]
 
-  build_prefix(g, state, bps, rc, nq_max, nr_max, prefix, blockIdx.x == 0);
+  // the whole ring of a pair is one unit (kRingAll tokens per ring unit)
+  build_unit_plan(g, state, max_blk, 1, kRingAll, plan, red, blockIdx.x == 0);
+  if (blockIdx.x == 0)
+    for (int i = threadIdx.x; i < pints; i += blockDim.x) ws_plan[i] = plan[i];
+  auto qs_of = [&](int b, int& Q, int& S) {
+    Q = state[4 * b + kStateQ];
+    S = state[4 * b + kStateS];
+  };
+  auto nblk_of = [&](int b) { return min(state[4 * b + kStateQ] / g.G, max_blk); };
 
-  const int W = g.Hkv * prefix[g.B];
+  const int units = plan[kPlanUnits];
   const int ng = g.ng;
-  for (int w = blockIdx.x * kWaves + wave; w < W; w += gridDim.x * kWaves) {
-    const ItemRef it = locate_item(g, prefix, w);
-    const int b = it.b, h = it.h, item = it.item;
+  for (int w = blockIdx.x * kWaves + wave; w < units; w += gridDim.x * kWaves) {
+    const Unit un = locate_unit(g, plan, w, qs_of, nblk_of);
+    const int b = un.b, h = un.h;
     const int pair = b * g.Hkv + h;
     const int Q = state[4 * b + kStateQ];
     const int S = state[4 * b + kStateS];
-    bool unused_flag = false;
-    const ItemCounts cnt = items_of(Q, S, g.G, bps, rc, nq_max, nr_max, &unused_flag);
 
     float qv[kNgMax][CPL], o[kNgMax][CPL], m[kNgMax], l[kNgMax];
 #pragma unroll
@@ -97,10 +105,9 @@ __global__ __launch_bounds__(256) void decode_generic_kernel(
       wave_lds_fence();
     };
 
-    if (item < cnt.nq) {
-      // ---- quantized blocks [item*bps, ...) ----
-      const int nblk = Q / g.G;
-      const int blk0 = item * bps, blk1 = min(blk0 + bps, nblk);
+    if (!un.ring) {
+      // ---- quantized blocks of this unit ----
+      const int blk0 = un.begin, blk1 = un.end;
       const int kP = 32 / g.kb;
       const uint32_t kmask = (1u << g.kb) - 1, vmask = (1u << g.vb) - 1;
       for (int blk = blk0; blk < blk1; ++blk) {
@@ -170,8 +177,8 @@ __global__ __launch_bounds__(256) void decode_generic_kernel(
         wave_lds_fence();
       }
     } else {
-      // ---- full-precision ring tokens of this chunk ----
-      const int r0 = Q + (item - cnt.nq) * rc, r1 = min(S, r0 + rc);
+      // ---- full-precision ring tokens of this pair ----
+      const int r0 = un.begin, r1 = un.end;
 #pragma unroll
       for (int k = 0; k < CPL; ++k)
 #pragma unroll
@@ -209,7 +216,7 @@ __global__ __launch_bounds__(256) void decode_generic_kernel(
       }
     }
 
-    // partial state of this item, per query head of the group
+    // partial state of this unit, per query head of the group
 #pragma unroll
     for (int j = 0; j < kNgMax; ++j) {
       if (j >= ng) break;
@@ -226,45 +233,36 @@ __global__ __launch_bounds__(256) void decode_generic_kernel(
 
 // Merge the partial states of one (sequence, query head) (scores in log2
 // units): with M = max m_i, o = sum_i 2^(m_i - M) o_i / sum_i 2^(m_i - M) l_i.
+// The units of the pair come from the plan the decode kernel left in the
+// workspace.
 template <int D>
-__global__ __launch_bounds__(64) void combine_kernel(Geom g, const int32_t* __restrict__ state, int bps, int rc,
-                                                     int nq_max, int nr_max, const float* __restrict__ ws,
-                                                     float* __restrict__ out) {
+__global__ __launch_bounds__(64) void combine_kernel(Geom g, const int* __restrict__ plan,
+                                                     const float* __restrict__ ws, float* __restrict__ out) {
   constexpr int CPL = D / 64;
   const int bh = blockIdx.x;
   const int b = bh / g.Hq, hq = bh % g.Hq;
   const int h = hq / g.ng, j = hq % g.ng;
   const int lane = threadIdx.x;
-  bool unused_flag = false;
-  int part = 0;
-  for (int bb = lane; bb < b; bb += 64) {
-    const ItemCounts c = items_of(state[4 * bb + kStateQ], state[4 * bb + kStateS], g.G, bps, rc, nq_max, nr_max,
-                                  &unused_flag);
-    part += c.nq + c.nr;
-  }
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) part += __shfl_xor(part, off, 64);
-  const ItemCounts cc = items_of(state[4 * b + kStateQ], state[4 * b + kStateS], g.G, bps, rc, nq_max, nr_max,
-                                 &unused_flag);
-  const int cb = cc.nq + cc.nr;
-  const size_t base = (size_t)g.Hkv * part + (size_t)h * cb;
+  const PairUnits pu = pair_units(g, plan, b, h);
+  const int cb = pu.n;
+  auto slot = [&](int i) -> int { return pu.slot(i); };
   const size_t stride = (size_t)g.ng * (D + 2);
-  const float* src0 = ws + base * stride + (size_t)j * (D + 2);
+  const float* src0 = ws + (size_t)j * (D + 2);
 
-  // the item maxima, 64 at a time, then their maximum
+  // the unit maxima, 64 at a time, then their maximum
   float M = -INFINITY;
-  for (int i = lane; i < cb; i += 64) M = fmaxf(M, src0[i * stride + D]);
+  for (int i = lane; i < cb; i += 64) M = fmaxf(M, src0[slot(i) * stride + D]);
   M = wave_max(M);
   float L = 0.f, acc[CPL];
 #pragma unroll
   for (int k = 0; k < CPL; ++k) acc[k] = 0.f;
   if (M != -INFINITY) {
     int i = 0;
-    for (; i + 4 <= cb; i += 4) {   // four independent item loads in flight
+    for (; i + 4 <= cb; i += 4) {   // four independent unit loads in flight
       float e[4], l[4], v[4][CPL];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        const float* src = src0 + (i + u) * stride;
+        const float* src = src0 + slot(i + u) * stride;
         e[u] = src[D];
         l[u] = src[D + 1];
 #pragma unroll
@@ -279,7 +277,7 @@ __global__ __launch_bounds__(64) void combine_kernel(Geom g, const int32_t* __re
       }
     }
     for (; i < cb; ++i) {
-      const float* src = src0 + i * stride;
+      const float* src = src0 + slot(i) * stride;
       const float wgt = exp2f(src[D] - M);
       L += wgt * src[D + 1];
 #pragma unroll
@@ -294,13 +292,13 @@ __global__ __launch_bounds__(64) void combine_kernel(Geom g, const int32_t* __re
 template <int D, bool BF16>
 hipError_t launch_generic(const Geom& g, const kvq_cache& c, const void* q, float scale, const DecodePlan& plan,
                           void* ws, hipStream_t s) {
-  const int wgs = (int)std::min<size_t>((plan.items_max + kWaves - 1) / kWaves, 2048);
-  const size_t lds = (size_t)((g.B + 4) & ~3) * 4 + (size_t)kWaves * (kNgMax * D + kNgMax * 64) * 4;
+  const int wgs = (int)std::min<size_t>((plan.units_max + kWaves - 1) / kWaves, 2048);
+  const size_t lds = (size_t)((plan_ints(g.B) + 16 * kSections + 3) & ~3) * 4 + (size_t)kWaves * (kNgMax * D + kNgMax * 64) * 4;
   hipLaunchKernelGGL((decode_generic_kernel<D, BF16>), dim3(wgs), dim3(256), lds, s, g,
                      static_cast<const uint8_t*>(c.blocks), c.block_table,
                      static_cast<const uint16_t*>(c.k_ring), static_cast<const uint16_t*>(c.v_ring), c.state,
-                     static_cast<const uint16_t*>(q), scale * 1.4426950408889634f, plan.bps, plan.rc, plan.nq_max,
-                     plan.nr_max, static_cast<float*>(ws));
+                     static_cast<const uint16_t*>(q), scale * 1.4426950408889634f, plan.max_blk,
+                     static_cast<int*>(ws), reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + plan_bytes(g.B)));
   return hipGetLastError();
 }
 
@@ -310,26 +308,10 @@ DecodePlan plan_decode(const Geom& g, int max_seq_tokens) {
   DecodePlan p{};
   int nb_set = 1;
   p.fast = fast_supported(g, &nb_set);
-  const int maxblk = std::max(max_seq_tokens - g.R, 0) / g.G;
-  if (p.fast) {
-    // About one split per wave slot of the GPU (256 CUs x 8), 512..4096 tokens,
-    // a whole number of sets.
-    const double total = (double)g.B * g.Hkv * std::max(max_seq_tokens, 1);
-    int split = 512;
-    while (split < 4096 && total / split > 2048.0) split *= 2;
-    const int set_tok = nb_set * g.G;
-    split = std::max(set_tok, split / set_tok * set_tok);
-    p.bps = split / g.G;
-    p.rc = 32;
-    p.nr_max = (g.C + p.rc - 1) / p.rc;
-  } else {
-    p.bps = 8;
-    p.rc = g.C;
-    p.nr_max = 1;
-  }
-  p.nq_max = (maxblk + p.bps - 1) / p.bps;
-  p.items_max = (size_t)g.B * g.Hkv * (size_t)(p.nq_max + p.nr_max);
-  p.ws_bytes = p.items_max * (size_t)g.ng * (size_t)(g.d + 2) * 4;
+  p.nb_set = p.fast ? nb_set : 1;
+  p.max_blk = std::max(max_seq_tokens - g.R, 0) / g.G;
+  p.units_max = units_max(g, p.max_blk, p.nb_set, p.fast ? fast_ring_chunk() : kRingAll);
+  p.ws_bytes = plan_bytes(g.B) + p.units_max * (size_t)g.ng * (size_t)(g.d + 2) * 4;
   return p;
 }
 
@@ -347,12 +329,12 @@ hipError_t launch_decode(const Geom& g, const kvq_cache& c, const void* q, float
     e = bf16 ? launch_generic<64, true>(g, c, q, scale, plan, ws, s)
              : launch_generic<64, false>(g, c, q, scale, plan, ws, s);
   if (e != hipSuccess) return e;
+  const int* planp = static_cast<const int*>(ws);
+  const float* parts = reinterpret_cast<const float*>(static_cast<const uint8_t*>(ws) + plan_bytes(g.B));
   if (g.d == 128)
-    hipLaunchKernelGGL((combine_kernel<128>), dim3(g.B * g.Hq), dim3(64), 0, s, g, c.state, plan.bps, plan.rc,
-                       plan.nq_max, plan.nr_max, static_cast<const float*>(ws), out);
+    hipLaunchKernelGGL((combine_kernel<128>), dim3(g.B * g.Hq), dim3(64), 0, s, g, planp, parts, out);
   else
-    hipLaunchKernelGGL((combine_kernel<64>), dim3(g.B * g.Hq), dim3(64), 0, s, g, c.state, plan.bps, plan.rc,
-                       plan.nq_max, plan.nr_max, static_cast<const float*>(ws), out);
+    hipLaunchKernelGGL((combine_kernel<64>), dim3(g.B * g.Hq), dim3(64), 0, s, g, planp, parts, out);
   return hipGetLastError();
 }
 

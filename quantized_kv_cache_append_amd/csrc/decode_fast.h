@@ -38,7 +38,7 @@
 #include <type_traits>
 
 #include "common.h"
-#include "decode_items.h"
+#include "decode_units.h"
 
 namespace kvq {
 namespace fast {
@@ -298,13 +298,15 @@ struct WaveLds {
 };
 
 // ---------------------------------------------------------------------------------
-// A chunk of up to 32 full-precision ring tokens [t0, t1).
-// Scores on MFMA (A = key rows as stored, B = query hi/lo), P.V on the vector ALUs.
+// The full-precision ring tokens [t_begin, t_end) of one (sequence, kv head), in
+// chunks of 32: scores on MFMA (A = key rows as stored, B = query hi/lo),
+// online softmax across the chunks, P.V on the vector ALUs. Needs the scaled
+// query in L.qs.
 // ---------------------------------------------------------------------------------
 template <class C>
-__device__ __forceinline__ void ring_chunk(const Geom& g, const WaveLds<C>& L, const uint16_t* __restrict__ k_ring,
-                                           const uint16_t* __restrict__ v_ring, int pair, int t0, int t1,
-                                           float* __restrict__ out_part) {
+__device__ __forceinline__ void ring_unit(const Geom& g, const WaveLds<C>& L, const uint16_t* __restrict__ k_ring,
+                                          const uint16_t* __restrict__ v_ring, int pair, int t_begin, int t_end,
+                                          float* __restrict__ out_part) {
   constexpr int NG = C::NG, D = C::D;
   const int lane = threadIdx.x & 63, gq = lane >> 4, n = lane & 15;
   // B operand: q' hi/lo, column n = head, k position e of k-step ks = channel 32gq + 8ks + e
@@ -331,70 +333,92 @@ __device__ __forceinline__ void ring_chunk(const Geom& g, const WaveLds<C>& L, c
     bq_hi[ks] = make_uint4(hi[0], hi[1], hi[2], hi[3]);
     bq_lo[ks] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
   }
-  float s[2][4];
-#pragma unroll
-  for (int tt = 0; tt < 2; ++tt) {
-    const int t = t0 + 16 * tt + n;   // A row = token
-    const bool tv = t < t1;
-    const uint16_t* krow = k_ring + ((size_t)pair * g.C + (tv ? t % g.C : 0)) * D + 32 * gq;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const uint4 a = tv ? *reinterpret_cast<const uint4*>(krow + 8 * ks) : make_uint4(0, 0, 0, 0);
-      if constexpr (C::BF16) {
-        acc = mfma_bf16(a, bq_hi[ks], acc);
-        acc = mfma_bf16(a, bq_lo[ks], acc);
-      } else {
-        acc = mfma_f16(a, bq_hi[ks], acc);
-        acc = mfma_f16(a, bq_lo[ks], acc);
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int tok = t0 + 16 * tt + 4 * gq + i;   // D row = token, column n = head
-      s[tt][i] = (n < NG && tok < t1) ? acc[i] / escale : -INFINITY;
-    }
-  }
-  float mx = -INFINITY;
-#pragma unroll
-  for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[tt][i]);
-  mx = reduce_rows(mx, OpMax{});
-  float lsum = 0.f;
-  float* pl = reinterpret_cast<float*>(L.buf);   // [32 tokens][NG]
-#pragma unroll
-  for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float p = s[tt][i] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(s[tt][i] - mx);
-      lsum += p;
-      if (n < NG) pl[(16 * tt + 4 * gq + i) * NG + n] = p;
-    }
-  lsum = reduce_rows(lsum, OpAdd{});
-  wave_lds_fence();
-  // P.V on the vector ALUs: lane owns channels 2*lane, 2*lane+1. All the
-  // chunk's value rows are loaded first (independent loads in flight), rows
-  // past t1 read row t0 and get probability 0.
-  uint32_t vv[kRingChunk];
-#pragma unroll
-  for (int u = 0; u < kRingChunk; ++u) {
-    const int t = t0 + u < t1 ? t0 + u : t0;
-    vv[u] = *reinterpret_cast<const uint32_t*>(v_ring + ((size_t)pair * g.C + t % g.C) * D + 2 * lane);
-  }
-  float o0[NG], o1[NG];
+  const float inv_escale = 1.0f / escale;   // exact: a power of two
+  const size_t ring_base = (size_t)pair * g.C;
+  float m_run = -INFINITY, l_run = 0.f;   // per lane: head n (lanes n < NG)
+  float o0[NG], o1[NG];                   // per lane: channels 2*lane, 2*lane+1 of every head
 #pragma unroll
   for (int j = 0; j < NG; ++j) o0[j] = o1[j] = 0.f;
+  float* pl = reinterpret_cast<float*>(L.buf);   // [32 tokens][NG]
+
+  for (int t0 = t_begin; t0 < t_end; t0 += kRingChunk) {
+    const int t1 = min(t_end, t0 + kRingChunk);
+    // value rows of the chunk (rows past t1 read row t0 and get probability 0)
+    // and key rows, all in flight together
+    uint32_t vv[kRingChunk];
 #pragma unroll
-  for (int u = 0; u < kRingChunk; ++u) {
-    const float v0 = in_val<C>(vv[u] & 0xffffu), v1 = in_val<C>(vv[u] >> 16);
-    const float* prow = pl + u * NG;
+    for (int u = 0; u < kRingChunk; ++u) {
+      const int t = t0 + u < t1 ? t0 + u : t0;
+      vv[u] = *reinterpret_cast<const uint32_t*>(v_ring + (ring_base + t % g.C) * D + 2 * lane);
+    }
+    uint4 ka[2][4];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      const int t = t0 + 16 * tt + n;   // A row = token
+      const uint16_t* krow = k_ring + (ring_base + (t < t1 ? t : t0) % g.C) * D + 32 * gq;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) ka[tt][ks] = *reinterpret_cast<const uint4*>(krow + 8 * ks);
+    }
+    float s[2][4];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        if constexpr (C::BF16) {
+          acc = mfma_bf16(ka[tt][ks], bq_hi[ks], acc);
+          acc = mfma_bf16(ka[tt][ks], bq_lo[ks], acc);
+        } else {
+          acc = mfma_f16(ka[tt][ks], bq_hi[ks], acc);
+          acc = mfma_f16(ka[tt][ks], bq_lo[ks], acc);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int tok = t0 + 16 * tt + 4 * gq + i;   // D row = token, column n = head
+        s[tt][i] = (n < NG && tok < t1) ? acc[i] * inv_escale : -INFINITY;
+      }
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[tt][i]);
+    mx = reduce_rows(mx, OpMax{});
+    const float m_new = fmaxf(m_run, mx);
+    const float alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
+    m_run = m_new;
+    float lsum = 0.f;
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float p = s[tt][i] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(s[tt][i] - m_new);
+        lsum += p;
+        if (n < NG) pl[(16 * tt + 4 * gq + i) * NG + n] = p;
+      }
+    lsum = reduce_rows(lsum, OpAdd{});
+    l_run = l_run * alpha + lsum;
+    if (gq == 0 && n < NG) L.alpha[n] = alpha;
+    wave_lds_fence();
 #pragma unroll
     for (int j = 0; j < NG; ++j) {
-      const float p = prow[j];   // 0 for rows past t1
-      o0[j] = fmaf(p, v0, o0[j]);
-      o1[j] = fmaf(p, v1, o1[j]);
+      const float a = L.alpha[j];
+      o0[j] *= a;
+      o1[j] *= a;
     }
+#pragma unroll
+    for (int u = 0; u < kRingChunk; ++u) {
+      const float v0 = in_val<C>(vv[u] & 0xffffu), v1 = in_val<C>(vv[u] >> 16);
+      const float* prow = pl + u * NG;
+#pragma unroll
+      for (int j = 0; j < NG; ++j) {
+        const float p = prow[j];   // 0 for rows past t1
+        o0[j] = fmaf(p, v0, o0[j]);
+        o1[j] = fmaf(p, v1, o1[j]);
+      }
+    }
+    wave_lds_fence();   // pl and alpha are rewritten by the next chunk
   }
 #pragma unroll
   for (int j = 0; j < NG; ++j) {
@@ -402,44 +426,53 @@ __device__ __forceinline__ void ring_chunk(const Geom& g, const WaveLds<C>& L, c
     *reinterpret_cast<float2*>(dst + 2 * lane) = make_float2(o0[j], o1[j]);
   }
   if (gq == 0 && n < NG) {
-    out_part[n * (D + 2) + D] = mx;
-    out_part[n * (D + 2) + D + 1] = lsum;
+    out_part[n * (D + 2) + D] = m_run;
+    out_part[n * (D + 2) + D + 1] = l_run;
   }
 }
 
 // ---------------------------------------------------------------------------------
-// Quantized blocks [blk_begin, blk_end) of one (sequence, kv head), in sets of NB.
+// Quantized blocks: a wave's stream of units.
 // ---------------------------------------------------------------------------------
+
+// A run of quantized blocks [begin, end) of (sequence b, kv head h).
+struct Span {
+  int b, h, begin, end;
+};
+
+// Record of block blk of span sp (blk is clamped into the span). The dense store
+// keeps a pair's blocks contiguous; the paged store looks the page up (an
+// out-of-range page reads page 0 and the block is masked out).
 template <class C>
-__device__ __forceinline__ void quant_item(const Geom& g, const WaveLds<C>& L, const uint8_t* __restrict__ blocks,
-                                           const int32_t* __restrict__ table, int b, int h, int blk_begin,
-                                           int blk_end, float* __restrict__ out_part) {
+__device__ __forceinline__ const uint8_t* span_rec(const Geom& g, const uint8_t* __restrict__ blocks,
+                                                   const int32_t* __restrict__ table, Span sp, int blk) {
+  blk = min(blk, sp.end - 1);
+  if constexpr (!C::PAGED) {
+    return blocks + (((size_t)sp.b * g.Hkv + sp.h) * g.max_blocks + blk) * (size_t)C::REC;
+  } else {
+    int page = table[(size_t)sp.b * g.max_blocks + blk];
+    page = (page >= 0 && page < g.num_pages) ? page : 0;
+    return blocks + ((size_t)page * g.Hkv + sp.h) * (size_t)C::REC;
+  }
+}
+
+// The quantized units of a wave, from `first` on, taking the next unit from the
+// queue counter: one continuous stream of sets in which the last set of a unit
+// already prefetches the first set (and the query) of the next one, so a new
+// unit costs no memory round trip. Each unit's partial state goes to its slot.
+// `issue()` starts a claim on the queue (its raw answer, valid in lane 0),
+// `claim(raw)` turns the answer into a unit index, `locate(u)` gives a
+// quantized unit's span.
+template <class C, class Locate, class Issue, class Claim>
+__device__ __forceinline__ void quant_stream(const Geom& g, const WaveLds<C>& L, const uint8_t* __restrict__ blocks,
+                                             const int32_t* __restrict__ table, const uint16_t* __restrict__ q,
+                                             float qscale, int units, int first, Span first_span, int claimed,
+                                             Locate locate, Issue issue, Claim claim, float* __restrict__ ws) {
   constexpr int NG = C::NG, D = C::D, NB = C::NB, TPB = C::TPB, NGR = C::NGR, KS_SET = C::KS_SET;
+  constexpr int QW = NG * D / 128;   // query words per lane
   const int lane = threadIdx.x & 63, gq = lane >> 4, n = lane & 15;
-  const int nsets = (blk_end - blk_begin + NB - 1) / NB;
   const int cbk = n / NG, chd = n % NG;   // column's block within the set, column's head
   const bool col_used = n < C::NCOL;
-
-  // Record of block blk of this pair. The dense store keeps a pair's blocks
-  // contiguous; the paged store looks the page up (an out-of-range page reads
-  // page 0 and the block is masked out). `blk` must lie in [blk_begin, blk_end).
-  const uint8_t* pair_base = blocks + ((size_t)b * g.Hkv + h) * (size_t)g.max_blocks * C::REC;
-  const int32_t* trow = table + (size_t)b * g.max_blocks;
-  auto page_ok = [&](int blk) -> bool {
-    if constexpr (!C::PAGED) return true;
-    const int page = trow[blk];
-    return page >= 0 && page < g.num_pages;
-  };
-  auto rec_at = [&](int blk) -> const uint8_t* {
-    if constexpr (!C::PAGED) {
-      return pair_base + (size_t)blk * C::REC;
-    } else {
-      int page = trow[blk];
-      page = (page >= 0 && page < g.num_pages) ? page : 0;
-      return blocks + ((size_t)page * g.Hkv + h) * (size_t)C::REC;
-    }
-  };
-  const int blk_last = blk_end - 1;
 
   // ---- register buffers for one set, refilled right after their last use ----
   uint4 ksz[8];                 // K scale (4 x 16 B) and zero (4 x 16 B), channels 32gq..+31, column block
@@ -447,26 +480,26 @@ __device__ __forceinline__ void quant_item(const Geom& g, const WaveLds<C>& L, c
   uint2 vsz[TPB][NGR][2];       // V scale / zero of the lane's 4 tokens per tile and group
   Chunk<C::VLANE> vc[KS_SET];   // value code chunks
 
-  // loaders for set si (blocks clamped into the item)
-  auto load_ksz = [&](int si) {
-    const uint8_t* p = rec_at(min(blk_begin + si * NB + cbk, blk_last)) + C::REC_KS + 64 * gq;
+  // loaders for set si of span sp
+  auto load_ksz = [&](Span sp, int si) {
+    const uint8_t* p = span_rec<C>(g, blocks, table, sp, sp.begin + si * NB + cbk) + C::REC_KS + 64 * gq;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       ksz[k] = *reinterpret_cast<const uint4*>(p + 16 * k);
       ksz[4 + k] = *reinterpret_cast<const uint4*>(p + (C::REC_KZ - C::REC_KS) + 16 * k);
     }
   };
-  auto load_kc = [&](int si) {
+  auto load_kc = [&](Span sp, int si) {
     const int off = C::REC_KC + n * C::KROW + gq * C::KLANE;
 #pragma unroll
     for (int bi = 0; bi < NB; ++bi) {
-      const uint8_t* p = rec_at(min(blk_begin + si * NB + bi, blk_last)) + off;
+      const uint8_t* p = span_rec<C>(g, blocks, table, sp, sp.begin + si * NB + bi) + off;
 #pragma unroll
       for (int tt = 0; tt < TPB; ++tt) kc[bi][tt] = load_chunk<C::KLANE>(p + 16 * tt * C::KROW);
     }
   };
-  auto load_vsz = [&](int si) {
-    const uint8_t* p = rec_at(min(blk_begin + si * NB + cbk, blk_last)) + C::REC_VS + 8 * gq;
+  auto load_vsz = [&](Span sp, int si) {
+    const uint8_t* p = span_rec<C>(g, blocks, table, sp, sp.begin + si * NB + cbk) + C::REC_VS + 8 * gq;
 #pragma unroll
     for (int tt = 0; tt < TPB; ++tt)
 #pragma unroll
@@ -476,41 +509,45 @@ __device__ __forceinline__ void quant_item(const Geom& g, const WaveLds<C>& L, c
         vsz[tt][j][1] = *reinterpret_cast<const uint2*>(p + (C::REC_VZ - C::REC_VS) + off);
       }
   };
-  auto load_vc = [&](int si) {
+  auto load_vc = [&](Span sp, int si) {
 #pragma unroll
     for (int ks = 0; ks < KS_SET; ++ks) {
       const int tok = 32 * ks + 8 * gq;   // set-relative first token of this lane group's run
       // for G >= 32 the k-step lies in one block (wave-uniform); G = 16 spans two
       const int bi = C::G >= 32 ? (32 * ks) / C::G : tok / C::G;
-      const uint8_t* p = rec_at(min(blk_begin + si * NB + bi, blk_last));
+      const uint8_t* p = span_rec<C>(g, blocks, table, sp, sp.begin + si * NB + bi);
       const int g8 = (tok % C::G) / 8;
       vc[ks] = load_chunk<C::VLANE>(p + C::REC_VC + (g8 * 16 + n) * C::VLANE);
     }
   };
-
-  if (nsets > 0) {
-    load_ksz(0);
-    load_kc(0);
-    load_vsz(0);
-    load_vc(0);
-  }
-
-  // running state: per lane for its column's head
-  float m_ref = -INFINITY, l_part = 0.f, lam[NGR];
+  auto page_ok = [&](Span sp, int blk) -> bool {
+    if constexpr (!C::PAGED) return true;
+    const int page = table[(size_t)sp.b * g.max_blocks + blk];
+    return page >= 0 && page < g.num_pages;
+  };
+  // the query of span sp: raw words, then scaled into L.qs
+  auto query_words = [&](Span sp, uint32_t (&w)[QW]) {
+    const uint32_t* src = reinterpret_cast<const uint32_t*>(q + ((size_t)sp.b * g.Hq + (size_t)sp.h * NG) * D);
 #pragma unroll
-  for (int j = 0; j < NGR; ++j) lam[j] = 0.f;
+    for (int k = 0; k < QW; ++k) w[k] = src[lane + 64 * k];
+  };
+  auto store_query = [&](const uint32_t (&w)[QW]) {
+#pragma unroll
+    for (int k = 0; k < QW; ++k)
+      *reinterpret_cast<float2*>(L.qs + 2 * (lane + 64 * k)) =
+          make_float2(in_val<C>(w[k] & 0xffffu) * qscale, in_val<C>(w[k] >> 16) * qscale);
+  };
+
+  // running state of the current unit: per lane for its column's head
+  float m_ref, l_part, lam[NGR];
   f32x4 dpv[8];
-#pragma unroll
-  for (int nt = 0; nt < 8; ++nt) dpv[nt] = {0.f, 0.f, 0.f, 0.f};
 
-  // One set. With `prefetch`, each register buffer is refilled for the next
-  // set right after its last use here; the last set is peeled off so that the
-  // loads are never under a branch (the compiler then keeps them in flight
-  // across the loop instead of waiting for them).
-  auto run_set = [&](int si, auto prefetch) {
-    constexpr bool PF = decltype(prefetch)::value;
-    const int my_b = blk_begin + si * NB + cbk;
-    const bool my_blk = col_used && my_b < blk_end && page_ok(min(my_b, blk_last));
+  // One set si of span cur; prefetches set nsi of span nsp into each register
+  // buffer right after its last use (always a valid set, so the loads are never
+  // under a branch and stay in flight across the loop).
+  auto run_set = [&](Span cur, int si, Span nsp, int nsi) {
+    const int my_b = cur.begin + si * NB + cbk;
+    const bool my_blk = col_used && my_b < cur.end && page_ok(cur, min(my_b, cur.end - 1));
     // ---- B operand: q~ = q' * s_K (hi/lo) and kappa = q' . z_K for the column ----
     uint4 bhi[4], blo[4];
     float kap = 0.f;
@@ -542,7 +579,7 @@ __device__ __forceinline__ void quant_item(const Geom& g, const WaveLds<C>& L, c
       }
       kap = reduce_rows(kap, OpAdd{});
     }
-    if constexpr (PF) load_ksz(si + 1);
+    load_ksz(nsp, nsi);
 
     // ---- scores: D[token][column] for every tile of every block of the set ----
     float sc[TPB][4];
@@ -567,7 +604,7 @@ __device__ __forceinline__ void quant_item(const Geom& g, const WaveLds<C>& L, c
         for (int i = 0; i < 4; ++i) sc[tt][i] = mine ? acc[i] : sc[tt][i];
       }
     }
-    if constexpr (PF) load_kc(si + 1);
+    load_kc(nsp, nsi);
     if (!my_blk) {
 #pragma unroll
       for (int tt = 0; tt < TPB; ++tt)
@@ -638,7 +675,7 @@ __device__ __forceinline__ void quant_item(const Geom& g, const WaveLds<C>& L, c
         }
       }
     }
-    if constexpr (PF) load_vsz(si + 1);
+    load_vsz(nsp, nsi);
     wave_lds_fence();
 
     // ---- P.V: D[head hi|lo][channel] += p~ . code ----
@@ -654,57 +691,119 @@ __device__ __forceinline__ void quant_item(const Geom& g, const WaveLds<C>& L, c
 #pragma unroll
       for (int nt = 0; nt < 8; ++nt) dpv[nt] = mfma_bf16(av[(16 * nt) / C::GV], bv[nt], dpv[nt]);
     }
-    if constexpr (PF) load_vc(si + 1);
+    load_vc(nsp, nsi);
     wave_lds_fence();
   };
 
-  for (int si = 0; si + 1 < nsets; ++si) run_set(si, std::true_type{});
-  if (nsets > 0) run_set(nsets - 1, std::false_type{});
+  // the unit's result: per head h', o = D[h'] + D[NG+h'] + lam(h', group)
+  auto finish_unit = [&](float* __restrict__ out_part) {
+    const float lsum = reduce_head<NG>(col_used ? l_part : 0.f, n, OpAdd{});
+    float lm[NGR];
+#pragma unroll
+    for (int j = 0; j < NGR; ++j) lm[j] = reduce_head<NG>(col_used ? lam[j] : 0.f, n, OpAdd{});
+    float* ol = reinterpret_cast<float*>(L.buf);   // [2NG][D]
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 4 * gq + i;
+        if (r < 2 * NG) ol[r * D + 16 * nt + n] = dpv[nt][i];
+      }
+    if (gq == 0 && n < NG) {
+#pragma unroll
+      for (int j = 0; j < NGR; ++j) L.lam[n * NGR + j] = lm[j];
+      out_part[n * (D + 2) + D] = m_ref;
+      out_part[n * (D + 2) + D + 1] = lsum;
+    }
+    wave_lds_fence();
+#pragma unroll
+    for (int j = 0; j < NG; ++j)
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const int c = lane + 64 * k;
+        out_part[j * (D + 2) + c] = ol[j * D + c] + ol[(NG + j) * D + c] + L.lam[j * NGR + c / C::GV];
+      }
+    wave_lds_fence();   // L.buf and L.lam are rewritten by the next unit
+  };
 
-  // ---- item result: per head h', o = D[h'] + D[NG+h'] + lam(h', group) ----
-  l_part = reduce_head<NG>(col_used ? l_part : 0.f, n, OpAdd{});
-#pragma unroll
-  for (int j = 0; j < NGR; ++j) lam[j] = reduce_head<NG>(col_used ? lam[j] : 0.f, n, OpAdd{});
-  float* ol = reinterpret_cast<float*>(L.buf);   // [2NG][D]
-#pragma unroll
-  for (int nt = 0; nt < 8; ++nt)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = 4 * gq + i;
-      if (r < 2 * NG) ol[r * D + 16 * nt + n] = dpv[nt][i];
-    }
-  if (gq == 0 && n < NG) {
-#pragma unroll
-    for (int j = 0; j < NGR; ++j) L.lam[n * NGR + j] = lam[j];
-    out_part[n * (D + 2) + D] = m_ref;
-    out_part[n * (D + 2) + D + 1] = l_part;
+  int u = first;
+  Span cur = first_span;
+  {
+    uint32_t w[QW];
+    query_words(cur, w);
+    store_query(w);
+    wave_lds_fence();
   }
+  load_ksz(cur, 0);
+  load_kc(cur, 0);
+  load_vsz(cur, 0);
+  load_vc(cur, 0);
+  while (true) {
+    m_ref = -INFINITY;
+    l_part = 0.f;
+#pragma unroll
+    for (int j = 0; j < NGR; ++j) lam[j] = 0.f;
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt) dpv[nt] = {0.f, 0.f, 0.f, 0.f};
+    const int nsets = (cur.end - cur.begin + NB - 1) / NB;
+    for (int si = 0; si + 1 < nsets; ++si) run_set(cur, si, cur, si + 1);
+    // last set: its prefetch is the next unit's first set (or, at the end of
+    // the stream, this set again: cache hits)
+    const int nu = claim(claimed);
+    const bool more = nu < units;
+    const Span nxt = more ? locate(nu) : cur;
+    uint32_t qn[QW];
+    query_words(nxt, qn);
+    run_set(cur, nsets - 1, nxt, more ? 0 : nsets - 1);
+    finish_unit(ws + (size_t)u * NG * (D + 2));
+    if (!more) break;
+    store_query(qn);
+    wave_lds_fence();
+    u = nu;
+    cur = nxt;
+    claimed = issue();
+  }
+}
+
+// The query of (sequence b, kv head h), scaled to log2 units, into L.qs: one
+// batch of independent loads, then the LDS writes.
+template <class C>
+__device__ __forceinline__ void load_query(const Geom& g, const WaveLds<C>& L, const uint16_t* __restrict__ q,
+                                           float qscale, int b, int h) {
+  constexpr int QW = C::NG * C::D / 128;   // 32-bit words per lane
+  const int lane = threadIdx.x & 63;
+  const uint32_t* src = reinterpret_cast<const uint32_t*>(q + ((size_t)b * g.Hq + (size_t)h * C::NG) * C::D);
+  uint32_t w[QW];
+#pragma unroll
+  for (int k = 0; k < QW; ++k) w[k] = src[lane + 64 * k];
+#pragma unroll
+  for (int k = 0; k < QW; ++k)
+    *reinterpret_cast<float2*>(L.qs + 2 * (lane + 64 * k)) =
+        make_float2(in_val<C>(w[k] & 0xffffu) * qscale, in_val<C>(w[k] >> 16) * qscale);
   wave_lds_fence();
-#pragma unroll
-  for (int j = 0; j < NG; ++j)
-#pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      const int c = lane + 64 * k;
-      out_part[j * (D + 2) + c] = ol[j * D + c] + ol[(NG + j) * D + c] + L.lam[j * NGR + c / C::GV];
-    }
 }
 
 // ------------------------------------------------------------------------------------
-// The kernel. One wave = one work item; 4 waves per workgroup share the item
-// table in LDS and nothing else.
+// The kernel: persistent waves (2 per SIMD). The units are dealt to kQueues
+// queues (unit u to queue u % kQueues) served by the workgroups with
+// blockIdx.x % kQueues == queue -- with the usual round-robin placement of
+// workgroups that is one queue per XCD, so the counters, each on its own cache
+// line, are not all hit by every wave. A wave's first unit of its queue is
+// fixed by its index; later ones come from the queue's counter in the state
+// words. The last wave to finish re-arms the counters. 4 waves per workgroup
+// share the unit plan in LDS and nothing else.
 // ------------------------------------------------------------------------------------
 template <class C>
-__global__ __launch_bounds__(256) void decode_fast_kernel(Geom g, const uint8_t* __restrict__ blocks,
-                                                          const int32_t* __restrict__ table,
-                                                          const uint16_t* __restrict__ k_ring,
-                                                          const uint16_t* __restrict__ v_ring,
-                                                          const int32_t* __restrict__ state,
-                                                          const uint16_t* __restrict__ q, float qscale, int bps,
-                                                          int nq_max, int nr_max, float* __restrict__ ws) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void decode_fast_kernel(
+    Geom g, const uint8_t* __restrict__ blocks, const int32_t* __restrict__ table,
+    const uint16_t* __restrict__ k_ring, const uint16_t* __restrict__ v_ring, int32_t* __restrict__ state,
+    const uint16_t* __restrict__ q, float qscale, int max_blk, int* __restrict__ ws_plan, float* __restrict__ ws) {
   constexpr int NG = C::NG, D = C::D;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  int* prefix = reinterpret_cast<int*>(smem);
-  const int pre_bytes = ((g.B + 1) * 4 + 15) & ~15;
+  int* plan = reinterpret_cast<int*>(smem);
+  const int pints = plan_ints(g.B);
+  int* red = plan + pints;
+  const int pre_bytes = ((pints + 16 * kSections) * 4 + 15) & ~15;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   uint8_t* wl = smem + pre_bytes + wave * C::LDS_WAVE;
   WaveLds<C> L;
@@ -714,45 +813,68 @@ __global__ __launch_bounds__(256) void decode_fast_kernel(Geom g, const uint8_t*
   L.lam = L.alpha + 16;
   L.zero16 = reinterpret_cast<uint4*>(L.lam + NG * C::NGR);
 
-  build_prefix(g, state, bps, kRingChunk, nq_max, nr_max, prefix, blockIdx.x == 0);
-  const int w = blockIdx.x * kWaves + wave;
-  if (w >= g.Hkv * prefix[g.B]) return;
-  const ItemRef it = locate_item(g, prefix, w);
-  // the item is the same for every lane of the wave: keep it in scalar registers
-  const int b = __builtin_amdgcn_readfirstlane(it.b);
-  const int h = __builtin_amdgcn_readfirstlane(it.h);
-  const int item = __builtin_amdgcn_readfirstlane(it.item);
-  const int Q = state[4 * b + kStateQ], S = state[4 * b + kStateS];
-  bool unused_flag = false;
-  const ItemCounts cnt = items_of(Q, S, g.G, bps, kRingChunk, nq_max, nr_max, &unused_flag);
+  build_unit_plan(g, state, max_blk, C::NB, kRingChunk, plan, red, blockIdx.x == 0);
+  if (blockIdx.x == 0)
+    for (int i = threadIdx.x; i < pints; i += blockDim.x) ws_plan[i] = plan[i];
   if (lane == 0) *L.zero16 = make_uint4(0, 0, 0, 0);
+  const int units = plan[kPlanUnits];
+  // queue of this workgroup; gridDim.x is a multiple of kQueues
+  const int queue = blockIdx.x % kQueues;
+  const int qwaves = (int)(gridDim.x / kQueues) * kWaves;   // waves serving the queue
+  int* counter = state + state_queue_word(g.B, queue);
+  int* done = state + state_done_word(g.B);
+  auto qs_of = [&](int b, int& Q, int& S) {
+    Q = state[4 * b + kStateQ];
+    S = state[4 * b + kStateS];
+  };
+  auto nblk_of = [&](int b) { return min(state[4 * b + kStateQ] / g.G, max_blk); };
 
-  // scaled query, log2 units: q' = q * softmax_scale * log2(e)
-  for (int idx = lane; idx < NG * D; idx += 64) {
-    const int j = idx / D, c = idx % D;
-    L.qs[idx] = in_val<C>(q[((size_t)b * g.Hq + h * NG + j) * D + c]) * qscale;
+  auto issue = [&]() -> int {
+    int v = 0;
+    if (lane == 0) v = atomicAdd(counter, 1);
+    return v;
+  };
+  auto claim = [&](int raw) -> int { return queue + kQueues * (qwaves + __builtin_amdgcn_readfirstlane(raw)); };
+  auto span_of = [&](int uu) -> Span {
+    const Unit un = locate_unit(g, plan, uu, qs_of, nblk_of);
+    Span sp;
+    sp.b = __builtin_amdgcn_readfirstlane(un.b);
+    sp.h = __builtin_amdgcn_readfirstlane(un.h);
+    sp.begin = __builtin_amdgcn_readfirstlane(un.begin);
+    sp.end = __builtin_amdgcn_readfirstlane(un.end);
+    return sp;
+  };
+
+  // ring units come first in every queue; the claim for the next unit is in
+  // flight while a unit runs
+  int u = queue + kQueues * ((int)(blockIdx.x / kQueues) * kWaves + wave);
+  int claimed = issue();
+  while (u < units && u < plan[kPlanSec]) {
+    const Span sp = span_of(u);
+    load_query<C>(g, L, q, qscale, sp.b, sp.h);
+    ring_unit<C>(g, L, k_ring, v_ring, sp.b * g.Hkv + sp.h, sp.begin, sp.end, ws + (size_t)u * NG * (D + 2));
+    u = claim(claimed);
+    claimed = issue();
   }
-  wave_lds_fence();
-
-  float* out_part = ws + (size_t)w * NG * (D + 2);
-  if (item >= cnt.nq) {
-    const int t0 = Q + (item - cnt.nq) * kRingChunk;
-    ring_chunk<C>(g, L, k_ring, v_ring, b * g.Hkv + h, t0, min(S, t0 + kRingChunk), out_part);
-  } else {
-    const int blk_begin = item * bps;
-    quant_item<C>(g, L, blocks, table, b, h, blk_begin, min(blk_begin + bps, Q / g.G), out_part);
+  if (u < units) quant_stream<C>(g, L, blocks, table, q, qscale, units, u, span_of(u), claimed, span_of, issue, claim, ws);
+  if (lane == 0) {
+    __threadfence();
+    if (atomicAdd(done, 1) == (int)gridDim.x * kWaves - 1) {
+      for (int k = 0; k < kQueues; ++k) atomicExch(state + state_queue_word(g.B, k), 0);
+      atomicExch(done, 0);
+    }
   }
 }
 
 template <class C>
-hipError_t launch_fast(const Geom& g, const kvq_cache& c, const void* q, float scale, int bps, int nq_max,
-                       int nr_max, size_t items_max, void* ws, hipStream_t s) {
-  const int wgs = (int)((items_max + kWaves - 1) / kWaves);
-  const size_t lds = (size_t)(((g.B + 1) * 4 + 15) & ~15) + (size_t)kWaves * C::LDS_WAVE;
-  hipLaunchKernelGGL((decode_fast_kernel<C>), dim3(wgs), dim3(256), lds, s, g,
+hipError_t launch_fast(const Geom& g, const kvq_cache& c, const void* q, float scale, int max_blk, int grid,
+                       void* ws, hipStream_t s) {
+  const size_t lds = (size_t)(((plan_ints(g.B) + 16 * kSections) * 4 + 15) & ~15) + (size_t)kWaves * C::LDS_WAVE;
+  hipLaunchKernelGGL((decode_fast_kernel<C>), dim3(grid), dim3(256), lds, s, g,
                      static_cast<const uint8_t*>(c.blocks), c.block_table, static_cast<const uint16_t*>(c.k_ring),
                      static_cast<const uint16_t*>(c.v_ring), c.state, static_cast<const uint16_t*>(q),
-                     scale * kLog2e, bps, nq_max, nr_max, static_cast<float*>(ws));
+                     scale * kLog2e, max_blk, static_cast<int*>(ws),
+                     reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + plan_bytes(g.B)));
   return hipGetLastError();
 }
 

@@ -13,8 +13,7 @@ struct FastEntry {
   int ng, kb, vb, G, GV, dtype;
   bool paged;
   int nb_set;
-  hipError_t (*launch)(const Geom&, const kvq_cache&, const void*, float, int, int, int, size_t, void*,
-                       hipStream_t);
+  hipError_t (*launch)(const Geom&, const kvq_cache&, const void*, float, int, int, void*, hipStream_t);
 };
 
 template <int NG, int KB, int VB, int G, int GV, bool BF16, bool PAGED>
@@ -47,17 +46,33 @@ const FastEntry* find(const Geom& g) {
 
 }  // namespace
 
+int fast_ring_chunk() { return fast::kRingChunk; }
+
 bool fast_supported(const Geom& g, int* blocks_per_set) {
   const FastEntry* e = find(g);
   if (e && blocks_per_set) *blocks_per_set = e->nb_set;
   return e != nullptr;
 }
 
+// Persistent grid: two 4-wave workgroups per compute unit (the kernel is built
+// for 2 waves per SIMD), rounded up to a multiple of the work queues.
+int persistent_grid() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 64 * kQueues;
+  if (cached[dev] == 0) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+    cached[dev] = (2 * cus + kQueues - 1) / kQueues * kQueues;
+  }
+  return cached[dev];
+}
+
 hipError_t launch_decode_fast(const Geom& g, const kvq_cache& c, const void* q, float scale, const DecodePlan& p,
                               void* ws, hipStream_t s) {
   const FastEntry* e = find(g);
   if (e == nullptr) return hipErrorInvalidValue;
-  return e->launch(g, c, q, scale, p.bps, p.nq_max, p.nr_max, p.items_max, ws, s);
+  return e->launch(g, c, q, scale, p.max_blk, persistent_grid(), ws, s);
 }
 
 }  // namespace kvq

@@ -1,0 +1,262 @@
+// Work units of the split-sequence decode, shared by the decode kernels and the
+// combine kernel (gfx950).
+//
+// Every (sequence b, kv head h) pair ("pair" p = b*H_kv + h) contributes:
+//   - ring units: its full-precision tokens [Q_b, S_b) in runs of `rc` tokens;
+//   - big units of `ub` quantized blocks covering its leading blocks;
+//   - then up to kTailUnits medium units of `um` blocks and up to kTailUnits
+//     small units of `us` blocks (one set) covering its last blocks.
+// Units are numbered section by section -- all ring units, then all big, all
+// medium and all small units -- and within a section by sequence, kv head and
+// position. Waves take units in that order, so the latency-bound ring units
+// start first and the units shrink towards the end of the launch, which keeps
+// the last waves from idling the GPU. Each unit leaves one partial softmax state per
+// query head of its group in slot u of the workspace; the combine kernel merges
+// the partials of each pair.
+//
+// The unit sizes follow from the total number of quantized blocks on the
+// device (about kUnitsTarget big units in all), so they depend only on the
+// lengths and the configuration: the partition -- and with it every rounding
+// in the result -- is the same from run to run, whichever wave takes a unit.
+#pragma once
+
+#include "common.h"
+
+namespace kvq {
+
+constexpr int kUnitsTarget = 8192;   // about 4 big units per wave slot of a 256-CU GPU at 2 waves per SIMD
+constexpr int kMaxUnitSets = 64;     // cap on the sets of one big unit
+constexpr int kTailUnits = 4;        // medium and small units per pair (at most)
+
+// Plan words, at the start of the workspace (written by the decode kernel, read
+// by the combine kernel) and in each decode workgroup's LDS.
+enum {
+  kPlanUnits = 0,   // units in all
+  kPlanSec = 1,     // units in all of sections 0..3 (ring, big, medium, small): words 1..4
+  kPlanUb = 5,      // blocks per big unit
+  kPlanUm = 6,      // blocks per medium unit
+  kPlanUs = 7,      // blocks per small unit
+  kPlanRc = 8,      // ring tokens per ring unit
+  kPlanHdr = 12,    // then pre[s][B + 1] for each section s: exclusive prefix over
+};                  // sequences of the section's units of one kv head
+constexpr int kSections = 4;
+
+__host__ __device__ inline int plan_ints(int B) { return kPlanHdr + kSections * (B + 1); }
+inline size_t plan_bytes(int B) { return ((size_t)plan_ints(B) * 4 + 255) & ~(size_t)255; }
+
+// Upper bound on the units when no sequence has more than max_blk quantized
+// blocks, sets hold nb_set blocks and ring units rc tokens: ceil(C/rc) ring
+// units per pair, at most max(kUnitsTarget, P*ceil(max_blk/(kMaxUnitSets*nb_set)))
+// + P big units, and at most kTailUnits medium and kTailUnits small units per
+// pair.
+inline size_t units_max(const Geom& g, int max_blk, int nb_set, int rc) {
+  const size_t P = (size_t)g.B * g.Hkv;
+  const size_t cap = (size_t)kMaxUnitSets * nb_set;
+  const size_t big = std::max<size_t>(kUnitsTarget, P * ((max_blk + cap - 1) / cap));
+  return P * (size_t)((g.C + rc - 1) / rc) + big + P + 2 * P * kTailUnits;
+}
+
+// Blocks of sequence b's pair in each quantized section: big units cover
+// [0, body), medium [body, body + mid), small [body + mid, nblk).
+struct Tail {
+  int mid, small;
+};
+__host__ __device__ inline Tail tail_of(int nblk, int um, int us) {
+  Tail t;
+  t.small = nblk < kTailUnits * us ? nblk : kTailUnits * us;
+  const int rest = nblk - t.small;
+  t.mid = rest < kTailUnits * um ? rest : kTailUnits * um;
+  return t;
+}
+
+#ifdef __HIPCC__
+// Exclusive prefix sums of arr[k][0..n) in place (arr[k][n] gets the total),
+// by every thread of a workgroup of blockDim.x = 64*w threads (w <= 16).
+// `red` is LDS scratch of 16*K ints. Ends with a barrier.
+template <int K>
+__device__ inline void block_scan(int* (&arr)[K], int n, int* red) {
+  const int nt = blockDim.x, t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int per = (n + nt - 1) / nt;
+  const int lo = min(n, t * per), hi = min(n, lo + per);
+  int sum[K], inc[K];
+#pragma unroll
+  for (int k = 0; k < K; ++k) {
+    sum[k] = 0;
+    for (int i = lo; i < hi; ++i) sum[k] += arr[k][i];
+    inc[k] = sum[k];
+  }
+  // inclusive scan over the wave
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      const int y = __shfl_up(inc[k], off, 64);
+      if (lane >= off) inc[k] += y;
+    }
+  }
+  if (lane == 63) {
+#pragma unroll
+    for (int k = 0; k < K; ++k) red[16 * k + wave] = inc[k];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < K; ++k) {
+    int e = inc[k] - sum[k];   // exclusive prefix of this thread's range
+    for (int w = 0; w < wave; ++w) e += red[16 * k + w];
+    for (int i = lo; i < hi; ++i) {
+      const int v = arr[k][i];
+      arr[k][i] = e;
+      e += v;
+    }
+    if (t == nt - 1) arr[k][n] = e;
+  }
+  __syncthreads();
+}
+
+// Build the plan in LDS (`plan`, plan_ints(B) ints) from the device-side
+// lengths; every thread of the workgroup calls it. `red` is LDS scratch of 64
+// ints. Sequences with more than max_blk quantized blocks are cut to max_blk
+// (the caller's max_seq_tokens was too small) and, if report_too_long, flag
+// KVQ_DEV_TOO_LONG.
+__device__ inline void build_unit_plan(const Geom& g, int32_t* state, int max_blk, int nb_set, int rc, int* plan,
+                                       int* red, bool report_too_long) {
+  int* pre[kSections];
+  for (int k = 0; k < kSections; ++k) pre[k] = plan + kPlanHdr + k * (g.B + 1);
+  // total sets over all pairs
+  int sets = 0;
+  bool too_long = false;
+  for (int b = threadIdx.x; b < g.B; b += blockDim.x) {
+    const int Q = state[4 * b + kStateQ], S = state[4 * b + kStateS];
+    int nblk = Q / g.G;
+    if (nblk > max_blk) {
+      nblk = max_blk;
+      too_long = true;
+    }
+    const int r = min(max(S - Q, 0), g.C);
+    pre[0][b] = (r + rc - 1) / rc;
+    pre[1][b] = nblk;   // stash
+    sets += (nblk + nb_set - 1) / nb_set;
+  }
+  if (too_long && report_too_long) atomicOr(&state[4 * g.B], KVQ_DEV_TOO_LONG);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) sets += __shfl_xor(sets, off, 64);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = sets;
+  __syncthreads();
+  long long tot = 0;
+  for (int w = 0; w < (int)(blockDim.x >> 6); ++w) tot += red[w];
+  tot *= g.Hkv;
+  int ub_sets = (int)((tot + kUnitsTarget - 1) / kUnitsTarget);
+  ub_sets = max(1, min(kMaxUnitSets, ub_sets));
+  const int ub = ub_sets * nb_set, um = max(1, ub_sets / 4) * nb_set, us = nb_set;
+  __syncthreads();   // red is reused by the scan
+  for (int b = threadIdx.x; b < g.B; b += blockDim.x) {
+    const int nblk = pre[1][b];
+    const Tail t = tail_of(nblk, um, us);
+    pre[1][b] = (nblk - t.mid - t.small + ub - 1) / ub;
+    pre[2][b] = (t.mid + um - 1) / um;
+    pre[3][b] = (t.small + us - 1) / us;
+  }
+  __syncthreads();
+  block_scan<kSections>(pre, g.B, red);
+  if (threadIdx.x == 0) {
+    int tot_units = 0;
+    for (int k = 0; k < kSections; ++k) {
+      plan[kPlanSec + k] = g.Hkv * pre[k][g.B];
+      tot_units += plan[kPlanSec + k];
+    }
+    plan[kPlanUnits] = tot_units;
+    plan[kPlanUb] = ub;
+    plan[kPlanUm] = um;
+    plan[kPlanUs] = us;
+    plan[kPlanRc] = rc;
+  }
+  __syncthreads();
+}
+
+// What unit u is.
+struct Unit {
+  int b, h;
+  bool ring;
+  int begin, end;   // ring: token range; else quantized block range
+};
+
+// Largest b in [0, B) with pre[b] * Hkv <= v (pre non-decreasing, pre[0] = 0).
+__device__ __forceinline__ int find_seq(const int* pre, int B, int Hkv, int v) {
+  int lo = 0, hi = B - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (Hkv * pre[mid] <= v) lo = mid;
+    else hi = mid - 1;
+  }
+  return lo;
+}
+
+// `qs_of(b, Q, S)` gives the quantized prefix and length of sequence b;
+// `nblk_of(b)` its (clamped) quantized blocks.
+template <class QsOf, class NblkOf>
+__device__ inline Unit locate_unit(const Geom& g, const int* plan, int u, QsOf qs_of, NblkOf nblk_of) {
+  int v = u, sec = 0;
+  while (sec < kSections - 1 && v >= plan[kPlanSec + sec]) {
+    v -= plan[kPlanSec + sec];
+    ++sec;
+  }
+  const int* pre = plan + kPlanHdr + sec * (g.B + 1);
+  const int b = find_seq(pre, g.B, g.Hkv, v);
+  const int n = pre[b + 1] - pre[b];
+  v -= g.Hkv * pre[b];
+  Unit r;
+  r.b = b;
+  r.h = v / n;
+  const int i = v % n;
+  r.ring = sec == 0;
+  if (sec == 0) {
+    int Q, S;
+    qs_of(b, Q, S);
+    const int rc = plan[kPlanRc];
+    r.begin = Q + i * rc;
+    r.end = min(S, r.begin + rc);
+  } else {
+    const int nblk = nblk_of(b);
+    const int um = plan[kPlanUm], us = plan[kPlanUs];
+    const Tail t = tail_of(nblk, um, us);
+    const int body = nblk - t.mid - t.small;
+    const int size = sec == 1 ? plan[kPlanUb] : (sec == 2 ? um : us);
+    const int start = sec == 1 ? 0 : (sec == 2 ? body : body + t.mid);
+    const int stop = sec == 1 ? body : (sec == 2 ? body + t.mid : nblk);
+    r.begin = start + i * size;
+    r.end = min(stop, r.begin + size);
+  }
+  return r;
+}
+
+// Slot of the i-th partial of pair (b, h): its units section by section.
+struct PairUnits {
+  int n;                      // partials of the pair
+  int cnt[kSections];         // per section
+  int first[kSections];       // first slot per section
+  __device__ __forceinline__ int slot(int i) const {
+#pragma unroll
+    for (int k = 0; k < kSections - 1; ++k) {
+      if (i < cnt[k]) return first[k] + i;
+      i -= cnt[k];
+    }
+    return first[kSections - 1] + i;
+  }
+};
+__device__ inline PairUnits pair_units(const Geom& g, const int* plan, int b, int h) {
+  PairUnits p;
+  p.n = 0;
+  int base = 0;
+#pragma unroll
+  for (int k = 0; k < kSections; ++k) {
+    const int* pre = plan + kPlanHdr + k * (g.B + 1);
+    p.cnt[k] = pre[b + 1] - pre[b];
+    p.first[k] = base + g.Hkv * pre[b] + h * p.cnt[k];
+    p.n += p.cnt[k];
+    base += plan[kPlanSec + k];
+  }
+  return p;
+}
+#endif
+
+}  // namespace kvq
