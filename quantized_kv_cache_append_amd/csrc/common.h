@@ -121,6 +121,19 @@ __device__ __forceinline__ bool last_arrival(int* counter, int total) {
   }
   return false;
 }
+// Persistent grid of a kernel of 256-thread workgroups: as many workgroups as
+// stay resident at once (from the runtime's occupancy for this kernel and LDS
+// size), rounded up to a multiple of the decode work queues.
+template <class K>
+inline int persistent_grid(K kernel, size_t lds_bytes) {
+  int dev = 0, cus = 0, per_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    cus = 256;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 256, lds_bytes) != hipSuccess || per_cu < 1)
+    per_cu = 1;
+  return (cus * per_cu + kQueues - 1) / kQueues * kQueues;
+}
 #endif
 
 // Launch wrappers (defined in the .hip files). Return hipSuccess or the error.
@@ -136,16 +149,17 @@ hipError_t launch_decode(const Geom& g, const kvq_cache& c, const void* q, float
 struct DecodePlan {
   bool fast;          // MFMA kernel (else the generic VALU kernel)
   int nb_set;         // blocks per set (unit sizes are whole sets)
+  int ring_chunk;     // ring tokens per ring unit
   int max_blk;        // quantized blocks per (sequence, kv head) the workspace is sized for
   size_t units_max;   // upper bound on work units
   size_t ws_bytes;    // workspace bytes: the unit plan, then the partial states
 };
 DecodePlan plan_decode(const Geom& g, int max_seq_tokens);
 
-// MFMA path (decode_fast_dispatch.hip): whether a configuration has an
-// instantiation, its blocks per set, and the launch.
-bool fast_supported(const Geom& g, int* blocks_per_set);
-int fast_ring_chunk();   // ring tokens per ring unit of the MFMA path
+// Specialised paths (decode_fast_dispatch.hip): whether a configuration has an
+// instantiation, its blocks per set and ring tokens per ring unit, and the
+// launch.
+bool fast_supported(const Geom& g, int* blocks_per_set, int* ring_chunk);
 hipError_t launch_decode_fast(const Geom& g, const kvq_cache& c, const void* q, float scale, const DecodePlan& p,
                               void* ws, hipStream_t s);
 

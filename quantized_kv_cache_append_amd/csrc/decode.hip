@@ -234,59 +234,71 @@ __global__ __launch_bounds__(256) void decode_generic_kernel(
 // Merge the partial states of one (sequence, query head) (scores in log2
 // units): with M = max m_i, o = sum_i 2^(m_i - M) o_i / sum_i 2^(m_i - M) l_i.
 // The units of the pair come from the plan the decode kernel left in the
-// workspace.
+// workspace. One workgroup of kCombineThreads per output row: thread (slice,
+// channel) merges partials slice, slice + SL, ... of its channel with a running
+// maximum, all of its loads in flight together for up to eight partials; the
+// slices are then merged through LDS.
+constexpr int kCombineThreads = 1024;
+
 template <int D>
-__global__ __launch_bounds__(64) void combine_kernel(Geom g, const int* __restrict__ plan,
-                                                     const float* __restrict__ ws, float* __restrict__ out) {
-  constexpr int CPL = D / 64;
+__global__ __launch_bounds__(kCombineThreads) void combine_kernel(Geom g, const int* __restrict__ plan,
+                                                                  const float* __restrict__ ws,
+                                                                  float* __restrict__ out) {
+  constexpr int SL = kCombineThreads / D;   // slices of the partials
+  __shared__ float sm[SL], sl_sum[SL], part[SL][D];
   const int bh = blockIdx.x;
   const int b = bh / g.Hq, hq = bh % g.Hq;
   const int h = hq / g.ng, j = hq % g.ng;
-  const int lane = threadIdx.x;
+  const int t = threadIdx.x, c = t % D, sl = t / D;
   const PairUnits pu = pair_units(g, plan, b, h);
-  const int cb = pu.n;
-  auto slot = [&](int i) -> int { return pu.slot(i); };
   const size_t stride = (size_t)g.ng * (D + 2);
   const float* src0 = ws + (size_t)j * (D + 2);
 
-  // the unit maxima, 64 at a time, then their maximum
-  float M = -INFINITY;
-  for (int i = lane; i < cb; i += 64) M = fmaxf(M, src0[slot(i) * stride + D]);
-  M = wave_max(M);
-  float L = 0.f, acc[CPL];
+  float m = -INFINITY, L = 0.f, acc = 0.f;
+  for (int i0 = sl; i0 < pu.n; i0 += 8 * SL) {
+    float e[8], l[8], v[8];
 #pragma unroll
-  for (int k = 0; k < CPL; ++k) acc[k] = 0.f;
-  if (M != -INFINITY) {
-    int i = 0;
-    for (; i + 4 <= cb; i += 4) {   // four independent unit loads in flight
-      float e[4], l[4], v[4][CPL];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const float* src = src0 + slot(i + u) * stride;
-        e[u] = src[D];
-        l[u] = src[D + 1];
-#pragma unroll
-        for (int k = 0; k < CPL; ++k) v[u][k] = src[lane + 64 * k];
-      }
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const float wgt = exp2f(e[u] - M);
-        L += wgt * l[u];
-#pragma unroll
-        for (int k = 0; k < CPL; ++k) acc[k] += wgt * v[u][k];
-      }
+    for (int u = 0; u < 8; ++u) {
+      const int i = i0 + u * SL;
+      const float* src = src0 + (size_t)pu.slot(i < pu.n ? i : sl) * stride;
+      e[u] = i < pu.n ? src[D] : -INFINITY;
+      l[u] = src[D + 1];
+      v[u] = src[c];
     }
-    for (; i < cb; ++i) {
-      const float* src = src0 + slot(i) * stride;
-      const float wgt = exp2f(src[D] - M);
-      L += wgt * src[D + 1];
+    float mn = m;
 #pragma unroll
-      for (int k = 0; k < CPL; ++k) acc[k] += wgt * src[lane + 64 * k];
+    for (int u = 0; u < 8; ++u) mn = fmaxf(mn, e[u]);
+    if (mn != -INFINITY) {
+      const float a = m == -INFINITY ? 0.f : exp2f(m - mn);
+      L *= a;
+      acc *= a;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const float wgt = e[u] == -INFINITY ? 0.f : exp2f(e[u] - mn);
+        L += wgt * l[u];
+        acc += wgt * v[u];
+      }
+      m = mn;
     }
   }
-  const float inv = (L > 0.f) ? 1.f / L : 0.f;
+  if (c == 0) sm[sl] = m;
+  __syncthreads();
+  float M = -INFINITY;
 #pragma unroll
-  for (int k = 0; k < CPL; ++k) out[((size_t)b * g.Hq + hq) * D + lane + 64 * k] = acc[k] * inv;
+  for (int k = 0; k < SL; ++k) M = fmaxf(M, sm[k]);
+  const float w = (m == -INFINITY) ? 0.f : exp2f(m - M);
+  part[sl][c] = w * acc;
+  if (c == 0) sl_sum[sl] = w * L;
+  __syncthreads();
+  if (t < D) {
+    float o = 0.f, Lt = 0.f;
+#pragma unroll
+    for (int k = 0; k < SL; ++k) {
+      o += part[k][t];
+      Lt += sl_sum[k];
+    }
+    out[((size_t)b * g.Hq + hq) * D + t] = (Lt > 0.f) ? o / Lt : 0.f;
+  }
 }
 
 template <int D, bool BF16>
@@ -306,11 +318,12 @@ hipError_t launch_generic(const Geom& g, const kvq_cache& c, const void* q, floa
 
 DecodePlan plan_decode(const Geom& g, int max_seq_tokens) {
   DecodePlan p{};
-  int nb_set = 1;
-  p.fast = fast_supported(g, &nb_set);
+  int nb_set = 1, rc = kRingAll;
+  p.fast = fast_supported(g, &nb_set, &rc);
   p.nb_set = p.fast ? nb_set : 1;
+  p.ring_chunk = p.fast ? rc : kRingAll;
   p.max_blk = std::max(max_seq_tokens - g.R, 0) / g.G;
-  p.units_max = units_max(g, p.max_blk, p.nb_set, p.fast ? fast_ring_chunk() : kRingAll);
+  p.units_max = units_max(g, p.max_blk, p.nb_set, p.ring_chunk);
   p.ws_bytes = plan_bytes(g.B) + p.units_max * (size_t)g.ng * (size_t)(g.d + 2) * 4;
   return p;
 }
@@ -332,9 +345,9 @@ hipError_t launch_decode(const Geom& g, const kvq_cache& c, const void* q, float
   const int* planp = static_cast<const int*>(ws);
   const float* parts = reinterpret_cast<const float*>(static_cast<const uint8_t*>(ws) + plan_bytes(g.B));
   if (g.d == 128)
-    hipLaunchKernelGGL((combine_kernel<128>), dim3(g.B * g.Hq), dim3(64), 0, s, g, planp, parts, out);
+    hipLaunchKernelGGL((combine_kernel<128>), dim3(g.B * g.Hq), dim3(kCombineThreads), 0, s, g, planp, parts, out);
   else
-    hipLaunchKernelGGL((combine_kernel<64>), dim3(g.B * g.Hq), dim3(64), 0, s, g, planp, parts, out);
+    hipLaunchKernelGGL((combine_kernel<64>), dim3(g.B * g.Hq), dim3(kCombineThreads), 0, s, g, planp, parts, out);
   return hipGetLastError();
 }
 

@@ -857,8 +857,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     claimed = issue();
   }
   if (u < units) quant_stream<C>(g, L, blocks, table, q, qscale, units, u, span_of(u), claimed, span_of, issue, claim, ws);
+  // All of this wave's claims have returned, so once every wave has counted
+  // itself here no claim is outstanding and the counters can be re-armed (no
+  // fence: the partial states reach the combine kernel at the launch boundary).
   if (lane == 0) {
-    __threadfence();
     if (atomicAdd(done, 1) == (int)gridDim.x * kWaves - 1) {
       for (int k = 0; k < kQueues; ++k) atomicExch(state + state_queue_word(g.B, k), 0);
       atomicExch(done, 0);
@@ -867,9 +869,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 }
 
 template <class C>
-hipError_t launch_fast(const Geom& g, const kvq_cache& c, const void* q, float scale, int max_blk, int grid,
-                       void* ws, hipStream_t s) {
+hipError_t launch_fast(const Geom& g, const kvq_cache& c, const void* q, float scale, int max_blk, void* ws,
+                       hipStream_t s) {
   const size_t lds = (size_t)(((plan_ints(g.B) + 16 * kSections) * 4 + 15) & ~15) + (size_t)kWaves * C::LDS_WAVE;
+  const int grid = persistent_grid(decode_fast_kernel<C>, lds);
   hipLaunchKernelGGL((decode_fast_kernel<C>), dim3(grid), dim3(256), lds, s, g,
                      static_cast<const uint8_t*>(c.blocks), c.block_table, static_cast<const uint16_t*>(c.k_ring),
                      static_cast<const uint16_t*>(c.v_ring), c.state, static_cast<const uint16_t*>(q),
