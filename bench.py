@@ -1,20 +1,29 @@
-"""Benchmark of one decode step of the quantized KV-cache hot path on one MI355X.
+"""Benchmark of the quantized KV-cache decode step on one MI355X.
 
-A step is the whole path for one batch: append one new key/value token per
-sequence into the full-precision ring, flush (quantize + pack any block that
-leaves the window), and decode attention of one query token per sequence over
-the packed cache plus the ring. Inputs are seeded synthetic tensors shaped like
-the workload and already resident in HBM when timing starts. To measure HBM
-rather than the 256 MB Infinity Cache, the step rotates over enough copies of
-the cache that their total exceeds 3x that size.
+A step is the whole hot path for one batch: append one new key/value token per
+sequence into the full-precision ring and flush (quantize + pack) any block
+that leaves the window -- one fused launch -- then decode attention of one
+query token per sequence over the packed cache plus the ring: the partial
+states of every work unit (the dominant kernel) and their merge. Inputs are
+seeded synthetic tensors shaped like the workload and already resident in HBM
+when timing starts. To measure HBM rather than the 256 MB Infinity Cache, the
+steps rotate over enough copies of the cache that their total exceeds 3x that
+size.
 
 Prints one JSON line on stdout; human-readable detail goes to stderr.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+`value` is the step's algorithmic bytes over its time (effective GB/s of the
+whole step); `roofline` is the decode-partials kernel's algorithmic bytes over
+its own event-timed duration, against the 8 TB/s HBM peak; `traffic` is the
+HBM traffic rocprofv3 counters measured for that kernel (profiles/), reported
+only while the kernel sources still hash to the ones measured.
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import math
 import os
@@ -27,6 +36,7 @@ sys.path.insert(0, ROOT)
 METRIC = "quantized-KV decode attention: effective HBM GB/s & % of peak; µs/step"
 PEAK_HBM_GBPS = 8000.0
 MALL_BYTES = 256 << 20
+PROFILES = os.path.join(ROOT, "profiles")
 
 
 def log(*a):
@@ -37,22 +47,74 @@ def quantized_prefix(S, R, G):
     return G * (max(S - R, 0) // G)
 
 
-def decode_bytes(w, lengths, record_bytes):
-    """Algorithmic HBM bytes of one decode-attention launch: packed codes and fp16
-    scale/zero of every quantized token, the full-precision ring tokens, q and out."""
+def partial_bytes(w, lengths, record_bytes):
+    """Algorithmic HBM bytes the decode-partials launch must move: packed codes and
+    fp16 scale/zero of every quantized token, the full-precision ring tokens, q."""
     per_tok = record_bytes / w.k_group
     total = 0.0
     for S in lengths:
         Q = quantized_prefix(S, w.residual, w.k_group)
         total += w.num_kv_heads * (Q * per_tok + (S - Q) * w.head_dim * 2 * 2)
-    total += w.batch * w.num_q_heads * w.head_dim * (2 + 4)
+    total += w.batch * w.num_q_heads * w.head_dim * 2
     return total
+
+
+def out_bytes(w):
+    return w.batch * w.num_q_heads * w.head_dim * 4
+
+
+def append_flush_bytes(w, lengths_before, record_bytes):
+    """Algorithmic bytes of appending one token per sequence (read K, V rows, write
+    them to the ring) and of flushing the blocks that leave the window (read the
+    block's ring rows, write its record)."""
+    row = w.head_dim * 2
+    total = 0.0
+    for S0 in lengths_before:
+        total += w.num_kv_heads * 2 * row * 2           # read new k, v; write to the ring
+        q0 = quantized_prefix(S0, w.residual, w.k_group)
+        q1 = quantized_prefix(S0 + 1, w.residual, w.k_group)
+        blocks = (q1 - q0) // w.k_group
+        total += blocks * w.num_kv_heads * (w.k_group * 2 * row + record_bytes)
+    return total
+
+
+def source_hash() -> str:
+    """sha256 over the library sources (kernels and header); names the build the
+    counters in profiles/ were taken with."""
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "quantized_kv_cache_append_amd", "csrc")
+    paths = sorted(os.path.join(csrc, f) for f in os.listdir(csrc) if f.endswith((".h", ".hip")))
+    paths.append(os.path.join(ROOT, "include", "kvq.h"))
+    for p in paths:
+        h.update(os.path.basename(p).encode())
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per decode-partials launch from the counter summary in profiles/,
+    or None if there is none or the sources changed since it was taken."""
+    path = os.path.join(PROFILES, f"decode_traffic_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                kv[k.strip()] = v.strip()
+    if kv.get("source_hash") != source_hash():
+        return None
+    try:
+        return float(kv["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def cpu_baseline(w, inp, lengths, budget_s=15.0):
     """Time the oracle's decode attention on a bounded sample of (sequence, kv head)
     pairs of the same workload; returns GB/s of the same algorithmic bytes."""
-    import numpy as np
     from threadpoolctl import threadpool_limits
 
     from oracle import kivi
@@ -96,10 +158,12 @@ def main():
     ap.add_argument("--workload", default="llama2-7b-layer")
     ap.add_argument("--copies", type=int, default=0, help="cache copies to rotate (0: auto, > 3x MALL)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe-mb", type=int, default=0,
+                    help="after timing, run device-to-device copies of this many MiB (counter calibration)")
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); this build has no multi-GPU path",
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); this library has no multi-GPU path",
               file=sys.stderr)
         sys.exit(2)
 
@@ -150,55 +214,70 @@ def main():
     max_len = max(lengths0) + steps_per_copy
     ws_bytes = max(c.workspace_bytes(max_len) for c in caches)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
-    lens = [list(lengths0) for _ in caches]
 
     def step(i, ev=None):
-        ci = i % copies
-        c = caches[ci]
+        c = caches[i % copies]
         kn, vn, q = toks[i % pool]
         c.append_flush(kn, vn)
-        lens[ci] = [s + 1 for s in lens[ci]]
         if ev is not None:
             ev[0].record()
-        c.decode(q, out=outs[ci], max_seq_tokens=max_len, workspace=ws)
+        c.decode_partials(q, max_seq_tokens=max_len, workspace=ws)
         if ev is not None:
             ev[1].record()
+        c.decode_combine(out=outs[i % copies], max_seq_tokens=max_len, workspace=ws)
 
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    step_bytes = []
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record()
     for j in range(args.steps):
-        i = args.warmup + j
-        step(i, evs[j])
+        step(args.warmup + j, evs[j])
     end.record()
     torch.cuda.synchronize()
     ms_total = start.elapsed_time(end)
-    # bytes of each timed decode launch, from the lengths it saw
-    lens_replay = [list(lengths0) for _ in caches]
-    for i in range(total_steps):
-        ci = i % copies
-        lens_replay[ci] = [s + 1 for s in lens_replay[ci]]
-        if i >= args.warmup:
-            step_bytes.append(decode_bytes(w, lens_replay[ci], rec))
     err = max(c.read_device_error() for c in caches)
     if err:
         raise SystemExit(f"device error word {err} after the timed steps")
 
-    ms_step = ms_total / args.steps
-    avg_bytes = sum(step_bytes) / len(step_bytes)
-    dec_ms = [a.elapsed_time(b) for a, b in evs]
-    dec_avg_ms = sum(dec_ms) / len(dec_ms)
-    value = avg_bytes / (ms_step * 1e-3) / 1e9
-    achieved = avg_bytes / (dec_avg_ms * 1e-3) / 1e9
-    log(f"[bench] {ms_step * 1e3:.1f} us/step, decode launch {dec_avg_ms * 1e3:.1f} us, "
-        f"{avg_bytes / 1e6:.1f} MB/step -> step {value:.0f} GB/s, decode {achieved:.0f} GB/s "
-        f"({achieved / PEAK_HBM_GBPS * 100:.1f}% of 8 TB/s)")
+    # algorithmic bytes of every timed step, from the lengths each launch saw
+    lens = [list(lengths0) for _ in caches]
+    step_bytes, part_bytes = [], []
+    for i in range(total_steps):
+        ci = i % copies
+        before = lens[ci]
+        after = [s + 1 for s in before]
+        if i >= args.warmup:
+            pb = partial_bytes(w, after, rec)
+            part_bytes.append(pb)
+            step_bytes.append(append_flush_bytes(w, before, rec) + pb + out_bytes(w))
+        lens[ci] = after
 
+    ms_step = ms_total / args.steps
+    part_ms = [a.elapsed_time(b) for a, b in evs]
+    part_avg_ms = sum(part_ms) / len(part_ms)
+    avg_step_bytes = sum(step_bytes) / len(step_bytes)
+    avg_part_bytes = sum(part_bytes) / len(part_bytes)
+    value = avg_step_bytes / (ms_step * 1e-3) / 1e9
+    achieved = avg_part_bytes / (part_avg_ms * 1e-3) / 1e9
+    traffic = measured_traffic(w.name)
+    log(f"[bench] {ms_step * 1e3:.1f} us/step ({avg_step_bytes / 1e6:.1f} MB) -> {value:.0f} GB/s; "
+        f"decode partials {part_avg_ms * 1e3:.1f} us, {avg_part_bytes / 1e6:.1f} MB -> {achieved:.0f} GB/s "
+        f"({achieved / PEAK_HBM_GBPS * 100:.1f}% of 8 TB/s); sources {source_hash()}")
+
+    if args.copy_probe_mb > 0:
+        n = args.copy_probe_mb << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] copy probe: 3 device-to-device copies of {n} bytes")
+
+    kernel = ("decode_mha_kernel" if w.n_g == 1 else "decode_fast_kernel") if w.head_dim == 128 else \
+        "decode_generic_kernel"
     result = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -218,10 +297,10 @@ def main():
                    "v_group": w.v_group, "residual": w.residual, "paged": w.paged,
                    "cache_copies_rotated": copies},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                     "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": None,
-                     "kernel": "kvq_decode_attention (split decode + combine)",
-                     "us_per_launch": round(dec_avg_ms * 1e3, 2),
-                     "bytes_per_launch": int(avg_bytes)},
+                     "frac": round(achieved / PEAK_HBM_GBPS, 4),
+                     "traffic": None if traffic is None else round(traffic),
+                     "kernel": kernel, "us_per_launch": round(part_avg_ms * 1e3, 2),
+                     "bytes_per_launch": int(avg_part_bytes)},
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

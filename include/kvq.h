@@ -184,6 +184,22 @@ kvq_status kvq_decode_attention(const kvq_config* cfg, const kvq_cache* cache,
                                 int32_t max_seq_tokens, void* workspace,
                                 size_t workspace_bytes, void* stream);
 
+/* The two launches of kvq_decode_attention, callable separately (same
+ * arguments and errors; the workspace carries the split states from the first
+ * call to the second, which must follow it on the same stream with the same
+ * cache, configuration and max_seq_tokens, nothing touching the cache or the
+ * workspace in between). kvq_decode_partials computes the partial softmax
+ * state (running maximum, sum and unnormalised output, [P1] Minima-KV) of
+ * every work unit -- a run of quantized blocks or of ring tokens of one
+ * (sequence, kv head) -- into the workspace; kvq_decode_combine merges them
+ * into out. Useful to time or overlap the two phases. */
+kvq_status kvq_decode_partials(const kvq_config* cfg, const kvq_cache* cache,
+                               const void* q, float softmax_scale, int32_t max_seq_tokens,
+                               void* workspace, size_t workspace_bytes, void* stream);
+kvq_status kvq_decode_combine(const kvq_config* cfg, const kvq_cache* cache, float* out,
+                              int32_t max_seq_tokens, void* workspace, size_t workspace_bytes,
+                              void* stream);
+
 /* Copies the cache's sticky error word (an OR of KVQ_DEV_* bits; 0 = nothing
  * so far) into *err after the stream's earlier work, waiting for the stream. */
 kvq_status kvq_read_device_error(const kvq_config* cfg, const kvq_cache* cache, void* stream,

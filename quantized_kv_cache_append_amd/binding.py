@@ -19,7 +19,8 @@ KVQ_F16, KVQ_BF16 = 0, 1
 KVQ_DEV_RESIDUAL_FULL, KVQ_DEV_BLOCKS_FULL, KVQ_DEV_BAD_PAGE, KVQ_DEV_BAD_COUNT, KVQ_DEV_TOO_LONG = 1, 2, 4, 8, 16
 
 EXPORTED = ("kvq_get_layout", "kvq_workspace_size", "kvq_append", "kvq_append_flush", "kvq_flush_residual",
-            "kvq_decode_attention", "kvq_read_device_error", "kvq_status_string")
+            "kvq_decode_attention", "kvq_decode_partials", "kvq_decode_combine", "kvq_read_device_error",
+            "kvq_status_string")
 
 
 class kvq_config(ctypes.Structure):
@@ -67,6 +68,8 @@ def load():
         "kvq_append_flush": [cfgp, cachep, P, P, P, I32, P],
         "kvq_flush_residual": [cfgp, cachep, P],
         "kvq_decode_attention": [cfgp, cachep, P, P, F, I32, P, SZ, P],
+        "kvq_decode_partials": [cfgp, cachep, P, F, I32, P, SZ, P],
+        "kvq_decode_combine": [cfgp, cachep, P, I32, P, SZ, P],
         "kvq_read_device_error": [cfgp, cachep, P, ctypes.POINTER(I32)],
         "kvq_status_string": [ctypes.c_int],
     }
@@ -120,6 +123,16 @@ def kvq_decode_attention(cfg, cache, q_ptr, out_ptr, softmax_scale, max_seq_toke
     _check(load().kvq_decode_attention(ctypes.byref(cfg), ctypes.byref(cache), q_ptr, out_ptr,
                                        float(softmax_scale), int(max_seq_tokens), ws_ptr, int(ws_bytes),
                                        stream), "kvq_decode_attention")
+
+
+def kvq_decode_partials(cfg, cache, q_ptr, softmax_scale, max_seq_tokens, ws_ptr, ws_bytes, stream):
+    _check(load().kvq_decode_partials(ctypes.byref(cfg), ctypes.byref(cache), q_ptr, float(softmax_scale),
+                                      int(max_seq_tokens), ws_ptr, int(ws_bytes), stream), "kvq_decode_partials")
+
+
+def kvq_decode_combine(cfg, cache, out_ptr, max_seq_tokens, ws_ptr, ws_bytes, stream):
+    _check(load().kvq_decode_combine(ctypes.byref(cfg), ctypes.byref(cache), out_ptr, int(max_seq_tokens), ws_ptr,
+                                     int(ws_bytes), stream), "kvq_decode_combine")
 
 
 def kvq_read_device_error(cfg, cache, stream) -> int:

@@ -140,6 +140,38 @@ class QuantizedKVCache:
                                _stream_handle())
         return out
 
+    def _workspace(self, msl: int, workspace: torch.Tensor | None) -> torch.Tensor:
+        need = B.kvq_workspace_size(self.cfg, msl)
+        if workspace is not None:
+            return workspace
+        if self._ws is None or self._ws.numel() < need:
+            self._ws = torch.empty(max(need, 16), dtype=torch.uint8, device=self.device)
+        return self._ws
+
+    def decode_partials(self, q: torch.Tensor, softmax_scale: float = 0.0, max_seq_tokens: int | None = None,
+                        workspace: torch.Tensor | None = None) -> torch.Tensor:
+        """First launch of decode(): the units' partial softmax states into the workspace (returned)."""
+        c = self.cfg
+        self._check(q, (c.batch, c.num_q_heads, c.head_dim), self.dtype, "q")
+        msl = self.max_len_bound if max_seq_tokens is None else int(max_seq_tokens)
+        ws = self._workspace(msl, workspace)
+        B.kvq_decode_partials(c, self.cache, q.data_ptr(), softmax_scale, msl, ws.data_ptr(),
+                              ws.numel() * ws.element_size(), _stream_handle())
+        return ws
+
+    def decode_combine(self, out: torch.Tensor | None = None, max_seq_tokens: int | None = None,
+                       workspace: torch.Tensor | None = None) -> torch.Tensor:
+        """Second launch of decode(): merge the partial states left by decode_partials()."""
+        c = self.cfg
+        if out is None:
+            out = torch.empty(c.batch, c.num_q_heads, c.head_dim, dtype=torch.float32, device=self.device)
+        self._check(out, (c.batch, c.num_q_heads, c.head_dim), torch.float32, "out")
+        msl = self.max_len_bound if max_seq_tokens is None else int(max_seq_tokens)
+        ws = self._workspace(msl, workspace)
+        B.kvq_decode_combine(c, self.cache, out.data_ptr(), msl, ws.data_ptr(), ws.numel() * ws.element_size(),
+                             _stream_handle())
+        return out
+
     def prefill(self, k: torch.Tensor, v: torch.Tensor, lengths, chunk: int):
         """Append every sequence's first lengths[b] tokens of k, v ([B][H_kv][>=S][d])
         in chunks of `chunk` (ragged counts per sequence), flushing after each chunk.

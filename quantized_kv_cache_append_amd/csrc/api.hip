@@ -114,20 +114,57 @@ kvq_status kvq_flush_residual(const kvq_config* cfg, const kvq_cache* cache, voi
   return launched(kvq::launch_flush(kvq::make_geom(*cfg), *cache, static_cast<hipStream_t>(stream)));
 }
 
-kvq_status kvq_decode_attention(const kvq_config* cfg, const kvq_cache* cache, const void* q, float* out,
-                                float softmax_scale, int32_t max_seq_tokens, void* workspace,
-                                size_t workspace_bytes, void* stream) {
+namespace {
+// Shared argument checks of the decode entry points; fills g, plan and scale.
+kvq_status decode_args(const kvq_config* cfg, const kvq_cache* cache, int32_t max_seq_tokens, void* workspace,
+                       size_t workspace_bytes, float softmax_scale, Geom& g, kvq::DecodePlan& plan,
+                       float& scale) {
   kvq_status st = validate(cfg);
   if (st != KVQ_OK) return st;
   if ((st = validate_cache(cfg, cache)) != KVQ_OK) return st;
-  if (q == nullptr || out == nullptr || max_seq_tokens < 0 || !std::isfinite(softmax_scale))
-    return KVQ_ERR_INVALID_ARG;
-  const Geom g = kvq::make_geom(*cfg);
-  const kvq::DecodePlan plan = kvq::plan_decode(g, max_seq_tokens);
+  if (max_seq_tokens < 0 || !std::isfinite(softmax_scale)) return KVQ_ERR_INVALID_ARG;
+  g = kvq::make_geom(*cfg);
+  plan = kvq::plan_decode(g, max_seq_tokens);
   if (workspace == nullptr || workspace_bytes < plan.ws_bytes) return KVQ_ERR_WORKSPACE;
-  const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt((float)g.d);
-  return launched(kvq::launch_decode(g, *cache, q, out, scale, max_seq_tokens, workspace,
-                                     static_cast<hipStream_t>(stream)));
+  scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt((float)g.d);
+  return KVQ_OK;
+}
+}  // namespace
+
+kvq_status kvq_decode_attention(const kvq_config* cfg, const kvq_cache* cache, const void* q, float* out,
+                                float softmax_scale, int32_t max_seq_tokens, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  if (q == nullptr || out == nullptr) return KVQ_ERR_INVALID_ARG;
+  Geom g;
+  kvq::DecodePlan plan;
+  float scale;
+  const kvq_status st = decode_args(cfg, cache, max_seq_tokens, workspace, workspace_bytes, softmax_scale, g, plan, scale);
+  if (st != KVQ_OK) return st;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (kvq::launch_decode_partials(g, *cache, q, scale, plan, workspace, s) != hipSuccess) return KVQ_ERR_LAUNCH;
+  return launched(kvq::launch_decode_combine(g, *cache, out, workspace, s));
+}
+
+kvq_status kvq_decode_partials(const kvq_config* cfg, const kvq_cache* cache, const void* q, float softmax_scale,
+                               int32_t max_seq_tokens, void* workspace, size_t workspace_bytes, void* stream) {
+  if (q == nullptr) return KVQ_ERR_INVALID_ARG;
+  Geom g;
+  kvq::DecodePlan plan;
+  float scale;
+  const kvq_status st = decode_args(cfg, cache, max_seq_tokens, workspace, workspace_bytes, softmax_scale, g, plan, scale);
+  if (st != KVQ_OK) return st;
+  return launched(kvq::launch_decode_partials(g, *cache, q, scale, plan, workspace, static_cast<hipStream_t>(stream)));
+}
+
+kvq_status kvq_decode_combine(const kvq_config* cfg, const kvq_cache* cache, float* out, int32_t max_seq_tokens,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+  if (out == nullptr) return KVQ_ERR_INVALID_ARG;
+  Geom g;
+  kvq::DecodePlan plan;
+  float scale;
+  const kvq_status st = decode_args(cfg, cache, max_seq_tokens, workspace, workspace_bytes, 0.f, g, plan, scale);
+  if (st != KVQ_OK) return st;
+  return launched(kvq::launch_decode_combine(g, *cache, out, workspace, static_cast<hipStream_t>(stream)));
 }
 
 kvq_status kvq_read_device_error(const kvq_config* cfg, const kvq_cache* cache, void* stream,

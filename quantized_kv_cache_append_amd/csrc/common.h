@@ -123,16 +123,29 @@ __device__ __forceinline__ bool last_arrival(int* counter, int total) {
 }
 // Persistent grid of a kernel of 256-thread workgroups: as many workgroups as
 // stay resident at once (from the runtime's occupancy for this kernel and LDS
-// size), rounded up to a multiple of the decode work queues.
+// size), rounded up to a multiple of the decode work queues. The answer is
+// remembered per kernel, device and LDS size (the occupancy query is slow next
+// to a launch).
 template <class K>
 inline int persistent_grid(K kernel, size_t lds_bytes) {
-  int dev = 0, cus = 0, per_cu = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
-    cus = 256;
+  struct Memo {
+    int dev;
+    size_t lds;
+    int grid;
+  };
+  static Memo memo[16] = {};
+  static int used = 0;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+  for (int i = 0; i < used; ++i)
+    if (memo[i].dev == dev && memo[i].lds == lds_bytes) return memo[i].grid;
+  int cus = 0, per_cu = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 256, lds_bytes) != hipSuccess || per_cu < 1)
     per_cu = 1;
-  return (cus * per_cu + kQueues - 1) / kQueues * kQueues;
+  const int grid = (cus * per_cu + kQueues - 1) / kQueues * kQueues;
+  if (used < 16) memo[used++] = Memo{dev, lds_bytes, grid};
+  return grid;
 }
 #endif
 
@@ -142,8 +155,10 @@ hipError_t launch_append(const Geom& g, const kvq_cache& c, const void* k_new, c
 hipError_t launch_flush(const Geom& g, const kvq_cache& c, hipStream_t s);
 hipError_t launch_append_flush(const Geom& g, const kvq_cache& c, const void* k_new, const void* v_new,
                                const int32_t* n_new, int n_max, hipStream_t s);
-hipError_t launch_decode(const Geom& g, const kvq_cache& c, const void* q, float* out, float scale,
-                         int max_seq_tokens, void* ws, hipStream_t s);
+struct DecodePlan;
+hipError_t launch_decode_partials(const Geom& g, const kvq_cache& c, const void* q, float scale,
+                                  const DecodePlan& plan, void* ws, hipStream_t s);
+hipError_t launch_decode_combine(const Geom& g, const kvq_cache& c, float* out, void* ws, hipStream_t s);
 
 // Decode work decomposition shared by the workspace sizing and the kernels.
 struct DecodePlan {

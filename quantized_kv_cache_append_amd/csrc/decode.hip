@@ -328,20 +328,19 @@ DecodePlan plan_decode(const Geom& g, int max_seq_tokens) {
   return p;
 }
 
-hipError_t launch_decode(const Geom& g, const kvq_cache& c, const void* q, float* out, float scale,
-                         int max_seq_tokens, void* ws, hipStream_t s) {
-  const DecodePlan plan = plan_decode(g, max_seq_tokens);
+hipError_t launch_decode_partials(const Geom& g, const kvq_cache& c, const void* q, float scale,
+                                  const DecodePlan& plan, void* ws, hipStream_t s) {
   const bool bf16 = g.dtype == KVQ_BF16;
-  hipError_t e;
-  if (plan.fast)
-    e = launch_decode_fast(g, c, q, scale, plan, ws, s);
-  else if (g.d == 128)
-    e = bf16 ? launch_generic<128, true>(g, c, q, scale, plan, ws, s)
-             : launch_generic<128, false>(g, c, q, scale, plan, ws, s);
-  else
-    e = bf16 ? launch_generic<64, true>(g, c, q, scale, plan, ws, s)
-             : launch_generic<64, false>(g, c, q, scale, plan, ws, s);
-  if (e != hipSuccess) return e;
+  if (plan.fast) return launch_decode_fast(g, c, q, scale, plan, ws, s);
+  if (g.d == 128)
+    return bf16 ? launch_generic<128, true>(g, c, q, scale, plan, ws, s)
+                : launch_generic<128, false>(g, c, q, scale, plan, ws, s);
+  return bf16 ? launch_generic<64, true>(g, c, q, scale, plan, ws, s)
+              : launch_generic<64, false>(g, c, q, scale, plan, ws, s);
+}
+
+hipError_t launch_decode_combine(const Geom& g, const kvq_cache& c, float* out, void* ws, hipStream_t s) {
+  (void)c;
   const int* planp = static_cast<const int*>(ws);
   const float* parts = reinterpret_cast<const float*>(static_cast<const uint8_t*>(ws) + plan_bytes(g.B));
   if (g.d == 128)

@@ -70,6 +70,18 @@ def test_decode_is_deterministic():
     assert torch.equal(out, again)
 
 
+@pytest.mark.parametrize("name", ["llama2-reduced", "llama3-int2-reduced", "ragged-paged-reduced", "tiny-full"])
+def test_two_phase_decode_equals_one_call(name):
+    # kvq_decode_partials + kvq_decode_combine is the same computation as
+    # kvq_decode_attention: the unit partition depends only on the lengths
+    w, cache, inp, lengths, out = _run_case(name)
+    q = inp.q.cuda()
+    cache.decode_partials(q)
+    out2 = cache.decode_combine()
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2)
+
+
 @pytest.mark.parametrize("S", [1, 40, 127, 128, 159, 160, 161, 191, 192])
 def test_window_boundaries(S):
     # R = 128, G = 32: nothing is quantized until S reaches R + G = 160
