@@ -184,7 +184,7 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     lengths0 = W.sequence_lengths(w)
-    total_steps = args.warmup + args.steps
+    total_steps = args.warmup + 2 * args.steps
     log(f"[bench] workload {w.name}: {w.description}")
 
     inp = W.make_layer(w, device=dev, lengths=lengths0)
@@ -229,30 +229,36 @@ def main():
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    # the K timed steps: one event pair around all of them (events between the
+    # launches would add their own gaps to the step)
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
     start.record()
     for j in range(args.steps):
-        step(args.warmup + j, evs[j])
+        step(args.warmup + j)
     end.record()
     torch.cuda.synchronize()
     ms_total = start.elapsed_time(end)
+    # then K more steps with an event pair around each decode-partials launch,
+    # on the stream it runs on, for the kernel's own duration
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for j in range(args.steps):
+        step(args.warmup + args.steps + j, evs[j])
+    torch.cuda.synchronize()
     err = max(c.read_device_error() for c in caches)
     if err:
         raise SystemExit(f"device error word {err} after the timed steps")
 
-    # algorithmic bytes of every timed step, from the lengths each launch saw
+    # algorithmic bytes of every step, from the lengths each launch saw
     lens = [list(lengths0) for _ in caches]
     step_bytes, part_bytes = [], []
     for i in range(total_steps):
         ci = i % copies
         before = lens[ci]
         after = [s + 1 for s in before]
-        if i >= args.warmup:
-            pb = partial_bytes(w, after, rec)
-            part_bytes.append(pb)
-            step_bytes.append(append_flush_bytes(w, before, rec) + pb + out_bytes(w))
+        if args.warmup <= i < args.warmup + args.steps:
+            step_bytes.append(append_flush_bytes(w, before, rec) + partial_bytes(w, after, rec) + out_bytes(w))
+        elif i >= args.warmup + args.steps:
+            part_bytes.append(partial_bytes(w, after, rec))
         lens[ci] = after
 
     ms_step = ms_total / args.steps

@@ -234,71 +234,68 @@ __global__ __launch_bounds__(256) void decode_generic_kernel(
 // Merge the partial states of one (sequence, query head) (scores in log2
 // units): with M = max m_i, o = sum_i 2^(m_i - M) o_i / sum_i 2^(m_i - M) l_i.
 // The units of the pair come from the plan the decode kernel left in the
-// workspace. One workgroup of kCombineThreads per output row: thread (slice,
-// channel) merges partials slice, slice + SL, ... of its channel with a running
-// maximum, all of its loads in flight together for up to eight partials; the
-// slices are then merged through LDS.
-constexpr int kCombineThreads = 1024;
+// workspace. One wave per output row, lane holding D/64 channels: the partials
+// go in batches of kCombineBatch, each batch one round of loads (lane i also
+// fetches m and l of partial i), merged into a running maximum. Small
+// workgroups keep the launch quick: the rows are few and short, and the cost
+// of this kernel is its dispatch and load latency, not its bandwidth.
+constexpr int kCombineWaves = 4;
+constexpr int kCombineBatch = 64;
 
 template <int D>
-__global__ __launch_bounds__(kCombineThreads) void combine_kernel(Geom g, const int* __restrict__ plan,
-                                                                  const float* __restrict__ ws,
-                                                                  float* __restrict__ out) {
-  constexpr int SL = kCombineThreads / D;   // slices of the partials
-  __shared__ float sm[SL], sl_sum[SL], part[SL][D];
-  const int bh = blockIdx.x;
-  const int b = bh / g.Hq, hq = bh % g.Hq;
+__global__ __launch_bounds__(64 * kCombineWaves) void combine_kernel(Geom g, const int* __restrict__ plan,
+                                                                     const float* ws,   // (not restrict: the
+                                                                     // compiler barrier below must order its loads)
+                                                                     float* __restrict__ out) {
+  constexpr int CPL = D / 64;   // channels per lane
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * kCombineWaves + __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  if (row >= g.B * g.Hq) return;
+  const int b = row / g.Hq, hq = row % g.Hq;
   const int h = hq / g.ng, j = hq % g.ng;
-  const int t = threadIdx.x, c = t % D, sl = t / D;
   const PairUnits pu = pair_units(g, plan, b, h);
   const size_t stride = (size_t)g.ng * (D + 2);
   const float* src0 = ws + (size_t)j * (D + 2);
 
-  float m = -INFINITY, L = 0.f, acc = 0.f;
-  for (int i0 = sl; i0 < pu.n; i0 += 8 * SL) {
-    float e[8], l[8], v[8];
+  float m = -INFINITY, L = 0.f, acc[CPL];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int i = i0 + u * SL;
-      const float* src = src0 + (size_t)pu.slot(i < pu.n ? i : sl) * stride;
-      e[u] = i < pu.n ? src[D] : -INFINITY;
-      l[u] = src[D + 1];
-      v[u] = src[c];
-    }
-    float mn = m;
+  for (int k = 0; k < CPL; ++k) acc[k] = 0.f;
+  for (int i0 = 0; i0 < pu.n; i0 += kCombineBatch) {
+    const int cnt = min(kCombineBatch, pu.n - i0);
+    float v[kCombineBatch][CPL];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) mn = fmaxf(mn, e[u]);
-    if (mn != -INFINITY) {
-      const float a = m == -INFINITY ? 0.f : exp2f(m - mn);
-      L *= a;
-      acc *= a;
+    for (int u = 0; u < kCombineBatch; ++u) {
+      const float* src = src0 + (size_t)pu.slot(i0 + (u < cnt ? u : 0)) * stride + CPL * lane;
+      if constexpr (CPL == 2) {
+        const float2 x = *reinterpret_cast<const float2*>(src);
+        v[u][0] = x.x;
+        v[u][1] = x.y;
+      } else {
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const float wgt = e[u] == -INFINITY ? 0.f : exp2f(e[u] - mn);
-        L += wgt * l[u];
-        acc += wgt * v[u];
+        for (int k = 0; k < CPL; ++k) v[u][k] = src[k];
       }
-      m = mn;
     }
-  }
-  if (c == 0) sm[sl] = m;
-  __syncthreads();
-  float M = -INFINITY;
+    const float2 ml = *reinterpret_cast<const float2*>(src0 + (size_t)pu.slot(i0 + min(lane, cnt - 1)) * stride + D);
+    asm volatile("" ::: "memory");   // the whole batch is in flight before the first wait
+    const float mi = lane < cnt ? ml.x : -INFINITY, li = lane < cnt ? ml.y : 0.f;
+    const float mn = fmaxf(m, wave_max(mi));
+    if (mn == -INFINITY) continue;   // wave-uniform: nothing but empty partials so far
+    const float a = m == -INFINITY ? 0.f : exp2f(m - mn);
+    const float w = mi == -INFINITY ? 0.f : exp2f(mi - mn);   // weight of partial i0 + lane
+    L = L * a + wave_sum(w * li);
 #pragma unroll
-  for (int k = 0; k < SL; ++k) M = fmaxf(M, sm[k]);
-  const float w = (m == -INFINITY) ? 0.f : exp2f(m - M);
-  part[sl][c] = w * acc;
-  if (c == 0) sl_sum[sl] = w * L;
-  __syncthreads();
-  if (t < D) {
-    float o = 0.f, Lt = 0.f;
+    for (int k = 0; k < CPL; ++k) acc[k] *= a;
 #pragma unroll
-    for (int k = 0; k < SL; ++k) {
-      o += part[k][t];
-      Lt += sl_sum[k];
+    for (int u = 0; u < kCombineBatch; ++u) {
+      const float wu = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), u));   // 0 past cnt
+#pragma unroll
+      for (int k = 0; k < CPL; ++k) acc[k] = fmaf(wu, v[u][k], acc[k]);
     }
-    out[((size_t)b * g.Hq + hq) * D + t] = (Lt > 0.f) ? o / Lt : 0.f;
+    m = mn;
   }
+  float* dst = out + (size_t)row * D + CPL * lane;
+#pragma unroll
+  for (int k = 0; k < CPL; ++k) dst[k] = L > 0.f ? acc[k] / L : 0.f;
 }
 
 template <int D, bool BF16>
@@ -343,10 +340,11 @@ hipError_t launch_decode_combine(const Geom& g, const kvq_cache& c, float* out, 
   (void)c;
   const int* planp = static_cast<const int*>(ws);
   const float* parts = reinterpret_cast<const float*>(static_cast<const uint8_t*>(ws) + plan_bytes(g.B));
+  const int grid = (g.B * g.Hq + kCombineWaves - 1) / kCombineWaves;
   if (g.d == 128)
-    hipLaunchKernelGGL((combine_kernel<128>), dim3(g.B * g.Hq), dim3(kCombineThreads), 0, s, g, planp, parts, out);
+    hipLaunchKernelGGL((combine_kernel<128>), dim3(grid), dim3(64 * kCombineWaves), 0, s, g, planp, parts, out);
   else
-    hipLaunchKernelGGL((combine_kernel<64>), dim3(g.B * g.Hq), dim3(kCombineThreads), 0, s, g, planp, parts, out);
+    hipLaunchKernelGGL((combine_kernel<64>), dim3(grid), dim3(64 * kCombineWaves), 0, s, g, planp, parts, out);
   return hipGetLastError();
 }
 

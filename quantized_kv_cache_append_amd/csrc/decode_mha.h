@@ -266,10 +266,13 @@ __device__ __forceinline__ void quant_stream(const Geom& g, const WaveLds<C>& L,
   const int lane = threadIdx.x & 63, n = lane & 15, rr = lane >> 4;
 
   // ---- register buffers of one set ----
-  uint4 kc[kTokLane][C::KW / 4];   // key code rows of tokens lane, lane + 64
-  uint4 ksz[C::KSZ_LD];    // 16-byte chunks of the set's key scale/zero sections
-  uint4 vc[C::RPL][C::VW / 4];     // value code chunks of runs rr, rr + 4, ...
-  uint4 vsz[C::VSZ_LD];    // 16-byte chunks of the set's value scale/zero sections
+  struct SetBuf {
+    uint4 kc[kTokLane][C::KW / 4];   // key code rows of tokens lane (+ 64 ...)
+    uint4 ksz[C::KSZ_LD];            // 16-byte chunks of the set's key scale/zero sections
+    uint4 vc[C::RPL][C::VW / 4];     // value code chunks of runs rr, rr + 4, ...
+    uint4 vsz[C::VSZ_LD];            // 16-byte chunks of the set's value scale/zero sections
+  };
+  SetBuf cb;   // the set being computed (the next one loads into a second buffer meanwhile)
 
   // chunk k of lane of the set's [block][scale|zero] sections of `bytes_per_block`
   auto sz_chunk = [&](int k, int bytes_per_block, int& bi, int& off) {
@@ -277,21 +280,21 @@ __device__ __forceinline__ void quant_stream(const Geom& g, const WaveLds<C>& L,
     bi = o / bytes_per_block;
     off = o % bytes_per_block;
   };
-  auto load_set = [&](Span sp, int si) {
+  auto load_set = [&](SetBuf& b, Span sp, int si) {
     const int blk0 = sp.begin + si * NBS;
 #pragma unroll
     for (int tl = 0; tl < kTokLane; ++tl) {
       const int tok = lane + 64 * tl;
       const uint8_t* r = span_rec<C>(g, blocks, table, sp, blk0 + tok / G) + C::REC_KC + (tok % G) * C::KROW;
 #pragma unroll
-      for (int k = 0; k < C::KW / 4; ++k) kc[tl][k] = reinterpret_cast<const uint4*>(r)[k];
+      for (int k = 0; k < C::KW / 4; ++k) b.kc[tl][k] = reinterpret_cast<const uint4*>(r)[k];
     }
 #pragma unroll
     for (int k = 0; k < C::KSZ_LD; ++k) {
       int bi, off;
       sz_chunk(k, 4 * D, bi, off);
       bi = bi < NBS ? bi : NBS - 1;
-      ksz[k] = *reinterpret_cast<const uint4*>(span_rec<C>(g, blocks, table, sp, blk0 + bi) + C::REC_KS + off);
+      b.ksz[k] = *reinterpret_cast<const uint4*>(span_rec<C>(g, blocks, table, sp, blk0 + bi) + C::REC_KS + off);
     }
 #pragma unroll
     for (int h2 = 0; h2 < C::RPL; ++h2) {
@@ -299,14 +302,14 @@ __device__ __forceinline__ void quant_stream(const Geom& g, const WaveLds<C>& L,
       const int bi = run / (G / 8), R = run % (G / 8);
       const uint8_t* r = span_rec<C>(g, blocks, table, sp, blk0 + bi) + C::REC_VC + (R * 16 + n) * C::VRUN;
 #pragma unroll
-      for (int k = 0; k < C::VW / 4; ++k) vc[h2][k] = reinterpret_cast<const uint4*>(r)[k];
+      for (int k = 0; k < C::VW / 4; ++k) b.vc[h2][k] = reinterpret_cast<const uint4*>(r)[k];
     }
 #pragma unroll
     for (int k = 0; k < C::VSZ_LD; ++k) {
       int bi, off;
       sz_chunk(k, 4 * NGR * G, bi, off);
       bi = bi < NBS ? bi : NBS - 1;
-      vsz[k] = *reinterpret_cast<const uint4*>(span_rec<C>(g, blocks, table, sp, blk0 + bi) + C::REC_VS + off);
+      b.vsz[k] = *reinterpret_cast<const uint4*>(span_rec<C>(g, blocks, table, sp, blk0 + bi) + C::REC_VS + off);
     }
   };
   auto blk_ok = [&](Span sp, int blk) -> bool {
@@ -321,6 +324,9 @@ __device__ __forceinline__ void quant_stream(const Geom& g, const WaveLds<C>& L,
 
   auto run_set = [&](Span cur, int si, Span nsp, int nsi) {
     const int blk0 = cur.begin + si * NBS;
+    // the next set's loads go out first and stay in flight through this set
+    SetBuf nb;
+    load_set(nb, nsp, nsi);
     // ---- q~ = q' * s_K and kappa partials from the key scale/zero chunks ----
 #pragma unroll
     for (int k = 0; k < C::KSZ_LD; ++k) {
@@ -331,7 +337,7 @@ __device__ __forceinline__ void quant_stream(const Geom& g, const WaveLds<C>& L,
         const int c0 = (off % (2 * D)) / 2;   // 8 channels c0..c0+7
         const float4 qa = *reinterpret_cast<const float4*>(L.q + c0);
         const float4 qb = *reinterpret_cast<const float4*>(L.q + c0 + 4);
-        const uint4 w = ksz[k];
+        const uint4 w = cb.ksz[k];
         const float x[8] = {qa.x * h2f_lo(w.x), qa.y * h2f_hi(w.x), qa.z * h2f_lo(w.y), qa.w * h2f_hi(w.y),
                             qb.x * h2f_lo(w.z), qb.y * h2f_hi(w.z), qb.z * h2f_lo(w.w), qb.w * h2f_hi(w.w)};
         if (!zero) {
@@ -356,7 +362,7 @@ __device__ __forceinline__ void quant_stream(const Geom& g, const WaveLds<C>& L,
       const float* qt = L.qt + sbi * D;
 #pragma unroll
       for (int wi = 0; wi < C::KW; ++wi) {
-        const uint32_t w = reinterpret_cast<const uint32_t*>(&kc[tl][wi / 4])[wi % 4];
+        const uint32_t w = reinterpret_cast<const uint32_t*>(&cb.kc[tl][wi / 4])[wi % 4];
         constexpr int PER = 32 / C::KB;   // channels per word
         float cf[PER];
         word_codes<C::KB>(w, cf);
@@ -406,7 +412,7 @@ __device__ __forceinline__ void quant_stream(const Geom& g, const WaveLds<C>& L,
         const int j = e0 / G, t = bi * G + e0 % G;  // group, set-relative first token
         const float4 pa = *reinterpret_cast<const float4*>(L.p + t);
         const float4 pb = *reinterpret_cast<const float4*>(L.p + t + 4);
-        const uint4 w = vsz[k];
+        const uint4 w = cb.vsz[k];
         const float x[8] = {pa.x * h2f_lo(w.x), pa.y * h2f_hi(w.x), pa.z * h2f_lo(w.y), pa.w * h2f_hi(w.y),
                             pb.x * h2f_lo(w.z), pb.y * h2f_hi(w.z), pb.z * h2f_lo(w.w), pb.w * h2f_hi(w.w)};
         if (!zero) {
@@ -427,7 +433,7 @@ __device__ __forceinline__ void quant_stream(const Geom& g, const WaveLds<C>& L,
       const int t0 = 8 * (rr + 4 * h2);   // set-relative first token of the run
 #pragma unroll
       for (int wi = 0; wi < C::VW; ++wi) {
-        const uint32_t w = reinterpret_cast<const uint32_t*>(&vc[h2][wi / 4])[wi % 4];
+        const uint32_t w = reinterpret_cast<const uint32_t*>(&cb.vc[h2][wi / 4])[wi % 4];
         constexpr int PER = 32 / C::VB;   // codes per word = (channels per word) x 8 tokens
         float cf[PER];
         word_codes<C::VB>(w, cf);
@@ -452,10 +458,7 @@ __device__ __forceinline__ void quant_stream(const Geom& g, const WaveLds<C>& L,
       }
       asm volatile("" ::: "memory");   // one run's operands live at a time
     }
-    // prefetch the next set into the (now free) register buffers; the barrier
-    // keeps the loads (and their registers) below the last use of the buffers
-    asm volatile("" ::: "memory");
-    load_set(nsp, nsi);
+    cb = nb;
     wave_lds_fence();   // L.qt, L.p and L.pv are rewritten by the next set
   };
 
@@ -498,8 +501,8 @@ __device__ __forceinline__ void quant_stream(const Geom& g, const WaveLds<C>& L,
 
   int u = first;
   Span cur = first_span;
+  load_set(cb, cur, 0);
   load_query<C>(g, L, q, qscale, cur.b, cur.h);
-  load_set(cur, 0);
   while (true) {
     m_run = -INFINITY;
     l_lane = 0.f;

@@ -234,13 +234,16 @@ struct PairUnits {
   int n;                      // partials of the pair
   int cnt[kSections];         // per section
   int first[kSections];       // first slot per section
+  // branch-free: the last section that starts at or before i (empty sections
+  // start where the next one does)
   __device__ __forceinline__ int slot(int i) const {
+    int r = first[0] + i, start = 0;
 #pragma unroll
-    for (int k = 0; k < kSections - 1; ++k) {
-      if (i < cnt[k]) return first[k] + i;
-      i -= cnt[k];
+    for (int k = 1; k < kSections; ++k) {
+      start += cnt[k - 1];
+      r = i >= start ? first[k] + (i - start) : r;
     }
-    return first[kSections - 1] + i;
+    return r;
   }
 };
 __device__ inline PairUnits pair_units(const Geom& g, const int* plan, int b, int h) {
