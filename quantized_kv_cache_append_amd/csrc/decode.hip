@@ -59,16 +59,11 @@ __global__ __launch_bounds__(256) void decode_generic_kernel(
   build_unit_plan(g, state, max_blk, 1, kRingAll, plan, red, blockIdx.x == 0);
   if (blockIdx.x == 0)
     for (int i = threadIdx.x; i < pints; i += blockDim.x) ws_plan[i] = plan[i];
-  auto qs_of = [&](int b, int& Q, int& S) {
-    Q = state[4 * b + kStateQ];
-    S = state[4 * b + kStateS];
-  };
-  auto nblk_of = [&](int b) { return min(state[4 * b + kStateQ] / g.G, max_blk); };
 
   const int units = plan[kPlanUnits];
   const int ng = g.ng;
   for (int w = blockIdx.x * kWaves + wave; w < units; w += gridDim.x * kWaves) {
-    const Unit un = locate_unit(g, plan, w, qs_of, nblk_of);
+    const Unit un = locate_unit(g, plan, w, max_blk);
     const int b = un.b, h = un.h;
     const int pair = b * g.Hkv + h;
     const int Q = state[4 * b + kStateQ];

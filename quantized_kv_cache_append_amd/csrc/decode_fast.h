@@ -823,11 +823,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int qwaves = (int)(gridDim.x / kQueues) * kWaves;   // waves serving the queue
   int* counter = state + state_queue_word(g.B, queue);
   int* done = state + state_done_word(g.B);
-  auto qs_of = [&](int b, int& Q, int& S) {
-    Q = state[4 * b + kStateQ];
-    S = state[4 * b + kStateS];
-  };
-  auto nblk_of = [&](int b) { return min(state[4 * b + kStateQ] / g.G, max_blk); };
 
   auto issue = [&]() -> int {
     int v = 0;
@@ -836,7 +831,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   };
   auto claim = [&](int raw) -> int { return queue + kQueues * (qwaves + __builtin_amdgcn_readfirstlane(raw)); };
   auto span_of = [&](int uu) -> Span {
-    const Unit un = locate_unit(g, plan, uu, qs_of, nblk_of);
+    const Unit un = locate_unit(g, plan, uu, max_blk);
     Span sp;
     sp.b = __builtin_amdgcn_readfirstlane(un.b);
     sp.h = __builtin_amdgcn_readfirstlane(un.h);

@@ -22,11 +22,11 @@
 // Arithmetic (log2 units, q' = q * softmax_scale * log2 e):
 //   score_t = sum_c (q'_c s_c) code_tc + sum_c q'_c z_c            (keys, per block)
 //   o_c     = sum_t (p_t s_tj) code_tc + sum_t p_t z_tj, j = c / G_V (values)
-// A set is 128 tokens (128/G blocks), so that each wave keeps about 12 KB of
-// loads in flight. Score phase: lane holds tokens lane and lane + 64, reading
-// their key code rows. P.V phase: lane (n = lane % 16, r = lane / 16) owns
-// channels c = 16 cj + n (cj < 8) and four runs of 8 tokens (r, r+4, r+8,
-// r+12), each run's codes one contiguous chunk of the value-code layout.
+// A set is 64 tokens (64/G blocks); the next set's loads are in flight while a
+// set is computed. Score phase: lane = token, reading its key code row. P.V
+// phase: lane (n = lane % 16, r = lane / 16) owns channels c = 16 cj + n
+// (cj < 8) and the runs of 8 tokens r and r + 4, each run's codes one
+// contiguous chunk of the value-code layout.
 #pragma once
 
 #include "common.h"
@@ -73,8 +73,7 @@ struct Cfg {
   static constexpr int L_KAP = 16;            // kappa per block (NBS <= 4)
   static constexpr int L_P = kSetTok;         // p per token of the set
   static constexpr int L_PV = NGR * kSetTok;  // p * s_V per group and token
-  static constexpr int L_RED = 64 * VSZ_LD;   // end-of-unit reductions
-  static constexpr int L_WAVE = L_Q + L_QT + L_KAP + L_P + L_PV + L_RED;
+  static constexpr int L_WAVE = L_Q + L_QT + L_KAP + L_P + L_PV;
   static_assert(G == 16 || G == 32 || G == 64, "blocks of 16, 32 or 64 tokens");
   static_assert(GV >= 16 && D % GV == 0, "value groups of whole 16-channel tiles");
   static_assert(KB == 2 || KB == 4, "2- or 4-bit keys");
@@ -98,22 +97,25 @@ __device__ __forceinline__ float row_sum16(float x) {
   x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xF, 0xF, false));   // row_ror 8
   return x;
 }
-__device__ __forceinline__ float wave_max64(float v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
-  return v;
-}
-__device__ __forceinline__ float wave_sum64(float v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
-  return v;
-}
 // sum over the four lanes n, n+16, n+32, n+48
 __device__ __forceinline__ float rows_sum4(float x) {
   auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   x = __uint_as_float(r16[0]) + __uint_as_float(r16[1]);
   auto r32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float(r32[0]) + __uint_as_float(r32[1]);
+}
+// Reductions over the wave with row rotations (DPP) and row swaps (no LDS
+// traffic); every lane gets the result.
+__device__ __forceinline__ float wave_sum64(float v) { return rows_sum4(row_sum16(v)); }
+__device__ __forceinline__ float wave_max64(float x) {
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x121, 0xF, 0xF, false)));
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x122, 0xF, 0xF, false)));
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x124, 0xF, 0xF, false)));
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xF, 0xF, false)));
+  auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(r16[0]), __uint_as_float(r16[1]));
+  auto r32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r32[0]), __uint_as_float(r32[1]));
 }
 
 // Byte k of w as a float (the compiler selects v_cvt_f32_ubyte<k>).
@@ -122,13 +124,21 @@ __device__ __forceinline__ float ubyte(uint32_t w) {
   return (float)((w >> (8 * K)) & 0xffu);
 }
 
+// The masked word with its known bits hidden from the compiler, which would
+// otherwise narrow each byte read to a 2- or 4-bit field extract plus a
+// conversion instead of one byte conversion.
+__device__ __forceinline__ uint32_t opaque(uint32_t m) {
+  asm("" : "+v"(m));
+  return m;
+}
+
 // Codes of one 32-bit word as floats, in word order (slot i at bits [i*b, (i+1)*b)).
 template <int B>
 __device__ __forceinline__ void word_codes(uint32_t w, float (&out)[32 / B]) {
   if constexpr (B == 2) {
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      const uint32_t m = (w >> (2 * k)) & 0x03030303u;   // byte j holds slot 4j + k
+      const uint32_t m = opaque((w >> (2 * k)) & 0x03030303u);   // byte j holds slot 4j + k
       out[k] = ubyte<0>(m);
       out[4 + k] = ubyte<1>(m);
       out[8 + k] = ubyte<2>(m);
@@ -137,7 +147,7 @@ __device__ __forceinline__ void word_codes(uint32_t w, float (&out)[32 / B]) {
   } else {
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
-      const uint32_t m = (w >> (4 * k)) & 0x0F0F0F0Fu;   // byte j holds slot 2j + k
+      const uint32_t m = opaque((w >> (4 * k)) & 0x0F0F0F0Fu);   // byte j holds slot 2j + k
       out[k] = ubyte<0>(m);
       out[2 + k] = ubyte<1>(m);
       out[4 + k] = ubyte<2>(m);
@@ -171,19 +181,7 @@ struct WaveLds {
   float* kap;   // [16] kappa per block
   float* p;     // [64] p per set token
   float* pv;    // [NGR][64] p * s_V
-  float* red;   // [64]
 };
-
-// The query of (b, h) scaled to log2 units into L.q (lane holds channels 2l, 2l+1).
-template <class C>
-__device__ __forceinline__ void load_query(const Geom& g, const WaveLds<C>& L, const uint16_t* __restrict__ q,
-                                           float qscale, int b, int h) {
-  const int lane = threadIdx.x & 63;
-  const uint32_t w = reinterpret_cast<const uint32_t*>(q + ((size_t)b * g.Hq + h) * C::D)[lane];
-  *reinterpret_cast<float2*>(L.q + 2 * lane) =
-      make_float2(in_val<C>(w & 0xffffu) * qscale, in_val<C>(w >> 16) * qscale);
-  wave_lds_fence();
-}
 
 // ---------------------------------------------------------------------------------
 // Ring tokens [t0, t1) (at most 64) of one pair: lane = token for the scores
@@ -191,19 +189,40 @@ __device__ __forceinline__ void load_query(const Geom& g, const WaveLds<C>& L, c
 // ---------------------------------------------------------------------------------
 template <class C>
 __device__ __forceinline__ void ring_unit(const Geom& g, const WaveLds<C>& L, const uint16_t* __restrict__ k_ring,
-                                          const uint16_t* __restrict__ v_ring, int pair, int t0, int t1,
+                                          const uint16_t* __restrict__ v_ring, const uint16_t* __restrict__ q,
+                                          float qscale, int b, int h, int t0, int t1,
                                           float* __restrict__ out_part) {
   constexpr int D = C::D;
   const int lane = threadIdx.x & 63;
-  const size_t base = (size_t)pair * g.C;
+  const size_t base = (size_t)(b * g.Hkv + h) * g.C;
   const int n = t1 - t0;
-  // score of token t0 + lane
+  // ring slot of token t0 + u (u < n <= C): one wrap at most
+  const int s0 = t0 % g.C;
+  auto slot = [&](int u) { return s0 + u - (s0 + u >= g.C ? g.C : 0); };
+  // every load of the unit goes out together: the query, the key row of token
+  // t0 + lane and the lane's two channels of all value rows (rows past t1
+  // read row t0 and get probability 0)
+  const uint32_t qw = reinterpret_cast<const uint32_t*>(q + ((size_t)b * g.Hq + h) * D)[lane];
   const bool valid = lane < n;
-  const uint4* krow = reinterpret_cast<const uint4*>(k_ring + (base + (t0 + (valid ? lane : 0)) % g.C) * D);
+  const uint4* krow = reinterpret_cast<const uint4*>(k_ring + (base + slot(valid ? lane : 0)) * D);
+  uint4 kr[D / 8];
+#pragma unroll
+  for (int k = 0; k < D / 8; ++k) kr[k] = krow[k];
+  // (uniform row address + one shared lane offset: scalar-base addressing)
+  const uint8_t* vpair = reinterpret_cast<const uint8_t*>(v_ring + base * D);
+  const uint32_t loff = 4u * (uint32_t)lane;
+  uint32_t vv[kRingTok];
+#pragma unroll
+  for (int u = 0; u < kRingTok; ++u)
+    vv[u] = *reinterpret_cast<const uint32_t*>(vpair + (size_t)slot(u < n ? u : 0) * (2 * D) + loff);
+  *reinterpret_cast<float2*>(L.q + 2 * lane) =
+      make_float2(in_val<C>(qw & 0xffffu) * qscale, in_val<C>(qw >> 16) * qscale);
+  wave_lds_fence();
+  // score of token t0 + lane
   float acc[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int k = 0; k < D / 8; ++k) {
-    const uint4 kw = krow[k];
+    const uint4 kw = kr[k];
     const float4 qa = *reinterpret_cast<const float4*>(L.q + 8 * k);
     const float4 qb = *reinterpret_cast<const float4*>(L.q + 8 * k + 4);
     acc[0] = fmaf(qa.x, in_val<C>(kw.x & 0xffffu), acc[0]);
@@ -221,28 +240,17 @@ __device__ __forceinline__ void ring_unit(const Geom& g, const WaveLds<C>& L, co
   const float l = wave_sum64(p);
   L.p[lane] = p;
   wave_lds_fence();
-  // P.V: lane holds channels 2l, 2l+1; value rows in two batches of 32 tokens
-  // (rows past t1 read row t0 and get probability 0)
+  // P.V: lane holds channels 2l, 2l+1
   float o0 = 0.f, o1 = 0.f;
 #pragma unroll
-  for (int half = 0; half < 2; ++half) {
-    uint32_t vv[kRingTok / 2];
+  for (int u4 = 0; u4 < kRingTok / 4; ++u4) {
+    const float4 pp = *reinterpret_cast<const float4*>(L.p + 4 * u4);
+    const float pq[4] = {pp.x, pp.y, pp.z, pp.w};
 #pragma unroll
-    for (int u = 0; u < kRingTok / 2; ++u) {
-      const int uu = half * (kRingTok / 2) + u;
-      const int t = t0 + (uu < n ? uu : 0);
-      vv[u] = reinterpret_cast<const uint32_t*>(v_ring + (base + t % g.C) * D)[lane];
-    }
-#pragma unroll
-    for (int u4 = 0; u4 < kRingTok / 8; ++u4) {
-      const float4 pp = *reinterpret_cast<const float4*>(L.p + half * (kRingTok / 2) + 4 * u4);
-      const float pq[4] = {pp.x, pp.y, pp.z, pp.w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint32_t w = vv[4 * u4 + e];
-        o0 = fmaf(pq[e], in_val<C>(w & 0xffffu), o0);
-        o1 = fmaf(pq[e], in_val<C>(w >> 16), o1);
-      }
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t w = vv[4 * u4 + e];
+      o0 = fmaf(pq[e], in_val<C>(w & 0xffffu), o0);
+      o1 = fmaf(pq[e], in_val<C>(w >> 16), o1);
     }
   }
   *reinterpret_cast<float2*>(out_part + 2 * lane) = make_float2(o0, o1);
@@ -271,6 +279,7 @@ __device__ __forceinline__ void quant_stream(const Geom& g, const WaveLds<C>& L,
     uint4 ksz[C::KSZ_LD];            // 16-byte chunks of the set's key scale/zero sections
     uint4 vc[C::RPL][C::VW / 4];     // value code chunks of runs rr, rr + 4, ...
     uint4 vsz[C::VSZ_LD];            // 16-byte chunks of the set's value scale/zero sections
+    uint32_t qw;                     // the unit's query, channels 2 lane and 2 lane + 1
   };
   SetBuf cb;   // the set being computed (the next one loads into a second buffer meanwhile)
 
@@ -282,6 +291,7 @@ __device__ __forceinline__ void quant_stream(const Geom& g, const WaveLds<C>& L,
   };
   auto load_set = [&](SetBuf& b, Span sp, int si) {
     const int blk0 = sp.begin + si * NBS;
+    b.qw = reinterpret_cast<const uint32_t*>(q + ((size_t)sp.b * g.Hq + sp.h) * D)[lane];
 #pragma unroll
     for (int tl = 0; tl < kTokLane; ++tl) {
       const int tok = lane + 64 * tl;
@@ -321,12 +331,24 @@ __device__ __forceinline__ void quant_stream(const Geom& g, const WaveLds<C>& L,
 
   // running state of the current unit
   float m_run, l_lane, lam_k[C::VSZ_LD], o[8];
+  int lam_grp[C::VSZ_LD];   // value group of the lane's zero chunk k (-1: a scale chunk)
+#pragma unroll
+  for (int k = 0; k < C::VSZ_LD; ++k) {
+    int bi, off;
+    sz_chunk(k, 4 * NGR * G, bi, off);
+    lam_grp[k] = (bi < NBS && off >= 2 * NGR * G) ? ((off - 2 * NGR * G) / 2) / G : -1;
+  }
 
   auto run_set = [&](Span cur, int si, Span nsp, int nsi) {
     const int blk0 = cur.begin + si * NBS;
     // the next set's loads go out first and stay in flight through this set
     SetBuf nb;
     load_set(nb, nsp, nsi);
+    if (si == 0) {   // a unit's first set: its query (prefetched with the set) into LDS
+      *reinterpret_cast<float2*>(L.q + 2 * lane) =
+          make_float2(in_val<C>(cb.qw & 0xffffu) * qscale, in_val<C>(cb.qw >> 16) * qscale);
+      wave_lds_fence();
+    }
     // ---- q~ = q' * s_K and kappa partials from the key scale/zero chunks ----
 #pragma unroll
     for (int k = 0; k < C::KSZ_LD; ++k) {
@@ -465,27 +487,15 @@ __device__ __forceinline__ void quant_stream(const Geom& g, const WaveLds<C>& L,
   // the unit's result: o_c = sum over the 4 run lanes + lambda(group of c)
   auto finish_unit = [&](float* __restrict__ out_part) {
     const float lsum = wave_sum64(l_lane);
-    // lambda: chunk k of lane ln, if a zero chunk, belongs to group j(k, ln);
-    // every lane sums the partials of each group from LDS
-#pragma unroll
-    for (int k = 0; k < C::VSZ_LD; ++k) L.red[64 * k + lane] = lam_k[k];
-    wave_lds_fence();
+    // lambda of group j: the zero-chunk partials of every lane whose chunk
+    // belongs to group j, summed over the wave
     float lam[NGR];
 #pragma unroll
-    for (int j = 0; j < NGR; ++j) lam[j] = 0.f;
+    for (int j = 0; j < NGR; ++j) {
+      float x = 0.f;
 #pragma unroll
-    for (int k = 0; k < C::VSZ_LD; ++k) {
-#pragma unroll
-      for (int l4 = 0; l4 < 16; ++l4) {
-        const float4 v = *reinterpret_cast<const float4*>(L.red + 64 * k + 4 * l4);
-        const float vv[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int o2 = (k * 64 + 4 * l4 + e) * 16;   // chunk byte offset in the set's sections
-          const int bi = o2 / (4 * NGR * G), off = o2 % (4 * NGR * G);
-          if (bi < NBS && off >= 2 * NGR * G) lam[((off - 2 * NGR * G) / 2) / G] += vv[e];
-        }
-      }
+      for (int k = 0; k < C::VSZ_LD; ++k) x += lam_grp[k] == j ? lam_k[k] : 0.f;
+      lam[j] = wave_sum64(x);
     }
 #pragma unroll
     for (int cj = 0; cj < 8; ++cj) {
@@ -502,7 +512,6 @@ __device__ __forceinline__ void quant_stream(const Geom& g, const WaveLds<C>& L,
   int u = first;
   Span cur = first_span;
   load_set(cb, cur, 0);
-  load_query<C>(g, L, q, qscale, cur.b, cur.h);
   while (true) {
     m_run = -INFINITY;
     l_lane = 0.f;
@@ -515,13 +524,9 @@ __device__ __forceinline__ void quant_stream(const Geom& g, const WaveLds<C>& L,
     const int nu = claim(claimed);
     const bool more = nu < units;
     const Span nxt = more ? locate(nu) : cur;
-    const uint32_t qn = reinterpret_cast<const uint32_t*>(q + ((size_t)nxt.b * g.Hq + nxt.h) * D)[lane];
     run_set(cur, nsets - 1, nxt, more ? 0 : nsets - 1);
     finish_unit(ws + (size_t)u * (D + 2));
     if (!more) break;
-    *reinterpret_cast<float2*>(L.q + 2 * lane) =
-        make_float2(in_val<C>(qn & 0xffffu) * qscale, in_val<C>(qn >> 16) * qscale);
-    wave_lds_fence();
     u = nu;
     cur = nxt;
     claimed = issue();
@@ -533,7 +538,7 @@ __device__ __forceinline__ void quant_stream(const Geom& g, const WaveLds<C>& L,
 // matrix-core path does).
 // ------------------------------------------------------------------------------------
 template <class C>
-__global__ __launch_bounds__(256) void decode_mha_kernel(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void decode_mha_kernel(
     Geom g, const uint8_t* __restrict__ blocks, const int32_t* __restrict__ table,
     const uint16_t* __restrict__ k_ring, const uint16_t* __restrict__ v_ring, int32_t* __restrict__ state,
     const uint16_t* __restrict__ q, float qscale, int max_blk, int* __restrict__ ws_plan, float* __restrict__ ws) {
@@ -550,7 +555,6 @@ __global__ __launch_bounds__(256) void decode_mha_kernel(
   L.kap = L.qt + C::L_QT;
   L.p = L.kap + C::L_KAP;
   L.pv = L.p + C::L_P;
-  L.red = L.pv + C::L_PV;
 
   build_unit_plan(g, state, max_blk, C::NBS, kRingTok, plan, red, blockIdx.x == 0);
   if (blockIdx.x == 0)
@@ -560,11 +564,6 @@ __global__ __launch_bounds__(256) void decode_mha_kernel(
   const int qwaves = (int)(gridDim.x / kQueues) * kWaves;
   int* counter = state + state_queue_word(g.B, queue);
   int* done = state + state_done_word(g.B);
-  auto qs_of = [&](int b, int& Q, int& S) {
-    Q = state[4 * b + kStateQ];
-    S = state[4 * b + kStateS];
-  };
-  auto nblk_of = [&](int b) { return min(state[4 * b + kStateQ] / g.G, max_blk); };
   auto issue = [&]() -> int {
     int v = 0;
     if (lane == 0) v = atomicAdd(counter, 1);
@@ -572,7 +571,7 @@ __global__ __launch_bounds__(256) void decode_mha_kernel(
   };
   auto claim = [&](int raw) -> int { return queue + kQueues * (qwaves + __builtin_amdgcn_readfirstlane(raw)); };
   auto span_of = [&](int uu) -> Span {
-    const Unit un = locate_unit(g, plan, uu, qs_of, nblk_of);
+    const Unit un = locate_unit(g, plan, uu, max_blk);
     Span sp;
     sp.b = __builtin_amdgcn_readfirstlane(un.b);
     sp.h = __builtin_amdgcn_readfirstlane(un.h);
@@ -585,8 +584,7 @@ __global__ __launch_bounds__(256) void decode_mha_kernel(
   int claimed = issue();
   while (u < units && u < plan[kPlanSec]) {
     const Span sp = span_of(u);
-    load_query<C>(g, L, q, qscale, sp.b, sp.h);
-    ring_unit<C>(g, L, k_ring, v_ring, sp.b * g.Hkv + sp.h, sp.begin, sp.end, ws + (size_t)u * (C::D + 2));
+    ring_unit<C>(g, L, k_ring, v_ring, q, qscale, sp.b, sp.h, sp.begin, sp.end, ws + (size_t)u * (C::D + 2));
     u = claim(claimed);
     claimed = issue();
   }

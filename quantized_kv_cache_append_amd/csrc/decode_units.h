@@ -38,10 +38,12 @@ enum {
   kPlanUs = 7,      // blocks per small unit
   kPlanRc = 8,      // ring tokens per ring unit
   kPlanHdr = 12,    // then pre[s][B + 1] for each section s: exclusive prefix over
-};                  // sequences of the section's units of one kv head
+};                  // sequences of the section's units of one kv head; then the
+                    // lengths the plan was built from, Q[B] and S[B]
 constexpr int kSections = 4;
 
-__host__ __device__ inline int plan_ints(int B) { return kPlanHdr + kSections * (B + 1); }
+__host__ __device__ inline int plan_ints(int B) { return kPlanHdr + kSections * (B + 1) + 2 * B; }
+__host__ __device__ inline int plan_seq_off(int B) { return kPlanHdr + kSections * (B + 1); }
 inline size_t plan_bytes(int B) { return ((size_t)plan_ints(B) * 4 + 255) & ~(size_t)255; }
 
 // Upper bound on the units when no sequence has more than max_blk quantized
@@ -127,6 +129,8 @@ __device__ inline void build_unit_plan(const Geom& g, int32_t* state, int max_bl
   bool too_long = false;
   for (int b = threadIdx.x; b < g.B; b += blockDim.x) {
     const int Q = state[4 * b + kStateQ], S = state[4 * b + kStateS];
+    plan[plan_seq_off(g.B) + b] = Q;
+    plan[plan_seq_off(g.B) + g.B + b] = S;
     int nblk = Q / g.G;
     if (nblk > max_blk) {
       nblk = max_blk;
@@ -191,10 +195,9 @@ __device__ __forceinline__ int find_seq(const int* pre, int B, int Hkv, int v) {
   return lo;
 }
 
-// `qs_of(b, Q, S)` gives the quantized prefix and length of sequence b;
-// `nblk_of(b)` its (clamped) quantized blocks.
-template <class QsOf, class NblkOf>
-__device__ inline Unit locate_unit(const Geom& g, const int* plan, int u, QsOf qs_of, NblkOf nblk_of) {
+// Unit u of the plan (in LDS: every read of it is an LDS read). Sequences are
+// cut to max_blk quantized blocks, as when the plan was built.
+__device__ inline Unit locate_unit(const Geom& g, const int* plan, int u, int max_blk) {
   int v = u, sec = 0;
   while (sec < kSections - 1 && v >= plan[kPlanSec + sec]) {
     v -= plan[kPlanSec + sec];
@@ -209,14 +212,14 @@ __device__ inline Unit locate_unit(const Geom& g, const int* plan, int u, QsOf q
   r.h = v / n;
   const int i = v % n;
   r.ring = sec == 0;
+  const int Q = plan[plan_seq_off(g.B) + b];
   if (sec == 0) {
-    int Q, S;
-    qs_of(b, Q, S);
+    const int S = plan[plan_seq_off(g.B) + g.B + b];
     const int rc = plan[kPlanRc];
     r.begin = Q + i * rc;
     r.end = min(S, r.begin + rc);
   } else {
-    const int nblk = nblk_of(b);
+    const int nblk = min(Q / g.G, max_blk);
     const int um = plan[kPlanUm], us = plan[kPlanUs];
     const Tail t = tail_of(nblk, um, us);
     const int body = nblk - t.mid - t.small;
