@@ -49,14 +49,13 @@ __global__ __launch_bounds__(256) void decode_generic_kernel(
   extern __shared__ int smem[];
   int* plan = smem;
   const int pints = plan_ints(g.B);
-  int* red = plan + pints;
-  float* scratch = reinterpret_cast<float*>(smem + ((pints + 16 * kSections + 3) & ~3));
+  float* scratch = reinterpret_cast<float*>(smem + plan_lds_bytes(g.B) / 4);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   float* qt = scratch + wave * (kNgMax * D + kNgMax * 64);   // [8][D]
   float* pb = qt + kNgMax * D;                               // [8][64]
 
   // the whole ring of a pair is one unit (kRingAll tokens per ring unit)
-  build_unit_plan(g, state, max_blk, 1, kRingAll, plan, red, blockIdx.x == 0);
+  build_unit_plan(g, state, max_blk, 1, kRingAll, plan, blockIdx.x == 0);
   if (blockIdx.x == 0)
     for (int i = threadIdx.x; i < pints; i += blockDim.x) ws_plan[i] = plan[i];
 
@@ -297,7 +296,7 @@ template <int D, bool BF16>
 hipError_t launch_generic(const Geom& g, const kvq_cache& c, const void* q, float scale, const DecodePlan& plan,
                           void* ws, hipStream_t s) {
   const int wgs = (int)std::min<size_t>((plan.units_max + kWaves - 1) / kWaves, 2048);
-  const size_t lds = (size_t)((plan_ints(g.B) + 16 * kSections + 3) & ~3) * 4 + (size_t)kWaves * (kNgMax * D + kNgMax * 64) * 4;
+  const size_t lds = (size_t)plan_lds_bytes(g.B) + (size_t)kWaves * (kNgMax * D + kNgMax * 64) * 4;
   hipLaunchKernelGGL((decode_generic_kernel<D, BF16>), dim3(wgs), dim3(256), lds, s, g,
                      static_cast<const uint8_t*>(c.blocks), c.block_table,
                      static_cast<const uint16_t*>(c.k_ring), static_cast<const uint16_t*>(c.v_ring), c.state,

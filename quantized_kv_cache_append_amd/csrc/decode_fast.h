@@ -802,8 +802,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   int* plan = reinterpret_cast<int*>(smem);
   const int pints = plan_ints(g.B);
-  int* red = plan + pints;
-  const int pre_bytes = ((pints + 16 * kSections) * 4 + 15) & ~15;
+  const int pre_bytes = plan_lds_bytes(g.B);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   uint8_t* wl = smem + pre_bytes + wave * C::LDS_WAVE;
   WaveLds<C> L;
@@ -813,7 +812,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   L.lam = L.alpha + 16;
   L.zero16 = reinterpret_cast<uint4*>(L.lam + NG * C::NGR);
 
-  build_unit_plan(g, state, max_blk, C::NB, kRingChunk, plan, red, blockIdx.x == 0);
+  build_unit_plan(g, state, max_blk, C::NB, kRingChunk, plan, blockIdx.x == 0);
   if (blockIdx.x == 0)
     for (int i = threadIdx.x; i < pints; i += blockDim.x) ws_plan[i] = plan[i];
   if (lane == 0) *L.zero16 = make_uint4(0, 0, 0, 0);
@@ -866,7 +865,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 template <class C>
 hipError_t launch_fast(const Geom& g, const kvq_cache& c, const void* q, float scale, int max_blk, void* ws,
                        hipStream_t s) {
-  const size_t lds = (size_t)(((plan_ints(g.B) + 16 * kSections) * 4 + 15) & ~15) + (size_t)kWaves * C::LDS_WAVE;
+  const size_t lds = (size_t)plan_lds_bytes(g.B) + (size_t)kWaves * C::LDS_WAVE;
   const int grid = persistent_grid(decode_fast_kernel<C>, lds);
   hipLaunchKernelGGL((decode_fast_kernel<C>), dim3(grid), dim3(256), lds, s, g,
                      static_cast<const uint8_t*>(c.blocks), c.block_table, static_cast<const uint16_t*>(c.k_ring),

@@ -545,8 +545,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   int* plan = reinterpret_cast<int*>(smem);
   const int pints = plan_ints(g.B);
-  int* red = plan + pints;
-  const int pre_bytes = ((pints + 16 * kSections) * 4 + 15) & ~15;
+  const int pre_bytes = plan_lds_bytes(g.B);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   float* wl = reinterpret_cast<float*>(smem + pre_bytes) + wave * C::L_WAVE;
   WaveLds<C> L;
@@ -556,7 +555,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   L.p = L.kap + C::L_KAP;
   L.pv = L.p + C::L_P;
 
-  build_unit_plan(g, state, max_blk, C::NBS, kRingTok, plan, red, blockIdx.x == 0);
+  build_unit_plan(g, state, max_blk, C::NBS, kRingTok, plan, blockIdx.x == 0);
   if (blockIdx.x == 0)
     for (int i = threadIdx.x; i < pints; i += blockDim.x) ws_plan[i] = plan[i];
   const int units = plan[kPlanUnits];
@@ -604,7 +603,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 template <class C>
 hipError_t launch_mha(const Geom& g, const kvq_cache& c, const void* q, float scale, int max_blk, void* ws,
                       hipStream_t s) {
-  const size_t lds = (size_t)(((plan_ints(g.B) + 16 * kSections) * 4 + 15) & ~15) + (size_t)kWaves * C::L_WAVE * 4;
+  const size_t lds = (size_t)plan_lds_bytes(g.B) + (size_t)kWaves * C::L_WAVE * 4;
   const int grid = persistent_grid(decode_mha_kernel<C>, lds);
   hipLaunchKernelGGL((decode_mha_kernel<C>), dim3(grid), dim3(256), lds, s, g,
                      static_cast<const uint8_t*>(c.blocks), c.block_table, static_cast<const uint16_t*>(c.k_ring),

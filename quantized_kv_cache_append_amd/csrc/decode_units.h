@@ -45,6 +45,8 @@ constexpr int kSections = 4;
 __host__ __device__ inline int plan_ints(int B) { return kPlanHdr + kSections * (B + 1) + 2 * B; }
 __host__ __device__ inline int plan_seq_off(int B) { return kPlanHdr + kSections * (B + 1); }
 inline size_t plan_bytes(int B) { return ((size_t)plan_ints(B) * 4 + 255) & ~(size_t)255; }
+// LDS bytes a decode workgroup reserves for its copy of the plan (16-byte aligned)
+__host__ __device__ inline int plan_lds_bytes(int B) { return (plan_ints(B) * 4 + 15) & ~15; }
 
 // Upper bound on the units when no sequence has more than max_blk quantized
 // blocks, sets hold nb_set blocks and ring units rc tokens: ceil(C/rc) ring
@@ -72,107 +74,81 @@ __host__ __device__ inline Tail tail_of(int nblk, int um, int us) {
 }
 
 #ifdef __HIPCC__
-// Exclusive prefix sums of arr[k][0..n) in place (arr[k][n] gets the total),
-// by every thread of a workgroup of blockDim.x = 64*w threads (w <= 16).
-// `red` is LDS scratch of 16*K ints. Ends with a barrier.
-template <int K>
-__device__ inline void block_scan(int* (&arr)[K], int n, int* red) {
-  const int nt = blockDim.x, t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  const int per = (n + nt - 1) / nt;
-  const int lo = min(n, t * per), hi = min(n, lo + per);
-  int sum[K], inc[K];
-#pragma unroll
-  for (int k = 0; k < K; ++k) {
-    sum[k] = 0;
-    for (int i = lo; i < hi; ++i) sum[k] += arr[k][i];
-    inc[k] = sum[k];
-  }
-  // inclusive scan over the wave
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-#pragma unroll
-    for (int k = 0; k < K; ++k) {
-      const int y = __shfl_up(inc[k], off, 64);
-      if (lane >= off) inc[k] += y;
-    }
-  }
-  if (lane == 63) {
-#pragma unroll
-    for (int k = 0; k < K; ++k) red[16 * k + wave] = inc[k];
-  }
-  __syncthreads();
-#pragma unroll
-  for (int k = 0; k < K; ++k) {
-    int e = inc[k] - sum[k];   // exclusive prefix of this thread's range
-    for (int w = 0; w < wave; ++w) e += red[16 * k + w];
-    for (int i = lo; i < hi; ++i) {
-      const int v = arr[k][i];
-      arr[k][i] = e;
-      e += v;
-    }
-    if (t == nt - 1) arr[k][n] = e;
-  }
-  __syncthreads();
-}
-
 // Build the plan in LDS (`plan`, plan_ints(B) ints) from the device-side
-// lengths; every thread of the workgroup calls it. `red` is LDS scratch of 64
-// ints. Sequences with more than max_blk quantized blocks are cut to max_blk
-// (the caller's max_seq_tokens was too small) and, if report_too_long, flag
-// KVQ_DEV_TOO_LONG.
+// lengths: the first wave does all of it (one lane per sequence, 64 sequences
+// at a time), the others wait at the closing barrier; every thread of the
+// workgroup calls it. Sequences with more than max_blk quantized blocks are cut
+// to max_blk (the caller's max_seq_tokens was too small) and, if
+// report_too_long, flag KVQ_DEV_TOO_LONG.
 __device__ inline void build_unit_plan(const Geom& g, int32_t* state, int max_blk, int nb_set, int rc, int* plan,
-                                       int* red, bool report_too_long) {
-  int* pre[kSections];
-  for (int k = 0; k < kSections; ++k) pre[k] = plan + kPlanHdr + k * (g.B + 1);
-  // total sets over all pairs
-  int sets = 0;
-  bool too_long = false;
-  for (int b = threadIdx.x; b < g.B; b += blockDim.x) {
-    const int Q = state[4 * b + kStateQ], S = state[4 * b + kStateS];
-    plan[plan_seq_off(g.B) + b] = Q;
-    plan[plan_seq_off(g.B) + g.B + b] = S;
-    int nblk = Q / g.G;
-    if (nblk > max_blk) {
-      nblk = max_blk;
-      too_long = true;
+                                       bool report_too_long) {
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    int* seqQ = plan + plan_seq_off(g.B);
+    int* seqS = seqQ + g.B;
+    // pass 1: lengths into the plan, quantized sets in all
+    int sets = 0;
+    bool too_long = false;
+    for (int b = lane; b < g.B; b += 64) {
+      const int Q = state[4 * b + kStateQ], S = state[4 * b + kStateS];
+      seqQ[b] = Q;
+      seqS[b] = S;
+      const int nblk = Q / g.G;
+      too_long |= nblk > max_blk;
+      sets += (min(nblk, max_blk) + nb_set - 1) / nb_set;
     }
-    const int r = min(max(S - Q, 0), g.C);
-    pre[0][b] = (r + rc - 1) / rc;
-    pre[1][b] = nblk;   // stash
-    sets += (nblk + nb_set - 1) / nb_set;
-  }
-  if (too_long && report_too_long) atomicOr(&state[4 * g.B], KVQ_DEV_TOO_LONG);
+    if (too_long && report_too_long) atomicOr(&state[4 * g.B], KVQ_DEV_TOO_LONG);
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) sets += __shfl_xor(sets, off, 64);
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = sets;
-  __syncthreads();
-  long long tot = 0;
-  for (int w = 0; w < (int)(blockDim.x >> 6); ++w) tot += red[w];
-  tot *= g.Hkv;
-  int ub_sets = (int)((tot + kUnitsTarget - 1) / kUnitsTarget);
-  ub_sets = max(1, min(kMaxUnitSets, ub_sets));
-  const int ub = ub_sets * nb_set, um = max(1, ub_sets / 4) * nb_set, us = nb_set;
-  __syncthreads();   // red is reused by the scan
-  for (int b = threadIdx.x; b < g.B; b += blockDim.x) {
-    const int nblk = pre[1][b];
-    const Tail t = tail_of(nblk, um, us);
-    pre[1][b] = (nblk - t.mid - t.small + ub - 1) / ub;
-    pre[2][b] = (t.mid + um - 1) / um;
-    pre[3][b] = (t.small + us - 1) / us;
-  }
-  __syncthreads();
-  block_scan<kSections>(pre, g.B, red);
-  if (threadIdx.x == 0) {
-    int tot_units = 0;
-    for (int k = 0; k < kSections; ++k) {
-      plan[kPlanSec + k] = g.Hkv * pre[k][g.B];
-      tot_units += plan[kPlanSec + k];
+    for (int off = 32; off >= 1; off >>= 1) sets += __shfl_xor(sets, off, 64);
+    const long long tot = (long long)sets * g.Hkv;
+    int ub_sets = (int)((tot + kUnitsTarget - 1) / kUnitsTarget);
+    ub_sets = max(1, min(kMaxUnitSets, ub_sets));
+    const int ub = ub_sets * nb_set, um = max(1, ub_sets / 4) * nb_set, us = nb_set;
+    // pass 2: units per section and sequence, exclusive prefixes over sequences
+    int carry[kSections] = {0, 0, 0, 0};
+    for (int b0 = 0; b0 < g.B; b0 += 64) {
+      const int b = b0 + lane;
+      int cnt[kSections] = {0, 0, 0, 0};
+      if (b < g.B) {
+        const int Q = seqQ[b], S = seqS[b];
+        const int nblk = min(Q / g.G, max_blk);
+        const Tail t = tail_of(nblk, um, us);
+        cnt[0] = (min(max(S - Q, 0), g.C) + rc - 1) / rc;
+        cnt[1] = (nblk - t.mid - t.small + ub - 1) / ub;
+        cnt[2] = (t.mid + um - 1) / um;
+        cnt[3] = (t.small + us - 1) / us;
+      }
+      int inc[kSections];
+#pragma unroll
+      for (int k = 0; k < kSections; ++k) inc[k] = cnt[k];
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+#pragma unroll
+        for (int k = 0; k < kSections; ++k) {
+          const int y = __shfl_up(inc[k], off, 64);
+          if (lane >= off) inc[k] += y;
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < kSections; ++k) {
+        if (b < g.B) plan[kPlanHdr + k * (g.B + 1) + b] = carry[k] + inc[k] - cnt[k];
+        carry[k] += __shfl(inc[k], 63, 64);
+      }
     }
-    plan[kPlanUnits] = tot_units;
-    plan[kPlanUb] = ub;
-    plan[kPlanUm] = um;
-    plan[kPlanUs] = us;
-    plan[kPlanRc] = rc;
+    if (lane == 0) {
+      int tot_units = 0;
+#pragma unroll
+      for (int k = 0; k < kSections; ++k) {
+        plan[kPlanHdr + k * (g.B + 1) + g.B] = carry[k];
+        plan[kPlanSec + k] = g.Hkv * carry[k];
+        tot_units += g.Hkv * carry[k];
+      }
+      plan[kPlanUnits] = tot_units;
+      plan[kPlanUb] = ub;
+      plan[kPlanUm] = um;
+      plan[kPlanUs] = us;
+      plan[kPlanRc] = rc;
+    }
   }
   __syncthreads();
 }
