@@ -69,7 +69,9 @@ struct Cfg {
   static constexpr int VSZ_LD = (VSZ_SET + 1023) / 1024;
   // per-wave LDS (floats)
   static constexpr int L_Q = D;               // q'
-  static constexpr int L_QT = NBS * D;        // q' * s_K per block of the set
+  static constexpr int QT_STRIDE = D + 4;     // per-block rows 16 B apart in bank: the two blocks'
+                                              // broadcast reads of a set fall in different banks
+  static constexpr int L_QT = NBS * QT_STRIDE; // q' * s_K per block of the set
   static constexpr int L_KAP = 16;            // kappa per block (NBS <= 4)
   static constexpr int L_P = kSetTok;         // p per token of the set
   static constexpr int L_PV = NGR * kSetTok;  // p * s_V per group and token
@@ -363,7 +365,7 @@ __device__ __forceinline__ void quant_stream(const Geom& g, const WaveLds<C>& L,
         const float x[8] = {qa.x * h2f_lo(w.x), qa.y * h2f_hi(w.x), qa.z * h2f_lo(w.y), qa.w * h2f_hi(w.y),
                             qb.x * h2f_lo(w.z), qb.y * h2f_hi(w.z), qb.z * h2f_lo(w.w), qb.w * h2f_hi(w.w)};
         if (!zero) {
-          float* dst = L.qt + bi * D + c0;
+          float* dst = L.qt + bi * C::QT_STRIDE + c0;
           *reinterpret_cast<float4*>(dst) = make_float4(x[0], x[1], x[2], x[3]);
           *reinterpret_cast<float4*>(dst + 4) = make_float4(x[4], x[5], x[6], x[7]);
         }
@@ -381,7 +383,7 @@ __device__ __forceinline__ void quant_stream(const Geom& g, const WaveLds<C>& L,
       const int sbi = tok / G;
       const bool valid = blk_ok(cur, blk0 + sbi);
       float acc[4] = {0.f, 0.f, 0.f, 0.f};
-      const float* qt = L.qt + sbi * D;
+      const float* qt = L.qt + sbi * C::QT_STRIDE;
 #pragma unroll
       for (int wi = 0; wi < C::KW; ++wi) {
         const uint32_t w = reinterpret_cast<const uint32_t*>(&cb.kc[tl][wi / 4])[wi % 4];
