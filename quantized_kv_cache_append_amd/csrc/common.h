@@ -111,12 +111,15 @@ __device__ __forceinline__ void wave_lds_fence() {
 // One thread per workgroup calls this after the workgroup's work is done.
 // Returns true for exactly one caller among `total` arrivals on `counter`,
 // after every other arrival; that caller also re-arms the counter to 0.
+// No fences: callers use it only to let one workgroup publish values that all
+// of them computed alike from what they read before arriving (the length
+// words); nothing written by another workgroup is read after it, and the
+// next kernel sees every write at the launch boundary. (A device-scope fence
+// here is an L2 write-back per workgroup.)
 __device__ __forceinline__ bool last_arrival(int* counter, int total) {
-  __threadfence();
   const int old = atomicAdd(counter, 1);
   if (old == total - 1) {
     atomicExch(counter, 0);
-    __threadfence();
     return true;
   }
   return false;
