@@ -24,8 +24,12 @@
 
 namespace kvq {
 
-constexpr int kUnitsTarget = 8192;   // about 4 big units per wave slot of a 256-CU GPU at 2 waves per SIMD
-constexpr int kMaxUnitSets = 64;     // cap on the sets of one big unit
+// About 2 big units per wave slot of a 256-CU GPU at 2 waves per SIMD: a
+// unit change costs a few microseconds of a wave's time (its partial state,
+// the next unit's lookup and first loads), so units are as large as the tail
+// allows; the cap keeps ragged batches with many tiny sets balanced.
+constexpr int kUnitsTarget = 4096;
+constexpr int kMaxUnitSets = 16;     // cap on the sets of one big unit
 constexpr int kTailUnits = 4;        // medium and small units per pair (at most)
 
 // Plan words, at the start of the workspace (written by the decode kernel, read
