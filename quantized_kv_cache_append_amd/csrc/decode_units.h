@@ -30,7 +30,7 @@ namespace kvq {
 // allows; the cap keeps ragged batches with many tiny sets balanced.
 constexpr int kUnitsTarget = 4096;
 constexpr int kMaxUnitSets = 16;     // cap on the sets of one big unit
-constexpr int kTailUnits = 4;        // medium and small units per pair (at most)
+constexpr int kTailUnits = 2;        // medium and small units per pair (at most)
 
 // Plan words, at the start of the workspace (written by the decode kernel, read
 // by the combine kernel) and in each decode workgroup's LDS.
