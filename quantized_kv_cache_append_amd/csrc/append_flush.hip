@@ -10,13 +10,14 @@
 //        recent tokens in full precision next to the low-bit history.
 //   [P2] zubnet.ai survey, quantization family: keep every token, lower the bits.
 //
-// Flush is bandwidth-light (each token is quantized once, when it leaves the
-// window), so one workgroup quantizes one G-token block of one kv head at a
-// time: the tile is staged in LDS with 16-byte loads, column (key) and
+// A block (G tokens of one kv head) is quantized either by one wave, straight
+// from the ring in registers (quantize_wave.h: head_dim 128 and the key/value
+// bits and groups the workloads use), or, for any other shape, by one
+// workgroup: the tile is staged in LDS with 16-byte loads, column (key) and
 // row-group (value) min/max are taken from LDS, codes go to LDS and the packed
 // words are written with consecutive lanes on consecutive words.
 //
-// Three kernels share that block routine:
+// Three kernels share the block routines:
 //   append_kernel        copies new rows into the ring (grid: pair x 64-token chunk);
 //   flush_kernel         quantizes the complete blocks past the window
 //                        (grid: pair x Y, each workgroup strides over the blocks);
@@ -26,6 +27,7 @@
 // and the last of them to finish (an arrival counter in the state words)
 // publishes the new values, so no host synchronisation is needed.
 #include "common.h"
+#include "quantize_wave.h"
 
 namespace kvq {
 
@@ -33,32 +35,6 @@ namespace {
 
 constexpr int kAppendTokensPerWG = 64;
 constexpr int kThreads = 256;
-
-// Formula F on one group whose min and max are known (fp32 IEEE steps, round to
-// nearest even, no fused multiply-add). Returns the fp16 bits of scale and
-// zero and the reciprocal used for the codes (0 for a constant group).
-struct GroupParams {
-  uint16_t s16, z16;
-  float zf, inv;
-};
-__device__ __forceinline__ GroupParams group_params(float mn, float mx, int bits) {
-  GroupParams p;
-  p.z16 = f32_to_f16_bits(mn);
-  const float qmax = (float)((1 << bits) - 1);
-  const float range = __fsub_rn(mx, mn);
-  p.s16 = f32_to_f16_bits(__fdiv_rn(range, qmax));
-  const float sf = f16_to_f32(p.s16);
-  p.zf = f16_to_f32(p.z16);
-  p.inv = (sf == 0.0f) ? 0.0f : __fdiv_rn(1.0f, sf);
-  return p;
-}
-__device__ __forceinline__ uint32_t group_code(float x, const GroupParams& p, int bits) {
-  if (p.inv == 0.0f) return 0u;
-  const float t = __fmul_rn(__fsub_rn(x, p.zf), p.inv);
-  const float qmax = (float)((1 << bits) - 1);
-  const float r = fminf(fmaxf(rintf(t), 0.0f), qmax);
-  return (uint32_t)r;
-}
 
 // LDS of the block routine: raw tile [G][d] x 2 (16-bit), codes [G][d] x 2 (8-bit).
 __host__ __device__ inline size_t block_lds_bytes(int G, int d) { return (size_t)6 * G * d; }
@@ -212,7 +188,46 @@ __global__ __launch_bounds__(kThreads) void append_kernel(Geom g, const uint16_t
   }
 }
 
+// The two block routines behind one interface: Workers blocks at a time per
+// workgroup (the wave routine: one per wave; the workgroup routine: one).
 template <bool BF16>
+struct WgBlock {
+  static constexpr int kWorkers = 1;
+  static size_t lds(const Geom& g) { return block_lds_bytes(g.G, g.d); }
+  __device__ static void run(const Geom& g, uint8_t* rec, const uint16_t* kr, const uint16_t* vr, int pair,
+                             int blk, uint8_t* smem) {
+    quantize_block<BF16>(g, rec, kr, vr, pair, blk, smem);
+  }
+};
+template <class Q>
+struct WaveBlock {
+  static constexpr int kWorkers = kThreads / 64;
+  static size_t lds(const Geom&) { return 0; }
+  __device__ static void run(const Geom& g, uint8_t* rec, const uint16_t* kr, const uint16_t* vr, int pair,
+                             int blk, uint8_t*) {
+    qwave::quantize_block<Q>(g, rec, kr, vr, pair, blk);
+  }
+};
+
+// Blocks k0, k0 + stride, ... below nok of pair (b, h), by this thread's
+// worker (wave or workgroup); `bad` is set for a missing page.
+template <class P>
+__device__ __forceinline__ void flush_blocks(const Geom& g, uint8_t* blocks, const int32_t* table,
+                                             const uint16_t* k_ring, const uint16_t* v_ring, int pair, int b, int h,
+                                             int Q, int k0, int stride, int nok, int* bad, uint8_t* smem) {
+  const int worker = P::kWorkers > 1 ? (int)(threadIdx.x / (kThreads / P::kWorkers)) : 0;
+  for (int k = k0 * P::kWorkers + worker; k < nok; k += stride * P::kWorkers) {
+    const int blk = Q / g.G + k;
+    uint8_t* rec = const_cast<uint8_t*>(block_record(g, blocks, table, b, h, blk));
+    if (rec == nullptr) {
+      if (threadIdx.x % (kThreads / P::kWorkers) == 0) *bad = 1;
+      continue;
+    }
+    P::run(g, rec, k_ring, v_ring, pair, blk, smem);
+  }
+}
+
+template <class P>
 __global__ __launch_bounds__(kThreads) void flush_kernel(Geom g, uint8_t* __restrict__ blocks,
                                                          const int32_t* __restrict__ table,
                                                          const uint16_t* __restrict__ k_ring,
@@ -231,15 +246,7 @@ __global__ __launch_bounds__(kThreads) void flush_kernel(Geom g, uint8_t* __rest
     s_bad = 0;
   }
   __syncthreads();
-  for (int k = blockIdx.y; k < s_nok; k += gridDim.y) {
-    const int blk = s_Q / g.G + k;
-    uint8_t* rec = const_cast<uint8_t*>(block_record(g, blocks, table, b, h, blk));
-    if (rec == nullptr) {
-      if (threadIdx.x == 0) s_bad = 1;
-      continue;
-    }
-    quantize_block<BF16>(g, rec, k_ring, v_ring, pair, blk, smem);
-  }
+  flush_blocks<P>(g, blocks, table, k_ring, v_ring, pair, b, h, s_Q, blockIdx.y, gridDim.y, s_nok, &s_bad, smem);
   __syncthreads();
   if (threadIdx.x == 0) {
     if (s_bad) atomicOr(&state[4 * g.B], KVQ_DEV_BAD_PAGE);
@@ -253,7 +260,7 @@ __global__ __launch_bounds__(kThreads) void flush_kernel(Geom g, uint8_t* __rest
 // Append then flush, one workgroup per (sequence, kv head): the decode-step
 // path. Every workgroup of a sequence derives the same new lengths from the
 // same (Q_b, S_b, n_b); the last to finish publishes them.
-template <bool BF16>
+template <class P>
 __global__ __launch_bounds__(kThreads) void append_flush_kernel(Geom g, const uint16_t* __restrict__ k_new,
                                                                 const uint16_t* __restrict__ v_new,
                                                                 const int32_t* __restrict__ n_new, int n_max,
@@ -287,15 +294,7 @@ __global__ __launch_bounds__(kThreads) void append_flush_kernel(Geom g, const ui
   // workgroup's ring writes visible to all of its threads first
   __threadfence_block();
   __syncthreads();
-  for (int k = 0; k < s_nok; ++k) {
-    const int blk = s_Q / g.G + k;
-    uint8_t* rec = const_cast<uint8_t*>(block_record(g, blocks, table, b, h, blk));
-    if (rec == nullptr) {
-      if (threadIdx.x == 0) s_bad = 1;
-      continue;
-    }
-    quantize_block<BF16>(g, rec, k_ring, v_ring, pair, blk, smem);
-  }
+  flush_blocks<P>(g, blocks, table, k_ring, v_ring, pair, b, h, s_Q, 0, 1, s_nok, &s_bad, smem);
   __syncthreads();
   if (threadIdx.x == 0) {
     if (s_bad) atomicOr(&state[4 * g.B], KVQ_DEV_BAD_PAGE);
@@ -320,24 +319,65 @@ hipError_t launch_append(const Geom& g, const kvq_cache& c, const void* k_new, c
   return hipGetLastError();
 }
 
-hipError_t launch_flush(const Geom& g, const kvq_cache& c, hipStream_t s) {
+namespace {
+
+template <class P>
+hipError_t launch_flush_p(const Geom& g, const kvq_cache& c, hipStream_t s) {
   // A ring of C slots holds at most (C - R) / G complete blocks past the
   // window; spread them over up to Y workgroups per pair, Y chosen so that a
-  // large flush fills the GPU and a decode-sized one launches one per pair.
+  // large flush fills the GPU (about 8192 block workers) and a decode-sized one
+  // launches one workgroup per pair.
   const int max_fl = std::max((g.C - g.R) / g.G, 1);
   const int pairs = g.B * g.Hkv;
-  const int Y = std::max(1, std::min(max_fl, (2048 + pairs - 1) / pairs));
-  dim3 grid(pairs, Y);
-  const size_t lds = block_lds_bytes(g.G, g.d);
-  if (g.dtype == KVQ_BF16)
-    hipLaunchKernelGGL(flush_kernel<true>, grid, dim3(kThreads), lds, s, g, static_cast<uint8_t*>(c.blocks),
-                       c.block_table, static_cast<const uint16_t*>(c.k_ring),
-                       static_cast<const uint16_t*>(c.v_ring), c.state);
-  else
-    hipLaunchKernelGGL(flush_kernel<false>, grid, dim3(kThreads), lds, s, g, static_cast<uint8_t*>(c.blocks),
-                       c.block_table, static_cast<const uint16_t*>(c.k_ring),
-                       static_cast<const uint16_t*>(c.v_ring), c.state);
+  const int per_wg = P::kWorkers;
+  const int Y = std::max(1, std::min((max_fl + per_wg - 1) / per_wg, (8192 + pairs * per_wg - 1) / (pairs * per_wg)));
+  hipLaunchKernelGGL((flush_kernel<P>), dim3(pairs, Y), dim3(kThreads), P::lds(g), s, g,
+                     static_cast<uint8_t*>(c.blocks), c.block_table, static_cast<const uint16_t*>(c.k_ring),
+                     static_cast<const uint16_t*>(c.v_ring), c.state);
   return hipGetLastError();
+}
+
+template <class P>
+hipError_t launch_append_flush_p(const Geom& g, const kvq_cache& c, const void* k_new, const void* v_new,
+                                 const int32_t* n_new, int n_max, hipStream_t s) {
+  hipLaunchKernelGGL((append_flush_kernel<P>), dim3(g.B * g.Hkv), dim3(kThreads), P::lds(g), s, g,
+                     static_cast<const uint16_t*>(k_new), static_cast<const uint16_t*>(v_new), n_new, n_max,
+                     static_cast<uint8_t*>(c.blocks), c.block_table, static_cast<uint16_t*>(c.k_ring),
+                     static_cast<uint16_t*>(c.v_ring), c.state);
+  return hipGetLastError();
+}
+
+using FlushFn = hipError_t (*)(const Geom&, const kvq_cache&, hipStream_t);
+using AppendFlushFn = hipError_t (*)(const Geom&, const kvq_cache&, const void*, const void*, const int32_t*, int,
+                                     hipStream_t);
+struct QuantEntry {
+  int G, kb, vb, GV, dtype;
+  FlushFn flush;
+  AppendFlushFn append_flush;
+};
+template <bool BF16, int G, int KB, int VB, int GV>
+QuantEntry wave_entry() {
+  using P = WaveBlock<qwave::Cfg<BF16, G, KB, VB, GV>>;
+  return QuantEntry{G, KB, VB, GV, BF16 ? KVQ_BF16 : KVQ_F16, &launch_flush_p<P>, &launch_append_flush_p<P>};
+}
+// head_dim 128: the key/value bits and groups of the workloads, fp16 and bf16
+#define KVQ_WAVE(G, KB, VB, GV) wave_entry<false, G, KB, VB, GV>(), wave_entry<true, G, KB, VB, GV>()
+const QuantEntry* find_wave(const Geom& g) {
+  static const QuantEntry kTable[] = {
+      KVQ_WAVE(32, 2, 2, 32), KVQ_WAVE(32, 4, 4, 32), KVQ_WAVE(64, 2, 2, 64), KVQ_WAVE(16, 4, 2, 32),
+  };
+  if (g.d != 128) return nullptr;
+  for (const QuantEntry& e : kTable)
+    if (e.G == g.G && e.kb == g.kb && e.vb == g.vb && e.GV == g.GV && e.dtype == g.dtype) return &e;
+  return nullptr;
+}
+#undef KVQ_WAVE
+
+}  // namespace
+
+hipError_t launch_flush(const Geom& g, const kvq_cache& c, hipStream_t s) {
+  if (const QuantEntry* e = find_wave(g)) return e->flush(g, c, s);
+  return g.dtype == KVQ_BF16 ? launch_flush_p<WgBlock<true>>(g, c, s) : launch_flush_p<WgBlock<false>>(g, c, s);
 }
 
 hipError_t launch_append_flush(const Geom& g, const kvq_cache& c, const void* k_new, const void* v_new,
@@ -347,20 +387,9 @@ hipError_t launch_append_flush(const Geom& g, const kvq_cache& c, const void* k_
     hipError_t e = launch_append(g, c, k_new, v_new, n_new, n_max, s);
     return e != hipSuccess ? e : launch_flush(g, c, s);
   }
-  const size_t lds = block_lds_bytes(g.G, g.d);
-  dim3 grid(g.B * g.Hkv);
-  const auto* kn = static_cast<const uint16_t*>(k_new);
-  const auto* vn = static_cast<const uint16_t*>(v_new);
-  auto* blocks = static_cast<uint8_t*>(c.blocks);
-  auto* kr = static_cast<uint16_t*>(c.k_ring);
-  auto* vr = static_cast<uint16_t*>(c.v_ring);
-  if (g.dtype == KVQ_BF16)
-    hipLaunchKernelGGL(append_flush_kernel<true>, grid, dim3(kThreads), lds, s, g, kn, vn, n_new, n_max, blocks,
-                       c.block_table, kr, vr, c.state);
-  else
-    hipLaunchKernelGGL(append_flush_kernel<false>, grid, dim3(kThreads), lds, s, g, kn, vn, n_new, n_max, blocks,
-                       c.block_table, kr, vr, c.state);
-  return hipGetLastError();
+  if (const QuantEntry* e = find_wave(g)) return e->append_flush(g, c, k_new, v_new, n_new, n_max, s);
+  return g.dtype == KVQ_BF16 ? launch_append_flush_p<WgBlock<true>>(g, c, k_new, v_new, n_new, n_max, s)
+                             : launch_append_flush_p<WgBlock<false>>(g, c, k_new, v_new, n_new, n_max, s);
 }
 
 }  // namespace kvq
