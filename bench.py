@@ -18,7 +18,9 @@ Prints one JSON line on stdout; human-readable detail goes to stderr.
 whole step); `roofline` is the decode-partials kernel's algorithmic bytes over
 its own event-timed duration, against the 8 TB/s HBM peak; `traffic` is the
 HBM traffic rocprofv3 counters measured for that kernel (profiles/), reported
-only while the kernel sources still hash to the ones measured.
+only while the kernel sources still hash to the ones measured. `quantize` is
+the flush (quantize + pack) rate over the workload's whole quantized prefix:
+every token appended into one ring, then one kvq_flush_residual, timed.
 """
 from __future__ import annotations
 
@@ -110,6 +112,40 @@ def measured_traffic(workload: str):
         return float(kv["traffic_bytes_per_launch"])
     except (KeyError, ValueError):
         return None
+
+
+def quantize_rate(w, inp, lengths, dev, reps=5):
+    """Full-prefix flush: all of every sequence's tokens appended into a ring
+    that holds them, then one kvq_flush_residual quantizes and packs every
+    complete block past the window (event-timed, median of `reps`). Bytes are
+    the fp16/bf16 rows read plus the records written."""
+    import torch
+    from quantized_kv_cache_append_amd.cache import cache_for_workload
+    S = max(lengths)
+    c = cache_for_workload(w, lengths, S, device=dev)
+    lens = torch.tensor(list(lengths), dtype=torch.int32, device=dev)
+    k, v = inp.k[:, :, :S].contiguous(), inp.v[:, :, :S].contiguous()
+    ts = []
+    for _ in range(reps):
+        c.state.zero_()
+        c.append(k, v, lens)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        c.flush()
+        b.record()
+        torch.cuda.synchronize()
+        ts.append(a.elapsed_time(b) * 1e-3)
+    if c.read_device_error():
+        raise SystemExit("device error word set by the quantize measurement")
+    q_tok = sum(quantized_prefix(s, w.residual, w.k_group) for s in lengths) * w.num_kv_heads
+    nbytes = q_tok * w.head_dim * 2 * 2 + (q_tok // w.k_group) * c.record_bytes
+    t = sorted(ts)[len(ts) // 2]
+    del c, k, v
+    torch.cuda.empty_cache()
+    gbps = nbytes / t / 1e9
+    return {"value": round(gbps, 1), "unit": "GB/s", "frac": round(gbps / PEAK_HBM_GBPS, 4),
+            "us_per_flush": round(t * 1e6, 1), "bytes": int(nbytes), "kernel": "flush_kernel",
+            "sample": f"one flush of every pair's whole quantized prefix ({q_tok} token-heads), median of {reps}"}
 
 
 def cpu_baseline(w, inp, lengths, budget_s=15.0):
@@ -307,8 +343,12 @@ def main():
                      "traffic": None if traffic is None else round(traffic),
                      "kernel": kernel, "us_per_launch": round(part_avg_ms * 1e3, 2),
                      "bytes_per_launch": int(avg_part_bytes)},
+        "quantize": None,
         "cpu_baseline": None,
     }
+    result["quantize"] = quantize_rate(w, inp, lengths0, dev)
+    log(f"[bench] quantize: full-prefix flush {result['quantize']['us_per_flush']:.1f} us, "
+        f"{result['quantize']['bytes'] / 1e6:.1f} MB -> {result['quantize']['value']:.0f} GB/s")
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, inp, [s + 0 for s in lengths0])
         log(f"[bench] oracle on the host: {result['cpu_baseline']['value']:.3f} GB/s")
