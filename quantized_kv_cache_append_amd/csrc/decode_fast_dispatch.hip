@@ -7,6 +7,7 @@
 // any other configuration runs the generic kernel in decode.hip.
 #include "decode_fast.h"
 #include "decode_mha.h"
+#include "decode_mx.h"
 
 namespace kvq {
 
@@ -28,6 +29,12 @@ FastEntry mfma_entry() {
   return FastEntry{NG, KB, VB, G, GV, BF16 ? KVQ_BF16 : KVQ_F16, PAGED, C::NB, fast::kRingChunk,
                    &fast::launch_fast<C>};
 }
+template <bool BF16, bool PAGED>
+FastEntry mx_entry() {
+  using C = mx::Cfg<BF16, PAGED>;
+  return FastEntry{1, C::KB, C::VB, C::G, C::GV, BF16 ? KVQ_BF16 : KVQ_F16, PAGED, mx::kSetBlk, mx::kRingTok,
+                   &mx::launch_mx<C>};
+}
 template <int KB, int VB, int G, int GV, bool BF16, bool PAGED>
 FastEntry mha_entry() {
   using C = mha::Cfg<KB, VB, G, GV, BF16, PAGED>;
@@ -39,11 +46,12 @@ FastEntry mha_entry() {
 #define KVQ_MFMA(NG, KB, VB, G, GV, BF16) \
   mfma_entry<NG, KB, VB, G, GV, BF16, false>(), mfma_entry<NG, KB, VB, G, GV, BF16, true>()
 #define KVQ_MHA(KB, VB, G, GV, BF16) mha_entry<KB, VB, G, GV, BF16, false>(), mha_entry<KB, VB, G, GV, BF16, true>()
+#define KVQ_MX(BF16) mx_entry<BF16, false>(), mx_entry<BF16, true>()
 
 const FastEntry* table() {
   static const FastEntry kFast[] = {
-      KVQ_MHA(2, 2, 32, 32, false),        // MHA, INT2, G = G_V = 32, fp16 (a Llama-2-7B-shaped layer)
-      KVQ_MHA(2, 2, 32, 32, true),
+      KVQ_MX(false),                       // MHA, INT2, G = G_V = 32, fp16 (a Llama-2-7B-shaped layer)
+      KVQ_MX(true),
       KVQ_MHA(4, 4, 32, 32, false),        // MHA, INT4
       KVQ_MHA(4, 4, 32, 32, true),
       KVQ_MFMA(4, 4, 4, 32, 32, true),     // GQA 4, INT4 (a Llama-3-8B-shaped layer)
@@ -56,6 +64,7 @@ const FastEntry* table() {
 constexpr int kEntries = 16;
 #undef KVQ_MFMA
 #undef KVQ_MHA
+#undef KVQ_MX
 
 const FastEntry* find(const Geom& g) {
   if (g.d != 128) return nullptr;

@@ -186,10 +186,10 @@ struct WaveLds {
 };
 
 // ---------------------------------------------------------------------------------
-// Ring tokens [t0, t1) (at most 64) of one pair: lane = token for the scores
-// (fp16/bf16 key row against q' in LDS), lane = 2 channels for P.V.
+// Ring tokens [t0, t1) (at most RT <= 64) of one pair: lane = token for the
+// scores (fp16/bf16 key row against q' in LDS), lane = 2 channels for P.V.
 // ---------------------------------------------------------------------------------
-template <class C>
+template <class C, int RT = kRingTok>
 __device__ __forceinline__ void ring_unit(const Geom& g, const WaveLds<C>& L, const uint16_t* __restrict__ k_ring,
                                           const uint16_t* __restrict__ v_ring, const uint16_t* __restrict__ q,
                                           float qscale, int b, int h, int t0, int t1,
@@ -213,9 +213,10 @@ __device__ __forceinline__ void ring_unit(const Geom& g, const WaveLds<C>& L, co
   // (uniform row address + one shared lane offset: scalar-base addressing)
   const uint8_t* vpair = reinterpret_cast<const uint8_t*>(v_ring + base * D);
   const uint32_t loff = 4u * (uint32_t)lane;
-  uint32_t vv[kRingTok];
+  static_assert(RT % 4 == 0 && RT <= 64, "ring units of at most 64 tokens");
+  uint32_t vv[RT];
 #pragma unroll
-  for (int u = 0; u < kRingTok; ++u)
+  for (int u = 0; u < RT; ++u)
     vv[u] = *reinterpret_cast<const uint32_t*>(vpair + (size_t)slot(u < n ? u : 0) * (2 * D) + loff);
   *reinterpret_cast<float2*>(L.q + 2 * lane) =
       make_float2(in_val<C>(qw & 0xffffu) * qscale, in_val<C>(qw >> 16) * qscale);
@@ -245,7 +246,7 @@ __device__ __forceinline__ void ring_unit(const Geom& g, const WaveLds<C>& L, co
   // P.V: lane holds channels 2l, 2l+1
   float o0 = 0.f, o1 = 0.f;
 #pragma unroll
-  for (int u4 = 0; u4 < kRingTok / 4; ++u4) {
+  for (int u4 = 0; u4 < RT / 4; ++u4) {
     const float4 pp = *reinterpret_cast<const float4*>(L.p + 4 * u4);
     const float pq[4] = {pp.x, pp.y, pp.z, pp.w};
 #pragma unroll

@@ -78,6 +78,17 @@ __host__ __device__ inline Tail tail_of(int nblk, int um, int us) {
 }
 
 #ifdef __HIPCC__
+// Inclusive prefix sum over the 64 lanes with row shifts and row broadcasts
+// (DPP: no LDS round trips on the plan's critical path at kernel start).
+__device__ __forceinline__ int wave_incl_scan(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, false);   // row_shr 1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, false);   // row_shr 2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, false);   // row_shr 4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, false);   // row_shr 8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false);   // row_bcast 15 -> rows 1, 3
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false);   // row_bcast 31 -> rows 2, 3
+  return x;
+}
 // Build the plan in LDS (`plan`, plan_ints(B) ints) from the device-side
 // lengths: the first wave does all of it (one lane per sequence, 64 sequences
 // at a time), the others wait at the closing barrier; every thread of the
@@ -102,8 +113,7 @@ __device__ inline void build_unit_plan(const Geom& g, int32_t* state, int max_bl
       sets += (min(nblk, max_blk) + nb_set - 1) / nb_set;
     }
     if (too_long && report_too_long) atomicOr(&state[4 * g.B], KVQ_DEV_TOO_LONG);
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) sets += __shfl_xor(sets, off, 64);
+    sets = __builtin_amdgcn_readlane(wave_incl_scan(sets), 63);
     const long long tot = (long long)sets * g.Hkv;
     int ub_sets = (int)((tot + kUnitsTarget - 1) / kUnitsTarget);
     ub_sets = max(1, min(kMaxUnitSets, ub_sets));
@@ -124,19 +134,11 @@ __device__ inline void build_unit_plan(const Geom& g, int32_t* state, int max_bl
       }
       int inc[kSections];
 #pragma unroll
-      for (int k = 0; k < kSections; ++k) inc[k] = cnt[k];
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-#pragma unroll
-        for (int k = 0; k < kSections; ++k) {
-          const int y = __shfl_up(inc[k], off, 64);
-          if (lane >= off) inc[k] += y;
-        }
-      }
+      for (int k = 0; k < kSections; ++k) inc[k] = wave_incl_scan(cnt[k]);
 #pragma unroll
       for (int k = 0; k < kSections; ++k) {
         if (b < g.B) plan[kPlanHdr + k * (g.B + 1) + b] = carry[k] + inc[k] - cnt[k];
-        carry[k] += __shfl(inc[k], 63, 64);
+        carry[k] += __builtin_amdgcn_readlane(inc[k], 63);
       }
     }
     if (lane == 0) {
