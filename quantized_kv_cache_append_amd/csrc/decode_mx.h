@@ -416,40 +416,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   build_unit_plan(g, state, max_blk, kSetBlk, kRingTok, plan, blockIdx.x == 0);
   if (blockIdx.x == 0)
     for (int i = threadIdx.x; i < pints; i += blockDim.x) ws_plan[i] = plan[i];
-  // Static partition: the units, in plan order, are split into W contiguous
-  // ranges of equal estimated cost (bytes streamed; ring tokens weighted by
-  // kRingWeight), one per wave. Cost is piecewise linear over the plan's
-  // sections, so a wave finds its range in O(1); each unit still writes its
-  // own partial state, so the combine is unchanged. No claims: the next unit
-  // of a wave is always the following one.
-  const int units = __builtin_amdgcn_readfirstlane(plan[kPlanUnits]);
-  int nsec[kSections];
-  long long cost[kSections];
-#pragma unroll
-  for (int k = 0; k < kSections; ++k) nsec[k] = __builtin_amdgcn_readfirstlane(plan[kPlanSec + k]);
-  cost[0] = (long long)kRingTok * 4 * C::D * kRingWeight / 4;
-  cost[1] = (long long)__builtin_amdgcn_readfirstlane(plan[kPlanUb]) * C::REC;
-  cost[2] = (long long)__builtin_amdgcn_readfirstlane(plan[kPlanUm]) * C::REC;
-  cost[3] = (long long)__builtin_amdgcn_readfirstlane(plan[kPlanUs]) * C::REC;
-  long long total = 0;
-#pragma unroll
-  for (int k = 0; k < kSections; ++k) total += nsec[k] * cost[k];
-  // first unit whose start cost is >= c
-  auto unit_at = [&](long long c) -> int {
-    long long cbase = 0;
-    int ubase = 0;
-#pragma unroll
-    for (int k = 0; k < kSections; ++k) {
-      const long long sec = nsec[k] * cost[k];
-      if (nsec[k] > 0 && c <= cbase + sec) return ubase + (int)((c - cbase + cost[k] - 1) / cost[k]);
-      cbase += sec;
-      ubase += nsec[k];
-    }
-    return units;
-  };
-  const long long W = (long long)gridDim.x * kWaves, wv = (long long)blockIdx.x * kWaves + wave;
-  int u = unit_at(total * wv / W);
-  const int u_end = unit_at(total * (wv + 1) / W);
+  const UnitRange range = static_unit_range(plan, (long long)kRingTok * 4 * C::D * kRingWeight / 4, C::REC,
+                                            (long long)blockIdx.x * kWaves + wave, (long long)gridDim.x * kWaves);
+  int u = range.begin;
+  const int u_end = range.end;
+  const int ring_units = __builtin_amdgcn_readfirstlane(plan[kPlanSec]);
   auto span_of = [&](int uu) -> mha::Span {
     const Unit un = locate_unit(g, plan, uu, max_blk);
     mha::Span sp;
@@ -459,7 +430,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     sp.end = __builtin_amdgcn_readfirstlane(un.end);
     return sp;
   };
-  for (; u < u_end && u < nsec[0]; ++u) {
+  for (; u < u_end && u < ring_units; ++u) {
     const mha::Span sp = span_of(u);
     mha::ring_unit<typename C::Ring, kRingTok>(g, L, k_ring, v_ring, q, qscale, sp.b, sp.h, sp.begin, sp.end,
                                                ws + (size_t)u * (C::D + 2));

@@ -214,6 +214,51 @@ __device__ inline Unit locate_unit(const Geom& g, const int* plan, int u, int ma
   return r;
 }
 
+// Static partition of the plan's units over W persistent waves: contiguous
+// ranges, in plan order, of equal estimated cost (bytes streamed; a ring
+// unit costs `ring_cost`, a quantized unit its blocks times `rec_bytes`).
+// The cost is piecewise linear over the sections, so each wave finds its range
+// in O(1) and no work is claimed at run time; every unit still writes its own
+// partial state. All values are wave-uniform.
+struct UnitRange {
+  int begin, end;
+};
+__device__ inline UnitRange static_unit_range(const int* plan, long long ring_cost, long long rec_bytes, long long wv,
+                                              long long W) {
+  int nsec[kSections];
+  long long cost[kSections];
+#pragma unroll
+  for (int k = 0; k < kSections; ++k) nsec[k] = __builtin_amdgcn_readfirstlane(plan[kPlanSec + k]);
+  cost[0] = ring_cost;
+  cost[1] = (long long)__builtin_amdgcn_readfirstlane(plan[kPlanUb]) * rec_bytes;
+  cost[2] = (long long)__builtin_amdgcn_readfirstlane(plan[kPlanUm]) * rec_bytes;
+  cost[3] = (long long)__builtin_amdgcn_readfirstlane(plan[kPlanUs]) * rec_bytes;
+  long long total = 0;
+  int units = 0;
+#pragma unroll
+  for (int k = 0; k < kSections; ++k) {
+    total += nsec[k] * cost[k];
+    units += nsec[k];
+  }
+  // first unit whose start cost is >= c
+  auto unit_at = [&](long long c) -> int {
+    long long cbase = 0;
+    int ubase = 0;
+#pragma unroll
+    for (int k = 0; k < kSections; ++k) {
+      const long long sec = nsec[k] * cost[k];
+      if (nsec[k] > 0 && c <= cbase + sec) return ubase + (int)((c - cbase + cost[k] - 1) / cost[k]);
+      cbase += sec;
+      ubase += nsec[k];
+    }
+    return units;
+  };
+  UnitRange r;
+  r.begin = unit_at(total * wv / W);
+  r.end = unit_at(total * (wv + 1) / W);
+  return r;
+}
+
 // Slot of the i-th partial of pair (b, h): its units section by section.
 struct PairUnits {
   int n;                      // partials of the pair
