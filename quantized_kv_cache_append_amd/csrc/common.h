@@ -168,6 +168,7 @@ struct DecodePlan {
   bool fast;          // MFMA kernel (else the generic VALU kernel)
   int nb_set;         // blocks per set (unit sizes are whole sets)
   int ring_chunk;     // ring tokens per ring unit
+  int unit_sets;      // fixed sets per quantized unit (0: sized from the lengths)
   int max_blk;        // quantized blocks per (sequence, kv head) the workspace is sized for
   size_t units_max;   // upper bound on work units
   size_t ws_bytes;    // workspace bytes: the unit plan, then the partial states
@@ -175,9 +176,9 @@ struct DecodePlan {
 DecodePlan plan_decode(const Geom& g, int max_seq_tokens);
 
 // Specialised paths (decode_fast_dispatch.hip): whether a configuration has an
-// instantiation, its blocks per set and ring tokens per ring unit, and the
-// launch.
-bool fast_supported(const Geom& g, int* blocks_per_set, int* ring_chunk);
+// instantiation, its blocks per set, ring tokens per ring unit and fixed sets
+// per unit (0: sized from the lengths), and the launch.
+bool fast_supported(const Geom& g, int* blocks_per_set, int* ring_chunk, int* unit_sets);
 hipError_t launch_decode_fast(const Geom& g, const kvq_cache& c, const void* q, float scale, const DecodePlan& p,
                               void* ws, hipStream_t s);
 

@@ -283,7 +283,7 @@ __global__ __launch_bounds__(64 * kCombineWaves) void combine_kernel(Geom g, con
     for (int u = 0; u < kCombineBatch; ++u) {
       const float wu = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), u));   // 0 past cnt
 #pragma unroll
-      for (int k = 0; k < CPL; ++k) acc[k] = fmaf(wu, v[u][k], acc[k]);
+      for (int k = 0; k < CPL; ++k) acc[k] = wu == 0.f ? acc[k] : fmaf(wu, v[u][k], acc[k]);   // (empty partials: o unset)
     }
     m = mn;
   }
@@ -309,12 +309,13 @@ hipError_t launch_generic(const Geom& g, const kvq_cache& c, const void* q, floa
 
 DecodePlan plan_decode(const Geom& g, int max_seq_tokens) {
   DecodePlan p{};
-  int nb_set = 1, rc = kRingAll;
-  p.fast = fast_supported(g, &nb_set, &rc);
+  int nb_set = 1, rc = kRingAll, us = 0;
+  p.fast = fast_supported(g, &nb_set, &rc, &us);
   p.nb_set = p.fast ? nb_set : 1;
   p.ring_chunk = p.fast ? rc : kRingAll;
+  p.unit_sets = p.fast ? us : 0;
   p.max_blk = std::max(max_seq_tokens - g.R, 0) / g.G;
-  p.units_max = units_max(g, p.max_blk, p.nb_set, p.ring_chunk);
+  p.units_max = units_max(g, p.max_blk, p.nb_set, p.ring_chunk, p.unit_sets);
   p.ws_bytes = plan_bytes(g.B) + p.units_max * (size_t)g.ng * (size_t)(g.d + 2) * 4;
   return p;
 }

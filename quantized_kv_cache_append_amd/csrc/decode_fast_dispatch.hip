@@ -20,25 +20,26 @@ struct FastEntry {
   bool paged;
   int nb_set;      // blocks per set
   int ring_chunk;  // ring tokens per ring unit
+  int unit_sets;   // fixed sets per quantized unit (0: sized from the lengths)
   LaunchFn launch;
 };
 
 template <int NG, int KB, int VB, int G, int GV, bool BF16, bool PAGED>
 FastEntry mfma_entry() {
   using C = fast::Cfg<NG, KB, VB, G, GV, BF16, PAGED>;
-  return FastEntry{NG, KB, VB, G, GV, BF16 ? KVQ_BF16 : KVQ_F16, PAGED, C::NB, fast::kRingChunk,
+  return FastEntry{NG, KB, VB, G, GV, BF16 ? KVQ_BF16 : KVQ_F16, PAGED, C::NB, fast::kRingChunk, 0,
                    &fast::launch_fast<C>};
 }
 template <bool BF16, bool PAGED>
 FastEntry mx_entry() {
   using C = mx::Cfg<BF16, PAGED>;
   return FastEntry{1, C::KB, C::VB, C::G, C::GV, BF16 ? KVQ_BF16 : KVQ_F16, PAGED, mx::kSetBlk, mx::kRingTok,
-                   &mx::launch_mx<C>};
+                   mx::kUnitSets, &mx::launch_mx<C>};
 }
 template <int KB, int VB, int G, int GV, bool BF16, bool PAGED>
 FastEntry mha_entry() {
   using C = mha::Cfg<KB, VB, G, GV, BF16, PAGED>;
-  return FastEntry{1, KB, VB, G, GV, BF16 ? KVQ_BF16 : KVQ_F16, PAGED, C::NBS, mha::kRingTok,
+  return FastEntry{1, KB, VB, G, GV, BF16 ? KVQ_BF16 : KVQ_F16, PAGED, C::NBS, mha::kRingTok, 0,
                    &mha::launch_mha<C>};
 }
 
@@ -80,10 +81,11 @@ const FastEntry* find(const Geom& g) {
 
 }  // namespace
 
-bool fast_supported(const Geom& g, int* blocks_per_set, int* ring_chunk) {
+bool fast_supported(const Geom& g, int* blocks_per_set, int* ring_chunk, int* unit_sets) {
   const FastEntry* e = find(g);
   if (e && blocks_per_set) *blocks_per_set = e->nb_set;
   if (e && ring_chunk) *ring_chunk = e->ring_chunk;
+  if (e && unit_sets) *unit_sets = e->unit_sets;
   return e != nullptr;
 }
 

@@ -69,6 +69,7 @@ constexpr int kSetTok = 128;       // tokens per set
 constexpr int kLimbs = 4;          // e4m3 limbs per real-valued operand
 constexpr int kRingTok = 32;       // ring tokens per ring unit: every load of a unit in flight at once
 constexpr int kRingWeight = 6;     // cost of a ring byte in quarters of a quantized byte (slower loads)
+constexpr int kUnitSets = 1;       // sets per quantized unit: the static partition cuts at set granularity
 constexpr float kRescaleLog2 = 8.0f;
 constexpr int kCodeScale = 128;    // E8M0 2^1: an fp4 code nibble reads c / 2
 
@@ -224,11 +225,11 @@ __device__ __forceinline__ void quant_stream(const Geom& g, float* __restrict__ 
   float m_run, l_lane, lam_lane;
   v4f acc[8];
 
-  auto run_set = [&](mha::Span cur, int si, mha::Span nsp, int nsi) {
+  auto run_set = [&](mha::Span cur, int si, mha::Span nsp, int nsi, bool new_query) {
     const int blk0 = cur.begin + si * kSetBlk;
     SetBuf nb;
     load_set(nb, nsp, nsi);
-    if (si == 0) {   // a unit's first set: its query into LDS
+    if (new_query) {   // a new pair's first set: its query into LDS
       *reinterpret_cast<float2*>(lq + 2 * lane) =
           make_float2(in_val<C>(cb.qw & 0xffffu) * qscale, in_val<C>(cb.qw >> 16) * qscale);
       wave_lds_fence();
@@ -364,22 +365,34 @@ __device__ __forceinline__ void quant_stream(const Geom& g, float* __restrict__ 
     }
   };
 
+  // Consecutive units that continue the same pair share one running state:
+  // the state's partial goes to the slot of the run's last unit and the other
+  // slots get an empty partial (m = -inf, l = 0), which the combine skips.
   int u = first;
   mha::Span cur = first_span;
+  bool cont = false;
   load_set(cb, cur, 0);
   while (true) {
-    m_run = -INFINITY;
-    l_lane = 0.f;
-    lam_lane = 0.f;
+    if (!cont) {
+      m_run = -INFINITY;
+      l_lane = 0.f;
+      lam_lane = 0.f;
 #pragma unroll
-    for (int t = 0; t < 8; ++t) acc[t] = v4f{0.f, 0.f, 0.f, 0.f};
+      for (int t = 0; t < 8; ++t) acc[t] = v4f{0.f, 0.f, 0.f, 0.f};
+    }
     const int nsets = (cur.end - cur.begin + kSetBlk - 1) / kSetBlk;
-    for (int si = 0; si + 1 < nsets; ++si) run_set(cur, si, cur, si + 1);
+    for (int si = 0; si + 1 < nsets; ++si) run_set(cur, si, cur, si + 1, si == 0 && !cont);
     const int nu = claim(claimed);
     const bool more = nu < units;
     const mha::Span nxt = more ? locate(nu) : cur;
-    run_set(cur, nsets - 1, nxt, more ? 0 : nsets - 1);
-    finish_unit(ws + (size_t)u * (D + 2));
+    run_set(cur, nsets - 1, nxt, more ? 0 : nsets - 1, nsets == 1 && !cont);
+    cont = more && nxt.b == cur.b && nxt.h == cur.h && nxt.begin == cur.end;   // wave-uniform
+    float* out_part = ws + (size_t)u * (D + 2);
+    if (cont) {
+      if (lane == 0) *reinterpret_cast<float2*>(out_part + D) = make_float2(-INFINITY, 0.f);
+    } else {
+      finish_unit(out_part);
+    }
     if (!more) break;
     u = nu;
     cur = nxt;
@@ -413,7 +426,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   L.p = lp;
   L.pv = nullptr;
 
-  build_unit_plan(g, state, max_blk, kSetBlk, kRingTok, plan, blockIdx.x == 0);
+  build_unit_plan(g, state, max_blk, kSetBlk, kRingTok, plan, blockIdx.x == 0, kUnitSets);
   if (blockIdx.x == 0)
     for (int i = threadIdx.x; i < pints; i += blockDim.x) ws_plan[i] = plan[i];
   const UnitRange range = static_unit_range(plan, (long long)kRingTok * 4 * C::D * kRingWeight / 4, C::REC,
@@ -430,6 +443,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     sp.end = __builtin_amdgcn_readfirstlane(un.end);
     return sp;
   };
+  // The quantized units of a pair are consecutive and one set each: the unit
+  // after `last` continues its pair while blocks remain (no plan lookup).
+  mha::Span last{};
+  int last_u = -2, last_stop = 0;
+  auto next_span = [&](int uu) -> mha::Span {
+    if (uu == last_u + 1 && last.end < last_stop) {
+      last.begin = last.end;
+      last.end = min(last_stop, last.end + kSetBlk * kUnitSets);
+    } else {
+      last = span_of(uu);
+      last_stop = min(__builtin_amdgcn_readfirstlane(plan[plan_seq_off(g.B) + last.b]) / C::G, max_blk);
+    }
+    last_u = uu;
+    return last;
+  };
   for (; u < u_end && u < ring_units; ++u) {
     const mha::Span sp = span_of(u);
     mha::ring_unit<typename C::Ring, kRingTok>(g, L, k_ring, v_ring, q, qscale, sp.b, sp.h, sp.begin, sp.end,
@@ -439,8 +467,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     int next = u;
     auto issue = []() -> int { return 0; };
     auto claim = [&](int) -> int { return ++next; };
-    quant_stream<C>(g, lq, lp, qimg, pimg, blocks, table, q, qscale, u_end, u, span_of(u), 0, span_of, issue, claim,
-                    ws);
+    quant_stream<C>(g, lq, lp, qimg, pimg, blocks, table, q, qscale, u_end, u, next_span(u), 0, next_span, issue,
+                    claim, ws);
   }
 }
 

@@ -6,6 +6,9 @@
 //   - big units of `ub` quantized blocks covering its leading blocks;
 //   - then up to kTailUnits medium units of `um` blocks and up to kTailUnits
 //     small units of `us` blocks (one set) covering its last blocks.
+// A kernel that partitions the units statically over its waves instead asks
+// for units of a fixed number of sets (`unit_sets`): then every quantized unit
+// is a big unit of that size and there are no medium or small units.
 // Units are numbered section by section -- all ring units, then all big, all
 // medium and all small units -- and within a section by sequence, kv head and
 // position. Waves take units in that order, so the latency-bound ring units
@@ -41,6 +44,7 @@ enum {
   kPlanUm = 6,      // blocks per medium unit
   kPlanUs = 7,      // blocks per small unit
   kPlanRc = 8,      // ring tokens per ring unit
+  kPlanTails = 9,   // medium and small units per pair (at most): kTailUnits or 0
   kPlanHdr = 12,    // then pre[s][B + 1] for each section s: exclusive prefix over
 };                  // sequences of the section's units of one kv head; then the
                     // lengths the plan was built from, Q[B] and S[B]
@@ -57,11 +61,16 @@ __host__ __device__ inline int plan_lds_bytes(int B) { return (plan_ints(B) * 4 
 // units per pair, at most max(kUnitsTarget, P*ceil(max_blk/(kMaxUnitSets*nb_set)))
 // + P big units, and at most kTailUnits medium and kTailUnits small units per
 // pair.
-inline size_t units_max(const Geom& g, int max_blk, int nb_set, int rc) {
+inline size_t units_max(const Geom& g, int max_blk, int nb_set, int rc, int unit_sets = 0) {
   const size_t P = (size_t)g.B * g.Hkv;
+  const size_t ring = P * (size_t)((g.C + rc - 1) / rc);
+  if (unit_sets > 0) {
+    const size_t ub = (size_t)unit_sets * nb_set;
+    return ring + P * ((max_blk + ub - 1) / ub);
+  }
   const size_t cap = (size_t)kMaxUnitSets * nb_set;
   const size_t big = std::max<size_t>(kUnitsTarget, P * ((max_blk + cap - 1) / cap));
-  return P * (size_t)((g.C + rc - 1) / rc) + big + P + 2 * P * kTailUnits;
+  return ring + big + P + 2 * P * kTailUnits;
 }
 
 // Blocks of sequence b's pair in each quantized section: big units cover
@@ -69,11 +78,11 @@ inline size_t units_max(const Geom& g, int max_blk, int nb_set, int rc) {
 struct Tail {
   int mid, small;
 };
-__host__ __device__ inline Tail tail_of(int nblk, int um, int us) {
+__host__ __device__ inline Tail tail_of(int nblk, int um, int us, int tails) {
   Tail t;
-  t.small = nblk < kTailUnits * us ? nblk : kTailUnits * us;
+  t.small = nblk < tails * us ? nblk : tails * us;
   const int rest = nblk - t.small;
-  t.mid = rest < kTailUnits * um ? rest : kTailUnits * um;
+  t.mid = rest < tails * um ? rest : tails * um;
   return t;
 }
 
@@ -96,7 +105,7 @@ __device__ __forceinline__ int wave_incl_scan(int x) {
 // to max_blk (the caller's max_seq_tokens was too small) and, if
 // report_too_long, flag KVQ_DEV_TOO_LONG.
 __device__ inline void build_unit_plan(const Geom& g, int32_t* state, int max_blk, int nb_set, int rc, int* plan,
-                                       bool report_too_long) {
+                                       bool report_too_long, int unit_sets = 0) {
   if (threadIdx.x < 64) {
     const int lane = threadIdx.x;
     int* seqQ = plan + plan_seq_off(g.B);
@@ -117,7 +126,10 @@ __device__ inline void build_unit_plan(const Geom& g, int32_t* state, int max_bl
     const long long tot = (long long)sets * g.Hkv;
     int ub_sets = (int)((tot + kUnitsTarget - 1) / kUnitsTarget);
     ub_sets = max(1, min(kMaxUnitSets, ub_sets));
-    const int ub = ub_sets * nb_set, um = max(1, ub_sets / 4) * nb_set, us = nb_set;
+    if (unit_sets > 0) ub_sets = unit_sets;
+    const int tails = unit_sets > 0 ? 0 : kTailUnits;
+    const int ub = ub_sets * nb_set, um = unit_sets > 0 ? ub : max(1, ub_sets / 4) * nb_set;
+    const int us = unit_sets > 0 ? ub : nb_set;
     // pass 2: units per section and sequence, exclusive prefixes over sequences
     int carry[kSections] = {0, 0, 0, 0};
     for (int b0 = 0; b0 < g.B; b0 += 64) {
@@ -126,7 +138,7 @@ __device__ inline void build_unit_plan(const Geom& g, int32_t* state, int max_bl
       if (b < g.B) {
         const int Q = seqQ[b], S = seqS[b];
         const int nblk = min(Q / g.G, max_blk);
-        const Tail t = tail_of(nblk, um, us);
+        const Tail t = tail_of(nblk, um, us, tails);
         cnt[0] = (min(max(S - Q, 0), g.C) + rc - 1) / rc;
         cnt[1] = (nblk - t.mid - t.small + ub - 1) / ub;
         cnt[2] = (t.mid + um - 1) / um;
@@ -154,6 +166,7 @@ __device__ inline void build_unit_plan(const Geom& g, int32_t* state, int max_bl
       plan[kPlanUm] = um;
       plan[kPlanUs] = us;
       plan[kPlanRc] = rc;
+      plan[kPlanTails] = tails;
     }
   }
   __syncthreads();
@@ -203,7 +216,7 @@ __device__ inline Unit locate_unit(const Geom& g, const int* plan, int u, int ma
   } else {
     const int nblk = min(Q / g.G, max_blk);
     const int um = plan[kPlanUm], us = plan[kPlanUs];
-    const Tail t = tail_of(nblk, um, us);
+    const Tail t = tail_of(nblk, um, us, plan[kPlanTails]);
     const int body = nblk - t.mid - t.small;
     const int size = sec == 1 ? plan[kPlanUb] : (sec == 2 ? um : us);
     const int start = sec == 1 ? 0 : (sec == 2 ? body : body + t.mid);
