@@ -68,7 +68,7 @@ constexpr int kSetBlk = 4;         // blocks per set
 constexpr int kSetTok = 128;       // tokens per set
 constexpr int kLimbs = 4;          // e4m3 limbs per real-valued operand
 constexpr int kRingTok = 32;       // ring tokens per ring unit: every load of a unit in flight at once
-constexpr int kRingWeight = 6;     // cost of a ring byte in quarters of a quantized byte (slower loads)
+constexpr int kRingWeight = 3;     // cost of a ring byte in quarters of a quantized byte (measured: a 16 KB ring unit takes about as long as a 12 KB set)
 constexpr int kUnitSets = 1;       // sets per quantized unit: the static partition cuts at set granularity
 constexpr float kRescaleLog2 = 8.0f;
 constexpr int kCodeScale = 128;    // E8M0 2^1: an fp4 code nibble reads c / 2
@@ -192,8 +192,6 @@ __device__ __forceinline__ void quant_stream(const Geom& g, float* __restrict__ 
     uint4 vs, vz;    // value scale / zero of group gq, tokens 8 (n % 4) .. + 7 of block n / 4
     uint32_t qw;     // the unit's query, channels 2 lane and 2 lane + 1
   };
-  SetBuf cb;
-
   auto rec_of = [&](mha::Span sp, int blk) -> const uint8_t* {
     return mha::span_rec<typename C::Ring>(g, blocks, table, sp, blk);
   };
@@ -225,10 +223,8 @@ __device__ __forceinline__ void quant_stream(const Geom& g, float* __restrict__ 
   float m_run, l_lane, lam_lane;
   v4f acc[8];
 
-  auto run_set = [&](mha::Span cur, int si, mha::Span nsp, int nsi, bool new_query) {
-    const int blk0 = cur.begin + si * kSetBlk;
-    SetBuf nb;
-    load_set(nb, nsp, nsi);
+  auto compute_set = [&](const SetBuf& cb, mha::Span cur, bool new_query) {
+    const int blk0 = cur.begin;
     if (new_query) {   // a new pair's first set: its query into LDS
       *reinterpret_cast<float2*>(lq + 2 * lane) =
           make_float2(in_val<C>(cb.qw & 0xffffu) * qscale, in_val<C>(cb.qw >> 16) * qscale);
@@ -342,7 +338,6 @@ __device__ __forceinline__ void quant_stream(const Geom& g, float* __restrict__ 
         }
       }
     }
-    cb = nb;
     wave_lds_fence();   // the images and p are rewritten by the next set
   };
 
@@ -365,14 +360,22 @@ __device__ __forceinline__ void quant_stream(const Geom& g, float* __restrict__ 
     }
   };
 
-  // Consecutive units that continue the same pair share one running state:
-  // the state's partial goes to the slot of the run's last unit and the other
-  // slots get an empty partial (m = -inf, l = 0), which the combine skips.
-  int u = first;
-  mha::Span cur = first_span;
+  // Every unit is one set; two register buffers alternate (the loads of unit
+  // k + 1 are in flight while unit k is computed). Consecutive units that
+  // continue the same pair share one running state: the state's partial goes
+  // to the slot of the run's last unit and the other slots get an empty
+  // partial (m = -inf, l = 0), which the combine skips.
+  SetBuf b0, b1;
+  int k = first;
+  mha::Span s0 = first_span, s1 = first_span;
+  load_set(b0, s0, 0);
   bool cont = false;
-  load_set(cb, cur, 0);
-  while (true) {
+  auto step = [&](const SetBuf& cb, SetBuf& pf) -> bool {
+    const bool more = k + 1 < units;   // wave-uniform
+    if (more) {
+      s1 = locate(k + 1);
+      load_set(pf, s1, 0);
+    }
     if (!cont) {
       m_run = -INFINITY;
       l_lane = 0.f;
@@ -380,23 +383,23 @@ __device__ __forceinline__ void quant_stream(const Geom& g, float* __restrict__ 
 #pragma unroll
       for (int t = 0; t < 8; ++t) acc[t] = v4f{0.f, 0.f, 0.f, 0.f};
     }
-    const int nsets = (cur.end - cur.begin + kSetBlk - 1) / kSetBlk;
-    for (int si = 0; si + 1 < nsets; ++si) run_set(cur, si, cur, si + 1, si == 0 && !cont);
-    const int nu = claim(claimed);
-    const bool more = nu < units;
-    const mha::Span nxt = more ? locate(nu) : cur;
-    run_set(cur, nsets - 1, nxt, more ? 0 : nsets - 1, nsets == 1 && !cont);
-    cont = more && nxt.b == cur.b && nxt.h == cur.h && nxt.begin == cur.end;   // wave-uniform
-    float* out_part = ws + (size_t)u * (D + 2);
-    if (cont) {
+    compute_set(cb, s0, !cont);
+    const bool nc = more && s1.b == s0.b && s1.h == s0.h && s1.begin == s0.end;   // wave-uniform
+    float* out_part = ws + (size_t)k * (D + 2);
+    if (nc) {
       if (lane == 0) *reinterpret_cast<float2*>(out_part + D) = make_float2(-INFINITY, 0.f);
     } else {
       finish_unit(out_part);
     }
-    if (!more) break;
-    u = nu;
-    cur = nxt;
-    claimed = issue();
+    cont = nc;
+    ++k;
+    s0 = s1;
+    return more;
+  };
+  (void)claimed;
+  (void)issue;
+  (void)claim;
+  while (step(b0, b1) && step(b1, b0)) {
   }
 }
 
