@@ -432,8 +432,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   build_unit_plan(g, state, max_blk, kSetBlk, kRingTok, plan, blockIdx.x == 0, kUnitSets);
   if (blockIdx.x == 0)
     for (int i = threadIdx.x; i < pints; i += blockDim.x) ws_plan[i] = plan[i];
-  const UnitRange range = static_unit_range(plan, (long long)kRingTok * 4 * C::D * kRingWeight / 4, C::REC,
-                                            (long long)blockIdx.x * kWaves + wave, (long long)gridDim.x * kWaves);
+  const UnitRange range = static_unit_range(plan, (float)(kRingTok * 4 * C::D * kRingWeight / 4), (float)C::REC,
+                                            (int)blockIdx.x * kWaves + wave, (int)gridDim.x * kWaves);
   int u = range.begin;
   const int u_end = range.end;
   const int ring_units = __builtin_amdgcn_readfirstlane(plan[kPlanSec]);

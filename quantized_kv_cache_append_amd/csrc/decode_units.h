@@ -236,39 +236,48 @@ __device__ inline Unit locate_unit(const Geom& g, const int* plan, int u, int ma
 struct UnitRange {
   int begin, end;
 };
-__device__ inline UnitRange static_unit_range(const int* plan, long long ring_cost, long long rec_bytes, long long wv,
-                                              long long W) {
+// (fp32 arithmetic: a boundary shared by two waves is the same expression on
+// the same inputs for both, and unit_at is monotone in c, so the ranges tile
+// [0, units) exactly whatever the rounding; 64-bit integer division would cost
+// the launch thousands of instructions before its first load.)
+__device__ inline UnitRange static_unit_range(const int* plan, float ring_cost, float rec_bytes, int wv, int W) {
   int nsec[kSections];
-  long long cost[kSections];
+  float cost[kSections];
 #pragma unroll
   for (int k = 0; k < kSections; ++k) nsec[k] = __builtin_amdgcn_readfirstlane(plan[kPlanSec + k]);
   cost[0] = ring_cost;
-  cost[1] = (long long)__builtin_amdgcn_readfirstlane(plan[kPlanUb]) * rec_bytes;
-  cost[2] = (long long)__builtin_amdgcn_readfirstlane(plan[kPlanUm]) * rec_bytes;
-  cost[3] = (long long)__builtin_amdgcn_readfirstlane(plan[kPlanUs]) * rec_bytes;
-  long long total = 0;
+  cost[1] = (float)__builtin_amdgcn_readfirstlane(plan[kPlanUb]) * rec_bytes;
+  cost[2] = (float)__builtin_amdgcn_readfirstlane(plan[kPlanUm]) * rec_bytes;
+  cost[3] = (float)__builtin_amdgcn_readfirstlane(plan[kPlanUs]) * rec_bytes;
+  float total = 0.f;
   int units = 0;
 #pragma unroll
   for (int k = 0; k < kSections; ++k) {
-    total += nsec[k] * cost[k];
+    total += (float)nsec[k] * cost[k];
     units += nsec[k];
   }
   // first unit whose start cost is >= c
-  auto unit_at = [&](long long c) -> int {
-    long long cbase = 0;
-    int ubase = 0;
+  // (branch-free: the section is found with selects, the result made scalar)
+  auto unit_at = [&](float c) -> int {
+    float cbase = 0.f;
+    int ubase = 0, r = units;
+    bool found = false;
 #pragma unroll
     for (int k = 0; k < kSections; ++k) {
-      const long long sec = nsec[k] * cost[k];
-      if (nsec[k] > 0 && c <= cbase + sec) return ubase + (int)((c - cbase + cost[k] - 1) / cost[k]);
+      const float sec = (float)nsec[k] * cost[k];
+      const bool here = !found && nsec[k] > 0 && c <= cbase + sec;
+      const int i = min(nsec[k], (int)ceilf((c - cbase) * __builtin_amdgcn_rcpf(cost[k])));
+      r = here ? ubase + max(i, 0) : r;
+      found = found || here;
       cbase += sec;
       ubase += nsec[k];
     }
-    return units;
+    return __builtin_amdgcn_readfirstlane(r);
   };
+  const float per_wave = total / (float)W;
   UnitRange r;
-  r.begin = unit_at(total * wv / W);
-  r.end = unit_at(total * (wv + 1) / W);
+  r.begin = wv == 0 ? 0 : unit_at(per_wave * (float)wv);
+  r.end = wv + 1 == W ? units : unit_at(per_wave * (float)(wv + 1));
   return r;
 }
 
