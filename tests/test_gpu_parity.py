@@ -27,6 +27,15 @@ CASES = {
                          [3000], 512),
     "ragged-paged-reduced": ("ragged-paged", dict(batch=5, num_q_heads=12, num_kv_heads=2),
                              [37, 300, 1111, 2048, 517], 256),
+    # the other instantiations of the multi-head paths (one query head per kv
+    # head): bf16 and paged INT2, ragged lengths; INT4
+    "mha-bf16-paged": ("llama2-7b-layer", dict(batch=3, num_q_heads=4, num_kv_heads=4, dtype="bf16", paged=True),
+                       [700, 1500, 2123], 256),
+    "mha-f16-paged": ("llama2-7b-layer", dict(batch=2, num_q_heads=4, num_kv_heads=4, paged=True), [1000, 1337], 256),
+    "mha-bf16-dense": ("llama2-7b-layer", dict(batch=3, num_q_heads=4, num_kv_heads=4, dtype="bf16"),
+                       [95, 900, 1800], 256),
+    "mha-int4": ("llama2-7b-layer", dict(batch=2, num_q_heads=4, num_kv_heads=4, k_bits=4, v_bits=4), [1000, 1000],
+                 256),
 }
 
 
