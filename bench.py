@@ -14,6 +14,11 @@ Prints one JSON line on stdout; human-readable detail goes to stderr.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
+A multi-layer workload (the 80-layer 70B-shaped one) keeps one cache per layer
+resident (27 GB for 80 layers, so no copies are rotated) and times the full
+decode step: for each layer in turn, append+flush, decode partials and combine,
+all on one stream; `roofline` is then the per-layer decode-partials launch.
+
 `value` is the step's algorithmic bytes over its time (effective GB/s of the
 whole step); `roofline` is the decode-partials kernel's algorithmic bytes over
 its own event-timed duration, against the 8 TB/s HBM peak; `traffic` is the
@@ -148,6 +153,16 @@ def quantize_rate(w, inp, lengths, dev, reps=5):
             "sample": f"one flush of every pair's whole quantized prefix ({q_tok} token-heads), median of {reps}"}
 
 
+def decode_kernel_name(w) -> str:
+    """The decode-partials kernel a workload's configuration runs."""
+    if w.head_dim != 128:
+        return "decode_generic_kernel"
+    if w.n_g == 1:
+        mx = (w.k_bits, w.v_bits, w.k_group, w.v_group) == (2, 2, 32, 32)
+        return "decode_mx_kernel" if mx else "decode_mha_kernel"
+    return "decode_fast_kernel"
+
+
 def cpu_baseline(w, inp, lengths, budget_s=15.0):
     """Time the oracle's decode attention on a bounded sample of (sequence, kv head)
     pairs of the same workload; returns GB/s of the same algorithmic bytes."""
@@ -186,6 +201,130 @@ def cpu_baseline(w, inp, lengths, budget_s=15.0):
                       f"BLAS limited to 1 thread"}
 
 
+def bench_layers(w, args, dev):
+    """The full multi-layer decode step: one resident cache per layer; a step
+    is, for every layer in turn, append+flush of the new token, decode partials
+    and combine, on one stream."""
+    import torch
+
+    from quantized_kv_cache_append_amd import workloads as W
+    from quantized_kv_cache_append_amd.cache import cache_for_workload
+
+    L = w.layers
+    lengths0 = W.sequence_lengths(w)
+    total_steps = args.warmup + 2 * args.steps
+    chunk = 8192
+    log(f"[bench] workload {w.name}: {w.description}; {L} layers")
+    caches, toks, qs = [], [], []
+    t0 = time.perf_counter()
+    for layer in range(L):
+        inp = W.make_layer(w, device=dev, layer=layer, lengths=lengths0)
+        c = cache_for_workload(w, lengths0, chunk, extra_tokens=total_steps + 1, device=dev)
+        c.prefill(inp.k, inp.v, lengths0, chunk)
+        # this layer's decode tokens for the steps (distinct per layer and step)
+        toks.append([W.new_tokens(w, inp, 1, device=dev, step=layer * 100003 + s) for s in range(4)])
+        caches.append(c)
+        if layer == 0:
+            inp0 = inp   # kept for the quantize rate and the oracle sample
+        del inp
+        torch.cuda.synchronize()
+    rec = caches[0].record_bytes
+    log(f"[bench] {L} layer caches of {caches[0].blocks.numel() / 1e6:.1f} MB of records each, "
+        f"prefilled in {time.perf_counter() - t0:.1f} s")
+    max_len = max(lengths0) + total_steps + 1
+    ws = torch.empty(caches[0].workspace_bytes(max_len), dtype=torch.uint8, device=dev)
+    out = torch.empty(w.batch, w.num_q_heads, w.head_dim, dtype=torch.float32, device=dev)
+
+    def step(i, evs=None):
+        for layer, c in enumerate(caches):
+            kn, vn, q = toks[layer][i % 4]
+            c.append_flush(kn, vn)
+            if evs is not None:
+                evs[layer][0].record()
+            c.decode_partials(q, max_seq_tokens=max_len, workspace=ws)
+            if evs is not None:
+                evs[layer][1].record()
+            c.decode_combine(out=out, max_seq_tokens=max_len, workspace=ws)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for j in range(args.steps):
+        step(args.warmup + j)
+    end.record()
+    torch.cuda.synchronize()
+    ms_step = start.elapsed_time(end) / args.steps
+    part_ms = []
+    for j in range(args.steps):
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(L)]
+        step(args.warmup + args.steps + j, evs)
+        torch.cuda.synchronize()
+        part_ms += [a.elapsed_time(b) for a, b in evs]
+    err = max(c.read_device_error() for c in caches)
+    if err:
+        raise SystemExit(f"device error word {err} after the timed steps")
+
+    # algorithmic bytes: every layer sees the same lengths
+    lens = list(lengths0)
+    step_bytes, part_bytes = [], []
+    for i in range(total_steps):
+        after = [s + 1 for s in lens]
+        if args.warmup <= i < args.warmup + args.steps:
+            step_bytes.append(L * (append_flush_bytes(w, lens, rec) + partial_bytes(w, after, rec) + out_bytes(w)))
+        elif i >= args.warmup + args.steps:
+            part_bytes.append(partial_bytes(w, after, rec))
+        lens = after
+    avg_step_bytes = sum(step_bytes) / len(step_bytes)
+    avg_part_bytes = sum(part_bytes) / len(part_bytes)
+    part_avg_ms = sum(part_ms) / len(part_ms)
+    value = avg_step_bytes / (ms_step * 1e-3) / 1e9
+    achieved = avg_part_bytes / (part_avg_ms * 1e-3) / 1e9
+    log(f"[bench] {ms_step * 1e3:.1f} us/step over {L} layers ({avg_step_bytes / 1e6:.1f} MB) -> {value:.0f} GB/s; "
+        f"decode partials per layer {part_avg_ms * 1e3:.1f} us (x{L} = {part_avg_ms * L:.2f} ms), "
+        f"{avg_part_bytes / 1e6:.1f} MB -> {achieved:.0f} GB/s ({achieved / PEAK_HBM_GBPS * 100:.1f}% of 8 TB/s); "
+        f"sources {source_hash()}")
+    traffic = measured_traffic(w.name)
+    result = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "layers": L, "batch": w.batch, "num_q_heads": w.num_q_heads,
+                   "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim, "seq_len": max(lengths0),
+                   "input_dtype": w.dtype, "k_bits": w.k_bits, "v_bits": w.v_bits, "k_group": w.k_group,
+                   "v_group": w.v_group, "residual": w.residual, "paged": w.paged, "cache_copies_rotated": 1},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBPS, 4),
+                     "traffic": None if traffic is None else round(traffic),
+                     "kernel": decode_kernel_name(w), "us_per_launch": round(part_avg_ms * 1e3, 2),
+                     "bytes_per_launch": int(avg_part_bytes), "launches_per_step": L},
+        "quantize": None,
+        "cpu_baseline": None,
+    }
+    del caches, ws
+    torch.cuda.empty_cache()
+    result["quantize"] = quantize_rate(w, inp0, lengths0, dev)
+    result["quantize"]["sample"] += " (one layer)"
+    log(f"[bench] quantize (one layer): full-prefix flush {result['quantize']['us_per_flush']:.1f} us, "
+        f"{result['quantize']['bytes'] / 1e6:.1f} MB -> {result['quantize']['value']:.0f} GB/s")
+    if not args.no_cpu_baseline:
+        cb = cpu_baseline(w, inp0, list(lengths0))
+        cb["sample"] += f"; layer 0 only (a step is {L} such layers)"
+        result["cpu_baseline"] = cb
+        log(f"[bench] oracle on the host: {cb['value']:.3f} GB/s")
+    print(json.dumps(result), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -215,9 +354,9 @@ def main():
     binding.load()
 
     w = W.WORKLOADS[args.workload]
-    if w.layers != 1:
-        raise SystemExit("multi-layer workloads are run per layer: pick a single-layer workload")
     dev = torch.device("cuda:0")
+    if w.layers != 1:
+        return bench_layers(w, args, dev)
     torch.cuda.set_device(dev)
     lengths0 = W.sequence_lengths(w)
     total_steps = args.warmup + 2 * args.steps
@@ -318,8 +457,7 @@ def main():
         torch.cuda.synchronize()
         log(f"[bench] copy probe: 3 device-to-device copies of {n} bytes")
 
-    kernel = ("decode_mha_kernel" if w.n_g == 1 else "decode_fast_kernel") if w.head_dim == 128 else \
-        "decode_generic_kernel"
+    kernel = decode_kernel_name(w)
     result = {
         "metric": METRIC,
         "value": round(value, 1),
