@@ -22,7 +22,7 @@ import re
 import statistics
 import sys
 
-DECODE = re.compile(r"decode_(mha|fast|generic)_kernel")
+DECODE = re.compile(r"decode_(mx|mha|fast|generic)_kernel")
 COPY = "__amd_rocclr_copyBuffer"
 
 
