@@ -172,16 +172,16 @@ __device__ __forceinline__ float h2f(uint32_t w, int hi) {
 }
 
 // ---------------------------------------------------------------------------------
-// The quantized units of a wave, from `first` on, as one stream of sets: the
-// last set of a unit already loads the first set (and query) of the next unit.
+// The quantized units [first, units) of a wave, in order, as one stream of
+// sets: each set's loads go out while the previous set is computed, across
+// unit boundaries. locate(u) gives unit u's span (called for increasing u).
 // ---------------------------------------------------------------------------------
-template <class C, class Locate, class Issue, class Claim>
+template <class C, class Locate>
 __device__ __forceinline__ void quant_stream(const Geom& g, float* __restrict__ lq, float* __restrict__ lp,
                                              uint8_t* __restrict__ qimg, uint8_t* __restrict__ pimg,
                                              const uint8_t* __restrict__ blocks, const int32_t* __restrict__ table,
                                              const uint16_t* __restrict__ q, float qscale, int units, int first,
-                                             mha::Span first_span, int claimed, Locate locate, Issue issue,
-                                             Claim claim, float* __restrict__ ws) {
+                                             mha::Span first_span, Locate locate, float* __restrict__ ws) {
   constexpr int D = C::D;
   const int lane = threadIdx.x & 63, n = lane & 15, gq = lane >> 4;
 
@@ -396,9 +396,6 @@ __device__ __forceinline__ void quant_stream(const Geom& g, float* __restrict__ 
     s0 = s1;
     return more;
   };
-  (void)claimed;
-  (void)issue;
-  (void)claim;
   while (step(b0, b1) && step(b1, b0)) {
   }
 }
@@ -467,11 +464,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                                                ws + (size_t)u * (C::D + 2));
   }
   if (u < u_end) {
-    int next = u;
-    auto issue = []() -> int { return 0; };
-    auto claim = [&](int) -> int { return ++next; };
-    quant_stream<C>(g, lq, lp, qimg, pimg, blocks, table, q, qscale, u_end, u, next_span(u), 0, next_span, issue,
-                    claim, ws);
+    quant_stream<C>(g, lq, lp, qimg, pimg, blocks, table, q, qscale, u_end, u, next_span(u), next_span, ws);
   }
 }
 
