@@ -24,13 +24,21 @@
 // matrix-vector: a 2-bit code placed in a nibble is an exact fp4 (e2m1) value
 // c/2, so the codes go to the MFMA after three bit operations per 16 codes,
 // and the real-valued operand (q~ = q' s_K per block, p~ = p s_V per value
-// group) takes the otherwise idle rows: each of its values is split into four
-// e4m3 limbs x = sum_k l_k 16^-k (relative error below 2^-16, the precision of
-// a bf16 hi/lo pair), one row per limb, and the per-row E8M0 block scale of
-// the instruction restores each limb's weight. The products of e4m3 and e2m1
-// values are exact and the instruction sums them in fp32, so each score or
-// output is the fp32 sum of its limb rows. This leaves the vector ALUs about a
-// third of the instructions per token of the fp32 path.
+// group) takes the otherwise idle rows: its values, in units of 2^(e - 4)
+// where 2^e bounds them over the row, are written as three signed base-32
+// digits and an e4m3 remainder, x = D0 + D1/32 + D2/1024 + r/32768 (integers
+// |D_k| <= 16 and |r| <= 16: e4m3 holds every integer up to 16 exactly), one
+// row each, and the per-row E8M0 block scale of the instruction restores each
+// row's weight; the remainder's rounding leaves out at most 2^-19 of the row
+// maximum. Why digits and not limbs of each value's own significand:
+// the instruction does not sum its products exactly. Measured on gfx950, each
+// run of 8 consecutive k is aligned to its largest product and bits more than
+// about 2^13 below it are dropped (256 + 2^-9 sums to 256), while the sums of
+// the runs are exact. A row of digits holds only small integers, so each of its
+// products (at most 16 * 1.5, on a grid of 0.5) survives that alignment and the
+// row's sum is exact; only the remainder row loses bits, far below the digits.
+// Each score or output is then the fp32 sum of its four rows. This leaves the
+// vector ALUs about a third of the instructions per token of the fp32 path.
 //
 // Work of one wave: units of whole sets of 4 blocks (128 tokens), the next
 // set's loads in flight while a set is computed. Lane l = 16 g + n:
@@ -66,7 +74,7 @@ typedef float v2f __attribute__((ext_vector_type(2)));
 constexpr int kWaves = 4;          // waves per workgroup
 constexpr int kSetBlk = 4;         // blocks per set
 constexpr int kSetTok = 128;       // tokens per set
-constexpr int kLimbs = 4;          // e4m3 limbs per real-valued operand
+constexpr int kLimbs = 4;          // A-operand rows per real-valued operand: 3 digits + remainder
 constexpr int kRingTok = 32;       // ring tokens per ring unit: every load of a unit in flight at once
 constexpr int kRingWeight = 3;     // cost of a ring byte in quarters of a quantized byte (measured: a 16 KB ring unit takes about as long as a 12 KB set)
 constexpr int kUnitSets = 1;       // sets per quantized unit: the static partition cuts at set granularity
@@ -99,35 +107,29 @@ struct Cfg {
 // Building blocks
 // ---------------------------------------------------------------------------------
 
-// Split x0..x7 (already normalized below 2^8 in magnitude) into kLimbs e4m3 limb
-// rows of an A-operand image: limb k of x_e goes to byte e/2 of dword
-// `even_off` (e even) or `odd_off` (e odd) of row base + k, where a row's lane
-// image starts at 32 (row + 16 g) bytes.
+// Write x0..x7 (|x| < 16, in units of the first digit) as kLimbs e4m3 rows of
+// an A-operand image: rows 0 .. kLimbs - 2 hold the signed base-32 digits
+// D_k = round(t_k), t_0 = x, t_(k+1) = 32 (t_k - D_k) (|t_k| <= 16, so the
+// digits are integers in [-16, 16], exact in e4m3), the last row t_(kLimbs-1)
+// rounded to e4m3. Row k's value of x_e goes to byte e/2 of dword `off_even` (e even) or
+// `off_odd` (e odd) of row row0 + k, where a row's lane image starts at
+// 32 (row + 16 g) bytes.
 __device__ __forceinline__ void write_limbs(uint8_t* img, int row0, int off_even, int off_odd, float (&x)[8]) {
 #pragma unroll
   for (int k = 0; k < kLimbs; ++k) {
-    int ev = __builtin_amdgcn_cvt_pk_fp8_f32(x[0], x[2], 0, false);
-    ev = __builtin_amdgcn_cvt_pk_fp8_f32(x[4], x[6], ev, true);
-    int od = __builtin_amdgcn_cvt_pk_fp8_f32(x[1], x[3], 0, false);
-    od = __builtin_amdgcn_cvt_pk_fp8_f32(x[5], x[7], od, true);
+    float d[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) d[e] = k + 1 < kLimbs ? __builtin_rintf(x[e]) : x[e];
+    int ev = __builtin_amdgcn_cvt_pk_fp8_f32(d[0], d[2], 0, false);
+    ev = __builtin_amdgcn_cvt_pk_fp8_f32(d[4], d[6], ev, true);
+    int od = __builtin_amdgcn_cvt_pk_fp8_f32(d[1], d[3], 0, false);
+    od = __builtin_amdgcn_cvt_pk_fp8_f32(d[5], d[7], od, true);
     uint8_t* row = img + 32 * (row0 + k);
     *reinterpret_cast<int*>(row + off_even) = ev;
     *reinterpret_cast<int*>(row + off_odd) = od;
     if (k + 1 < kLimbs) {
-      // residual, scaled by 16 for the next limb (exact: x - limb is the
-      // rounding error of a 4-significant-bit rounding of x)
-      const v2f e0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(ev, 16.0f, false);
-      const v2f e1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(ev, 16.0f, true);
-      const v2f o0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(od, 16.0f, false);
-      const v2f o1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(od, 16.0f, true);
-      x[0] = fmaf(x[0], 16.0f, -e0.x);
-      x[2] = fmaf(x[2], 16.0f, -e0.y);
-      x[4] = fmaf(x[4], 16.0f, -e1.x);
-      x[6] = fmaf(x[6], 16.0f, -e1.y);
-      x[1] = fmaf(x[1], 16.0f, -o0.x);
-      x[3] = fmaf(x[3], 16.0f, -o0.y);
-      x[5] = fmaf(x[5], 16.0f, -o1.x);
-      x[7] = fmaf(x[7], 16.0f, -o1.y);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = (x[e] - d[e]) * 32.0f;   // exact
     }
   }
 }
@@ -142,16 +144,16 @@ __device__ __forceinline__ int row_exponent(float amax) {
   return max(__builtin_amdgcn_frexp_expf(amax), -100);
 }
 
-// E8M0 scale byte of A-operand row r (= 4 j + limb) of this lane, from the
-// exponents e_j of the four lane groups: limb k of a value normalized by
-// 2^(8 - e) weighs 2^(e - 8 - 4k).
+// E8M0 scale byte of A-operand row r (= 4 j + k) of this lane, from the
+// exponents e_j of the four lane groups: row k of a value written in units of
+// 2^(e - 4) weighs 2^(e - 4 - 5k).
 __device__ __forceinline__ int row_scale(int e_lane, int lane) {
   const int r = lane & 15;
   const int e0 = __builtin_amdgcn_readlane(e_lane, 0), e1 = __builtin_amdgcn_readlane(e_lane, 16);
   const int e2 = __builtin_amdgcn_readlane(e_lane, 32), e3 = __builtin_amdgcn_readlane(e_lane, 48);
   const int j = r >> 2;
   const int e = j == 0 ? e0 : (j == 1 ? e1 : (j == 2 ? e2 : e3));
-  return 127 + e - 8 - 4 * (r & 3);
+  return 127 + e - 4 - 5 * (r & 3);
 }
 
 // Even and odd 2-bit slots of a code word as fp4 nibbles (k order of the
@@ -248,7 +250,7 @@ __device__ __forceinline__ void quant_stream(const Geom& g, float* __restrict__ 
       }
       kap = mha::row_sum16(kap);
       const int ex = row_exponent(amax);
-      const float nrm = __builtin_amdgcn_ldexpf(1.0f, 8 - ex);
+      const float nrm = __builtin_amdgcn_ldexpf(1.0f, 4 - ex);
 #pragma unroll
       for (int e = 0; e < 8; ++e) x[e] *= nrm;
       // channels 8n + e sit at k = 16 (n / 2) + 4 (n % 2) + 8 (e % 2) + e / 2
@@ -305,7 +307,7 @@ __device__ __forceinline__ void quant_stream(const Geom& g, float* __restrict__ 
         amax = fmaxf(amax, fabsf(x[e]));
       }
       const int ex = row_exponent(amax);
-      const float nrm = __builtin_amdgcn_ldexpf(1.0f, 8 - ex);
+      const float nrm = __builtin_amdgcn_ldexpf(1.0f, 4 - ex);
 #pragma unroll
       for (int e = 0; e < 8; ++e) x[e] *= nrm;
       // token 8n + e of the set sits at k = 8n + (e even: e / 2, odd: 4 + e / 2)

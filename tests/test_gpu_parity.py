@@ -36,6 +36,10 @@ CASES = {
                        [95, 900, 1800], 256),
     "mha-int4": ("llama2-7b-layer", dict(batch=2, num_q_heads=4, num_kv_heads=4, k_bits=4, v_bits=4), [1000, 1000],
                  256),
+    # many pairs of very different lengths: the waves' static unit ranges cut
+    # across pairs and through runs of one pair's units
+    "mha-ragged-many": ("llama2-7b-layer", dict(batch=8, num_q_heads=8, num_kv_heads=8),
+                        [33, 160, 191, 500, 1024, 2049, 3000, 4100], 256),
 }
 
 
@@ -72,14 +76,16 @@ def test_decode_matches_oracle(name):
     print(f"[case {name}] max_abs={max_abs:.2e} rel_l2={rel:.2e}")
 
 
-def test_decode_is_deterministic():
-    w, cache, inp, lengths, out = _run_case("llama3-int2-reduced")
+@pytest.mark.parametrize("name", ["llama3-int2-reduced", "mha-bf16-paged"])
+def test_decode_is_deterministic(name):
+    w, cache, inp, lengths, out = _run_case(name)
     again = cache.decode(inp.q.cuda())
     torch.cuda.synchronize()
     assert torch.equal(out, again)
 
 
-@pytest.mark.parametrize("name", ["llama2-reduced", "llama3-int2-reduced", "ragged-paged-reduced", "tiny-full"])
+@pytest.mark.parametrize("name", ["llama2-reduced", "mha-bf16-paged", "llama3-int2-reduced", "ragged-paged-reduced",
+                                  "tiny-full"])
 def test_two_phase_decode_equals_one_call(name):
     # kvq_decode_partials + kvq_decode_combine is the same computation as
     # kvq_decode_attention: the unit partition depends only on the lengths
@@ -104,8 +110,11 @@ def test_window_boundaries(S):
     check_decode(out, spec, to_np(inp.q), to_np(inp.k), to_np(inp.v), [S], scale=default_scale(w.head_dim))
 
 
-def test_empty_sequence_in_batch_gives_zero_output():
-    w = W.WORKLOADS["llama3-8b-gqa-int4"].replace(batch=3, num_q_heads=8, num_kv_heads=2)
+@pytest.mark.parametrize("wname", ["llama3-8b-gqa-int4", "llama2-7b-layer"])
+def test_empty_sequence_in_batch_gives_zero_output(wname):
+    over = dict(batch=3, num_q_heads=8, num_kv_heads=2) if wname != "llama2-7b-layer" else \
+        dict(batch=3, num_q_heads=2, num_kv_heads=2)
+    w = W.WORKLOADS[wname].replace(**over)
     lengths = [500, 0, 300]
     inp = W.make_layer(w, device="cpu", seed=4, lengths=[500, 1, 300])
     cache = make_cache(w, lengths, 128)
@@ -113,7 +122,7 @@ def test_empty_sequence_in_batch_gives_zero_output():
     out = cache.decode(inp.q.cuda())
     assert torch.count_nonzero(out[1]) == 0
     spec = spec_of(w, cache.cfg.res_capacity)
-    pairs = [(b, h) for b in (0, 2) for h in range(2)]
+    pairs = [(b, h) for b in (0, 2) for h in range(w.num_kv_heads)]
     check_decode(out, spec, to_np(inp.q), to_np(inp.k), to_np(inp.v), lengths, pairs=pairs,
                  scale=default_scale(w.head_dim))
 
