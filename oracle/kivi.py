@@ -19,6 +19,13 @@ Written slowly and directly so that a reader can check it against the pages:
        GPU" and innovation 4 "Fenêtre résiduelle".
   [P1] ai-automate.fr -- "KV-cache compressé et modèles 4-bit ...", section on
        Minima-KV (partial attention states merged by an online softmax).
+  [P2'] the same zubnet.ai survey, paragraph on the eviction family:
+       StreamingLLM keeps the first tokens, which act as attention sinks,
+       beside a sliding window of recent ones.
+  [P3'] the same encorp.ai page, section "OSCAR compte parce que quelqu'un a
+       effectivement livré les parties brouillonnes": OSCAR keeps the sink
+       tokens and the recent tokens in BF16 and compresses the historical ones
+       to INT2.
 
 What the pages fix: keys are quantized per channel, values per token [P2; P4
 KIVI]; each channel carries its own min/max parameters [P4 KIVI]; codes are
@@ -39,7 +46,12 @@ of the readings list kept with the design notes):
   * the residual window keeps R <= r < R+G tokens: after a flush, the oldest
     complete G-token blocks beyond R are quantized, so Q = G*floor(max(S-R,0)/G);
   * attention uses softmax scale 1/sqrt(d) by default, query head h' reads kv
-    head floor(h'/n_g), and is evaluated in fp64 on the dequantized cache.
+    head floor(h'/n_g), and is evaluated in fp64 on the dequantized cache;
+  * an attention sink of P tokens (P = 0: none) [P2'; P3']: the first min(S, P)
+    tokens of a sequence stay in full precision and are never quantized; the
+    quantized blocks and the residual window cover the tokens after them,
+    exactly as if the sequence started at token P. The pages give no count, so
+    P is a parameter.
 """
 from __future__ import annotations
 
@@ -67,6 +79,7 @@ class CacheSpec:
     residual: int         # R
     res_capacity: int     # ring slots per (sequence, kv head)
     dtype: str            # "f16" or "bf16"
+    sink: int = 0         # P: leading tokens kept in full precision (attention sink)
 
     @property
     def n_g(self) -> int:
@@ -261,6 +274,17 @@ def quantized_prefix(S: int, R: int, G: int) -> int:
     return G * (max(S - R, 0) // G)
 
 
+def stream_split(spec: CacheSpec, S: int):
+    """Where the S tokens of one sequence live once the window is flushed
+    [P2'; P3' sink; P4 KIVI window]: (s, Q, r) with tokens [0, s) in the sink,
+    [P, P + Q) quantized and [P + Q, S) in the ring; s + Q + r = S."""
+    P = spec.sink
+    s = min(S, P)
+    post = max(S - P, 0)
+    Q = quantized_prefix(post, spec.residual, spec.k_group)
+    return s, Q, post - Q
+
+
 # ---------------------------------------------------------------------------
 # Expected cache state after appending S_b tokens per sequence and flushing.
 # ---------------------------------------------------------------------------
@@ -268,20 +292,21 @@ def expected_blocks(spec: CacheSpec, K: np.ndarray, V: np.ndarray, S_b: int):
     """Records of every quantized block of one (sequence, kv head).
 
     K, V: float32 [>=S_b][d] input values of that pair. Returns uint8
-    [Q/G][record_bytes].
+    [Q/G][record_bytes]; block j holds tokens P + jG .. P + jG + G - 1.
     """
-    G = spec.k_group
-    Q = quantized_prefix(S_b, spec.residual, G)
-    recs = [block_to_bytes(quantize_block(spec, K[j * G:(j + 1) * G], V[j * G:(j + 1) * G]))
+    G, P = spec.k_group, spec.sink
+    _, Q, _ = stream_split(spec, S_b)
+    recs = [block_to_bytes(quantize_block(spec, K[P + j * G:P + (j + 1) * G], V[P + j * G:P + (j + 1) * G]))
             for j in range(Q // G)]
     if not recs:
         return np.zeros((0, record_bytes(spec)), np.uint8)
     return np.stack(recs)
 
 
-def ring_slots(Q: int, S: int, capacity: int) -> np.ndarray:
-    """Ring-buffer slots holding residual tokens Q..S-1 (token t lives at t mod C)."""
-    return np.arange(Q, S) % capacity
+def ring_slots(Q: int, S: int, capacity: int, sink: int = 0) -> np.ndarray:
+    """Ring-buffer slots holding the residual tokens P+Q .. S-1 of a sequence
+    with a sink of P tokens: token t lives at (t - P) mod C."""
+    return np.arange(Q, max(S - sink, 0)) % capacity
 
 
 # ---------------------------------------------------------------------------
@@ -300,17 +325,20 @@ def attention_fp64(q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float) ->
 
 
 def pair_cache_fp64(spec: CacheSpec, K: np.ndarray, V: np.ndarray, S_b: int):
-    """The attention inputs of one (sequence, kv head): dequantized blocks then
-    the exact residual tokens, in token order. Returns (Khat, Vhat) [S_b][d]."""
-    G = spec.k_group
-    Q = quantized_prefix(S_b, spec.residual, G)
-    ks, vs = [], []
+    """The attention inputs of one (sequence, kv head), in token order: the exact
+    sink tokens, the dequantized blocks, then the exact residual tokens.
+    Returns (Khat, Vhat) [S_b][d]."""
+    G, P = spec.k_group, spec.sink
+    s, Q, _ = stream_split(spec, S_b)
+    ks = [np.asarray(K[:s], np.float64)]
+    vs = [np.asarray(V[:s], np.float64)]
     for j in range(Q // G):
-        kh, vh = dequantize_block(spec, quantize_block(spec, K[j * G:(j + 1) * G], V[j * G:(j + 1) * G]))
+        lo = P + j * G
+        kh, vh = dequantize_block(spec, quantize_block(spec, K[lo:lo + G], V[lo:lo + G]))
         ks.append(kh)
         vs.append(vh)
-    ks.append(np.asarray(K[Q:S_b], np.float64))
-    vs.append(np.asarray(V[Q:S_b], np.float64))
+    ks.append(np.asarray(K[P + Q:S_b], np.float64))
+    vs.append(np.asarray(V[P + Q:S_b], np.float64))
     return np.concatenate(ks, axis=0), np.concatenate(vs, axis=0)
 
 
