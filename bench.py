@@ -12,7 +12,11 @@ size.
 
 Prints one JSON line on stdout; human-readable detail goes to stderr.
 
-  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--sink P]
+
+With --sink P the first P tokens of every sequence stay in full precision
+beside the quantized blocks and the ring (attention sink); the decode-partials
+time then covers the sink kernel's launch as well.
 
 A multi-layer workload (the 80-layer 70B-shaped one) keeps one cache per layer
 resident (27 GB for 80 layers, so no copies are rotated) and times the full
@@ -54,13 +58,15 @@ def quantized_prefix(S, R, G):
     return G * (max(S - R, 0) // G)
 
 
-def partial_bytes(w, lengths, record_bytes):
+def partial_bytes(w, lengths, record_bytes, sink=0):
     """Algorithmic HBM bytes the decode-partials launch must move: packed codes and
-    fp16 scale/zero of every quantized token, the full-precision ring tokens, q."""
+    fp16 scale/zero of every quantized token, the full-precision ring and sink
+    tokens, q."""
     per_tok = record_bytes / w.k_group
     total = 0.0
     for S in lengths:
-        Q = quantized_prefix(S, w.residual, w.k_group)
+        post = max(S - sink, 0)
+        Q = quantized_prefix(post, w.residual, w.k_group)
         total += w.num_kv_heads * (Q * per_tok + (S - Q) * w.head_dim * 2 * 2)
     total += w.batch * w.num_q_heads * w.head_dim * 2
     return total
@@ -70,16 +76,16 @@ def out_bytes(w):
     return w.batch * w.num_q_heads * w.head_dim * 4
 
 
-def append_flush_bytes(w, lengths_before, record_bytes):
+def append_flush_bytes(w, lengths_before, record_bytes, sink=0):
     """Algorithmic bytes of appending one token per sequence (read K, V rows, write
-    them to the ring) and of flushing the blocks that leave the window (read the
-    block's ring rows, write its record)."""
+    them to the ring or the sink) and of flushing the blocks that leave the window
+    (read the block's ring rows, write its record)."""
     row = w.head_dim * 2
     total = 0.0
     for S0 in lengths_before:
         total += w.num_kv_heads * 2 * row * 2           # read new k, v; write to the ring
-        q0 = quantized_prefix(S0, w.residual, w.k_group)
-        q1 = quantized_prefix(S0 + 1, w.residual, w.k_group)
+        q0 = quantized_prefix(max(S0 - sink, 0), w.residual, w.k_group)
+        q1 = quantized_prefix(max(S0 + 1 - sink, 0), w.residual, w.k_group)
         blocks = (q1 - q0) // w.k_group
         total += blocks * w.num_kv_heads * (w.k_group * 2 * row + record_bytes)
     return total
@@ -163,14 +169,14 @@ def decode_kernel_name(w) -> str:
     return "decode_fast_kernel"
 
 
-def cpu_baseline(w, inp, lengths, budget_s=15.0):
+def cpu_baseline(w, inp, lengths, budget_s=15.0, sink=0):
     """Time the oracle's decode attention on a bounded sample of (sequence, kv head)
     pairs of the same workload; returns GB/s of the same algorithmic bytes."""
     from threadpoolctl import threadpool_limits
 
     from oracle import kivi
     spec = kivi.CacheSpec(w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim, w.k_bits, w.v_bits,
-                          w.k_group, w.v_group, w.residual, w.residual + w.k_group, w.dtype)
+                          w.k_group, w.v_group, w.residual, w.residual + w.k_group, w.dtype, sink=sink)
     q = inp.q.float().cpu().numpy()
     pairs = [(b, h) for b in range(w.batch) for h in range(w.num_kv_heads)]
     done, nbytes, t_used = 0, 0.0, 0.0
@@ -190,7 +196,7 @@ def cpu_baseline(w, inp, lengths, budget_s=15.0):
             kivi.decode_attention(spec, q, _P(k), _P(v), lengths, pairs=[(b, h)])
             t_used += time.perf_counter() - t0
             S = lengths[b]
-            Q = quantized_prefix(S, w.residual, w.k_group)
+            Q = quantized_prefix(max(S - sink, 0), w.residual, w.k_group)
             nbytes += Q * per_tok + (S - Q) * w.head_dim * 4 + w.num_q_heads // w.num_kv_heads * w.head_dim * 6
             done += 1
             if t_used > budget_s:
@@ -335,6 +341,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="after timing, run device-to-device copies of this many MiB (counter calibration)")
+    ap.add_argument("--sink", type=int, default=0,
+                    help="keep the first SINK tokens of every sequence in full precision (attention sink)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -356,7 +364,10 @@ def main():
     w = W.WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
     if w.layers != 1:
+        if args.sink:
+            raise SystemExit("--sink is measured on single-layer workloads")
         return bench_layers(w, args, dev)
+    P = args.sink
     torch.cuda.set_device(dev)
     lengths0 = W.sequence_lengths(w)
     total_steps = args.warmup + 2 * args.steps
@@ -364,16 +375,17 @@ def main():
 
     inp = W.make_layer(w, device=dev, lengths=lengths0)
     chunk = 512
-    probe = cache_for_workload(w, lengths0, chunk, extra_tokens=0, device=dev)
+    probe = cache_for_workload(w, lengths0, chunk, extra_tokens=0, device=dev, sink=P)
     rec = probe.record_bytes
-    per_copy = probe.blocks.numel() + 2 * probe.k_ring.numel() * 2
+    per_copy = probe.blocks.numel() + 2 * probe.k_ring.numel() * 2 + \
+        (2 * probe.k_sink.numel() * 2 if probe.k_sink is not None else 0)
     del probe
     copies = args.copies or max(1, math.ceil(3 * MALL_BYTES / per_copy))
     steps_per_copy = math.ceil(total_steps / copies) + 1
     caches = []
     t_fill = 0.0
     for i in range(copies):
-        c = cache_for_workload(w, lengths0, chunk, extra_tokens=steps_per_copy, device=dev)
+        c = cache_for_workload(w, lengths0, chunk, extra_tokens=steps_per_copy, device=dev, sink=P)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         c.prefill(inp.k, inp.v, lengths0, chunk)
@@ -431,9 +443,9 @@ def main():
         before = lens[ci]
         after = [s + 1 for s in before]
         if args.warmup <= i < args.warmup + args.steps:
-            step_bytes.append(append_flush_bytes(w, before, rec) + partial_bytes(w, after, rec) + out_bytes(w))
+            step_bytes.append(append_flush_bytes(w, before, rec, P) + partial_bytes(w, after, rec, P) + out_bytes(w))
         elif i >= args.warmup + args.steps:
-            part_bytes.append(partial_bytes(w, after, rec))
+            part_bytes.append(partial_bytes(w, after, rec, P))
         lens[ci] = after
 
     ms_step = ms_total / args.steps
@@ -458,6 +470,9 @@ def main():
         log(f"[bench] copy probe: 3 device-to-device copies of {n} bytes")
 
     kernel = decode_kernel_name(w)
+    if P > 0:   # the partials window then holds the sink kernel's launch too
+        kernel = "sink_kernel+" + kernel
+        log(f"[bench] sink of {P} tokens: the decode-partials time covers the sink kernel and {kernel[12:]}")
     result = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -474,7 +489,7 @@ def main():
         "config": {"workload": w.name, "batch": w.batch, "num_q_heads": w.num_q_heads,
                    "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim, "seq_len": max(lengths0),
                    "input_dtype": w.dtype, "k_bits": w.k_bits, "v_bits": w.v_bits, "k_group": w.k_group,
-                   "v_group": w.v_group, "residual": w.residual, "paged": w.paged,
+                   "v_group": w.v_group, "residual": w.residual, "paged": w.paged, "sink": P,
                    "cache_copies_rotated": copies},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBPS, 4),
@@ -488,7 +503,7 @@ def main():
     log(f"[bench] quantize: full-prefix flush {result['quantize']['us_per_flush']:.1f} us, "
         f"{result['quantize']['bytes'] / 1e6:.1f} MB -> {result['quantize']['value']:.0f} GB/s")
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(w, inp, [s + 0 for s in lengths0])
+        result["cpu_baseline"] = cpu_baseline(w, inp, [s + 0 for s in lengths0], sink=P)
         log(f"[bench] oracle on the host: {result['cpu_baseline']['value']:.3f} GB/s")
     print(json.dumps(result), flush=True)
 

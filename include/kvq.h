@@ -20,6 +20,10 @@
  *   [P1] ai-automate.fr, "KV-cache compressé et modèles 4-bit ...", section on
  *        Minima-KV: partial attention states merged by a globally normalised
  *        online softmax.
+ *   Attention sink: [P2], paragraph on the eviction family (StreamingLLM keeps
+ *        the first tokens as attention sinks beside a recent window); [P3],
+ *        section on OSCAR (sink and recent tokens kept in BF16, the history
+ *        compressed to INT2).
  *
  * Memory model. The caller owns every buffer (sized with kvq_get_layout and
  * kvq_workspace_size). The library allocates nothing, keeps no global state,
@@ -27,12 +31,17 @@
  * the caller's HIP stream (passed as void*; NULL is the default stream). All
  * pointers in kvq_cache and every tensor argument are DEVICE pointers.
  *
- * One kvq_cache is one layer. For each (sequence b, kv head h):
- *   - tokens [0, Q_b) are quantized, in blocks of G tokens (a "record" each);
- *   - tokens [Q_b, S_b) sit in a full-precision ring buffer of res_capacity
- *     slots; token t lives in slot t mod res_capacity;
- *   - after kvq_flush_residual, R <= S_b - Q_b < R + G whenever S_b >= R,
- *     i.e. Q_b = G * floor(max(S_b - R, 0) / G).
+ * One kvq_cache is one layer. For each (sequence b, kv head h), with a sink of
+ * P >= 0 tokens (kvq_config.sink; P = 0: none):
+ *   - tokens [0, min(S_b, P)) sit in the full-precision sink buffers, row t;
+ *     they are never quantized;
+ *   - tokens [P, P + Q_b) are quantized, in blocks of G tokens (a "record"
+ *     each; block j holds tokens P + jG .. P + jG + G - 1);
+ *   - tokens [P + Q_b, S_b) sit in a full-precision ring buffer of
+ *     res_capacity slots; token t lives in slot (t - P) mod res_capacity;
+ *   - after kvq_flush_residual, R <= S_b - P - Q_b < R + G whenever
+ *     S_b - P >= R, i.e. Q_b = G * floor(max(S_b - P - R, 0) / G).
+ * With P = 0 the sink is absent and everything else reads as written.
  *
  * Record of one block (little-endian, sections in this order, no padding):
  *   K codes  uint32 [G][d*k_bits/32]   token-major; word w of token t holds
@@ -111,6 +120,7 @@ typedef struct {
   int32_t max_blocks;     /* dense: blocks per (sequence, kv head); paged: block_table width */
   int32_t num_pages;      /* 0: dense store; > 0: paged store with this many pages         */
   int32_t dtype;          /* KVQ_F16 or KVQ_BF16: K, V, q and the ring                     */
+  int32_t sink;           /* P >= 0: leading tokens of every sequence kept in full precision */
 } kvq_config;
 
 typedef struct {
@@ -119,6 +129,7 @@ typedef struct {
   size_t block_table;     /* bytes of the page table (int32 [B][max_blocks]); 0 if dense     */
   size_t ring;            /* bytes of EACH of k_ring and v_ring: [B][H_kv][res_capacity][d]  */
   size_t state;           /* bytes of the state words; must be zeroed before first use       */
+  size_t sink;            /* bytes of EACH of k_sink and v_sink: [B][H_kv][P][d]; 0 if P = 0 */
 } kvq_layout;
 
 typedef struct {
@@ -129,6 +140,8 @@ typedef struct {
   int32_t* state;              /* [B][4] {Q_b, S_b, internal, internal}, then the error word
                                   and internal decode counters (kvq_layout.state bytes in all);
                                   zero-filled by the caller for an empty cache                 */
+  void* k_sink;                /* [B][H_kv][P][d] of dtype, 16-byte aligned; NULL if P = 0     */
+  void* v_sink;
 } kvq_cache;
 
 /* Host only. Validates cfg and fills the byte sizes of every cache buffer.
@@ -136,17 +149,20 @@ typedef struct {
 kvq_status kvq_get_layout(const kvq_config* cfg, kvq_layout* out);
 
 /* Host only. Bytes of the decode workspace for sequences of at most
- * max_seq_tokens tokens (partial softmax states of the sequence splits). */
+ * max_seq_tokens tokens (partial softmax states of the sequence splits, and
+ * of the sink when P > 0). */
 kvq_status kvq_workspace_size(const kvq_config* cfg, int32_t max_seq_tokens, size_t* bytes);
 
 /* Append new key/value rows to the full-precision ring ([P4] KIVI: recent
- * tokens stay in full precision).
+ * tokens stay in full precision); rows whose position is below P go to the
+ * sink instead.
  *   k_new, v_new: [B][H_kv][n_max][d] of dtype (device);
  *   n_new: device int32 [B], tokens to take from each sequence's first rows
  *          (0 <= n_new[b] <= n_max), or NULL to take n_max from every sequence.
- * S_b grows by n_new[b]. A sequence whose ring would overflow
- * (S_b - Q_b + n_new[b] > res_capacity) takes nothing and sets
- * KVQ_DEV_RESIDUAL_FULL; call kvq_flush_residual between large chunks. */
+ * S_b grows by n_new[b]. A sequence whose ring would overflow (its ring tokens
+ * after the call, max(S_b + n_new[b] - P, 0) - Q_b, exceed res_capacity) takes
+ * nothing and sets KVQ_DEV_RESIDUAL_FULL; call kvq_flush_residual between
+ * large chunks. */
 kvq_status kvq_append(const kvq_config* cfg, const kvq_cache* cache,
                       const void* k_new, const void* v_new,
                       const int32_t* n_new, int32_t n_max, void* stream);
@@ -175,7 +191,9 @@ kvq_status kvq_append_flush(const kvq_config* cfg, const kvq_cache* cache,
  *                   lengths are read on the device);
  *   workspace: device scratch of at least kvq_workspace_size(cfg, max_seq_tokens)
  *              bytes; its contents need no initialisation.
- * A sequence with S_b == 0 gets a zero output. The launch hands out its work
+ * A sequence with S_b == 0 gets a zero output. The sink tokens of a sequence
+ * (P > 0) enter as one more partial state per (sequence, query head). The
+ * launch hands out its work
  * through counters in the cache's state words (and re-arms them when it ends),
  * so decode calls on one cache, like calls that share a workspace, must be
  * ordered on one stream. */

@@ -26,16 +26,17 @@ EXPORTED = ("kvq_get_layout", "kvq_workspace_size", "kvq_append", "kvq_append_fl
 class kvq_config(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "batch", "num_q_heads", "num_kv_heads", "head_dim", "k_bits", "v_bits", "k_group", "v_group",
-        "residual", "res_capacity", "max_blocks", "num_pages", "dtype")]
+        "residual", "res_capacity", "max_blocks", "num_pages", "dtype", "sink")]
 
 
 class kvq_layout(ctypes.Structure):
-    _fields_ = [(n, ctypes.c_size_t) for n in ("record", "blocks", "block_table", "ring", "state")]
+    _fields_ = [(n, ctypes.c_size_t) for n in ("record", "blocks", "block_table", "ring", "state", "sink")]
 
 
 class kvq_cache(ctypes.Structure):
     _fields_ = [("blocks", ctypes.c_void_p), ("block_table", ctypes.c_void_p),
-                ("k_ring", ctypes.c_void_p), ("v_ring", ctypes.c_void_p), ("state", ctypes.c_void_p)]
+                ("k_ring", ctypes.c_void_p), ("v_ring", ctypes.c_void_p), ("state", ctypes.c_void_p),
+                ("k_sink", ctypes.c_void_p), ("v_sink", ctypes.c_void_p)]
 
 
 class KVQError(RuntimeError):

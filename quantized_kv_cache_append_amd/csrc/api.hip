@@ -18,6 +18,7 @@ using kvq::Geom;
 namespace {
 
 constexpr int kMaxBatch = 4096;
+constexpr int kMaxSink = 1 << 20;   // sink tokens per sequence
 
 bool pow2_in(int v, int lo, int hi) { return v >= lo && v <= hi && (v & (v - 1)) == 0; }
 
@@ -25,7 +26,7 @@ kvq_status validate(const kvq_config* c) {
   if (c == nullptr) return KVQ_ERR_INVALID_ARG;
   if (c->batch <= 0 || c->num_q_heads <= 0 || c->num_kv_heads <= 0 || c->head_dim <= 0 ||
       c->k_group <= 0 || c->v_group <= 0 || c->residual < 0 || c->res_capacity <= 0 || c->max_blocks < 0 ||
-      c->num_pages < 0)
+      c->num_pages < 0 || c->sink < 0)
     return KVQ_ERR_INVALID_ARG;
   if (c->num_q_heads % c->num_kv_heads != 0) return KVQ_ERR_INVALID_ARG;
   if (c->dtype != KVQ_F16 && c->dtype != KVQ_BF16) return KVQ_ERR_INVALID_ARG;
@@ -36,6 +37,7 @@ kvq_status validate(const kvq_config* c) {
   if (!pow2_in(c->k_group, 16, 64) || !pow2_in(c->v_group, 16, 64)) return KVQ_ERR_UNSUPPORTED;
   if (c->num_q_heads / c->num_kv_heads > 8) return KVQ_ERR_UNSUPPORTED;
   if (c->batch > kMaxBatch) return KVQ_ERR_UNSUPPORTED;
+  if (c->sink > kMaxSink) return KVQ_ERR_UNSUPPORTED;
   if ((long long)c->k_group * c->v_bits < 32) return KVQ_ERR_UNSUPPORTED;
   return KVQ_OK;
 }
@@ -47,6 +49,9 @@ kvq_status validate_cache(const kvq_config* c, const kvq_cache* k) {
   if ((c->num_pages > 0) != (k->block_table != nullptr)) return KVQ_ERR_INVALID_ARG;
   if ((reinterpret_cast<uintptr_t>(k->blocks) | reinterpret_cast<uintptr_t>(k->k_ring) |
        reinterpret_cast<uintptr_t>(k->v_ring)) & 15)
+    return KVQ_ERR_INVALID_ARG;
+  if (c->sink > 0 && (k->k_sink == nullptr || k->v_sink == nullptr ||
+                      ((reinterpret_cast<uintptr_t>(k->k_sink) | reinterpret_cast<uintptr_t>(k->v_sink)) & 15)))
     return KVQ_ERR_INVALID_ARG;
   return KVQ_OK;
 }
@@ -72,6 +77,7 @@ kvq_status kvq_get_layout(const kvq_config* cfg, kvq_layout* out) {
   }
   out->ring = (size_t)g.B * g.Hkv * (size_t)g.C * g.d * 2;
   out->state = (size_t)kvq::state_words(g.B) * sizeof(int32_t);
+  out->sink = (size_t)g.B * g.Hkv * (size_t)g.P * g.d * 2;
   return KVQ_OK;
 }
 
@@ -142,7 +148,7 @@ kvq_status kvq_decode_attention(const kvq_config* cfg, const kvq_cache* cache, c
   if (st != KVQ_OK) return st;
   const hipStream_t s = static_cast<hipStream_t>(stream);
   if (kvq::launch_decode_partials(g, *cache, q, scale, plan, workspace, s) != hipSuccess) return KVQ_ERR_LAUNCH;
-  return launched(kvq::launch_decode_combine(g, *cache, out, workspace, s));
+  return launched(kvq::launch_decode_combine(g, *cache, out, plan, workspace, s));
 }
 
 kvq_status kvq_decode_partials(const kvq_config* cfg, const kvq_cache* cache, const void* q, float softmax_scale,
@@ -164,7 +170,7 @@ kvq_status kvq_decode_combine(const kvq_config* cfg, const kvq_cache* cache, flo
   float scale;
   const kvq_status st = decode_args(cfg, cache, max_seq_tokens, workspace, workspace_bytes, 0.f, g, plan, scale);
   if (st != KVQ_OK) return st;
-  return launched(kvq::launch_decode_combine(g, *cache, out, workspace, static_cast<hipStream_t>(stream)));
+  return launched(kvq::launch_decode_combine(g, *cache, out, plan, workspace, static_cast<hipStream_t>(stream)));
 }
 
 kvq_status kvq_read_device_error(const kvq_config* cfg, const kvq_cache* cache, void* stream,

@@ -128,15 +128,16 @@ __device__ void quantize_block(const Geom& g, uint8_t* __restrict__ rec, const u
 }
 
 // Copy tokens i in [t_lo, t_hi) of pair `pair` from the new rows into the ring,
-// starting at absolute position S (16-byte vectors).
+// new row i at ring position base + i (>= 0 for every copied row; positions
+// count the tokens after the sink), 16-byte vectors.
 __device__ __forceinline__ void copy_to_ring(const Geom& g, const uint16_t* __restrict__ k_new,
                                              const uint16_t* __restrict__ v_new, int n_max, uint16_t* k_ring,
-                                             uint16_t* v_ring, int pair, int S, int t_lo, int t_hi) {
+                                             uint16_t* v_ring, int pair, int base, int t_lo, int t_hi) {
   const int vec_per_tok = g.d / 8;
   for (int idx = threadIdx.x; idx < (t_hi - t_lo) * vec_per_tok; idx += kThreads) {
     const int i = t_lo + idx / vec_per_tok;
     const int v = idx % vec_per_tok;
-    const int slot = (S + i) % g.C;
+    const int slot = (base + i) % g.C;
     const size_t src = ((size_t)pair * n_max + i) * g.d + (size_t)v * 8;
     const size_t dst = ((size_t)pair * g.C + slot) * g.d + (size_t)v * 8;
     *reinterpret_cast<uint4*>(k_ring + dst) = *reinterpret_cast<const uint4*>(k_new + src);
@@ -144,8 +145,40 @@ __device__ __forceinline__ void copy_to_ring(const Geom& g, const uint16_t* __re
   }
 }
 
-// Blocks a flush takes for a sequence with Q quantized of S tokens, and how
-// many of those fit under max_blocks.
+// Copy tokens i in [t_lo, t_hi) of pair `pair` from the new rows into sink
+// rows S + i (all below P).
+__device__ __forceinline__ void copy_to_sink(const Geom& g, const uint16_t* __restrict__ k_new,
+                                             const uint16_t* __restrict__ v_new, int n_max, uint16_t* k_sink,
+                                             uint16_t* v_sink, int pair, int S, int t_lo, int t_hi) {
+  const int vec_per_tok = g.d / 8;
+  for (int idx = threadIdx.x; idx < (t_hi - t_lo) * vec_per_tok; idx += kThreads) {
+    const int i = t_lo + idx / vec_per_tok;
+    const int v = idx % vec_per_tok;
+    const size_t src = ((size_t)pair * n_max + i) * g.d + (size_t)v * 8;
+    const size_t dst = ((size_t)pair * g.P + S + i) * g.d + (size_t)v * 8;
+    *reinterpret_cast<uint4*>(k_sink + dst) = *reinterpret_cast<const uint4*>(k_new + src);
+    *reinterpret_cast<uint4*>(v_sink + dst) = *reinterpret_cast<const uint4*>(v_new + src);
+  }
+}
+
+// Where n new tokens of a sequence of S tokens go: rows [0, n_sink) to sink
+// rows S.., the others to the ring (row i at ring position S + i - P); `post`
+// is the sequence's token count after the sink once they are in.
+struct AppendSplit {
+  int n_sink, post;
+};
+__device__ __forceinline__ AppendSplit append_split(const Geom& g, int S, int n) {
+  AppendSplit a;
+  a.n_sink = min(max(g.P - S, 0), n);
+  a.post = max(S + n - g.P, 0);
+  return a;
+}
+
+// Tokens after the sink of a sequence of S tokens.
+__device__ __forceinline__ int post_sink(const Geom& g, int S) { return max(S - g.P, 0); }
+
+// Blocks a flush takes for a sequence with Q quantized of S tokens after the
+// sink, and how many of those fit under max_blocks.
 struct FlushPlan {
   int nfl, nok;
 };
@@ -161,7 +194,9 @@ __global__ __launch_bounds__(kThreads) void append_kernel(Geom g, const uint16_t
                                                           const uint16_t* __restrict__ v_new,
                                                           const int32_t* __restrict__ n_new, int n_max,
                                                           uint16_t* __restrict__ k_ring,
-                                                          uint16_t* __restrict__ v_ring, int32_t* __restrict__ state) {
+                                                          uint16_t* __restrict__ v_ring,
+                                                          uint16_t* __restrict__ k_sink,
+                                                          uint16_t* __restrict__ v_sink, int32_t* __restrict__ state) {
   const int pair = blockIdx.x;
   const int b = pair / g.Hkv;
   __shared__ int s_S, s_n, s_ok;
@@ -172,12 +207,14 @@ __global__ __launch_bounds__(kThreads) void append_kernel(Geom g, const uint16_t
     const bool count_ok = n >= 0 && n <= n_max;
     s_S = S;
     s_n = n;
-    s_ok = count_ok ? ((S - Q) + n <= g.C ? 1 : 2) : 0;   // 1 ok, 2 ring full, 0 bad count
+    s_ok = count_ok ? (append_split(g, S, n).post - Q <= g.C ? 1 : 2) : 0;   // 1 ok, 2 ring full, 0 bad count
   }
   __syncthreads();
   if (s_ok == 1) {
-    const int t0 = blockIdx.y * kAppendTokensPerWG;
-    copy_to_ring(g, k_new, v_new, n_max, k_ring, v_ring, pair, s_S, t0, min(t0 + kAppendTokensPerWG, s_n));
+    const int t0 = blockIdx.y * kAppendTokensPerWG, t1 = min(t0 + kAppendTokensPerWG, s_n);
+    const int ns = append_split(g, s_S, s_n).n_sink;
+    copy_to_sink(g, k_new, v_new, n_max, k_sink, v_sink, pair, s_S, t0, min(t1, ns));
+    copy_to_ring(g, k_new, v_new, n_max, k_ring, v_ring, pair, s_S - g.P, max(t0, ns), t1);
   }
   __syncthreads();
   if (threadIdx.x == 0 && last_arrival(&state[4 * b + kStateAppendCnt], g.Hkv * gridDim.y)) {
@@ -239,7 +276,7 @@ __global__ __launch_bounds__(kThreads) void flush_kernel(Geom g, uint8_t* __rest
   __shared__ int s_Q, s_nfl, s_nok, s_bad;
   if (threadIdx.x == 0) {
     const int Q = state[4 * b + kStateQ];
-    const FlushPlan f = flush_plan(g, Q, state[4 * b + kStateS]);
+    const FlushPlan f = flush_plan(g, Q, post_sink(g, state[4 * b + kStateS]));
     s_Q = Q;
     s_nfl = f.nfl;
     s_nok = f.nok;
@@ -268,6 +305,8 @@ __global__ __launch_bounds__(kThreads) void append_flush_kernel(Geom g, const ui
                                                                 const int32_t* __restrict__ table,
                                                                 uint16_t* __restrict__ k_ring,
                                                                 uint16_t* __restrict__ v_ring,
+                                                                uint16_t* __restrict__ k_sink,
+                                                                uint16_t* __restrict__ v_sink,
                                                                 int32_t* __restrict__ state) {
   extern __shared__ uint8_t smem[];
   const int pair = blockIdx.x;
@@ -278,8 +317,9 @@ __global__ __launch_bounds__(kThreads) void append_flush_kernel(Geom g, const ui
     const int S = state[4 * b + kStateS];
     const int n = n_new ? n_new[b] : n_max;
     const bool count_ok = n >= 0 && n <= n_max;
-    const int ok = count_ok ? ((S - Q) + n <= g.C ? 1 : 2) : 0;
-    const FlushPlan f = flush_plan(g, Q, ok == 1 ? S + n : S);
+    const int post = count_ok ? append_split(g, S, n).post : 0;
+    const int ok = count_ok ? (post - Q <= g.C ? 1 : 2) : 0;
+    const FlushPlan f = flush_plan(g, Q, ok == 1 ? post : post_sink(g, S));
     s_Q = Q;
     s_S = S;
     s_n = n;
@@ -289,7 +329,11 @@ __global__ __launch_bounds__(kThreads) void append_flush_kernel(Geom g, const ui
     s_bad = 0;
   }
   __syncthreads();
-  if (s_ok == 1) copy_to_ring(g, k_new, v_new, n_max, k_ring, v_ring, pair, s_S, 0, s_n);
+  if (s_ok == 1) {
+    const int ns = append_split(g, s_S, s_n).n_sink;
+    copy_to_sink(g, k_new, v_new, n_max, k_sink, v_sink, pair, s_S, 0, ns);
+    copy_to_ring(g, k_new, v_new, n_max, k_ring, v_ring, pair, s_S - g.P, ns, s_n);
+  }
   // the block routine reads the ring through plain loads: make this
   // workgroup's ring writes visible to all of its threads first
   __threadfence_block();
@@ -315,7 +359,8 @@ hipError_t launch_append(const Geom& g, const kvq_cache& c, const void* k_new, c
   dim3 grid(g.B * g.Hkv, chunks > 0 ? chunks : 1);
   hipLaunchKernelGGL(append_kernel, grid, dim3(kThreads), 0, s, g,
                      static_cast<const uint16_t*>(k_new), static_cast<const uint16_t*>(v_new), n_new,
-                     n_max, static_cast<uint16_t*>(c.k_ring), static_cast<uint16_t*>(c.v_ring), c.state);
+                     n_max, static_cast<uint16_t*>(c.k_ring), static_cast<uint16_t*>(c.v_ring),
+                     static_cast<uint16_t*>(c.k_sink), static_cast<uint16_t*>(c.v_sink), c.state);
   return hipGetLastError();
 }
 
@@ -343,7 +388,8 @@ hipError_t launch_append_flush_p(const Geom& g, const kvq_cache& c, const void* 
   hipLaunchKernelGGL((append_flush_kernel<P>), dim3(g.B * g.Hkv), dim3(kThreads), P::lds(g), s, g,
                      static_cast<const uint16_t*>(k_new), static_cast<const uint16_t*>(v_new), n_new, n_max,
                      static_cast<uint8_t*>(c.blocks), c.block_table, static_cast<uint16_t*>(c.k_ring),
-                     static_cast<uint16_t*>(c.v_ring), c.state);
+                     static_cast<uint16_t*>(c.v_ring), static_cast<uint16_t*>(c.k_sink),
+                     static_cast<uint16_t*>(c.v_sink), c.state);
   return hipGetLastError();
 }
 

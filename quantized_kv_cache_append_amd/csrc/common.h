@@ -27,6 +27,7 @@ struct Geom {
   int rec_kc, rec_ks, rec_kz, rec_vc, rec_vs, rec_vz, rec_bytes;
   int k_words;   // uint32 words of K codes per token: d*kb/32
   int v_words;   // uint32 words of V codes per channel: G*vb/32
+  int P;         // sink: leading tokens of a sequence kept in full precision
 };
 
 // Fill the derived fields of a Geom from a validated config.
@@ -46,6 +47,7 @@ inline Geom make_geom(const kvq_config& c) {
   g.rec_vs = g.rec_vc + g.d * g.v_words * 4;
   g.rec_vz = g.rec_vs + 2 * (g.d / g.GV) * g.G;
   g.rec_bytes = g.rec_vz + 2 * (g.d / g.GV) * g.G;
+  g.P = c.sink;
   return g;
 }
 
@@ -161,7 +163,8 @@ hipError_t launch_append_flush(const Geom& g, const kvq_cache& c, const void* k_
 struct DecodePlan;
 hipError_t launch_decode_partials(const Geom& g, const kvq_cache& c, const void* q, float scale,
                                   const DecodePlan& plan, void* ws, hipStream_t s);
-hipError_t launch_decode_combine(const Geom& g, const kvq_cache& c, float* out, void* ws, hipStream_t s);
+hipError_t launch_decode_combine(const Geom& g, const kvq_cache& c, float* out, const DecodePlan& plan, void* ws,
+                                 hipStream_t s);
 
 // Decode work decomposition shared by the workspace sizing and the kernels.
 struct DecodePlan {
@@ -171,7 +174,8 @@ struct DecodePlan {
   int unit_sets;      // fixed sets per quantized unit (0: sized from the lengths)
   int max_blk;        // quantized blocks per (sequence, kv head) the workspace is sized for
   size_t units_max;   // upper bound on work units
-  size_t ws_bytes;    // workspace bytes: the unit plan, then the partial states
+  size_t sink_off;    // byte offset of the sink partial states (one per output row); 0 if P == 0
+  size_t ws_bytes;    // workspace bytes: the unit plan, the partial states, then the sink's
 };
 DecodePlan plan_decode(const Geom& g, int max_seq_tokens);
 

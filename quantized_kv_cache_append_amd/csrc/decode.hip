@@ -66,7 +66,7 @@ __global__ __launch_bounds__(256) void decode_generic_kernel(
     const int b = un.b, h = un.h;
     const int pair = b * g.Hkv + h;
     const int Q = state[4 * b + kStateQ];
-    const int S = state[4 * b + kStateS];
+    const int S = max(state[4 * b + kStateS] - g.P, 0);   // tokens after the sink
 
     float qv[kNgMax][CPL], o[kNgMax][CPL], m[kNgMax], l[kNgMax];
 #pragma unroll
@@ -240,6 +240,7 @@ template <int D>
 __global__ __launch_bounds__(64 * kCombineWaves) void combine_kernel(Geom g, const int* __restrict__ plan,
                                                                      const float* ws,   // (not restrict: the
                                                                      // compiler barrier below must order its loads)
+                                                                     const float* __restrict__ sink_parts,
                                                                      float* __restrict__ out) {
   constexpr int CPL = D / 64;   // channels per lane
   const int lane = threadIdx.x & 63;
@@ -254,6 +255,16 @@ __global__ __launch_bounds__(64 * kCombineWaves) void combine_kernel(Geom g, con
   float m = -INFINITY, L = 0.f, acc[CPL];
 #pragma unroll
   for (int k = 0; k < CPL; ++k) acc[k] = 0.f;
+  if (sink_parts != nullptr) {   // the sink's partial state opens the merge
+    const float* sp = sink_parts + (size_t)row * (D + 2);
+    const float2 ml = *reinterpret_cast<const float2*>(sp + D);
+    if (ml.x != -INFINITY) {   // wave-uniform
+      m = ml.x;
+      L = ml.y;
+#pragma unroll
+      for (int k = 0; k < CPL; ++k) acc[k] = sp[CPL * lane + k];
+    }
+  }
   for (int i0 = 0; i0 < pu.n; i0 += kCombineBatch) {
     const int cnt = min(kCombineBatch, pu.n - i0);
     float v[kCombineBatch][CPL];
@@ -292,6 +303,108 @@ __global__ __launch_bounds__(64 * kCombineWaves) void combine_kernel(Geom g, con
   for (int k = 0; k < CPL; ++k) dst[k] = L > 0.f ? acc[k] / L : 0.f;
 }
 
+// Partial softmax state of the sink tokens of one (sequence b, query head):
+// the first min(S_b, P) tokens, kept in full precision (attention sink: the
+// zubnet.ai survey's paragraph on StreamingLLM's sink tokens, the encorp.ai
+// OSCAR section). One wave per output row and 64 tokens per round, all of a
+// round's loads issued together: lane t scores token t against the scaled
+// query (held in LDS), then lane l accumulates channels D/64 * l .. over the
+// round's tokens. Scores in log2 units like every other partial; written in
+// the partial layout {o[D], m, l}, the empty state (m = -inf, l = 0) for
+// S_b == 0.
+template <int D, bool BF16>
+__global__ __launch_bounds__(64 * kCombineWaves) void sink_kernel(Geom g, const uint16_t* __restrict__ k_sink,
+                                                                  const uint16_t* __restrict__ v_sink,
+                                                                  const int32_t* __restrict__ state,
+                                                                  const uint16_t* __restrict__ q, float qscale,
+                                                                  float* __restrict__ out_part) {
+  constexpr int CPL = D / 64;             // channels per lane in the P.V phase
+  constexpr int VEC = D / 8;              // 16-byte vectors per row
+  constexpr int VW = CPL == 1 ? 1 : CPL / 2;   // words per lane of a value row (d = 64: a half word)
+  __shared__ float lq[kCombineWaves][D];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int row = blockIdx.x * kCombineWaves + wave;
+  if (row >= g.B * g.Hq) return;
+  const int b = row / g.Hq, h = (row % g.Hq) / g.ng;
+  const int n = __builtin_amdgcn_readfirstlane(min(state[4 * b + kStateS], g.P));
+  float* qs = lq[wave];
+#pragma unroll
+  for (int k = 0; k < CPL; ++k) qs[CPL * lane + k] = in_to_f32<BF16>(q[(size_t)row * D + CPL * lane + k]) * qscale;
+  wave_lds_fence();
+  const size_t pair_row0 = (size_t)(b * g.Hkv + h) * g.P;
+  float m = -INFINITY, l = 0.f, acc[CPL];
+#pragma unroll
+  for (int k = 0; k < CPL; ++k) acc[k] = 0.f;
+  for (int t0 = 0; t0 < n; t0 += 64) {
+    const int cnt = min(64, n - t0);   // wave-uniform
+    // this round's loads: lane's key row (token t0 + lane), and its channels of every value row
+    const uint4* kr = reinterpret_cast<const uint4*>(k_sink + (pair_row0 + t0 + min(lane, cnt - 1)) * D);
+    uint4 kv[VEC];
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) kv[i] = kr[i];
+    uint32_t vw[64][VW];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      if (16 * c >= cnt) break;   // wave-uniform: only the chunks of 16 tokens the round has
+#pragma unroll
+      for (int u = 16 * c; u < 16 * c + 16; ++u) {
+        const uint16_t* vr = v_sink + (pair_row0 + t0 + min(u, cnt - 1)) * D + CPL * lane;
+        if constexpr (CPL == 1) {
+          vw[u][0] = vr[0];
+        } else {
+#pragma unroll
+          for (int k = 0; k < VW; ++k) vw[u][k] = reinterpret_cast<const uint32_t*>(vr)[k];
+        }
+      }
+    }
+    // score of token t0 + lane
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) {
+      const float4 qa = *reinterpret_cast<const float4*>(qs + 8 * i);
+      const float4 qb = *reinterpret_cast<const float4*>(qs + 8 * i + 4);
+      const uint32_t w[4] = {kv[i].x, kv[i].y, kv[i].z, kv[i].w};
+      s = fmaf(qa.x, in_to_f32<BF16>(w[0] & 0xffffu), s);
+      s = fmaf(qa.y, in_to_f32<BF16>(w[0] >> 16), s);
+      s = fmaf(qa.z, in_to_f32<BF16>(w[1] & 0xffffu), s);
+      s = fmaf(qa.w, in_to_f32<BF16>(w[1] >> 16), s);
+      s = fmaf(qb.x, in_to_f32<BF16>(w[2] & 0xffffu), s);
+      s = fmaf(qb.y, in_to_f32<BF16>(w[2] >> 16), s);
+      s = fmaf(qb.z, in_to_f32<BF16>(w[3] & 0xffffu), s);
+      s = fmaf(qb.w, in_to_f32<BF16>(w[3] >> 16), s);
+    }
+    s = lane < cnt ? s : -INFINITY;
+    const float mn = fmaxf(m, wave_max(s));
+    const float alpha = m == -INFINITY ? 0.f : exp2f(m - mn);
+    const float p = lane < cnt ? exp2f(s - mn) : 0.f;
+    l = l * alpha + wave_sum(p);
+#pragma unroll
+    for (int k = 0; k < CPL; ++k) acc[k] *= alpha;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      if (16 * c >= cnt) break;
+#pragma unroll
+      for (int u = 16 * c; u < 16 * c + 16; ++u) {
+        const float pu = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(p), u));   // 0 past cnt
+#pragma unroll
+        for (int k = 0; k < CPL; ++k) {
+          const uint32_t w = vw[u][k / 2];
+          acc[k] = fmaf(pu, in_to_f32<BF16>(CPL == 1 ? w : (k % 2 ? (w >> 16) : (w & 0xffffu))), acc[k]);
+        }
+      }
+    }
+    m = mn;
+  }
+  float* dst = out_part + (size_t)row * (D + 2);
+#pragma unroll
+  for (int k = 0; k < CPL; ++k) dst[CPL * lane + k] = acc[k];
+  if (lane == 0) {
+    dst[D] = m;
+    dst[D + 1] = l;
+  }
+}
+
 template <int D, bool BF16>
 hipError_t launch_generic(const Geom& g, const kvq_cache& c, const void* q, float scale, const DecodePlan& plan,
                           void* ws, hipStream_t s) {
@@ -317,12 +430,37 @@ DecodePlan plan_decode(const Geom& g, int max_seq_tokens) {
   p.max_blk = std::max(max_seq_tokens - g.R, 0) / g.G;
   p.units_max = units_max(g, p.max_blk, p.nb_set, p.ring_chunk, p.unit_sets);
   p.ws_bytes = plan_bytes(g.B) + p.units_max * (size_t)g.ng * (size_t)(g.d + 2) * 4;
+  p.sink_off = 0;
+  if (g.P > 0) {   // one sink partial per output row, 16-byte aligned
+    p.sink_off = (p.ws_bytes + 15) & ~(size_t)15;
+    p.ws_bytes = p.sink_off + (size_t)g.B * g.Hq * (g.d + 2) * 4;
+  }
   return p;
 }
+
+namespace {
+template <int D, bool BF16>
+hipError_t launch_sink(const Geom& g, const kvq_cache& c, const void* q, float scale, const DecodePlan& plan,
+                       void* ws, hipStream_t s) {
+  const int grid = (g.B * g.Hq + kCombineWaves - 1) / kCombineWaves;
+  hipLaunchKernelGGL((sink_kernel<D, BF16>), dim3(grid), dim3(64 * kCombineWaves), 0, s, g,
+                     static_cast<const uint16_t*>(c.k_sink), static_cast<const uint16_t*>(c.v_sink), c.state,
+                     static_cast<const uint16_t*>(q), scale * 1.4426950408889634f,
+                     reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + plan.sink_off));
+  return hipGetLastError();
+}
+}  // namespace
 
 hipError_t launch_decode_partials(const Geom& g, const kvq_cache& c, const void* q, float scale,
                                   const DecodePlan& plan, void* ws, hipStream_t s) {
   const bool bf16 = g.dtype == KVQ_BF16;
+  if (g.P > 0) {
+    const hipError_t e = g.d == 128 ? (bf16 ? launch_sink<128, true>(g, c, q, scale, plan, ws, s)
+                                            : launch_sink<128, false>(g, c, q, scale, plan, ws, s))
+                                    : (bf16 ? launch_sink<64, true>(g, c, q, scale, plan, ws, s)
+                                            : launch_sink<64, false>(g, c, q, scale, plan, ws, s));
+    if (e != hipSuccess) return e;
+  }
   if (plan.fast) return launch_decode_fast(g, c, q, scale, plan, ws, s);
   if (g.d == 128)
     return bf16 ? launch_generic<128, true>(g, c, q, scale, plan, ws, s)
@@ -331,15 +469,20 @@ hipError_t launch_decode_partials(const Geom& g, const kvq_cache& c, const void*
               : launch_generic<64, false>(g, c, q, scale, plan, ws, s);
 }
 
-hipError_t launch_decode_combine(const Geom& g, const kvq_cache& c, float* out, void* ws, hipStream_t s) {
+hipError_t launch_decode_combine(const Geom& g, const kvq_cache& c, float* out, const DecodePlan& plan, void* ws,
+                                 hipStream_t s) {
   (void)c;
   const int* planp = static_cast<const int*>(ws);
   const float* parts = reinterpret_cast<const float*>(static_cast<const uint8_t*>(ws) + plan_bytes(g.B));
+  const float* sink = g.P > 0 ? reinterpret_cast<const float*>(static_cast<const uint8_t*>(ws) + plan.sink_off)
+                              : nullptr;
   const int grid = (g.B * g.Hq + kCombineWaves - 1) / kCombineWaves;
   if (g.d == 128)
-    hipLaunchKernelGGL((combine_kernel<128>), dim3(grid), dim3(64 * kCombineWaves), 0, s, g, planp, parts, out);
+    hipLaunchKernelGGL((combine_kernel<128>), dim3(grid), dim3(64 * kCombineWaves), 0, s, g, planp, parts, sink,
+                       out);
   else
-    hipLaunchKernelGGL((combine_kernel<64>), dim3(grid), dim3(64 * kCombineWaves), 0, s, g, planp, parts, out);
+    hipLaunchKernelGGL((combine_kernel<64>), dim3(grid), dim3(64 * kCombineWaves), 0, s, g, planp, parts, sink,
+                       out);
   return hipGetLastError();
 }
 

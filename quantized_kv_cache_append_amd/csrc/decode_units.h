@@ -114,7 +114,7 @@ __device__ inline void build_unit_plan(const Geom& g, int32_t* state, int max_bl
     int sets = 0;
     bool too_long = false;
     for (int b = lane; b < g.B; b += 64) {
-      const int Q = state[4 * b + kStateQ], S = state[4 * b + kStateS];
+      const int Q = state[4 * b + kStateQ], S = max(state[4 * b + kStateS] - g.P, 0);   // tokens after the sink
       seqQ[b] = Q;
       seqS[b] = S;
       const int nblk = Q / g.G;

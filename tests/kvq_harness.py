@@ -15,14 +15,16 @@ ATOL = 2e-3     # max-abs error against the fp64 oracle on the same dequantized 
 RTOL_L2 = 1e-3  # relative L2 error over the whole output
 
 
-def spec_of(w: W.Workload, res_capacity: int) -> kivi.CacheSpec:
+def spec_of(w: W.Workload, res_capacity: int, sink: int = 0) -> kivi.CacheSpec:
     return kivi.CacheSpec(batch=w.batch, num_q_heads=w.num_q_heads, num_kv_heads=w.num_kv_heads,
                           head_dim=w.head_dim, k_bits=w.k_bits, v_bits=w.v_bits, k_group=w.k_group,
-                          v_group=w.v_group, residual=w.residual, res_capacity=res_capacity, dtype=w.dtype)
+                          v_group=w.v_group, residual=w.residual, res_capacity=res_capacity, dtype=w.dtype,
+                          sink=sink)
 
 
-def make_cache(w: W.Workload, lengths, chunk: int, extra_tokens: int = 0, device="cuda", seed: int = 0):
-    return cache_for_workload(w, lengths, chunk, extra_tokens=extra_tokens, device=device, seed=seed)
+def make_cache(w: W.Workload, lengths, chunk: int, extra_tokens: int = 0, device="cuda", seed: int = 0,
+               sink: int = 0):
+    return cache_for_workload(w, lengths, chunk, extra_tokens=extra_tokens, device=device, seed=seed, sink=sink)
 
 
 def errors(got: np.ndarray, ref: np.ndarray):
@@ -33,12 +35,14 @@ def errors(got: np.ndarray, ref: np.ndarray):
 
 
 def check_records(cache: QuantizedKVCache, spec: kivi.CacheSpec, k_np, v_np, lengths, pairs):
-    """Bit-exact comparison of every quantized block of the given (b, h) pairs."""
+    """Bit-exact comparison of every quantized block of the given (b, h) pairs,
+    of their rings and of their sink rows."""
     Qs, Ss = cache.lengths()
     n_blocks = 0
+    P = spec.sink
     for b, h in pairs:
         S_b = int(lengths[b])
-        Q = kivi.quantized_prefix(S_b, spec.residual, spec.k_group)
+        s, Q, _ = kivi.stream_split(spec, S_b)
         assert Qs[b] == Q and Ss[b] == S_b, f"lengths of seq {b}: got (Q={Qs[b]}, S={Ss[b]}), want ({Q}, {S_b})"
         exp = kivi.expected_blocks(spec, k_np[b, h], v_np[b, h], S_b)
         for j in range(Q // spec.k_group):
@@ -48,11 +52,17 @@ def check_records(cache: QuantizedKVCache, spec: kivi.CacheSpec, k_np, v_np, len
                 raise AssertionError(f"record (b={b}, h={h}, blk={j}) differs at {bad.size} bytes, first {bad[:8]}")
             n_blocks += 1
         # the ring holds the residual tokens bit for bit
-        slots = kivi.ring_slots(Q, S_b, spec.res_capacity)
+        slots = kivi.ring_slots(Q, S_b, spec.res_capacity, sink=P)
         kr = cache.k_ring[b, h].float().cpu().numpy()[slots]
         vr = cache.v_ring[b, h].float().cpu().numpy()[slots]
-        assert np.array_equal(kr, k_np[b, h, Q:S_b]) and np.array_equal(vr, v_np[b, h, Q:S_b]), \
+        assert np.array_equal(kr, k_np[b, h, P + Q:S_b]) and np.array_equal(vr, v_np[b, h, P + Q:S_b]), \
             f"ring of (b={b}, h={h}) differs"
+        # and the sink its tokens
+        if P > 0:
+            ks = cache.k_sink[b, h, :s].float().cpu().numpy()
+            vs = cache.v_sink[b, h, :s].float().cpu().numpy()
+            assert np.array_equal(ks, k_np[b, h, :s]) and np.array_equal(vs, v_np[b, h, :s]), \
+                f"sink of (b={b}, h={h}) differs"
     return n_blocks
 
 

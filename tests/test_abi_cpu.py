@@ -118,6 +118,36 @@ def test_workspace_grows_with_sequence_bound(kvq_lib):
     assert B.kvq_workspace_size(cfg, 0) > 0   # every pair has its ring unit
 
 
+def test_ctypes_structs_follow_the_header(kvq_lib):
+    # the binding's field lists are the header's, in order
+    from quantized_kv_cache_append_amd import binding as B
+    header = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "kvq.h")).read(), flags=re.S)
+    for struct in (B.kvq_config, B.kvq_layout, B.kvq_cache):
+        body = re.search(r"typedef struct \{([^{}]*)\}\s*" + struct.__name__ + ";", header)
+        assert body, struct.__name__
+        fields = re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\**(\w+);", body.group(1), re.M)
+        assert fields == [f[0] for f in struct._fields_], struct.__name__
+
+
+def test_sink_layout_and_checks(kvq_lib):
+    from quantized_kv_cache_append_amd import binding as B
+    cfg = _cfg(B, sink=4)
+    lay = B.kvq_get_layout(cfg)
+    assert lay.sink == 8 * 32 * 4 * 128 * 2
+    assert B.kvq_get_layout(_cfg(B)).sink == 0
+    # one sink partial state per output row on top of the split states, 16-byte aligned
+    plain, with_sink = B.kvq_workspace_size(_cfg(B), 4096), B.kvq_workspace_size(cfg, 4096)
+    assert with_sink == ((plain + 15) // 16) * 16 + 8 * 32 * (128 + 2) * 4
+    bad = _cfg(B, sink=-1)
+    assert kvq_lib.kvq_get_layout(ctypes.byref(bad), ctypes.byref(B.kvq_layout())) == B.KVQ_ERR_INVALID_ARG
+    # a sink config needs both sink buffers, 16-byte aligned
+    no_sink = B.kvq_cache(blocks=0x1000, block_table=None, k_ring=0x2000, v_ring=0x3000, state=0x4000)
+    assert kvq_lib.kvq_flush_residual(ctypes.byref(cfg), ctypes.byref(no_sink), None) == 1
+    odd = B.kvq_cache(blocks=0x1000, block_table=None, k_ring=0x2000, v_ring=0x3000, state=0x4000,
+                      k_sink=0x8000, v_sink=0x9004)
+    assert kvq_lib.kvq_flush_residual(ctypes.byref(cfg), ctypes.byref(odd), None) == 1
+
+
 def test_status_strings(kvq_lib):
     from quantized_kv_cache_append_amd import binding as B
     assert B.status_string(0) == "ok"
