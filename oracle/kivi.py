@@ -26,6 +26,9 @@ Written slowly and directly so that a reader can check it against the pages:
        effectivement livré les parties brouillonnes": OSCAR keeps the sink
        tokens and the recent tokens in BF16 and compresses the historical ones
        to INT2.
+  [P3''] the same encorp.ai page, section on EpiCache (long prompts and long
+       conversations are different systems problems): block-wise prefill;
+       [P4] introduction: compatible with block decoding.
 
 What the pages fix: keys are quantized per channel, values per token [P2; P4
 KIVI]; each channel carries its own min/max parameters [P4 KIVI]; codes are
@@ -47,6 +50,10 @@ of the readings list kept with the design notes):
     complete G-token blocks beyond R are quantized, so Q = G*floor(max(S-R,0)/G);
   * attention uses softmax scale 1/sqrt(d) by default, query head h' reads kv
     head floor(h'/n_g), and is evaluated in fp64 on the dequantized cache;
+  * a multi-token query (block-wise prefill or the check of T drafted
+    tokens) [P3''; P4 introduction]: the T newest tokens of a sequence of S
+    tokens are queries, and query t (0 <= t < T) attends to tokens
+    0 .. S - T + t of the same cache state (causal within the block);
   * an attention sink of P tokens (P = 0: none) [P2'; P3']: the first min(S, P)
     tokens of a sequence stay in full precision and are never quantized; the
     quantized blocks and the residual window cover the tokens after them,
@@ -365,6 +372,39 @@ def decode_attention(spec: CacheSpec, q: np.ndarray, K: np.ndarray, V: np.ndarra
             continue
         Kh, Vh = pair_cache_fp64(spec, K[b, h], V[b, h], S_b)
         out[b, h * n_g:(h + 1) * n_g] = attention_fp64(q[b, h * n_g:(h + 1) * n_g], Kh, Vh, scale)
+    return out
+
+
+def decode_attention_multi(spec: CacheSpec, q: np.ndarray, K: np.ndarray, V: np.ndarray, lengths, T: int,
+                           scale: float | None = None, pairs=None) -> np.ndarray:
+    """Attention of the T newest tokens of every sequence over the quantized
+    cache, causal within the block [P3'' block-wise prefill; P4 block decoding],
+    fp64.
+
+    q: [B][H_q][T][d] (query t of sequence b is token S_b - T + t); K, V, lengths
+    as in decode_attention. Query t sees the first S_b - T + t + 1 tokens of the
+    cache state after all S_b tokens are in (sink, dequantized blocks, ring, in
+    token order); a query with no token to see gets a zero output.
+    Returns out [B][H_q][T][d] float64.
+    """
+    B, Hq, T_, d = q.shape
+    assert T_ == T
+    n_g = spec.n_g
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    out = np.full((B, Hq, T, d), np.nan)
+    if pairs is None:
+        pairs = [(b, h) for b in range(B) for h in range(spec.num_kv_heads)]
+    for b, h in pairs:
+        S_b = int(lengths[b])
+        Kh, Vh = pair_cache_fp64(spec, K[b, h], V[b, h], S_b) if S_b > 0 else (None, None)
+        for t in range(T):
+            seen = S_b - T + t + 1
+            for hq in range(h * n_g, (h + 1) * n_g):
+                if seen <= 0:
+                    out[b, hq, t] = 0.0
+                else:
+                    out[b, hq, t] = attention_fp64(q[b, hq, t][None], Kh[:seen], Vh[:seen], scale)[0]
     return out
 
 
