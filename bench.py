@@ -14,6 +14,10 @@ Prints one JSON line on stdout; human-readable detail goes to stderr.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--sink P]
 
+With --query-tokens T a step appends T tokens per sequence and runs the
+attention of all T of them, causal within the block (kvq_decode_attention_multi:
+block-wise prefill or checking T drafted tokens).
+
 With --sink P the first P tokens of every sequence stay in full precision
 beside the quantized blocks and the ring (attention sink); the decode-partials
 time then covers the sink kernel's launch as well.
@@ -76,16 +80,16 @@ def out_bytes(w):
     return w.batch * w.num_q_heads * w.head_dim * 4
 
 
-def append_flush_bytes(w, lengths_before, record_bytes, sink=0):
-    """Algorithmic bytes of appending one token per sequence (read K, V rows, write
+def append_flush_bytes(w, lengths_before, record_bytes, sink=0, T=1):
+    """Algorithmic bytes of appending T tokens per sequence (read K, V rows, write
     them to the ring or the sink) and of flushing the blocks that leave the window
     (read the block's ring rows, write its record)."""
     row = w.head_dim * 2
     total = 0.0
     for S0 in lengths_before:
-        total += w.num_kv_heads * 2 * row * 2           # read new k, v; write to the ring
+        total += T * w.num_kv_heads * 2 * row * 2       # read new k, v; write to the ring
         q0 = quantized_prefix(max(S0 - sink, 0), w.residual, w.k_group)
-        q1 = quantized_prefix(max(S0 + 1 - sink, 0), w.residual, w.k_group)
+        q1 = quantized_prefix(max(S0 + T - sink, 0), w.residual, w.k_group)
         blocks = (q1 - q0) // w.k_group
         total += blocks * w.num_kv_heads * (w.k_group * 2 * row + record_bytes)
     return total
@@ -159,14 +163,24 @@ def quantize_rate(w, inp, lengths, dev, reps=5):
             "sample": f"one flush of every pair's whole quantized prefix ({q_tok} token-heads), median of {reps}"}
 
 
-def decode_kernel_name(w) -> str:
-    """The decode-partials kernel a workload's configuration runs."""
+# (query rows per kv head, key bits, value bits, G, G_V, dtype) of the matrix-core
+# kernel's instantiations (csrc/decode_fast_dispatch.hip)
+FAST_CONFIGS = {(4, 4, 4, 32, 32, "bf16"), (4, 2, 2, 32, 32, "bf16"), (8, 2, 2, 64, 64, "bf16"),
+                (6, 4, 2, 16, 32, "bf16"), (4, 2, 2, 32, 32, "f16"), (8, 2, 2, 32, 32, "f16"),
+                (8, 2, 2, 32, 32, "bf16"), (8, 4, 4, 32, 32, "bf16")}
+
+
+def decode_kernel_name(w, T=1) -> str:
+    """The decode-partials kernel a workload's configuration runs (T query tokens per sequence)."""
+    rows = w.n_g * T
     if w.head_dim != 128:
         return "decode_generic_kernel"
-    if w.n_g == 1:
+    if rows == 1:
         mx = (w.k_bits, w.v_bits, w.k_group, w.v_group) == (2, 2, 32, 32)
         return "decode_mx_kernel" if mx else "decode_mha_kernel"
-    return "decode_fast_kernel"
+    if (rows, w.k_bits, w.v_bits, w.k_group, w.v_group, w.dtype) in FAST_CONFIGS:
+        return "decode_fast_kernel"
+    return "decode_generic_kernel"
 
 
 def cpu_baseline(w, inp, lengths, budget_s=15.0, sink=0):
@@ -341,6 +355,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="after timing, run device-to-device copies of this many MiB (counter calibration)")
+    ap.add_argument("--query-tokens", type=int, default=1,
+                    help="tokens per sequence per step, attended causally as one block")
     ap.add_argument("--sink", type=int, default=0,
                     help="keep the first SINK tokens of every sequence in full precision (attention sink)")
     args = ap.parse_args()
@@ -364,10 +380,11 @@ def main():
     w = W.WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
     if w.layers != 1:
-        if args.sink:
-            raise SystemExit("--sink is measured on single-layer workloads")
+        if args.sink or args.query_tokens != 1:
+            raise SystemExit("--sink and --query-tokens are measured on single-layer workloads")
         return bench_layers(w, args, dev)
     P = args.sink
+    T = args.query_tokens
     torch.cuda.set_device(dev)
     lengths0 = W.sequence_lengths(w)
     total_steps = args.warmup + 2 * args.steps
@@ -381,7 +398,7 @@ def main():
         (2 * probe.k_sink.numel() * 2 if probe.k_sink is not None else 0)
     del probe
     copies = args.copies or max(1, math.ceil(3 * MALL_BYTES / per_copy))
-    steps_per_copy = math.ceil(total_steps / copies) + 1
+    steps_per_copy = (math.ceil(total_steps / copies) + 1) * T
     caches = []
     t_fill = 0.0
     for i in range(copies):
@@ -396,10 +413,17 @@ def main():
 
     # decode-step inputs, drawn before timing
     pool = 16
-    toks = [W.new_tokens(w, inp, 1, device=dev, step=s) for s in range(pool)]
-    outs = [torch.empty(w.batch, w.num_q_heads, w.head_dim, dtype=torch.float32, device=dev) for _ in caches]
+    toks = [W.new_tokens(w, inp, T, device=dev, step=s) for s in range(pool)]
+    if T > 1:   # a query per new token: [B][H_q][T][d]
+        gq = torch.Generator(device=dev).manual_seed(4242)
+        toks = [(kn, vn, torch.randn(w.batch, w.num_q_heads, T, w.head_dim, generator=gq, device=dev)
+                 .to(w.torch_dtype)) for kn, vn, _ in toks]
+    outs = [torch.empty(w.batch, w.num_q_heads, *((T,) if T > 1 else ()), w.head_dim, dtype=torch.float32,
+                        device=dev) for _ in caches]
     max_len = max(lengths0) + steps_per_copy
     ws_bytes = max(c.workspace_bytes(max_len) for c in caches)
+    if T > 1:
+        ws_bytes = max(ws_bytes, binding.kvq_workspace_size_multi(caches[0].cfg, max_len, T))
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
 
     def step(i, ev=None):
@@ -408,10 +432,14 @@ def main():
         c.append_flush(kn, vn)
         if ev is not None:
             ev[0].record()
-        c.decode_partials(q, max_seq_tokens=max_len, workspace=ws)
+        if T > 1:
+            c.decode_multi(q, out=outs[i % copies], max_seq_tokens=max_len, workspace=ws)
+        else:
+            c.decode_partials(q, max_seq_tokens=max_len, workspace=ws)
         if ev is not None:
             ev[1].record()
-        c.decode_combine(out=outs[i % copies], max_seq_tokens=max_len, workspace=ws)
+        if T == 1:
+            c.decode_combine(out=outs[i % copies], max_seq_tokens=max_len, workspace=ws)
 
     for i in range(args.warmup):
         step(i)
@@ -441,11 +469,14 @@ def main():
     for i in range(total_steps):
         ci = i % copies
         before = lens[ci]
-        after = [s + 1 for s in before]
+        after = [s + T for s in before]
+        # the T-token block reads T query rows and, when T > 1, writes its T output rows in the timed window
+        q_extra = (T - 1) * w.batch * w.num_q_heads * w.head_dim * 2
         if args.warmup <= i < args.warmup + args.steps:
-            step_bytes.append(append_flush_bytes(w, before, rec, P) + partial_bytes(w, after, rec, P) + out_bytes(w))
+            step_bytes.append(append_flush_bytes(w, before, rec, P, T) + partial_bytes(w, after, rec, P) + q_extra
+                              + T * out_bytes(w))
         elif i >= args.warmup + args.steps:
-            part_bytes.append(partial_bytes(w, after, rec, P))
+            part_bytes.append(partial_bytes(w, after, rec, P) + (q_extra + T * out_bytes(w) if T > 1 else 0))
         lens[ci] = after
 
     ms_step = ms_total / args.steps
@@ -469,7 +500,10 @@ def main():
         torch.cuda.synchronize()
         log(f"[bench] copy probe: 3 device-to-device copies of {n} bytes")
 
-    kernel = decode_kernel_name(w)
+    kernel = decode_kernel_name(w, T)
+    if T > 1:   # the multi-token call's window holds its combine launch too
+        kernel += "+combine_kernel"
+        log(f"[bench] {T} query tokens per sequence per step (causal block); the decode time covers {kernel}")
     if P > 0:   # the partials window then holds the sink kernel's launch too
         kernel = "sink_kernel+" + kernel
         log(f"[bench] sink of {P} tokens: the decode-partials time covers the sink kernel and {kernel[12:]}")
@@ -489,7 +523,7 @@ def main():
         "config": {"workload": w.name, "batch": w.batch, "num_q_heads": w.num_q_heads,
                    "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim, "seq_len": max(lengths0),
                    "input_dtype": w.dtype, "k_bits": w.k_bits, "v_bits": w.v_bits, "k_group": w.k_group,
-                   "v_group": w.v_group, "residual": w.residual, "paged": w.paged, "sink": P,
+                   "v_group": w.v_group, "residual": w.residual, "paged": w.paged, "sink": P, "query_tokens": T,
                    "cache_copies_rotated": copies},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBPS, 4),
@@ -502,7 +536,9 @@ def main():
     result["quantize"] = quantize_rate(w, inp, lengths0, dev)
     log(f"[bench] quantize: full-prefix flush {result['quantize']['us_per_flush']:.1f} us, "
         f"{result['quantize']['bytes'] / 1e6:.1f} MB -> {result['quantize']['value']:.0f} GB/s")
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and T > 1:
+        log("[bench] the oracle baseline times single-token decode; skipped for --query-tokens > 1")
+    elif not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, inp, [s + 0 for s in lengths0], sink=P)
         log(f"[bench] oracle on the host: {result['cpu_baseline']['value']:.3f} GB/s")
     print(json.dumps(result), flush=True)

@@ -20,6 +20,8 @@
  *   [P1] ai-automate.fr, "KV-cache compressé et modèles 4-bit ...", section on
  *        Minima-KV: partial attention states merged by a globally normalised
  *        online softmax.
+ *   Multi-token query: [P3], section on EpiCache (block-wise prefill); [P4],
+ *        introduction (compatible with block decoding).
  *   Attention sink: [P2], paragraph on the eviction family (StreamingLLM keeps
  *        the first tokens as attention sinks beside a recent window); [P3],
  *        section on OSCAR (sink and recent tokens kept in BF16, the history
@@ -201,6 +203,29 @@ kvq_status kvq_decode_attention(const kvq_config* cfg, const kvq_cache* cache,
                                 const void* q, float* out, float softmax_scale,
                                 int32_t max_seq_tokens, void* workspace,
                                 size_t workspace_bytes, void* stream);
+
+/* Attention of the T newest tokens of every sequence, causal within the
+ * block: block-wise prefill, or checking T drafted tokens ([P3] EpiCache
+ * section; [P4] introduction). The caller has appended the T tokens (S_b
+ * counts them, and a flush may have run); query t of sequence b
+ * (0 <= t < T) is token S_b - T + t and attends to tokens 0 .. S_b - T + t.
+ *   q:   [B][H_q][T][d] of dtype (device);
+ *   out: [B][H_q][T][d] fp32 (device); a query that sees no token (S_b < T)
+ *        gets a zero row;
+ *   T:   1 <= T, and T <= R when T > 1 (the T tokens are then all in the
+ *        ring, so every quantized block is seen by every query), else
+ *        KVQ_ERR_INVALID_ARG; (H_q / H_kv) * T <= 8, else KVQ_ERR_UNSUPPORTED;
+ *   workspace: at least kvq_workspace_size_multi(cfg, max_seq_tokens, T)
+ *        bytes.
+ * Other arguments, errors and ordering as kvq_decode_attention, which is the
+ * case T = 1. */
+kvq_status kvq_decode_attention_multi(const kvq_config* cfg, const kvq_cache* cache, const void* q, int32_t T,
+                                      float* out, float softmax_scale, int32_t max_seq_tokens, void* workspace,
+                                      size_t workspace_bytes, void* stream);
+
+/* Host only. Workspace bytes of kvq_decode_attention_multi with T queries per
+ * sequence (T = 1: kvq_workspace_size). Rejects T as that call does. */
+kvq_status kvq_workspace_size_multi(const kvq_config* cfg, int32_t max_seq_tokens, int32_t T, size_t* bytes);
 
 /* The two launches of kvq_decode_attention, callable separately (same
  * arguments and errors; the workspace carries the split states from the first

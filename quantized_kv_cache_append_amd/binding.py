@@ -20,7 +20,7 @@ KVQ_DEV_RESIDUAL_FULL, KVQ_DEV_BLOCKS_FULL, KVQ_DEV_BAD_PAGE, KVQ_DEV_BAD_COUNT,
 
 EXPORTED = ("kvq_get_layout", "kvq_workspace_size", "kvq_append", "kvq_append_flush", "kvq_flush_residual",
             "kvq_decode_attention", "kvq_decode_partials", "kvq_decode_combine", "kvq_read_device_error",
-            "kvq_status_string")
+            "kvq_status_string", "kvq_decode_attention_multi", "kvq_workspace_size_multi")
 
 
 class kvq_config(ctypes.Structure):
@@ -73,6 +73,8 @@ def load():
         "kvq_decode_combine": [cfgp, cachep, P, I32, P, SZ, P],
         "kvq_read_device_error": [cfgp, cachep, P, ctypes.POINTER(I32)],
         "kvq_status_string": [ctypes.c_int],
+        "kvq_decode_attention_multi": [cfgp, cachep, P, I32, P, F, I32, P, SZ, P],
+        "kvq_workspace_size_multi": [cfgp, I32, I32, ctypes.POINTER(SZ)],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -106,6 +108,13 @@ def kvq_workspace_size(cfg: kvq_config, max_seq_tokens: int) -> int:
     return n.value
 
 
+def kvq_workspace_size_multi(cfg: kvq_config, max_seq_tokens: int, T: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check(load().kvq_workspace_size_multi(ctypes.byref(cfg), int(max_seq_tokens), int(T), ctypes.byref(n)),
+           "kvq_workspace_size_multi")
+    return n.value
+
+
 def kvq_append(cfg, cache, k_new_ptr, v_new_ptr, n_new_ptr, n_max, stream):
     _check(load().kvq_append(ctypes.byref(cfg), ctypes.byref(cache), k_new_ptr, v_new_ptr,
                              n_new_ptr, int(n_max), stream), "kvq_append")
@@ -124,6 +133,13 @@ def kvq_decode_attention(cfg, cache, q_ptr, out_ptr, softmax_scale, max_seq_toke
     _check(load().kvq_decode_attention(ctypes.byref(cfg), ctypes.byref(cache), q_ptr, out_ptr,
                                        float(softmax_scale), int(max_seq_tokens), ws_ptr, int(ws_bytes),
                                        stream), "kvq_decode_attention")
+
+
+def kvq_decode_attention_multi(cfg, cache, q_ptr, T, out_ptr, softmax_scale, max_seq_tokens, ws_ptr, ws_bytes,
+                               stream):
+    _check(load().kvq_decode_attention_multi(ctypes.byref(cfg), ctypes.byref(cache), q_ptr, int(T), out_ptr,
+                                             float(softmax_scale), int(max_seq_tokens), ws_ptr, int(ws_bytes),
+                                             stream), "kvq_decode_attention_multi")
 
 
 def kvq_decode_partials(cfg, cache, q_ptr, softmax_scale, max_seq_tokens, ws_ptr, ws_bytes, stream):

@@ -149,6 +149,29 @@ class QuantizedKVCache:
                                _stream_handle())
         return out
 
+    def decode_multi(self, q: torch.Tensor, out: torch.Tensor | None = None, softmax_scale: float = 0.0,
+                     max_seq_tokens: int | None = None, workspace: torch.Tensor | None = None) -> torch.Tensor:
+        """Attention of the T newest tokens of every sequence, causal within the
+        block (q, out: [B][H_q][T][d]); the T tokens must already be appended."""
+        c = self.cfg
+        if not isinstance(q, torch.Tensor) or q.dim() != 4:
+            raise ValueError("q must be a [B][H_q][T][d] tensor")
+        T = q.shape[2]
+        self._check(q, (c.batch, c.num_q_heads, T, c.head_dim), self.dtype, "q")
+        if out is None:
+            out = torch.empty(c.batch, c.num_q_heads, T, c.head_dim, dtype=torch.float32, device=self.device)
+        self._check(out, (c.batch, c.num_q_heads, T, c.head_dim), torch.float32, "out")
+        msl = self.max_len_bound if max_seq_tokens is None else int(max_seq_tokens)
+        need = B.kvq_workspace_size_multi(c, msl, T)
+        if workspace is None:
+            if self._ws is None or self._ws.numel() < need:
+                self._ws = torch.empty(max(need, 16), dtype=torch.uint8, device=self.device)
+            workspace = self._ws
+        B.kvq_decode_attention_multi(c, self.cache, q.data_ptr(), T, out.data_ptr(), softmax_scale, msl,
+                                     workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                                     _stream_handle())
+        return out
+
     def _workspace(self, msl: int, workspace: torch.Tensor | None) -> torch.Tensor:
         need = B.kvq_workspace_size(self.cfg, msl)
         if workspace is not None:

@@ -81,12 +81,38 @@ kvq_status kvq_get_layout(const kvq_config* cfg, kvq_layout* out) {
   return KVQ_OK;
 }
 
-kvq_status kvq_workspace_size(const kvq_config* cfg, int32_t max_seq_tokens, size_t* bytes) {
-  const kvq_status st = validate(cfg);
+}  // extern "C"
+
+namespace {
+// Geometry of a call with T queries per (sequence, query head): the T newest
+// tokens act as T query heads each, row j of a kv head's n_g * T rows being
+// token S_b - T + j % T. T <= R keeps all of them in the ring, so every
+// quantized block is seen by every query.
+kvq_status query_geom(const kvq_config* cfg, int32_t T, Geom& g) {
+  if (T < 1 || (T > 1 && T > cfg->residual)) return KVQ_ERR_INVALID_ARG;
+  g = kvq::make_geom(*cfg);
+  if ((long long)g.ng * T > kvq::kNgMax) return KVQ_ERR_UNSUPPORTED;
+  g.Hq *= T;
+  g.ng *= T;
+  g.T = T;
+  return KVQ_OK;
+}
+}  // namespace
+
+extern "C" {
+
+kvq_status kvq_workspace_size_multi(const kvq_config* cfg, int32_t max_seq_tokens, int32_t T, size_t* bytes) {
+  kvq_status st = validate(cfg);
   if (st != KVQ_OK) return st;
   if (bytes == nullptr || max_seq_tokens < 0) return KVQ_ERR_INVALID_ARG;
-  *bytes = kvq::plan_decode(kvq::make_geom(*cfg), max_seq_tokens).ws_bytes;
+  Geom g;
+  if ((st = query_geom(cfg, T, g)) != KVQ_OK) return st;
+  *bytes = kvq::plan_decode(g, max_seq_tokens).ws_bytes;
   return KVQ_OK;
+}
+
+kvq_status kvq_workspace_size(const kvq_config* cfg, int32_t max_seq_tokens, size_t* bytes) {
+  return kvq_workspace_size_multi(cfg, max_seq_tokens, 1, bytes);
 }
 
 kvq_status kvq_append(const kvq_config* cfg, const kvq_cache* cache, const void* k_new, const void* v_new,
@@ -124,12 +150,12 @@ namespace {
 // Shared argument checks of the decode entry points; fills g, plan and scale.
 kvq_status decode_args(const kvq_config* cfg, const kvq_cache* cache, int32_t max_seq_tokens, void* workspace,
                        size_t workspace_bytes, float softmax_scale, Geom& g, kvq::DecodePlan& plan,
-                       float& scale) {
+                       float& scale, int32_t T = 1) {
   kvq_status st = validate(cfg);
   if (st != KVQ_OK) return st;
   if ((st = validate_cache(cfg, cache)) != KVQ_OK) return st;
   if (max_seq_tokens < 0 || !std::isfinite(softmax_scale)) return KVQ_ERR_INVALID_ARG;
-  g = kvq::make_geom(*cfg);
+  if ((st = query_geom(cfg, T, g)) != KVQ_OK) return st;
   plan = kvq::plan_decode(g, max_seq_tokens);
   if (workspace == nullptr || workspace_bytes < plan.ws_bytes) return KVQ_ERR_WORKSPACE;
   scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt((float)g.d);
@@ -145,6 +171,21 @@ kvq_status kvq_decode_attention(const kvq_config* cfg, const kvq_cache* cache, c
   kvq::DecodePlan plan;
   float scale;
   const kvq_status st = decode_args(cfg, cache, max_seq_tokens, workspace, workspace_bytes, softmax_scale, g, plan, scale);
+  if (st != KVQ_OK) return st;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (kvq::launch_decode_partials(g, *cache, q, scale, plan, workspace, s) != hipSuccess) return KVQ_ERR_LAUNCH;
+  return launched(kvq::launch_decode_combine(g, *cache, out, plan, workspace, s));
+}
+
+kvq_status kvq_decode_attention_multi(const kvq_config* cfg, const kvq_cache* cache, const void* q, int32_t T,
+                                      float* out, float softmax_scale, int32_t max_seq_tokens, void* workspace,
+                                      size_t workspace_bytes, void* stream) {
+  if (q == nullptr || out == nullptr) return KVQ_ERR_INVALID_ARG;
+  Geom g;
+  kvq::DecodePlan plan;
+  float scale;
+  const kvq_status st =
+      decode_args(cfg, cache, max_seq_tokens, workspace, workspace_bytes, softmax_scale, g, plan, scale, T);
   if (st != KVQ_OK) return st;
   const hipStream_t s = static_cast<hipStream_t>(stream);
   if (kvq::launch_decode_partials(g, *cache, q, scale, plan, workspace, s) != hipSuccess) return KVQ_ERR_LAUNCH;

@@ -28,7 +28,11 @@ struct Geom {
   int k_words;   // uint32 words of K codes per token: d*kb/32
   int v_words;   // uint32 words of V codes per channel: G*vb/32
   int P;         // sink: leading tokens of a sequence kept in full precision
+  int T;         // queries per (sequence, query head): the T newest tokens, causal; Hq and ng count them
 };
+
+// Query rows per kv head one launch serves (n_g times T).
+constexpr int kNgMax = 8;
 
 // Fill the derived fields of a Geom from a validated config.
 inline Geom make_geom(const kvq_config& c) {
@@ -48,6 +52,7 @@ inline Geom make_geom(const kvq_config& c) {
   g.rec_vz = g.rec_vs + 2 * (g.d / g.GV) * g.G;
   g.rec_bytes = g.rec_vz + 2 * (g.d / g.GV) * g.G;
   g.P = c.sink;
+  g.T = 1;
   return g;
 }
 

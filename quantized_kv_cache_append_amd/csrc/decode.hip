@@ -37,7 +37,6 @@ namespace kvq {
 namespace {
 
 constexpr int kWaves = 4;
-constexpr int kNgMax = 8;
 constexpr int kRingAll = 1 << 30;   // ring tokens per ring unit of the generic kernel: all of them
 
 template <int D, bool BF16>
@@ -89,7 +88,7 @@ __global__ __launch_bounds__(256) void decode_generic_kernel(
         const float bm = wave_max(s);
         const float mn = fmaxf(m[j], bm);
         const float alpha = (m[j] == -INFINITY) ? 0.f : exp2f(m[j] - mn);
-        const float p = valid ? exp2f(s - mn) : 0.f;
+        const float p = (valid && s != -INFINITY) ? exp2f(s - mn) : 0.f;   // (-inf: a masked token)
         l[j] = l[j] * alpha + wave_sum(p);
         m[j] = mn;
 #pragma unroll
@@ -193,6 +192,11 @@ __global__ __launch_bounds__(256) void decode_generic_kernel(
             for (int j = 0; j < kNgMax; ++j)
               if (j < ng) sc[j] += qt[j * D + c] * x;
           }
+        }
+        if (g.T > 1) {   // query row j is token S - T + j % T (after the sink): later tokens are masked
+#pragma unroll
+          for (int j = 0; j < kNgMax; ++j)
+            if (j < ng && t > S - g.T + j % g.T) sc[j] = -INFINITY;
         }
         softmax_tile(sc, valid);
         const int nt = min(64, r1 - t0);
@@ -327,7 +331,9 @@ __global__ __launch_bounds__(64 * kCombineWaves) void sink_kernel(Geom g, const 
   const int row = blockIdx.x * kCombineWaves + wave;
   if (row >= g.B * g.Hq) return;
   const int b = row / g.Hq, h = (row % g.Hq) / g.ng;
-  const int n = __builtin_amdgcn_readfirstlane(min(state[4 * b + kStateS], g.P));
+  // row j of a T-token query block is token S_b - T + j % T: it sees sink rows up to there
+  const int S_b = state[4 * b + kStateS];
+  const int n = __builtin_amdgcn_readfirstlane(max(min(min(S_b, g.P), S_b - g.T + (row % g.Hq) % g.ng % g.T + 1), 0));
   float* qs = lq[wave];
 #pragma unroll
   for (int k = 0; k < CPL; ++k) qs[CPL * lane + k] = in_to_f32<BF16>(q[(size_t)row * D + CPL * lane + k]) * qscale;

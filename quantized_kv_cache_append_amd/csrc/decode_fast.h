@@ -301,14 +301,16 @@ struct WaveLds {
 // The full-precision ring tokens [t_begin, t_end) of one (sequence, kv head), in
 // chunks of 32: scores on MFMA (A = key rows as stored, B = query hi/lo),
 // online softmax across the chunks, P.V on the vector ALUs. Needs the scaled
-// query in L.qs.
+// query in L.qs. Query row n sees ring tokens up to last + n % T (a block of
+// T query tokens is causal; T = 1: last = the ring's last token).
 // ---------------------------------------------------------------------------------
 template <class C>
 __device__ __forceinline__ void ring_unit(const Geom& g, const WaveLds<C>& L, const uint16_t* __restrict__ k_ring,
                                           const uint16_t* __restrict__ v_ring, int pair, int t_begin, int t_end,
-                                          float* __restrict__ out_part) {
+                                          int last, float* __restrict__ out_part) {
   constexpr int NG = C::NG, D = C::D;
   const int lane = threadIdx.x & 63, gq = lane >> 4, n = lane & 15;
+  const int last_n = last + n % g.T;   // this lane's head column sees tokens up to here
   // B operand: q' hi/lo, column n = head, k position e of k-step ks = channel 32gq + 8ks + e
   uint4 bq_hi[4], bq_lo[4];
   float escale = 1.0f;
@@ -376,7 +378,7 @@ __device__ __forceinline__ void ring_unit(const Geom& g, const WaveLds<C>& L, co
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int tok = t0 + 16 * tt + 4 * gq + i;   // D row = token, column n = head
-        s[tt][i] = (n < NG && tok < t1) ? acc[i] * inv_escale : -INFINITY;
+        s[tt][i] = (n < NG && tok < t1 && tok <= last_n) ? acc[i] * inv_escale : -INFINITY;
       }
     }
     float mx = -INFINITY;
@@ -846,7 +848,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   while (u < units && u < plan[kPlanSec]) {
     const Span sp = span_of(u);
     load_query<C>(g, L, q, qscale, sp.b, sp.h);
-    ring_unit<C>(g, L, k_ring, v_ring, sp.b * g.Hkv + sp.h, sp.begin, sp.end, ws + (size_t)u * NG * (D + 2));
+    // ring tokens count after the sink; the last query token is the ring's last, S' - 1
+    const int s_post = plan[plan_seq_off(g.B) + g.B + sp.b];
+    ring_unit<C>(g, L, k_ring, v_ring, sp.b * g.Hkv + sp.h, sp.begin, sp.end, s_post - g.T,
+                 ws + (size_t)u * NG * (D + 2));
     u = claim(claimed);
     claimed = issue();
   }

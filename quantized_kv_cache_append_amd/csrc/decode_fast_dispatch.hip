@@ -59,10 +59,16 @@ const FastEntry* table() {
       KVQ_MFMA(4, 2, 2, 32, 32, true),     // GQA 4, INT2
       KVQ_MFMA(8, 2, 2, 64, 64, true),     // GQA 8, INT2, G = G_V = 64 (a 70B-shaped layer)
       KVQ_MFMA(6, 4, 2, 16, 32, true),     // GQA 6, INT4 keys / INT2 values, 16-token pages
+      // query blocks of T tokens (T * n_g query rows): MHA fp16 INT2 with T = 4 and 8,
+      // GQA 4 INT2 / INT4 with T = 2
+      KVQ_MFMA(4, 2, 2, 32, 32, false),
+      KVQ_MFMA(8, 2, 2, 32, 32, false),
+      KVQ_MFMA(8, 2, 2, 32, 32, true),
+      KVQ_MFMA(8, 4, 4, 32, 32, true),
   };
   return kFast;
 }
-constexpr int kEntries = 16;
+constexpr int kEntries = 24;
 #undef KVQ_MFMA
 #undef KVQ_MHA
 #undef KVQ_MX

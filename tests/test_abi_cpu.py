@@ -148,6 +148,28 @@ def test_sink_layout_and_checks(kvq_lib):
     assert kvq_lib.kvq_flush_residual(ctypes.byref(cfg), ctypes.byref(odd), None) == 1
 
 
+def test_multi_token_query_checks(kvq_lib):
+    from quantized_kv_cache_append_amd import binding as B
+    cfg = _cfg(B)   # MHA, R = 128
+    assert B.kvq_workspace_size_multi(cfg, 4096, 1) == B.kvq_workspace_size(cfg, 4096)
+    assert B.kvq_workspace_size_multi(cfg, 4096, 8) > B.kvq_workspace_size(cfg, 4096)   # 8 query rows per kv head
+    n = ctypes.c_size_t(0)
+    assert kvq_lib.kvq_workspace_size_multi(ctypes.byref(cfg), 4096, 0, ctypes.byref(n)) == B.KVQ_ERR_INVALID_ARG
+    assert kvq_lib.kvq_workspace_size_multi(ctypes.byref(cfg), 4096, 9, ctypes.byref(n)) == B.KVQ_ERR_UNSUPPORTED
+    gqa = _cfg(B, num_q_heads=32, num_kv_heads=8)   # n_g = 4: at most 2 tokens
+    assert kvq_lib.kvq_workspace_size_multi(ctypes.byref(gqa), 4096, 2, ctypes.byref(n)) == B.KVQ_OK
+    assert kvq_lib.kvq_workspace_size_multi(ctypes.byref(gqa), 4096, 3, ctypes.byref(n)) == B.KVQ_ERR_UNSUPPORTED
+    short = _cfg(B, residual=2, res_capacity=34)   # T > R: the block would reach the quantized part
+    assert kvq_lib.kvq_workspace_size_multi(ctypes.byref(short), 4096, 3, ctypes.byref(n)) == B.KVQ_ERR_INVALID_ARG
+    ok = B.kvq_cache(blocks=0x1000, block_table=None, k_ring=0x2000, v_ring=0x3000, state=0x4000)
+    need = B.kvq_workspace_size_multi(cfg, 4096, 4)
+    assert kvq_lib.kvq_decode_attention_multi(ctypes.byref(cfg), ctypes.byref(ok), ctypes.c_void_p(0x5000), 4,
+                                              ctypes.c_void_p(0x6000), ctypes.c_float(0.0), 4096,
+                                              ctypes.c_void_p(0x7000), need - 1, None) == B.KVQ_ERR_WORKSPACE
+    assert kvq_lib.kvq_decode_attention_multi(ctypes.byref(cfg), ctypes.byref(ok), None, 4, ctypes.c_void_p(0x6000),
+                                              ctypes.c_float(0.0), 4096, ctypes.c_void_p(0x7000), need, None) == 1
+
+
 def test_status_strings(kvq_lib):
     from quantized_kv_cache_append_amd import binding as B
     assert B.status_string(0) == "ok"
