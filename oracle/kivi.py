@@ -26,6 +26,10 @@ Written slowly and directly so that a reader can check it against the pages:
        effectivement livré les parties brouillonnes": OSCAR keeps the sink
        tokens and the recent tokens in BF16 and compresses the historical ones
        to INT2.
+  [P1'] the same ai-automate.fr page, section "Minima-KV : la compression sans
+       éviction": a mixed-format hierarchy in which recent and protected
+       pages stay in FP8 and older pages are compacted to low bits, partial
+       attention states of both merged by one online softmax.
   [P3''] the same encorp.ai page, section on EpiCache (long prompts and long
        conversations are different systems problems): block-wise prefill;
        [P4] introduction: compatible with block decoding.
@@ -54,6 +58,11 @@ of the readings list kept with the design notes):
     tokens) [P3''; P4 introduction]: the T newest tokens of a sequence of S
     tokens are queries, and query t (0 <= t < T) attends to tokens
     0 .. S - T + t of the same cache state (causal within the block);
+  * an FP8 tier of W blocks (W = 0: none) [P1']: the W most recent quantized
+    blocks of a sequence are also kept in FP8 (e4m3, one fp16 scale per token
+    row, formula F8 below) and attention reads them there; older blocks are
+    read from their low-bit records, which are still quantized from the
+    original values;
   * an attention sink of P tokens (P = 0: none) [P2'; P3']: the first min(S, P)
     tokens of a sequence stay in full precision and are never quantized; the
     quantized blocks and the residual window cover the tokens after them,
@@ -87,6 +96,7 @@ class CacheSpec:
     res_capacity: int     # ring slots per (sequence, kv head)
     dtype: str            # "f16" or "bf16"
     sink: int = 0         # P: leading tokens kept in full precision (attention sink)
+    fp8_blocks: int = 0   # W: most recent quantized blocks also kept (and read) in FP8
 
     @property
     def n_g(self) -> int:
@@ -259,6 +269,79 @@ def bytes_to_block(spec: CacheSpec, rec: np.ndarray):
     return out
 
 
+# ---------------------------------------------------------------------------
+# FP8 tier [P1' Minima-KV: recent pages in FP8]. Formula F8, per token row x
+# (d values), every step an fp32 IEEE operation rounded to nearest even:
+#   s = fp16(max|x| / 448);  s == 0 -> all codes 0;
+#   else code_c = e4m3(clamp(fp32(x_c / s), -448, 448)), e4m3 rounding to
+#   nearest with ties to the even code; x_hat_c = e4m3_value(code_c) * s.
+# e4m3: sign, 4 exponent bits (bias 7), 3 mantissa bits; exponent 0 is
+# subnormal (m/8 * 2^-6); 0x7f / 0xff are NaN and never produced; 448 is the
+# largest finite magnitude.
+# ---------------------------------------------------------------------------
+def e4m3_value(code) -> np.ndarray:
+    """float64 value of e4m3 codes (uint8 array)."""
+    c = np.asarray(code, np.int64)
+    e, m = (c >> 3) & 15, c & 7
+    mag = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1 + m / 8.0) * np.exp2(e - 7.0))
+    return np.where(c & 0x80, -mag, mag)
+
+
+_E4M3_POS = e4m3_value(np.arange(0x7f))   # codes 0x00 .. 0x7e, increasing
+
+
+def e4m3_encode(y) -> np.ndarray:
+    """Nearest e4m3 code (ties to the even code) of float values |y| <= 448."""
+    y = np.asarray(y, np.float64)
+    a = np.abs(y)
+    hi = np.clip(np.searchsorted(_E4M3_POS, a), 0, 0x7e)
+    lo = np.clip(hi - 1, 0, 0x7e)
+    dlo, dhi = a - _E4M3_POS[lo], _E4M3_POS[hi] - a
+    mag = np.where(dhi < dlo, hi, np.where(dlo < dhi, lo, np.where(lo % 2 == 0, lo, hi)))
+    return (mag | np.where(np.signbit(y), 0x80, 0)).astype(np.uint8)
+
+
+def quantize_fp8_rows(x: np.ndarray):
+    """Formula F8 on every row of x (float32 [n][d]): (codes uint8 [n][d], s16 [n])."""
+    x = np.asarray(x, F32)
+    a = np.max(np.abs(x), axis=1)
+    s16 = (a / F32(448.0)).astype(F32).astype(np.float16)
+    s = s16.astype(F32)
+    y = np.zeros_like(x)
+    nz = s != 0
+    y[nz] = np.clip(x[nz] / s[nz, None], F32(-448.0), F32(448.0))
+    codes = e4m3_encode(y)
+    codes[~nz] = 0
+    return codes, s16
+
+
+def fp8_record(kblk: np.ndarray, vblk: np.ndarray) -> np.ndarray:
+    """FP8 record of one block, as bytes: K codes u8 [G][d] (token-major), K
+    scales fp16 [G], V codes u8 [G][d], V scales fp16 [G]."""
+    kc, ks = quantize_fp8_rows(kblk)
+    vc, vs = quantize_fp8_rows(vblk)
+    return np.concatenate([kc.ravel(), ks.view(np.uint8), vc.ravel(), vs.view(np.uint8)])
+
+
+def fp8_record_bytes(spec: CacheSpec) -> int:
+    return 2 * spec.k_group * spec.head_dim + 4 * spec.k_group
+
+
+def dequantize_fp8_block(kblk: np.ndarray, vblk: np.ndarray):
+    """fp64 [G][d] key and value reconstructions of one block through F8."""
+    out = []
+    for x in (kblk, vblk):
+        c, s = quantize_fp8_rows(x)
+        out.append(e4m3_value(c) * s.astype(np.float64)[:, None])
+    return out[0], out[1]
+
+
+def fp8_window(spec: CacheSpec, S: int):
+    """Quantized blocks of a sequence of S tokens read through FP8: [f0, nblk)."""
+    nblk = stream_split(spec, S)[1] // spec.k_group
+    return nblk - min(nblk, spec.fp8_blocks), nblk
+
+
 def dequantize_block(spec: CacheSpec, sec):
     """fp64 [G][d] key and value reconstructions of one block."""
     G, d, gv = spec.k_group, spec.head_dim, spec.v_group
@@ -333,15 +416,20 @@ def attention_fp64(q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float) ->
 
 def pair_cache_fp64(spec: CacheSpec, K: np.ndarray, V: np.ndarray, S_b: int):
     """The attention inputs of one (sequence, kv head), in token order: the exact
-    sink tokens, the dequantized blocks, then the exact residual tokens.
+    sink tokens, the dequantized blocks (the W newest through F8), then the
+    exact residual tokens.
     Returns (Khat, Vhat) [S_b][d]."""
     G, P = spec.k_group, spec.sink
     s, Q, _ = stream_split(spec, S_b)
     ks = [np.asarray(K[:s], np.float64)]
     vs = [np.asarray(V[:s], np.float64)]
+    f0 = Q // G - min(Q // G, spec.fp8_blocks)   # blocks from here on are read through FP8
     for j in range(Q // G):
         lo = P + j * G
-        kh, vh = dequantize_block(spec, quantize_block(spec, K[lo:lo + G], V[lo:lo + G]))
+        if j >= f0:
+            kh, vh = dequantize_fp8_block(K[lo:lo + G], V[lo:lo + G])
+        else:
+            kh, vh = dequantize_block(spec, quantize_block(spec, K[lo:lo + G], V[lo:lo + G]))
         ks.append(kh)
         vs.append(vh)
     ks.append(np.asarray(K[P + Q:S_b], np.float64))
