@@ -18,6 +18,9 @@ With --query-tokens T a step appends T tokens per sequence and runs the
 attention of all T of them, causal within the block (kvq_decode_attention_multi:
 block-wise prefill or checking T drafted tokens).
 
+With --fp8-blocks W the W most recent quantized blocks of every (sequence, kv
+head) are also kept as FP8 records and decode reads them there (FP8 tier).
+
 With --sink P the first P tokens of every sequence stay in full precision
 beside the quantized blocks and the ring (attention sink); the decode-partials
 time then covers the sink kernel's launch as well.
@@ -62,16 +65,22 @@ def quantized_prefix(S, R, G):
     return G * (max(S - R, 0) // G)
 
 
-def partial_bytes(w, lengths, record_bytes, sink=0):
+def fp8_record_bytes(w):
+    return 2 * w.k_group * w.head_dim + 4 * w.k_group
+
+
+def partial_bytes(w, lengths, record_bytes, sink=0, fp8_blocks=0):
     """Algorithmic HBM bytes the decode-partials launch must move: packed codes and
-    fp16 scale/zero of every quantized token, the full-precision ring and sink
-    tokens, q."""
+    fp16 scale/zero of every quantized token (the FP8 records of the FP8 tier's
+    blocks instead), the full-precision ring and sink tokens, q."""
     per_tok = record_bytes / w.k_group
     total = 0.0
     for S in lengths:
         post = max(S - sink, 0)
         Q = quantized_prefix(post, w.residual, w.k_group)
-        total += w.num_kv_heads * (Q * per_tok + (S - Q) * w.head_dim * 2 * 2)
+        n8 = min(Q // w.k_group, fp8_blocks)
+        total += w.num_kv_heads * ((Q - n8 * w.k_group) * per_tok + n8 * fp8_record_bytes(w)
+                                   + (S - Q) * w.head_dim * 2 * 2)
     total += w.batch * w.num_q_heads * w.head_dim * 2
     return total
 
@@ -80,7 +89,7 @@ def out_bytes(w):
     return w.batch * w.num_q_heads * w.head_dim * 4
 
 
-def append_flush_bytes(w, lengths_before, record_bytes, sink=0, T=1):
+def append_flush_bytes(w, lengths_before, record_bytes, sink=0, T=1, fp8_blocks=0):
     """Algorithmic bytes of appending T tokens per sequence (read K, V rows, write
     them to the ring or the sink) and of flushing the blocks that leave the window
     (read the block's ring rows, write its record)."""
@@ -92,6 +101,7 @@ def append_flush_bytes(w, lengths_before, record_bytes, sink=0, T=1):
         q1 = quantized_prefix(max(S0 + T - sink, 0), w.residual, w.k_group)
         blocks = (q1 - q0) // w.k_group
         total += blocks * w.num_kv_heads * (w.k_group * 2 * row + record_bytes)
+        total += min(blocks, fp8_blocks) * w.num_kv_heads * fp8_record_bytes(w)   # their FP8 records
     return total
 
 
@@ -357,6 +367,8 @@ def main():
                     help="after timing, run device-to-device copies of this many MiB (counter calibration)")
     ap.add_argument("--query-tokens", type=int, default=1,
                     help="tokens per sequence per step, attended causally as one block")
+    ap.add_argument("--fp8-blocks", type=int, default=0,
+                    help="keep the W most recent quantized blocks also as FP8 records, read by decode")
     ap.add_argument("--sink", type=int, default=0,
                     help="keep the first SINK tokens of every sequence in full precision (attention sink)")
     args = ap.parse_args()
@@ -380,10 +392,11 @@ def main():
     w = W.WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
     if w.layers != 1:
-        if args.sink or args.query_tokens != 1:
-            raise SystemExit("--sink and --query-tokens are measured on single-layer workloads")
+        if args.sink or args.query_tokens != 1 or args.fp8_blocks:
+            raise SystemExit("--sink, --query-tokens and --fp8-blocks are measured on single-layer workloads")
         return bench_layers(w, args, dev)
     P = args.sink
+    W8 = args.fp8_blocks
     T = args.query_tokens
     torch.cuda.set_device(dev)
     lengths0 = W.sequence_lengths(w)
@@ -392,17 +405,18 @@ def main():
 
     inp = W.make_layer(w, device=dev, lengths=lengths0)
     chunk = 512
-    probe = cache_for_workload(w, lengths0, chunk, extra_tokens=0, device=dev, sink=P)
+    probe = cache_for_workload(w, lengths0, chunk, extra_tokens=0, device=dev, sink=P, fp8_blocks=W8)
     rec = probe.record_bytes
     per_copy = probe.blocks.numel() + 2 * probe.k_ring.numel() * 2 + \
-        (2 * probe.k_sink.numel() * 2 if probe.k_sink is not None else 0)
+        (2 * probe.k_sink.numel() * 2 if probe.k_sink is not None else 0) + \
+        (probe.fp8.numel() if probe.fp8 is not None else 0)
     del probe
     copies = args.copies or max(1, math.ceil(3 * MALL_BYTES / per_copy))
     steps_per_copy = (math.ceil(total_steps / copies) + 1) * T
     caches = []
     t_fill = 0.0
     for i in range(copies):
-        c = cache_for_workload(w, lengths0, chunk, extra_tokens=steps_per_copy, device=dev, sink=P)
+        c = cache_for_workload(w, lengths0, chunk, extra_tokens=steps_per_copy, device=dev, sink=P, fp8_blocks=W8)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         c.prefill(inp.k, inp.v, lengths0, chunk)
@@ -473,10 +487,10 @@ def main():
         # the T-token block reads T query rows and, when T > 1, writes its T output rows in the timed window
         q_extra = (T - 1) * w.batch * w.num_q_heads * w.head_dim * 2
         if args.warmup <= i < args.warmup + args.steps:
-            step_bytes.append(append_flush_bytes(w, before, rec, P, T) + partial_bytes(w, after, rec, P) + q_extra
-                              + T * out_bytes(w))
+            step_bytes.append(append_flush_bytes(w, before, rec, P, T, W8) + partial_bytes(w, after, rec, P, W8)
+                              + q_extra + T * out_bytes(w))
         elif i >= args.warmup + args.steps:
-            part_bytes.append(partial_bytes(w, after, rec, P) + (q_extra + T * out_bytes(w) if T > 1 else 0))
+            part_bytes.append(partial_bytes(w, after, rec, P, W8) + (q_extra + T * out_bytes(w) if T > 1 else 0))
         lens[ci] = after
 
     ms_step = ms_total / args.steps
@@ -504,9 +518,12 @@ def main():
     if T > 1:   # the multi-token call's window holds its combine launch too
         kernel += "+combine_kernel"
         log(f"[bench] {T} query tokens per sequence per step (causal block); the decode time covers {kernel}")
-    if P > 0:   # the partials window then holds the sink kernel's launch too
+    if W8 > 0:   # the partials window then holds the FP8 tier's launch too
+        kernel = "fp8_kernel+" + kernel
+        log(f"[bench] FP8 tier of {W8} blocks: the decode-partials time covers the FP8 kernel too")
+    if P > 0:   # and the sink kernel's
         kernel = "sink_kernel+" + kernel
-        log(f"[bench] sink of {P} tokens: the decode-partials time covers the sink kernel and {kernel[12:]}")
+        log(f"[bench] sink of {P} tokens: the decode-partials time covers the sink kernel too")
     result = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -524,6 +541,7 @@ def main():
                    "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim, "seq_len": max(lengths0),
                    "input_dtype": w.dtype, "k_bits": w.k_bits, "v_bits": w.v_bits, "k_group": w.k_group,
                    "v_group": w.v_group, "residual": w.residual, "paged": w.paged, "sink": P, "query_tokens": T,
+                   "fp8_blocks": W8,
                    "cache_copies_rotated": copies},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBPS, 4),

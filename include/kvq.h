@@ -20,6 +20,9 @@
  *   [P1] ai-automate.fr, "KV-cache compressé et modèles 4-bit ...", section on
  *        Minima-KV: partial attention states merged by a globally normalised
  *        online softmax.
+ *   FP8 tier: [P1], section on Minima-KV (recent and protected pages kept in
+ *        FP8, older pages compacted to low bits, one online softmax over
+ *        both).
  *   Multi-token query: [P3], section on EpiCache (block-wise prefill); [P4],
  *        introduction (compatible with block decoding).
  *   Attention sink: [P2], paragraph on the eviction family (StreamingLLM keeps
@@ -44,6 +47,19 @@
  *   - after kvq_flush_residual, R <= S_b - P - Q_b < R + G whenever
  *     S_b - P >= R, i.e. Q_b = G * floor(max(S_b - P - R, 0) / G).
  * With P = 0 the sink is absent and everything else reads as written.
+ *
+ * FP8 tier (kvq_config.fp8_blocks = W > 0): the W most recent quantized
+ * blocks of each (sequence, kv head), j >= n_b - W with n_b = Q_b / G, also
+ * have an FP8 record in the `fp8` store, and attention reads them there
+ * instead of their low-bit records (which are written as always). FP8 record
+ * of a block (formula F8 per token row x of d values, fp32 IEEE steps, round
+ * to nearest even: s = fp16(max|x| / 448); s == 0 -> codes 0; else code_c =
+ * e4m3(clamp(x_c / s, -448, 448)); x_hat = e4m3_value(code) * s):
+ *   K codes  uint8 [G][d]  e4m3, token-major
+ *   K scale  fp16  [G]
+ *   V codes  uint8 [G][d]
+ *   V scale  fp16  [G]
+ * Store: [B][H_kv][W] records; block j of a pair lives in slot j mod W.
  *
  * Record of one block (little-endian, sections in this order, no padding):
  *   K codes  uint32 [G][d*k_bits/32]   token-major; word w of token t holds
@@ -123,6 +139,7 @@ typedef struct {
   int32_t num_pages;      /* 0: dense store; > 0: paged store with this many pages         */
   int32_t dtype;          /* KVQ_F16 or KVQ_BF16: K, V, q and the ring                     */
   int32_t sink;           /* P >= 0: leading tokens of every sequence kept in full precision */
+  int32_t fp8_blocks;     /* W >= 0: most recent quantized blocks also kept, and read, in FP8 */
 } kvq_config;
 
 typedef struct {
@@ -132,6 +149,8 @@ typedef struct {
   size_t ring;            /* bytes of EACH of k_ring and v_ring: [B][H_kv][res_capacity][d]  */
   size_t state;           /* bytes of the state words; must be zeroed before first use       */
   size_t sink;            /* bytes of EACH of k_sink and v_sink: [B][H_kv][P][d]; 0 if P = 0 */
+  size_t fp8_record;      /* bytes of one FP8 record: 2*G*d + 4*G; 0 if W = 0               */
+  size_t fp8;             /* bytes of the FP8 store: [B][H_kv][W] records; 0 if W = 0        */
 } kvq_layout;
 
 typedef struct {
@@ -144,6 +163,7 @@ typedef struct {
                                   zero-filled by the caller for an empty cache                 */
   void* k_sink;                /* [B][H_kv][P][d] of dtype, 16-byte aligned; NULL if P = 0     */
   void* v_sink;
+  void* fp8;                   /* FP8 store, 16-byte aligned; NULL if W = 0                    */
 } kvq_cache;
 
 /* Host only. Validates cfg and fills the byte sizes of every cache buffer.
@@ -170,9 +190,11 @@ kvq_status kvq_append(const kvq_config* cfg, const kvq_cache* cache,
                       const int32_t* n_new, int32_t n_max, void* stream);
 
 /* Quantize and pack the oldest complete G-token blocks of every ring so that
- * R <= S_b - Q_b < R + G afterwards ([P4] KIVI per-channel keys / per-token
+ * R <= S_b - P - Q_b < R + G afterwards ([P4] KIVI per-channel keys / per-token
  * values; [P4] innovation 3 dense packing; innovation 4 residual window).
- * Does nothing for sequences whose ring holds fewer than R + G tokens. */
+ * With W > 0, the blocks of the call that end up among the W most recent also
+ * get their FP8 record. Does nothing for sequences whose ring holds fewer than
+ * R + G tokens. */
 kvq_status kvq_flush_residual(const kvq_config* cfg, const kvq_cache* cache, void* stream);
 
 /* kvq_append followed by kvq_flush_residual, as one launch when n_max <= 64
@@ -194,7 +216,8 @@ kvq_status kvq_append_flush(const kvq_config* cfg, const kvq_cache* cache,
  *   workspace: device scratch of at least kvq_workspace_size(cfg, max_seq_tokens)
  *              bytes; its contents need no initialisation.
  * A sequence with S_b == 0 gets a zero output. The sink tokens of a sequence
- * (P > 0) enter as one more partial state per (sequence, query head). The
+ * (P > 0) and its FP8 blocks (W > 0) each enter as one more partial state per
+ * (sequence, query head). The
  * launch hands out its work
  * through counters in the cache's state words (and re-arms them when it ends),
  * so decode calls on one cache, like calls that share a workspace, must be

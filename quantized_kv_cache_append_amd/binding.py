@@ -26,17 +26,18 @@ EXPORTED = ("kvq_get_layout", "kvq_workspace_size", "kvq_append", "kvq_append_fl
 class kvq_config(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "batch", "num_q_heads", "num_kv_heads", "head_dim", "k_bits", "v_bits", "k_group", "v_group",
-        "residual", "res_capacity", "max_blocks", "num_pages", "dtype", "sink")]
+        "residual", "res_capacity", "max_blocks", "num_pages", "dtype", "sink", "fp8_blocks")]
 
 
 class kvq_layout(ctypes.Structure):
-    _fields_ = [(n, ctypes.c_size_t) for n in ("record", "blocks", "block_table", "ring", "state", "sink")]
+    _fields_ = [(n, ctypes.c_size_t) for n in ("record", "blocks", "block_table", "ring", "state", "sink",
+                                               "fp8_record", "fp8")]
 
 
 class kvq_cache(ctypes.Structure):
     _fields_ = [("blocks", ctypes.c_void_p), ("block_table", ctypes.c_void_p),
                 ("k_ring", ctypes.c_void_p), ("v_ring", ctypes.c_void_p), ("state", ctypes.c_void_p),
-                ("k_sink", ctypes.c_void_p), ("v_sink", ctypes.c_void_p)]
+                ("k_sink", ctypes.c_void_p), ("v_sink", ctypes.c_void_p), ("fp8", ctypes.c_void_p)]
 
 
 class KVQError(RuntimeError):

@@ -30,12 +30,15 @@ class QuantizedKVCache:
     `num_pages`; one page holds one block of every kv head. `sink` > 0 keeps
     the first `sink` tokens of every sequence in full precision (attention
     sink); the quantized blocks and the ring then hold the tokens after them.
+    `fp8_blocks` > 0 keeps the most recent `fp8_blocks` quantized blocks of
+    every (sequence, kv head) also as FP8 records, which decode reads instead.
     """
 
     def __init__(self, batch: int, num_q_heads: int, num_kv_heads: int, head_dim: int, *,
                  k_bits: int, v_bits: int, k_group: int, v_group: int, residual: int,
                  dtype=torch.float16, max_tokens: int | None = None, res_capacity: int | None = None,
-                 page_table: torch.Tensor | None = None, num_pages: int = 0, sink: int = 0, device="cuda"):
+                 page_table: torch.Tensor | None = None, num_pages: int = 0, sink: int = 0, fp8_blocks: int = 0,
+                 device="cuda"):
         if dtype not in _DTYPES:
             raise TypeError(f"dtype must be float16 or bfloat16, got {dtype}")
         self.device = torch.device(device)
@@ -55,7 +58,8 @@ class QuantizedKVCache:
         self.cfg = B.kvq_config(batch=batch, num_q_heads=num_q_heads, num_kv_heads=num_kv_heads,
                                 head_dim=head_dim, k_bits=k_bits, v_bits=v_bits, k_group=k_group,
                                 v_group=v_group, residual=residual, res_capacity=res_capacity,
-                                max_blocks=max_blocks, num_pages=num_pages, dtype=_DTYPES[dtype], sink=sink)
+                                max_blocks=max_blocks, num_pages=num_pages, dtype=_DTYPES[dtype], sink=sink,
+                                fp8_blocks=fp8_blocks)
         self.layout = B.kvq_get_layout(self.cfg)
         dev = self.device
         self.blocks = torch.zeros(self.layout.blocks, dtype=torch.uint8, device=dev)
@@ -65,6 +69,7 @@ class QuantizedKVCache:
         self.v_ring = torch.zeros(ring_shape, dtype=dtype, device=dev)
         self.state = torch.zeros(self.layout.state // 4, dtype=torch.int32, device=dev)
         self.k_sink = self.v_sink = None
+        self.fp8 = torch.zeros(self.layout.fp8, dtype=torch.uint8, device=dev) if fp8_blocks > 0 else None
         if sink > 0:
             sink_shape = (batch, num_kv_heads, sink, head_dim)
             self.k_sink = torch.zeros(sink_shape, dtype=dtype, device=dev)
@@ -74,7 +79,8 @@ class QuantizedKVCache:
             block_table=self.page_table.data_ptr() if self.page_table is not None else None,
             k_ring=self.k_ring.data_ptr(), v_ring=self.v_ring.data_ptr(), state=self.state.data_ptr(),
             k_sink=self.k_sink.data_ptr() if self.k_sink is not None else None,
-            v_sink=self.v_sink.data_ptr() if self.v_sink is not None else None)
+            v_sink=self.v_sink.data_ptr() if self.v_sink is not None else None,
+            fp8=self.fp8.data_ptr() if self.fp8 is not None else None)
         self.max_len_bound = 0          # host-side upper bound on every S_b
         self._ws = None
 
@@ -229,6 +235,12 @@ class QuantizedKVCache:
         st = self.state[:4 * self.cfg.batch].view(self.cfg.batch, 4).cpu()
         return st[:, 0].tolist(), st[:, 1].tolist()
 
+    def fp8_record(self, b: int, h: int, blk: int) -> torch.Tensor:
+        """Bytes of the FP8 record of one block of the FP8 tier (slot blk mod W)."""
+        c, rb = self.cfg, self.layout.fp8_record
+        off = ((b * c.num_kv_heads + h) * c.fp8_blocks + blk % c.fp8_blocks) * rb
+        return self.fp8[off:off + rb]
+
     def record(self, b: int, h: int, blk: int) -> torch.Tensor:
         """Bytes of one block record (a view into the device store)."""
         c, rb = self.cfg, self.layout.record
@@ -240,7 +252,8 @@ class QuantizedKVCache:
         return self.blocks[off:off + rb]
 
 
-def cache_for_workload(w, lengths, chunk: int, extra_tokens: int = 0, device="cuda", seed: int = 0, sink: int = 0):
+def cache_for_workload(w, lengths, chunk: int, extra_tokens: int = 0, device="cuda", seed: int = 0, sink: int = 0,
+                       fp8_blocks: int = 0):
     """An empty cache for a `workloads.Workload`, sized for `lengths` plus
     `extra_tokens` of decode growth, whose ring takes `chunk` tokens per append
     on top of R + G - 1, with a sink of `sink` tokens. Paged workloads get a
@@ -248,7 +261,8 @@ def cache_for_workload(w, lengths, chunk: int, extra_tokens: int = 0, device="cu
     from . import workloads as W
     res_capacity = w.residual + w.k_group - 1 + max(chunk, 1)
     common = dict(k_bits=w.k_bits, v_bits=w.v_bits, k_group=w.k_group, v_group=w.v_group,
-                  residual=w.residual, dtype=w.torch_dtype, res_capacity=res_capacity, sink=sink, device=device)
+                  residual=w.residual, dtype=w.torch_dtype, res_capacity=res_capacity, sink=sink,
+                  fp8_blocks=fp8_blocks, device=device)
     if w.paged:
         table, num_pages = W.random_page_table(w, lengths, extra_tokens=extra_tokens, seed=seed)
         return QuantizedKVCache(w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim,

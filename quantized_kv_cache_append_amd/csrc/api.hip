@@ -19,6 +19,7 @@ namespace {
 
 constexpr int kMaxBatch = 4096;
 constexpr int kMaxSink = 1 << 20;   // sink tokens per sequence
+constexpr int kMaxFp8Blocks = 4096;  // FP8 blocks per (sequence, kv head)
 
 bool pow2_in(int v, int lo, int hi) { return v >= lo && v <= hi && (v & (v - 1)) == 0; }
 
@@ -26,7 +27,7 @@ kvq_status validate(const kvq_config* c) {
   if (c == nullptr) return KVQ_ERR_INVALID_ARG;
   if (c->batch <= 0 || c->num_q_heads <= 0 || c->num_kv_heads <= 0 || c->head_dim <= 0 ||
       c->k_group <= 0 || c->v_group <= 0 || c->residual < 0 || c->res_capacity <= 0 || c->max_blocks < 0 ||
-      c->num_pages < 0 || c->sink < 0)
+      c->num_pages < 0 || c->sink < 0 || c->fp8_blocks < 0)
     return KVQ_ERR_INVALID_ARG;
   if (c->num_q_heads % c->num_kv_heads != 0) return KVQ_ERR_INVALID_ARG;
   if (c->dtype != KVQ_F16 && c->dtype != KVQ_BF16) return KVQ_ERR_INVALID_ARG;
@@ -38,6 +39,7 @@ kvq_status validate(const kvq_config* c) {
   if (c->num_q_heads / c->num_kv_heads > 8) return KVQ_ERR_UNSUPPORTED;
   if (c->batch > kMaxBatch) return KVQ_ERR_UNSUPPORTED;
   if (c->sink > kMaxSink) return KVQ_ERR_UNSUPPORTED;
+  if (c->fp8_blocks > kMaxFp8Blocks) return KVQ_ERR_UNSUPPORTED;
   if ((long long)c->k_group * c->v_bits < 32) return KVQ_ERR_UNSUPPORTED;
   return KVQ_OK;
 }
@@ -52,6 +54,8 @@ kvq_status validate_cache(const kvq_config* c, const kvq_cache* k) {
     return KVQ_ERR_INVALID_ARG;
   if (c->sink > 0 && (k->k_sink == nullptr || k->v_sink == nullptr ||
                       ((reinterpret_cast<uintptr_t>(k->k_sink) | reinterpret_cast<uintptr_t>(k->v_sink)) & 15)))
+    return KVQ_ERR_INVALID_ARG;
+  if (c->fp8_blocks > 0 && (k->fp8 == nullptr || (reinterpret_cast<uintptr_t>(k->fp8) & 15)))
     return KVQ_ERR_INVALID_ARG;
   return KVQ_OK;
 }
@@ -78,6 +82,8 @@ kvq_status kvq_get_layout(const kvq_config* cfg, kvq_layout* out) {
   out->ring = (size_t)g.B * g.Hkv * (size_t)g.C * g.d * 2;
   out->state = (size_t)kvq::state_words(g.B) * sizeof(int32_t);
   out->sink = (size_t)g.B * g.Hkv * (size_t)g.P * g.d * 2;
+  out->fp8_record = g.W > 0 ? (size_t)g.rec8 : 0;
+  out->fp8 = (size_t)g.B * g.Hkv * (size_t)g.W * out->fp8_record;
   return KVQ_OK;
 }
 

@@ -225,11 +225,61 @@ __global__ __launch_bounds__(kThreads) void append_kernel(Geom g, const uint16_t
   }
 }
 
+// FP8 record of block `blk` of `pair` from its ring rows ([P1] ai-automate.fr,
+// section on Minima-KV: recent pages kept in FP8). Formula F8 per token row
+// x: s = fp16(max|x| / 448) (IEEE divide, then round to nearest even);
+// s == 0 -> codes 0; else code_c = e4m3(clamp(x_c / s, -448, 448)), the
+// packed conversion rounding to nearest even. One wave: tokens t0, t0 + dt, ...
+template <bool BF16>
+__device__ inline void write_fp8_rows(const Geom& g, uint8_t* __restrict__ rec8, const uint16_t* __restrict__ k_ring,
+                                      const uint16_t* __restrict__ v_ring, int pair, int blk, int t0, int dt) {
+  const int lane = threadIdx.x & 63;
+  const bool two = g.d == 128;   // channels per lane: 2 (d = 128) or 1 (d = 64)
+  for (int t = t0; t < g.G; t += dt) {
+    const size_t row = ((size_t)pair * g.C + (size_t)((blk * g.G + t) % g.C)) * g.d;
+#pragma unroll
+    for (int kv = 0; kv < 2; ++kv) {
+      const uint16_t* src = (kv == 0 ? k_ring : v_ring) + row;
+      float x0, x1 = 0.f;
+      if (two) {
+        const uint32_t w = *reinterpret_cast<const uint32_t*>(src + 2 * lane);
+        x0 = in_to_f32<BF16>(w & 0xffffu);
+        x1 = in_to_f32<BF16>(w >> 16);
+      } else {
+        x0 = in_to_f32<BF16>(src[lane]);
+      }
+      const float a = wave_max(fmaxf(fabsf(x0), fabsf(x1)));
+      const uint16_t s16 = f32_to_f16_bits(__fdiv_rn(a, 448.0f));
+      const float s = f16_to_f32(s16);
+      float y0 = 0.f, y1 = 0.f;
+      if (s != 0.f) {   // wave-uniform
+        y0 = fminf(fmaxf(__fdiv_rn(x0, s), -448.0f), 448.0f);
+        y1 = fminf(fmaxf(__fdiv_rn(x1, s), -448.0f), 448.0f);
+      }
+      const int pk = __builtin_amdgcn_cvt_pk_fp8_f32(y0, y1, 0, false);
+      uint8_t* codes = rec8 + (kv == 0 ? 0 : (size_t)g.G * g.d + 2 * g.G) + (size_t)t * g.d;
+      if (two)
+        *reinterpret_cast<uint16_t*>(codes + 2 * lane) = (uint16_t)pk;
+      else
+        codes[lane] = (uint8_t)pk;
+      if (lane == 0)
+        *reinterpret_cast<uint16_t*>(rec8 + (kv == 0 ? (size_t)g.G * g.d : 2 * (size_t)g.G * g.d + 2 * g.G) +
+                                     2 * t) = s16;
+    }
+  }
+}
+
 // The two block routines behind one interface: Workers blocks at a time per
 // workgroup (the wave routine: one per wave; the workgroup routine: one).
+// fp8() writes the block's FP8 record (every wave of a workgroup worker
+// takes a share of its tokens).
 template <bool BF16>
 struct WgBlock {
   static constexpr int kWorkers = 1;
+  __device__ static void fp8(const Geom& g, uint8_t* rec8, const uint16_t* kr, const uint16_t* vr, int pair,
+                             int blk) {
+    write_fp8_rows<BF16>(g, rec8, kr, vr, pair, blk, (int)(threadIdx.x >> 6), kThreads / 64);
+  }
   static size_t lds(const Geom& g) { return block_lds_bytes(g.G, g.d); }
   __device__ static void run(const Geom& g, uint8_t* rec, const uint16_t* kr, const uint16_t* vr, int pair,
                              int blk, uint8_t* smem) {
@@ -239,6 +289,10 @@ struct WgBlock {
 template <class Q>
 struct WaveBlock {
   static constexpr int kWorkers = kThreads / 64;
+  __device__ static void fp8(const Geom& g, uint8_t* rec8, const uint16_t* kr, const uint16_t* vr, int pair,
+                             int blk) {
+    write_fp8_rows<Q::BF16>(g, rec8, kr, vr, pair, blk, 0, 1);
+  }
   static size_t lds(const Geom&) { return 0; }
   __device__ static void run(const Geom& g, uint8_t* rec, const uint16_t* kr, const uint16_t* vr, int pair,
                              int blk, uint8_t*) {
@@ -247,12 +301,16 @@ struct WaveBlock {
 };
 
 // Blocks k0, k0 + stride, ... below nok of pair (b, h), by this thread's
-// worker (wave or workgroup); `bad` is set for a missing page.
+// worker (wave or workgroup); `bad` is set for a missing page. Blocks that end
+// up among the W most recent (the FP8 tier) also get their FP8 record, at
+// slot blk mod W of the pair (blocks older than that never share a slot with
+// them).
 template <class P>
-__device__ __forceinline__ void flush_blocks(const Geom& g, uint8_t* blocks, const int32_t* table,
+__device__ __forceinline__ void flush_blocks(const Geom& g, uint8_t* blocks, const int32_t* table, uint8_t* fp8,
                                              const uint16_t* k_ring, const uint16_t* v_ring, int pair, int b, int h,
                                              int Q, int k0, int stride, int nok, int* bad, uint8_t* smem) {
   const int worker = P::kWorkers > 1 ? (int)(threadIdx.x / (kThreads / P::kWorkers)) : 0;
+  const int fp8_from = Q / g.G + nok - g.W;   // first block of the tier after this flush
   for (int k = k0 * P::kWorkers + worker; k < nok; k += stride * P::kWorkers) {
     const int blk = Q / g.G + k;
     uint8_t* rec = const_cast<uint8_t*>(block_record(g, blocks, table, b, h, blk));
@@ -261,12 +319,13 @@ __device__ __forceinline__ void flush_blocks(const Geom& g, uint8_t* blocks, con
       continue;
     }
     P::run(g, rec, k_ring, v_ring, pair, blk, smem);
+    if (g.W > 0 && blk >= fp8_from) P::fp8(g, fp8 + ((size_t)pair * g.W + blk % g.W) * g.rec8, k_ring, v_ring, pair, blk);
   }
 }
 
 template <class P>
 __global__ __launch_bounds__(kThreads) void flush_kernel(Geom g, uint8_t* __restrict__ blocks,
-                                                         const int32_t* __restrict__ table,
+                                                         const int32_t* __restrict__ table, uint8_t* __restrict__ fp8,
                                                          const uint16_t* __restrict__ k_ring,
                                                          const uint16_t* __restrict__ v_ring,
                                                          int32_t* __restrict__ state) {
@@ -283,7 +342,7 @@ __global__ __launch_bounds__(kThreads) void flush_kernel(Geom g, uint8_t* __rest
     s_bad = 0;
   }
   __syncthreads();
-  flush_blocks<P>(g, blocks, table, k_ring, v_ring, pair, b, h, s_Q, blockIdx.y, gridDim.y, s_nok, &s_bad, smem);
+  flush_blocks<P>(g, blocks, table, fp8, k_ring, v_ring, pair, b, h, s_Q, blockIdx.y, gridDim.y, s_nok, &s_bad, smem);
   __syncthreads();
   if (threadIdx.x == 0) {
     if (s_bad) atomicOr(&state[4 * g.B], KVQ_DEV_BAD_PAGE);
@@ -303,6 +362,7 @@ __global__ __launch_bounds__(kThreads) void append_flush_kernel(Geom g, const ui
                                                                 const int32_t* __restrict__ n_new, int n_max,
                                                                 uint8_t* __restrict__ blocks,
                                                                 const int32_t* __restrict__ table,
+                                                                uint8_t* __restrict__ fp8,
                                                                 uint16_t* __restrict__ k_ring,
                                                                 uint16_t* __restrict__ v_ring,
                                                                 uint16_t* __restrict__ k_sink,
@@ -338,7 +398,7 @@ __global__ __launch_bounds__(kThreads) void append_flush_kernel(Geom g, const ui
   // workgroup's ring writes visible to all of its threads first
   __threadfence_block();
   __syncthreads();
-  flush_blocks<P>(g, blocks, table, k_ring, v_ring, pair, b, h, s_Q, 0, 1, s_nok, &s_bad, smem);
+  flush_blocks<P>(g, blocks, table, fp8, k_ring, v_ring, pair, b, h, s_Q, 0, 1, s_nok, &s_bad, smem);
   __syncthreads();
   if (threadIdx.x == 0) {
     if (s_bad) atomicOr(&state[4 * g.B], KVQ_DEV_BAD_PAGE);
@@ -377,7 +437,8 @@ hipError_t launch_flush_p(const Geom& g, const kvq_cache& c, hipStream_t s) {
   const int per_wg = P::kWorkers;
   const int Y = std::max(1, std::min((max_fl + per_wg - 1) / per_wg, (8192 + pairs * per_wg - 1) / (pairs * per_wg)));
   hipLaunchKernelGGL((flush_kernel<P>), dim3(pairs, Y), dim3(kThreads), P::lds(g), s, g,
-                     static_cast<uint8_t*>(c.blocks), c.block_table, static_cast<const uint16_t*>(c.k_ring),
+                     static_cast<uint8_t*>(c.blocks), c.block_table, static_cast<uint8_t*>(c.fp8),
+                     static_cast<const uint16_t*>(c.k_ring),
                      static_cast<const uint16_t*>(c.v_ring), c.state);
   return hipGetLastError();
 }
@@ -387,7 +448,8 @@ hipError_t launch_append_flush_p(const Geom& g, const kvq_cache& c, const void* 
                                  const int32_t* n_new, int n_max, hipStream_t s) {
   hipLaunchKernelGGL((append_flush_kernel<P>), dim3(g.B * g.Hkv), dim3(kThreads), P::lds(g), s, g,
                      static_cast<const uint16_t*>(k_new), static_cast<const uint16_t*>(v_new), n_new, n_max,
-                     static_cast<uint8_t*>(c.blocks), c.block_table, static_cast<uint16_t*>(c.k_ring),
+                     static_cast<uint8_t*>(c.blocks), c.block_table, static_cast<uint8_t*>(c.fp8),
+                     static_cast<uint16_t*>(c.k_ring),
                      static_cast<uint16_t*>(c.v_ring), static_cast<uint16_t*>(c.k_sink),
                      static_cast<uint16_t*>(c.v_sink), c.state);
   return hipGetLastError();

@@ -29,6 +29,8 @@ struct Geom {
   int v_words;   // uint32 words of V codes per channel: G*vb/32
   int P;         // sink: leading tokens of a sequence kept in full precision
   int T;         // queries per (sequence, query head): the T newest tokens, causal; Hq and ng count them
+  int W;         // FP8 tier: most recent quantized blocks also kept (and read) as FP8 records
+  int rec8;      // bytes of one FP8 record: K codes [G][d], K scales [G], V codes [G][d], V scales [G]
 };
 
 // Query rows per kv head one launch serves (n_g times T).
@@ -53,6 +55,8 @@ inline Geom make_geom(const kvq_config& c) {
   g.rec_bytes = g.rec_vz + 2 * (g.d / g.GV) * g.G;
   g.P = c.sink;
   g.T = 1;
+  g.W = c.fp8_blocks;
+  g.rec8 = 2 * g.G * g.d + 4 * g.G;
   return g;
 }
 
@@ -179,8 +183,9 @@ struct DecodePlan {
   int unit_sets;      // fixed sets per quantized unit (0: sized from the lengths)
   int max_blk;        // quantized blocks per (sequence, kv head) the workspace is sized for
   size_t units_max;   // upper bound on work units
-  size_t sink_off;    // byte offset of the sink partial states (one per output row); 0 if P == 0
-  size_t ws_bytes;    // workspace bytes: the unit plan, the partial states, then the sink's
+  int nside;          // side partial states per output row: the sink's (P > 0), then the FP8 tier's (W > 0)
+  size_t side_off;    // byte offset of the side partial states, [nside][B * H_q][d + 2]; 0 if none
+  size_t ws_bytes;    // workspace bytes: the unit plan, the partial states, then the side ones
 };
 DecodePlan plan_decode(const Geom& g, int max_seq_tokens);
 

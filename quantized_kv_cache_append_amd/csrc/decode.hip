@@ -244,8 +244,8 @@ template <int D>
 __global__ __launch_bounds__(64 * kCombineWaves) void combine_kernel(Geom g, const int* __restrict__ plan,
                                                                      const float* ws,   // (not restrict: the
                                                                      // compiler barrier below must order its loads)
-                                                                     const float* __restrict__ sink_parts,
-                                                                     float* __restrict__ out) {
+                                                                     const float* __restrict__ side_parts,
+                                                                     int nside, float* __restrict__ out) {
   constexpr int CPL = D / 64;   // channels per lane
   const int lane = threadIdx.x & 63;
   const int row = blockIdx.x * kCombineWaves + __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
@@ -259,15 +259,17 @@ __global__ __launch_bounds__(64 * kCombineWaves) void combine_kernel(Geom g, con
   float m = -INFINITY, L = 0.f, acc[CPL];
 #pragma unroll
   for (int k = 0; k < CPL; ++k) acc[k] = 0.f;
-  if (sink_parts != nullptr) {   // the sink's partial state opens the merge
-    const float* sp = sink_parts + (size_t)row * (D + 2);
+  for (int si = 0; si < nside; ++si) {   // the side partial states (sink, FP8 tier) open the merge
+    const float* sp = side_parts + ((size_t)si * g.B * g.Hq + row) * (D + 2);
     const float2 ml = *reinterpret_cast<const float2*>(sp + D);
-    if (ml.x != -INFINITY) {   // wave-uniform
-      m = ml.x;
-      L = ml.y;
+    if (ml.x == -INFINITY) continue;   // wave-uniform: an empty state
+    const float mn = fmaxf(m, ml.x);
+    const float a = m == -INFINITY ? 0.f : exp2f(m - mn);
+    const float w = exp2f(ml.x - mn);
+    L = L * a + w * ml.y;
 #pragma unroll
-      for (int k = 0; k < CPL; ++k) acc[k] = sp[CPL * lane + k];
-    }
+    for (int k = 0; k < CPL; ++k) acc[k] = fmaf(w, sp[CPL * lane + k], acc[k] * a);
+    m = mn;
   }
   for (int i0 = 0; i0 < pu.n; i0 += kCombineBatch) {
     const int cnt = min(kCombineBatch, pu.n - i0);
@@ -411,6 +413,109 @@ __global__ __launch_bounds__(64 * kCombineWaves) void sink_kernel(Geom g, const 
   }
 }
 
+// Partial softmax state of the FP8 tier of one (sequence b, query head): the
+// W most recent quantized blocks, read from their FP8 records ([P1]
+// ai-automate.fr, section on Minima-KV: recent pages in FP8, one online
+// softmax over both formats). One wave per output row and 64 tokens per round
+// (all of its loads issued together): lane t scores token t as
+// s_K(t) * sum_c q'_c e4m3(k_tc) against the scaled query in LDS; then lane l
+// accumulates channels D/64 * l .. as sum_t (p_t s_V(t)) e4m3(v_tc). Every
+// query of a T-token block sees these blocks (they precede the window).
+typedef float f32x2v __attribute__((ext_vector_type(2)));
+template <int D, bool BF16>
+__global__ __launch_bounds__(64 * kCombineWaves) void fp8_kernel(Geom g, const uint8_t* __restrict__ fp8,
+                                                                 const int32_t* __restrict__ state,
+                                                                 const uint16_t* __restrict__ q, float qscale,
+                                                                 float* __restrict__ out_part) {
+  constexpr int CPL = D / 64;   // channels per lane in the P.V phase
+  constexpr int VEC = D / 16;   // 16-byte vectors per code row
+  __shared__ float lq[kCombineWaves][D];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int row = blockIdx.x * kCombineWaves + wave;
+  if (row >= g.B * g.Hq) return;
+  const int b = row / g.Hq, h = (row % g.Hq) / g.ng;
+  const int nblk = __builtin_amdgcn_readfirstlane(state[4 * b + kStateQ] / g.G);
+  const int f0 = nblk - min(nblk, g.W);
+  const int n = (nblk - f0) * g.G;   // tokens of the tier
+  float* qs = lq[wave];
+#pragma unroll
+  for (int k = 0; k < CPL; ++k) qs[CPL * lane + k] = in_to_f32<BF16>(q[(size_t)row * D + CPL * lane + k]) * qscale;
+  wave_lds_fence();
+  const uint8_t* pair_recs = fp8 + (size_t)(b * g.Hkv + h) * g.W * g.rec8;
+  // record of tier token i (0 <= i < n): block f0 + i / G, row i % G
+  auto rec_of = [&](int i) { return pair_recs + (size_t)((f0 + i / g.G) % g.W) * g.rec8; };
+  const size_t ks_off = (size_t)g.G * D, vc_off = ks_off + 2 * g.G, vs_off = vc_off + (size_t)g.G * D;
+  float m = -INFINITY, l = 0.f, acc[CPL];
+#pragma unroll
+  for (int k = 0; k < CPL; ++k) acc[k] = 0.f;
+  for (int t0 = 0; t0 < n; t0 += 64) {
+    const int cnt = min(64, n - t0);   // wave-uniform
+    const int mine = t0 + min(lane, cnt - 1);
+    const uint8_t* mrec = rec_of(mine);
+    const int mrow = mine % g.G;
+    uint4 kv[VEC];
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) kv[i] = reinterpret_cast<const uint4*>(mrec + (size_t)mrow * D)[i];
+    const float sk = f16_to_f32(*reinterpret_cast<const uint16_t*>(mrec + ks_off + 2 * mrow));
+    const float sv = f16_to_f32(*reinterpret_cast<const uint16_t*>(mrec + vs_off + 2 * mrow));
+    uint32_t vw[64];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      if (16 * c >= cnt) break;   // wave-uniform: only the chunks of 16 tokens the round has
+#pragma unroll
+      for (int u = 16 * c; u < 16 * c + 16; ++u) {
+        const int i = t0 + min(u, cnt - 1);
+        const uint8_t* vr = rec_of(i) + vc_off + (size_t)(i % g.G) * D + CPL * lane;
+        vw[u] = CPL == 2 ? (uint32_t)*reinterpret_cast<const uint16_t*>(vr) : (uint32_t)*vr;
+      }
+    }
+    // score of token t0 + lane
+    float dot = 0.f;
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) {
+      const uint32_t w[4] = {kv[i].x, kv[i].y, kv[i].z, kv[i].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float4 qa = *reinterpret_cast<const float4*>(qs + 16 * i + 4 * e);
+        const f32x2v lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[e], false);
+        const f32x2v hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[e], true);
+        dot = fmaf(qa.x, lo.x, dot);
+        dot = fmaf(qa.y, lo.y, dot);
+        dot = fmaf(qa.z, hi.x, dot);
+        dot = fmaf(qa.w, hi.y, dot);
+      }
+    }
+    const float s = lane < cnt ? dot * sk : -INFINITY;
+    const float mn = fmaxf(m, wave_max(s));
+    const float alpha = m == -INFINITY ? 0.f : exp2f(m - mn);
+    const float p = lane < cnt ? exp2f(s - mn) : 0.f;
+    l = l * alpha + wave_sum(p);
+    const float pv = p * sv;   // the token's value scale folded into its probability
+#pragma unroll
+    for (int k = 0; k < CPL; ++k) acc[k] *= alpha;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      if (16 * c >= cnt) break;
+#pragma unroll
+      for (int u = 16 * c; u < 16 * c + 16; ++u) {
+        const float pu = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pv), u));   // 0 past cnt
+        const f32x2v x = __builtin_amdgcn_cvt_pk_f32_fp8((int)vw[u], false);
+        acc[0] = fmaf(pu, x.x, acc[0]);
+        if constexpr (CPL == 2) acc[1] = fmaf(pu, x.y, acc[1]);
+      }
+    }
+    m = mn;
+  }
+  float* dst = out_part + (size_t)row * (D + 2);
+#pragma unroll
+  for (int k = 0; k < CPL; ++k) dst[CPL * lane + k] = acc[k];
+  if (lane == 0) {
+    dst[D] = m;
+    dst[D + 1] = l;
+  }
+}
+
 template <int D, bool BF16>
 hipError_t launch_generic(const Geom& g, const kvq_cache& c, const void* q, float scale, const DecodePlan& plan,
                           void* ws, hipStream_t s) {
@@ -436,10 +541,11 @@ DecodePlan plan_decode(const Geom& g, int max_seq_tokens) {
   p.max_blk = std::max(max_seq_tokens - g.R, 0) / g.G;
   p.units_max = units_max(g, p.max_blk, p.nb_set, p.ring_chunk, p.unit_sets);
   p.ws_bytes = plan_bytes(g.B) + p.units_max * (size_t)g.ng * (size_t)(g.d + 2) * 4;
-  p.sink_off = 0;
-  if (g.P > 0) {   // one sink partial per output row, 16-byte aligned
-    p.sink_off = (p.ws_bytes + 15) & ~(size_t)15;
-    p.ws_bytes = p.sink_off + (size_t)g.B * g.Hq * (g.d + 2) * 4;
+  p.nside = (g.P > 0 ? 1 : 0) + (g.W > 0 ? 1 : 0);
+  p.side_off = 0;
+  if (p.nside > 0) {   // side partials per output row, 16-byte aligned
+    p.side_off = (p.ws_bytes + 15) & ~(size_t)15;
+    p.ws_bytes = p.side_off + (size_t)p.nside * g.B * g.Hq * (g.d + 2) * 4;
   }
   return p;
 }
@@ -452,7 +558,18 @@ hipError_t launch_sink(const Geom& g, const kvq_cache& c, const void* q, float s
   hipLaunchKernelGGL((sink_kernel<D, BF16>), dim3(grid), dim3(64 * kCombineWaves), 0, s, g,
                      static_cast<const uint16_t*>(c.k_sink), static_cast<const uint16_t*>(c.v_sink), c.state,
                      static_cast<const uint16_t*>(q), scale * 1.4426950408889634f,
-                     reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + plan.sink_off));
+                     reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + plan.side_off));
+  return hipGetLastError();
+}
+template <int D, bool BF16>
+hipError_t launch_fp8(const Geom& g, const kvq_cache& c, const void* q, float scale, const DecodePlan& plan,
+                      void* ws, hipStream_t s) {
+  const int grid = (g.B * g.Hq + kCombineWaves - 1) / kCombineWaves;
+  const size_t slot = g.P > 0 ? (size_t)g.B * g.Hq * (D + 2) * 4 : 0;   // after the sink's
+  hipLaunchKernelGGL((fp8_kernel<D, BF16>), dim3(grid), dim3(64 * kCombineWaves), 0, s, g,
+                     static_cast<const uint8_t*>(c.fp8), c.state, static_cast<const uint16_t*>(q),
+                     scale * 1.4426950408889634f,
+                     reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + plan.side_off + slot));
   return hipGetLastError();
 }
 }  // namespace
@@ -465,6 +582,13 @@ hipError_t launch_decode_partials(const Geom& g, const kvq_cache& c, const void*
                                             : launch_sink<128, false>(g, c, q, scale, plan, ws, s))
                                     : (bf16 ? launch_sink<64, true>(g, c, q, scale, plan, ws, s)
                                             : launch_sink<64, false>(g, c, q, scale, plan, ws, s));
+    if (e != hipSuccess) return e;
+  }
+  if (g.W > 0) {
+    const hipError_t e = g.d == 128 ? (bf16 ? launch_fp8<128, true>(g, c, q, scale, plan, ws, s)
+                                            : launch_fp8<128, false>(g, c, q, scale, plan, ws, s))
+                                    : (bf16 ? launch_fp8<64, true>(g, c, q, scale, plan, ws, s)
+                                            : launch_fp8<64, false>(g, c, q, scale, plan, ws, s));
     if (e != hipSuccess) return e;
   }
   if (plan.fast) return launch_decode_fast(g, c, q, scale, plan, ws, s);
@@ -480,15 +604,14 @@ hipError_t launch_decode_combine(const Geom& g, const kvq_cache& c, float* out, 
   (void)c;
   const int* planp = static_cast<const int*>(ws);
   const float* parts = reinterpret_cast<const float*>(static_cast<const uint8_t*>(ws) + plan_bytes(g.B));
-  const float* sink = g.P > 0 ? reinterpret_cast<const float*>(static_cast<const uint8_t*>(ws) + plan.sink_off)
-                              : nullptr;
+  const float* side = reinterpret_cast<const float*>(static_cast<const uint8_t*>(ws) + plan.side_off);
   const int grid = (g.B * g.Hq + kCombineWaves - 1) / kCombineWaves;
   if (g.d == 128)
-    hipLaunchKernelGGL((combine_kernel<128>), dim3(grid), dim3(64 * kCombineWaves), 0, s, g, planp, parts, sink,
-                       out);
+    hipLaunchKernelGGL((combine_kernel<128>), dim3(grid), dim3(64 * kCombineWaves), 0, s, g, planp, parts, side,
+                       plan.nside, out);
   else
-    hipLaunchKernelGGL((combine_kernel<64>), dim3(grid), dim3(64 * kCombineWaves), 0, s, g, planp, parts, sink,
-                       out);
+    hipLaunchKernelGGL((combine_kernel<64>), dim3(grid), dim3(64 * kCombineWaves), 0, s, g, planp, parts, side,
+                       plan.nside, out);
   return hipGetLastError();
 }
 

@@ -47,10 +47,13 @@ enum {
   kPlanTails = 9,   // medium and small units per pair (at most): kTailUnits or 0
   kPlanHdr = 12,    // then pre[s][B + 1] for each section s: exclusive prefix over
 };                  // sequences of the section's units of one kv head; then the
-                    // lengths the plan was built from, Q[B] and S[B]
+                    // lengths the plan was built from: Q[B] (tokens of the low-bit
+                    // blocks the units stream: all quantized blocks but the FP8
+                    // tier's), S[B] (tokens after the sink) and R[B] (the ring's
+                    // first token: every quantized token before it)
 constexpr int kSections = 4;
 
-__host__ __device__ inline int plan_ints(int B) { return kPlanHdr + kSections * (B + 1) + 2 * B; }
+__host__ __device__ inline int plan_ints(int B) { return kPlanHdr + kSections * (B + 1) + 3 * B; }
 __host__ __device__ inline int plan_seq_off(int B) { return kPlanHdr + kSections * (B + 1); }
 inline size_t plan_bytes(int B) { return ((size_t)plan_ints(B) * 4 + 255) & ~(size_t)255; }
 // LDS bytes a decode workgroup reserves for its copy of the plan (16-byte aligned)
@@ -110,14 +113,16 @@ __device__ inline void build_unit_plan(const Geom& g, int32_t* state, int max_bl
     const int lane = threadIdx.x;
     int* seqQ = plan + plan_seq_off(g.B);
     int* seqS = seqQ + g.B;
+    int* seqR = seqS + g.B;
     // pass 1: lengths into the plan, quantized sets in all
     int sets = 0;
     bool too_long = false;
     for (int b = lane; b < g.B; b += 64) {
       const int Q = state[4 * b + kStateQ], S = max(state[4 * b + kStateS] - g.P, 0);   // tokens after the sink
-      seqQ[b] = Q;
+      seqQ[b] = (Q / g.G - min(Q / g.G, g.W)) * g.G;   // the FP8 tier's blocks are read elsewhere
       seqS[b] = S;
-      const int nblk = Q / g.G;
+      seqR[b] = Q;
+      const int nblk = seqQ[b] / g.G;
       too_long |= nblk > max_blk;
       sets += (min(nblk, max_blk) + nb_set - 1) / nb_set;
     }
@@ -136,10 +141,10 @@ __device__ inline void build_unit_plan(const Geom& g, int32_t* state, int max_bl
       const int b = b0 + lane;
       int cnt[kSections] = {0, 0, 0, 0};
       if (b < g.B) {
-        const int Q = seqQ[b], S = seqS[b];
+        const int Q = seqQ[b], S = seqS[b], R0 = seqR[b];
         const int nblk = min(Q / g.G, max_blk);
         const Tail t = tail_of(nblk, um, us, tails);
-        cnt[0] = (min(max(S - Q, 0), g.C) + rc - 1) / rc;
+        cnt[0] = (min(max(S - R0, 0), g.C) + rc - 1) / rc;
         cnt[1] = (nblk - t.mid - t.small + ub - 1) / ub;
         cnt[2] = (t.mid + um - 1) / um;
         cnt[3] = (t.small + us - 1) / us;
@@ -211,7 +216,7 @@ __device__ inline Unit locate_unit(const Geom& g, const int* plan, int u, int ma
   if (sec == 0) {
     const int S = plan[plan_seq_off(g.B) + g.B + b];
     const int rc = plan[kPlanRc];
-    r.begin = Q + i * rc;
+    r.begin = plan[plan_seq_off(g.B) + 2 * g.B + b] + i * rc;
     r.end = min(S, r.begin + rc);
   } else {
     const int nblk = min(Q / g.G, max_blk);

@@ -15,16 +15,17 @@ ATOL = 2e-3     # max-abs error against the fp64 oracle on the same dequantized 
 RTOL_L2 = 1e-3  # relative L2 error over the whole output
 
 
-def spec_of(w: W.Workload, res_capacity: int, sink: int = 0) -> kivi.CacheSpec:
+def spec_of(w: W.Workload, res_capacity: int, sink: int = 0, fp8_blocks: int = 0) -> kivi.CacheSpec:
     return kivi.CacheSpec(batch=w.batch, num_q_heads=w.num_q_heads, num_kv_heads=w.num_kv_heads,
                           head_dim=w.head_dim, k_bits=w.k_bits, v_bits=w.v_bits, k_group=w.k_group,
                           v_group=w.v_group, residual=w.residual, res_capacity=res_capacity, dtype=w.dtype,
-                          sink=sink)
+                          sink=sink, fp8_blocks=fp8_blocks)
 
 
 def make_cache(w: W.Workload, lengths, chunk: int, extra_tokens: int = 0, device="cuda", seed: int = 0,
-               sink: int = 0):
-    return cache_for_workload(w, lengths, chunk, extra_tokens=extra_tokens, device=device, seed=seed, sink=sink)
+               sink: int = 0, fp8_blocks: int = 0):
+    return cache_for_workload(w, lengths, chunk, extra_tokens=extra_tokens, device=device, seed=seed, sink=sink,
+                              fp8_blocks=fp8_blocks)
 
 
 def errors(got: np.ndarray, ref: np.ndarray):
@@ -57,6 +58,18 @@ def check_records(cache: QuantizedKVCache, spec: kivi.CacheSpec, k_np, v_np, len
         vr = cache.v_ring[b, h].float().cpu().numpy()[slots]
         assert np.array_equal(kr, k_np[b, h, P + Q:S_b]) and np.array_equal(vr, v_np[b, h, P + Q:S_b]), \
             f"ring of (b={b}, h={h}) differs"
+        # the FP8 tier: the records of the W most recent blocks
+        if spec.fp8_blocks > 0:
+            f0, nblk = kivi.fp8_window(spec, S_b)
+            G = spec.k_group
+            for j in range(f0, nblk):
+                lo = P + j * G
+                exp8 = kivi.fp8_record(k_np[b, h, lo:lo + G], v_np[b, h, lo:lo + G])
+                got8 = cache.fp8_record(b, h, j).cpu().numpy()
+                if not np.array_equal(got8, exp8):
+                    bad = np.nonzero(got8 != exp8)[0]
+                    raise AssertionError(f"FP8 record (b={b}, h={h}, blk={j}) differs at {bad.size} bytes, "
+                                         f"first {bad[:8]}: got {got8[bad[:4]]}, want {exp8[bad[:4]]}")
         # and the sink its tokens
         if P > 0:
             ks = cache.k_sink[b, h, :s].float().cpu().numpy()

@@ -170,6 +170,24 @@ def test_multi_token_query_checks(kvq_lib):
                                               ctypes.c_float(0.0), 4096, ctypes.c_void_p(0x7000), need, None) == 1
 
 
+def test_fp8_tier_layout_and_checks(kvq_lib):
+    from quantized_kv_cache_append_amd import binding as B
+    cfg = _cfg(B, fp8_blocks=4)
+    lay = B.kvq_get_layout(cfg)
+    assert lay.fp8_record == 2 * 32 * 128 + 4 * 32
+    assert lay.fp8 == 8 * 32 * 4 * lay.fp8_record
+    assert B.kvq_get_layout(_cfg(B)).fp8 == 0
+    # one more side partial state per output row
+    plain, tier = B.kvq_workspace_size(_cfg(B), 4096), B.kvq_workspace_size(cfg, 4096)
+    assert tier == ((plain + 15) // 16) * 16 + 8 * 32 * (128 + 2) * 4
+    both = B.kvq_workspace_size(_cfg(B, fp8_blocks=4, sink=2), 4096)
+    assert both == ((plain + 15) // 16) * 16 + 2 * 8 * 32 * (128 + 2) * 4
+    bad = _cfg(B, fp8_blocks=-1)
+    assert kvq_lib.kvq_get_layout(ctypes.byref(bad), ctypes.byref(B.kvq_layout())) == B.KVQ_ERR_INVALID_ARG
+    no_store = B.kvq_cache(blocks=0x1000, block_table=None, k_ring=0x2000, v_ring=0x3000, state=0x4000)
+    assert kvq_lib.kvq_flush_residual(ctypes.byref(cfg), ctypes.byref(no_store), None) == 1
+
+
 def test_status_strings(kvq_lib):
     from quantized_kv_cache_append_amd import binding as B
     assert B.status_string(0) == "ok"
