@@ -183,7 +183,8 @@ struct DecodePlan {
   int unit_sets;      // fixed sets per quantized unit (0: sized from the lengths)
   int max_blk;        // quantized blocks per (sequence, kv head) the workspace is sized for
   size_t units_max;   // upper bound on work units
-  int nside;          // side partial states per output row: the sink's (P > 0), then the FP8 tier's (W > 0)
+  int fp8_rounds;     // side partial states of the FP8 tier per output row (64 of its tokens each)
+  int nside;          // side partial states per output row: the sink's (P > 0), then the FP8 tier's
   size_t side_off;    // byte offset of the side partial states, [nside][B * H_q][d + 2]; 0 if none
   size_t ws_bytes;    // workspace bytes: the unit plan, the partial states, then the side ones
 };

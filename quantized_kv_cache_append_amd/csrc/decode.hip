@@ -259,24 +259,19 @@ __global__ __launch_bounds__(64 * kCombineWaves) void combine_kernel(Geom g, con
   float m = -INFINITY, L = 0.f, acc[CPL];
 #pragma unroll
   for (int k = 0; k < CPL; ++k) acc[k] = 0.f;
-  for (int si = 0; si < nside; ++si) {   // the side partial states (sink, FP8 tier) open the merge
-    const float* sp = side_parts + ((size_t)si * g.B * g.Hq + row) * (D + 2);
-    const float2 ml = *reinterpret_cast<const float2*>(sp + D);
-    if (ml.x == -INFINITY) continue;   // wave-uniform: an empty state
-    const float mn = fmaxf(m, ml.x);
-    const float a = m == -INFINITY ? 0.f : exp2f(m - mn);
-    const float w = exp2f(ml.x - mn);
-    L = L * a + w * ml.y;
-#pragma unroll
-    for (int k = 0; k < CPL; ++k) acc[k] = fmaf(w, sp[CPL * lane + k], acc[k] * a);
-    m = mn;
-  }
-  for (int i0 = 0; i0 < pu.n; i0 += kCombineBatch) {
-    const int cnt = min(kCombineBatch, pu.n - i0);
+  // partial i: the side states (sink, FP8 tier rounds) first, then the pair's units
+  const size_t side_stride = (size_t)g.B * g.Hq * (D + 2);
+  const float* side0 = side_parts + (size_t)row * (D + 2);
+  auto part = [&](int i) -> const float* {
+    return i < nside ? side0 + (size_t)i * side_stride : src0 + (size_t)pu.slot(i - nside) * stride;
+  };
+  const int nparts = nside + pu.n;
+  for (int i0 = 0; i0 < nparts; i0 += kCombineBatch) {
+    const int cnt = min(kCombineBatch, nparts - i0);
     float v[kCombineBatch][CPL];
 #pragma unroll
     for (int u = 0; u < kCombineBatch; ++u) {
-      const float* src = src0 + (size_t)pu.slot(i0 + (u < cnt ? u : 0)) * stride + CPL * lane;
+      const float* src = part(i0 + (u < cnt ? u : 0)) + CPL * lane;
       if constexpr (CPL == 2) {
         const float2 x = *reinterpret_cast<const float2*>(src);
         v[u][0] = x.x;
@@ -286,7 +281,7 @@ __global__ __launch_bounds__(64 * kCombineWaves) void combine_kernel(Geom g, con
         for (int k = 0; k < CPL; ++k) v[u][k] = src[k];
       }
     }
-    const float2 ml = *reinterpret_cast<const float2*>(src0 + (size_t)pu.slot(i0 + min(lane, cnt - 1)) * stride + D);
+    const float2 ml = *reinterpret_cast<const float2*>(part(i0 + min(lane, cnt - 1)) + D);
     asm volatile("" ::: "memory");   // the whole batch is in flight before the first wait
     const float mi = lane < cnt ? ml.x : -INFINITY, li = lane < cnt ? ml.y : 0.f;
     const float mn = fmaxf(m, wave_max(mi));
@@ -413,11 +408,12 @@ __global__ __launch_bounds__(64 * kCombineWaves) void sink_kernel(Geom g, const 
   }
 }
 
-// Partial softmax state of the FP8 tier of one (sequence b, query head): the
+// Partial softmax states of the FP8 tier of one (sequence b, query head): the
 // W most recent quantized blocks, read from their FP8 records ([P1]
 // ai-automate.fr, section on Minima-KV: recent pages in FP8, one online
-// softmax over both formats). One wave per output row and 64 tokens per round
-// (all of its loads issued together): lane t scores token t as
+// softmax over both formats). One wave per (output row, round of 64 tier
+// tokens), all of its loads issued together, each writing its own side
+// partial (the empty state past the tier's end): lane t scores token t as
 // s_K(t) * sum_c q'_c e4m3(k_tc) against the scaled query in LDS; then lane l
 // accumulates channels D/64 * l .. as sum_t (p_t s_V(t)) e4m3(v_tc). Every
 // query of a T-token block sees these blocks (they precede the window).
@@ -426,14 +422,15 @@ template <int D, bool BF16>
 __global__ __launch_bounds__(64 * kCombineWaves) void fp8_kernel(Geom g, const uint8_t* __restrict__ fp8,
                                                                  const int32_t* __restrict__ state,
                                                                  const uint16_t* __restrict__ q, float qscale,
-                                                                 float* __restrict__ out_part) {
+                                                                 int rounds, float* __restrict__ out_part) {
   constexpr int CPL = D / 64;   // channels per lane in the P.V phase
   constexpr int VEC = D / 16;   // 16-byte vectors per code row
   __shared__ float lq[kCombineWaves][D];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
-  const int row = blockIdx.x * kCombineWaves + wave;
-  if (row >= g.B * g.Hq) return;
+  const int idx = blockIdx.x * kCombineWaves + wave;   // round * (B * H_q) + row
+  if (idx >= g.B * g.Hq * rounds) return;
+  const int row = idx % (g.B * g.Hq), round = idx / (g.B * g.Hq);
   const int b = row / g.Hq, h = (row % g.Hq) / g.ng;
   const int nblk = __builtin_amdgcn_readfirstlane(state[4 * b + kStateQ] / g.G);
   const int f0 = nblk - min(nblk, g.W);
@@ -449,7 +446,8 @@ __global__ __launch_bounds__(64 * kCombineWaves) void fp8_kernel(Geom g, const u
   float m = -INFINITY, l = 0.f, acc[CPL];
 #pragma unroll
   for (int k = 0; k < CPL; ++k) acc[k] = 0.f;
-  for (int t0 = 0; t0 < n; t0 += 64) {
+  const int t0 = 64 * round;
+  if (t0 < n) {
     const int cnt = min(64, n - t0);   // wave-uniform
     const int mine = t0 + min(lane, cnt - 1);
     const uint8_t* mrec = rec_of(mine);
@@ -507,7 +505,7 @@ __global__ __launch_bounds__(64 * kCombineWaves) void fp8_kernel(Geom g, const u
     }
     m = mn;
   }
-  float* dst = out_part + (size_t)row * (D + 2);
+  float* dst = out_part + ((size_t)round * g.B * g.Hq + row) * (D + 2);
 #pragma unroll
   for (int k = 0; k < CPL; ++k) dst[CPL * lane + k] = acc[k];
   if (lane == 0) {
@@ -541,7 +539,8 @@ DecodePlan plan_decode(const Geom& g, int max_seq_tokens) {
   p.max_blk = std::max(max_seq_tokens - g.R, 0) / g.G;
   p.units_max = units_max(g, p.max_blk, p.nb_set, p.ring_chunk, p.unit_sets);
   p.ws_bytes = plan_bytes(g.B) + p.units_max * (size_t)g.ng * (size_t)(g.d + 2) * 4;
-  p.nside = (g.P > 0 ? 1 : 0) + (g.W > 0 ? 1 : 0);
+  p.fp8_rounds = (g.W * g.G + 63) / 64;   // FP8 tier: one side partial per 64 of its tokens
+  p.nside = (g.P > 0 ? 1 : 0) + p.fp8_rounds;
   p.side_off = 0;
   if (p.nside > 0) {   // side partials per output row, 16-byte aligned
     p.side_off = (p.ws_bytes + 15) & ~(size_t)15;
@@ -564,11 +563,11 @@ hipError_t launch_sink(const Geom& g, const kvq_cache& c, const void* q, float s
 template <int D, bool BF16>
 hipError_t launch_fp8(const Geom& g, const kvq_cache& c, const void* q, float scale, const DecodePlan& plan,
                       void* ws, hipStream_t s) {
-  const int grid = (g.B * g.Hq + kCombineWaves - 1) / kCombineWaves;
+  const int grid = (g.B * g.Hq * plan.fp8_rounds + kCombineWaves - 1) / kCombineWaves;
   const size_t slot = g.P > 0 ? (size_t)g.B * g.Hq * (D + 2) * 4 : 0;   // after the sink's
   hipLaunchKernelGGL((fp8_kernel<D, BF16>), dim3(grid), dim3(64 * kCombineWaves), 0, s, g,
                      static_cast<const uint8_t*>(c.fp8), c.state, static_cast<const uint16_t*>(q),
-                     scale * 1.4426950408889634f,
+                     scale * 1.4426950408889634f, plan.fp8_rounds,
                      reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + plan.side_off + slot));
   return hipGetLastError();
 }

@@ -177,11 +177,11 @@ def test_fp8_tier_layout_and_checks(kvq_lib):
     assert lay.fp8_record == 2 * 32 * 128 + 4 * 32
     assert lay.fp8 == 8 * 32 * 4 * lay.fp8_record
     assert B.kvq_get_layout(_cfg(B)).fp8 == 0
-    # one more side partial state per output row
+    # side partial states per output row: one per 64 tokens of the tier (4 blocks of 32: 2), one for a sink
     plain, tier = B.kvq_workspace_size(_cfg(B), 4096), B.kvq_workspace_size(cfg, 4096)
-    assert tier == ((plain + 15) // 16) * 16 + 8 * 32 * (128 + 2) * 4
+    assert tier == ((plain + 15) // 16) * 16 + 2 * 8 * 32 * (128 + 2) * 4
     both = B.kvq_workspace_size(_cfg(B, fp8_blocks=4, sink=2), 4096)
-    assert both == ((plain + 15) // 16) * 16 + 2 * 8 * 32 * (128 + 2) * 4
+    assert both == ((plain + 15) // 16) * 16 + 3 * 8 * 32 * (128 + 2) * 4
     bad = _cfg(B, fp8_blocks=-1)
     assert kvq_lib.kvq_get_layout(ctypes.byref(bad), ctypes.byref(B.kvq_layout())) == B.KVQ_ERR_INVALID_ARG
     no_store = B.kvq_cache(blocks=0x1000, block_table=None, k_ring=0x2000, v_ring=0x3000, state=0x4000)
