@@ -240,7 +240,7 @@ __global__ __launch_bounds__(256) void decode_generic_kernel(
 constexpr int kCombineWaves = 4;
 constexpr int kCombineBatch = 64;
 
-template <int D>
+template <int D, bool SIDE>
 __global__ __launch_bounds__(64 * kCombineWaves) void combine_kernel(Geom g, const int* __restrict__ plan,
                                                                      const float* ws,   // (not restrict: the
                                                                      // compiler barrier below must order its loads)
@@ -263,9 +263,12 @@ __global__ __launch_bounds__(64 * kCombineWaves) void combine_kernel(Geom g, con
   const size_t side_stride = (size_t)g.B * g.Hq * (D + 2);
   const float* side0 = side_parts + (size_t)row * (D + 2);
   auto part = [&](int i) -> const float* {
-    return i < nside ? side0 + (size_t)i * side_stride : src0 + (size_t)pu.slot(i - nside) * stride;
+    if constexpr (SIDE)
+      return i < nside ? side0 + (size_t)i * side_stride : src0 + (size_t)pu.slot(i - nside) * stride;
+    else
+      return src0 + (size_t)pu.slot(i) * stride;
   };
-  const int nparts = nside + pu.n;
+  const int nparts = (SIDE ? nside : 0) + pu.n;
   for (int i0 = 0; i0 < nparts; i0 += kCombineBatch) {
     const int cnt = min(kCombineBatch, nparts - i0);
     float v[kCombineBatch][CPL];
@@ -605,12 +608,19 @@ hipError_t launch_decode_combine(const Geom& g, const kvq_cache& c, float* out, 
   const float* parts = reinterpret_cast<const float*>(static_cast<const uint8_t*>(ws) + plan_bytes(g.B));
   const float* side = reinterpret_cast<const float*>(static_cast<const uint8_t*>(ws) + plan.side_off);
   const int grid = (g.B * g.Hq + kCombineWaves - 1) / kCombineWaves;
-  if (g.d == 128)
-    hipLaunchKernelGGL((combine_kernel<128>), dim3(grid), dim3(64 * kCombineWaves), 0, s, g, planp, parts, side,
-                       plan.nside, out);
-  else
-    hipLaunchKernelGGL((combine_kernel<64>), dim3(grid), dim3(64 * kCombineWaves), 0, s, g, planp, parts, side,
-                       plan.nside, out);
+  const dim3 gd(grid), bd(64 * kCombineWaves);
+  const int ns = plan.nside;
+  if (g.d == 128) {
+    if (ns > 0)
+      hipLaunchKernelGGL((combine_kernel<128, true>), gd, bd, 0, s, g, planp, parts, side, ns, out);
+    else
+      hipLaunchKernelGGL((combine_kernel<128, false>), gd, bd, 0, s, g, planp, parts, side, ns, out);
+  } else {
+    if (ns > 0)
+      hipLaunchKernelGGL((combine_kernel<64, true>), gd, bd, 0, s, g, planp, parts, side, ns, out);
+    else
+      hipLaunchKernelGGL((combine_kernel<64, false>), gd, bd, 0, s, g, planp, parts, side, ns, out);
+  }
   return hipGetLastError();
 }
 
