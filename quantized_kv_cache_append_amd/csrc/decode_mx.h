@@ -42,22 +42,22 @@
 //
 // Work of one wave: units of whole sets of 4 blocks (128 tokens), the next
 // set's loads in flight while a set is computed. Lane l = 16 g + n:
-//   score MFMA (one per 16-token tile i; A = q~ limbs, rows 4 blk + limb; B =
+//   score MFMA (one per 16-token tile i; A = q~ digit rows, rows 4 blk + k; B =
 //     key codes of tokens 16 i + n, channels 32 g .. 32 g + 31): lane group g
-//     holds the four limb rows of block g, so the scores of block g's tokens
+//     holds the four digit rows of block g, so the scores of block g's tokens
 //     32 g + n and 32 g + 16 + n are sums of the lane's own accumulators;
-//   P.V MFMA (one per 16-channel tile; A = p~ limbs, rows 4 j + limb; B =
+//   P.V MFMA (one per 16-channel tile; A = p~ digit rows, rows 4 j + k; B =
 //     value codes of channel 16 nt + n, tokens 32 g .. 32 g + 31): lane group
-//     g holds the limb rows of value group g, so outputs 32 g + n and
+//     g holds the digit rows of value group g, so outputs 32 g + n and
 //     32 g + 16 + n are sums of its own accumulators;
-//   the q~ limbs of block g, kappa, the p~ limbs and lambda of group g are
+//   the q~ digit rows of block g, kappa, the p~ digit rows and lambda of group g are
 //     built by the 16 lanes of lane group g (8 channels or 8 tokens each).
 // Operand layouts of the instruction (measured): an fp4 operand lane of group
 // g holds k = 32 g .. 32 g + 31 (nibble j = k - 32 g); an fp8 operand lane
 // holds k = 16 g .. 16 g + 15 in bytes 0..15 and 64 + 16 g .. 64 + 16 g + 15
 // in bytes 16..31; the block scale of row r for k in [32 b, 32 b + 32) comes
 // from lane r + 16 b. The k order of the codes (even slots of a word, then odd
-// slots) is followed by the limb images the builders write to LDS.
+// slots) is followed by the digit-row images the builders write to LDS.
 #pragma once
 
 #include "common.h"
@@ -74,7 +74,7 @@ typedef float v2f __attribute__((ext_vector_type(2)));
 constexpr int kWaves = 4;          // waves per workgroup
 constexpr int kSetBlk = 4;         // blocks per set
 constexpr int kSetTok = 128;       // tokens per set
-constexpr int kLimbs = 4;          // A-operand rows per real-valued operand: 3 digits + remainder
+constexpr int kRows = 4;           // A-operand rows per real-valued operand: 3 digits + remainder
 constexpr int kRingTok = 32;       // ring tokens per ring unit: every load of a unit in flight at once
 constexpr int kRingWeight = 3;     // cost of a ring byte in quarters of a quantized byte (measured: a 16 KB ring unit takes about as long as a 12 KB set)
 constexpr int kUnitSets = 1;       // sets per quantized unit: the static partition cuts at set granularity
@@ -107,19 +107,19 @@ struct Cfg {
 // Building blocks
 // ---------------------------------------------------------------------------------
 
-// Write x0..x7 (|x| < 16, in units of the first digit) as kLimbs e4m3 rows of
-// an A-operand image: rows 0 .. kLimbs - 2 hold the signed base-32 digits
+// Write x0..x7 (|x| < 16, in units of the first digit) as kRows e4m3 rows of
+// an A-operand image: rows 0 .. kRows - 2 hold the signed base-32 digits
 // D_k = round(t_k), t_0 = x, t_(k+1) = 32 (t_k - D_k) (|t_k| <= 16, so the
-// digits are integers in [-16, 16], exact in e4m3), the last row t_(kLimbs-1)
+// digits are integers in [-16, 16], exact in e4m3), the last row t_(kRows-1)
 // rounded to e4m3. Row k's value of x_e goes to byte e/2 of dword `off_even` (e even) or
 // `off_odd` (e odd) of row row0 + k, where a row's lane image starts at
 // 32 (row + 16 g) bytes.
-__device__ __forceinline__ void write_limbs(uint8_t* img, int row0, int off_even, int off_odd, float (&x)[8]) {
+__device__ __forceinline__ void write_digit_rows(uint8_t* img, int row0, int off_even, int off_odd, float (&x)[8]) {
 #pragma unroll
-  for (int k = 0; k < kLimbs; ++k) {
+  for (int k = 0; k < kRows; ++k) {
     float d[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) d[e] = k + 1 < kLimbs ? __builtin_rintf(x[e]) : x[e];
+    for (int e = 0; e < 8; ++e) d[e] = k + 1 < kRows ? __builtin_rintf(x[e]) : x[e];
     int ev = __builtin_amdgcn_cvt_pk_fp8_f32(d[0], d[2], 0, false);
     ev = __builtin_amdgcn_cvt_pk_fp8_f32(d[4], d[6], ev, true);
     int od = __builtin_amdgcn_cvt_pk_fp8_f32(d[1], d[3], 0, false);
@@ -127,7 +127,7 @@ __device__ __forceinline__ void write_limbs(uint8_t* img, int row0, int off_even
     uint8_t* row = img + 32 * (row0 + k);
     *reinterpret_cast<int*>(row + off_even) = ev;
     *reinterpret_cast<int*>(row + off_odd) = od;
-    if (k + 1 < kLimbs) {
+    if (k + 1 < kRows) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) x[e] = (x[e] - d[e]) * 32.0f;   // exact
     }
@@ -135,7 +135,7 @@ __device__ __forceinline__ void write_limbs(uint8_t* img, int row0, int off_even
 }
 
 // Exponent e with max|x| < 2^e over the 16 lanes of a DPP row (every lane gets
-// it), floored so that the limb scales stay inside E8M0's range.
+// it), floored so that the rows' scales stay inside E8M0's range.
 __device__ __forceinline__ int row_exponent(float amax) {
   amax = fmaxf(amax, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(amax), 0x121, 0xF, 0xF, false)));
   amax = fmaxf(amax, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(amax), 0x122, 0xF, 0xF, false)));
@@ -232,7 +232,7 @@ __device__ __forceinline__ void quant_stream(const Geom& g, float* __restrict__ 
           make_float2(in_val<C>(cb.qw & 0xffffu) * qscale, in_val<C>(cb.qw >> 16) * qscale);
       wave_lds_fence();
     }
-    // ---- q~ limbs of block gq, channels 8n .. 8n + 7, and kappa of block gq ----
+    // ---- q~ digit rows of block gq, channels 8n .. 8n + 7, and kappa of block gq ----
     float kap;
     {
       const float4 qa = *reinterpret_cast<const float4*>(lq + 8 * n);
@@ -256,7 +256,7 @@ __device__ __forceinline__ void quant_stream(const Geom& g, float* __restrict__ 
       // channels 8n + e sit at k = 16 (n / 2) + 4 (n % 2) + 8 (e % 2) + e / 2
       const int kb = 16 * (n / 2) + 4 * (n % 2);
       const int lg = (kb % 64) / 16, off = 16 * (kb / 64) + kb % 16;
-      write_limbs(qimg + 32 * 16 * lg, 4 * gq, off, off + 8, x);
+      write_digit_rows(qimg + 32 * 16 * lg, 4 * gq, off, off + 8, x);
       const int sc = row_scale(ex, lane);
       wave_lds_fence();
       const v8i a = *reinterpret_cast<const v8i*>(qimg + 32 * lane);
@@ -292,7 +292,7 @@ __device__ __forceinline__ void quant_stream(const Geom& g, float* __restrict__ 
       lp[32 * gq + 16 + n] = p1;
     }
     wave_lds_fence();
-    // ---- p~ limbs of value group gq, tokens 8n .. 8n + 7 (run n), and lambda ----
+    // ---- p~ digit rows of value group gq, tokens 8n .. 8n + 7 (run n), and lambda ----
     {
       const float4 pa = *reinterpret_cast<const float4*>(lp + 8 * n);
       const float4 pb = *reinterpret_cast<const float4*>(lp + 8 * n + 4);
@@ -312,7 +312,7 @@ __device__ __forceinline__ void quant_stream(const Geom& g, float* __restrict__ 
       for (int e = 0; e < 8; ++e) x[e] *= nrm;
       // token 8n + e of the set sits at k = 8n + (e even: e / 2, odd: 4 + e / 2)
       const int lg = (n % 8) / 2, off = 16 * (n / 8) + 8 * (n % 2);
-      write_limbs(pimg + 32 * 16 * lg, 4 * gq, off, off + 4, x);
+      write_digit_rows(pimg + 32 * 16 * lg, 4 * gq, off, off + 4, x);
       const int sc = row_scale(ex, lane);
       wave_lds_fence();
       const v8i a = *reinterpret_cast<const v8i*>(pimg + 32 * lane);
