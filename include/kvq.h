@@ -257,8 +257,11 @@ kvq_status kvq_workspace_size_multi(const kvq_config* cfg, int32_t max_seq_token
  * workspace in between). kvq_decode_partials computes the partial softmax
  * state (running maximum, sum and unnormalised output, [P1] Minima-KV) of
  * every work unit -- a run of quantized blocks or of ring tokens of one
- * (sequence, kv head) -- into the workspace; kvq_decode_combine merges them
- * into out. Useful to time or overlap the two phases. */
+ * (sequence, kv head) -- into the workspace, and the side states of every
+ * output row: its sink tokens (P > 0) and its FP8 tier (W > 0, one state per
+ * 64 of the tier's tokens), each from a launch of its own before the units';
+ * kvq_decode_combine merges them all into out. Useful to time or overlap the
+ * two phases. */
 kvq_status kvq_decode_partials(const kvq_config* cfg, const kvq_cache* cache,
                                const void* q, float softmax_scale, int32_t max_seq_tokens,
                                void* workspace, size_t workspace_bytes, void* stream);
