@@ -1,0 +1,54 @@
+"""Limits of the decode path through the C ABI: a batch of several hundred
+ragged sequences (the unit plan takes 64 sequences per pass; empty sequences
+among them), and a sequence longer than the caller's max_seq_tokens (flagged
+on the device, its work capped to what the workspace was sized for)."""
+import numpy as np
+import pytest
+import torch
+
+from quantized_kv_cache_append_amd import workloads as W
+
+from kvq_harness import check_decode, check_records, default_scale, make_cache, spec_of, to_np
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("wname,over", [
+    ("llama2-7b-layer", dict(num_q_heads=1, num_kv_heads=1)),                  # block-scaled MHA kernel
+    ("llama3-8b-gqa-int2", dict(num_q_heads=4, num_kv_heads=1)),               # GQA matrix-core kernel
+])
+def test_several_hundred_ragged_sequences(wname, over):
+    rng = np.random.default_rng(17)
+    B = 300
+    lengths = [int(x) for x in rng.integers(0, 700, size=B)]
+    lengths[5] = lengths[77] = lengths[200] = 0
+    w = W.WORKLOADS[wname].replace(batch=B, **over)
+    print(f"[limits] {wname} B={B}", flush=True)
+    inp = W.make_layer(w, device="cpu", seed=18, lengths=lengths)
+    cache = make_cache(w, lengths, 256)
+    cache.prefill(inp.k.cuda(), inp.v.cuda(), lengths, 256)
+    out = cache.decode(inp.q.cuda())
+    torch.cuda.synchronize()
+    assert cache.read_device_error() == 0
+    assert torch.count_nonzero(out[5]) == 0 and torch.count_nonzero(out[200]) == 0
+    spec = spec_of(w, cache.cfg.res_capacity)
+    check_decode(out, spec, to_np(inp.q), to_np(inp.k), to_np(inp.v), lengths, scale=default_scale(w.head_dim))
+    check_records(cache, spec, to_np(inp.k), to_np(inp.v), lengths, [(b, 0) for b in range(0, B, 37)])
+
+
+def test_sequence_longer_than_the_bound_is_flagged():
+    w = W.WORKLOADS["llama2-7b-layer"].replace(batch=2, num_q_heads=2, num_kv_heads=2)
+    lengths = [1000, 300]
+    inp = W.make_layer(w, device="cpu", seed=19, lengths=lengths)
+    cache = make_cache(w, lengths, 256)
+    cache.prefill(inp.k.cuda(), inp.v.cuda(), lengths, 256)
+    torch.cuda.synchronize()
+    assert cache.read_device_error() == 0
+    out = cache.decode(inp.q.cuda(), max_seq_tokens=500)   # sequence 0 holds 27 blocks, the bound allows 11
+    torch.cuda.synchronize()
+    assert cache.read_device_error() & 16
+    assert torch.all(torch.isfinite(out))
+    # the sequence within the bound is still exact
+    spec = spec_of(w, cache.cfg.res_capacity)
+    check_decode(out, spec, to_np(inp.q), to_np(inp.k), to_np(inp.v), lengths, pairs=[(1, 0), (1, 1)],
+                 scale=default_scale(w.head_dim))
