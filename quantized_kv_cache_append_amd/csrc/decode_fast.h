@@ -482,26 +482,59 @@ __device__ __forceinline__ void quant_stream(const Geom& g, const WaveLds<C>& L,
   uint2 vsz[TPB][NGR][2];       // V scale / zero of the lane's 4 tokens per tile and group
   Chunk<C::VLANE> vc[KS_SET];   // value code chunks
 
-  // loaders for set si of span sp
-  auto load_ksz = [&](Span sp, int si) {
-    const uint8_t* p = span_rec<C>(g, blocks, table, sp, sp.begin + si * NB + cbk) + C::REC_KS + 64 * gq;
+  // The paged store reads a set's page numbers once, ahead of its record
+  // loads (raw values: an out-of-range page reads page 0 and its block is
+  // masked out), where a set spans at most two blocks; with four, the extra
+  // registers spill and each record load reads its own page number instead.
+  // The dense store needs none. The table index is the same in every lane.
+  constexpr bool EARLY = C::PAGED && NB <= 2;
+  auto set_pages = [&](Span sp, int si, int (&pg)[NB]) {
+    if constexpr (EARLY) {
+#pragma unroll
+      for (int bi = 0; bi < NB; ++bi) {
+        const int idx = __builtin_amdgcn_readfirstlane(sp.b * g.max_blocks + min(sp.begin + si * NB + bi, sp.end - 1));
+        pg[bi] = table[idx];
+      }
+    }
+  };
+  auto pick_page = [&](const int (&pg)[NB], int bi) -> int {
+    int page = pg[0];
+#pragma unroll
+    for (int k = 1; k < NB; ++k) page = bi == k ? pg[k] : page;
+    return page;
+  };
+  auto page_in_range = [&](int page) -> bool { return page >= 0 && page < g.num_pages; };
+  // record of block bi of set si of span sp
+  auto set_rec = [&](Span sp, int si, int bi, const int (&pg)[NB]) -> const uint8_t* {
+    if constexpr (!EARLY) {
+      return span_rec<C>(g, blocks, table, sp, sp.begin + si * NB + bi);
+    } else {
+      int page = pick_page(pg, bi);
+      page = page_in_range(page) ? page : 0;
+      return blocks + ((size_t)page * g.Hkv + sp.h) * (size_t)C::REC;
+    }
+  };
+
+  // loaders for set si of span sp, whose pages are pg
+  auto load_ksz = [&](Span sp, int si, const int (&pg)[NB]) {
+    const uint8_t* p = set_rec(sp, si, cbk, pg) + C::REC_KS + 64 * gq;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       ksz[k] = *reinterpret_cast<const uint4*>(p + 16 * k);
       ksz[4 + k] = *reinterpret_cast<const uint4*>(p + (C::REC_KZ - C::REC_KS) + 16 * k);
     }
   };
-  auto load_kc = [&](Span sp, int si) {
+  auto load_kc = [&](Span sp, int si, const int (&pg)[NB]) {
     const int off = C::REC_KC + n * C::KROW + gq * C::KLANE;
 #pragma unroll
     for (int bi = 0; bi < NB; ++bi) {
-      const uint8_t* p = span_rec<C>(g, blocks, table, sp, sp.begin + si * NB + bi) + off;
+      const uint8_t* p = set_rec(sp, si, bi, pg) + off;
 #pragma unroll
       for (int tt = 0; tt < TPB; ++tt) kc[bi][tt] = load_chunk<C::KLANE>(p + 16 * tt * C::KROW);
     }
   };
-  auto load_vsz = [&](Span sp, int si) {
-    const uint8_t* p = span_rec<C>(g, blocks, table, sp, sp.begin + si * NB + cbk) + C::REC_VS + 8 * gq;
+  auto load_vsz = [&](Span sp, int si, const int (&pg)[NB]) {
+    const uint8_t* p = set_rec(sp, si, cbk, pg) + C::REC_VS + 8 * gq;
 #pragma unroll
     for (int tt = 0; tt < TPB; ++tt)
 #pragma unroll
@@ -511,21 +544,16 @@ __device__ __forceinline__ void quant_stream(const Geom& g, const WaveLds<C>& L,
         vsz[tt][j][1] = *reinterpret_cast<const uint2*>(p + (C::REC_VZ - C::REC_VS) + off);
       }
   };
-  auto load_vc = [&](Span sp, int si) {
+  auto load_vc = [&](Span sp, int si, const int (&pg)[NB]) {
 #pragma unroll
     for (int ks = 0; ks < KS_SET; ++ks) {
       const int tok = 32 * ks + 8 * gq;   // set-relative first token of this lane group's run
       // for G >= 32 the k-step lies in one block (wave-uniform); G = 16 spans two
       const int bi = C::G >= 32 ? (32 * ks) / C::G : tok / C::G;
-      const uint8_t* p = span_rec<C>(g, blocks, table, sp, sp.begin + si * NB + bi);
+      const uint8_t* p = set_rec(sp, si, bi, pg);
       const int g8 = (tok % C::G) / 8;
       vc[ks] = load_chunk<C::VLANE>(p + C::REC_VC + (g8 * 16 + n) * C::VLANE);
     }
-  };
-  auto page_ok = [&](Span sp, int blk) -> bool {
-    if constexpr (!C::PAGED) return true;
-    const int page = table[(size_t)sp.b * g.max_blocks + blk];
-    return page >= 0 && page < g.num_pages;
   };
   // the query of span sp: raw words, then scaled into L.qs
   auto query_words = [&](Span sp, uint32_t (&w)[QW]) {
@@ -543,13 +571,18 @@ __device__ __forceinline__ void quant_stream(const Geom& g, const WaveLds<C>& L,
   // running state of the current unit: per lane for its column's head
   float m_ref, l_part, lam[NGR];
   f32x4 dpv[8];
+  bool page_ok = true;   // the page of this lane's column block in the set being computed is in range (EARLY)
 
   // One set si of span cur; prefetches set nsi of span nsp into each register
   // buffer right after its last use (always a valid set, so the loads are never
   // under a branch and stay in flight across the loop).
   auto run_set = [&](Span cur, int si, Span nsp, int nsi) {
+    int pgn[NB];   // pages of the prefetched set, read before its first record load
+    set_pages(nsp, nsi, pgn);
     const int my_b = cur.begin + si * NB + cbk;
-    const bool my_blk = col_used && my_b < cur.end && page_ok(cur, min(my_b, cur.end - 1));
+    bool my_blk = col_used && my_b < cur.end && page_ok;
+    if constexpr (C::PAGED && !EARLY)
+      my_blk = my_blk && page_in_range(table[(size_t)cur.b * g.max_blocks + min(my_b, cur.end - 1)]);
     // ---- B operand: q~ = q' * s_K (hi/lo) and kappa = q' . z_K for the column ----
     uint4 bhi[4], blo[4];
     float kap = 0.f;
@@ -581,7 +614,7 @@ __device__ __forceinline__ void quant_stream(const Geom& g, const WaveLds<C>& L,
       }
       kap = reduce_rows(kap, OpAdd{});
     }
-    load_ksz(nsp, nsi);
+    load_ksz(nsp, nsi, pgn);
 
     // ---- scores: D[token][column] for every tile of every block of the set ----
     float sc[TPB][4];
@@ -606,7 +639,7 @@ __device__ __forceinline__ void quant_stream(const Geom& g, const WaveLds<C>& L,
         for (int i = 0; i < 4; ++i) sc[tt][i] = mine ? acc[i] : sc[tt][i];
       }
     }
-    load_kc(nsp, nsi);
+    load_kc(nsp, nsi, pgn);
     if (!my_blk) {
 #pragma unroll
       for (int tt = 0; tt < TPB; ++tt)
@@ -677,7 +710,7 @@ __device__ __forceinline__ void quant_stream(const Geom& g, const WaveLds<C>& L,
         }
       }
     }
-    load_vsz(nsp, nsi);
+    load_vsz(nsp, nsi, pgn);
     wave_lds_fence();
 
     // ---- P.V: D[head hi|lo][channel] += p~ . code ----
@@ -693,8 +726,9 @@ __device__ __forceinline__ void quant_stream(const Geom& g, const WaveLds<C>& L,
 #pragma unroll
       for (int nt = 0; nt < 8; ++nt) dpv[nt] = mfma_bf16(av[(16 * nt) / C::GV], bv[nt], dpv[nt]);
     }
-    load_vc(nsp, nsi);
+    load_vc(nsp, nsi, pgn);
     wave_lds_fence();
+    if constexpr (EARLY) page_ok = page_in_range(pick_page(pgn, cbk));
   };
 
   // the unit's result: per head h', o = D[h'] + D[NG+h'] + lam(h', group)
@@ -736,10 +770,15 @@ __device__ __forceinline__ void quant_stream(const Geom& g, const WaveLds<C>& L,
     store_query(w);
     wave_lds_fence();
   }
-  load_ksz(cur, 0);
-  load_kc(cur, 0);
-  load_vsz(cur, 0);
-  load_vc(cur, 0);
+  {
+    int pg0[NB];
+    set_pages(cur, 0, pg0);
+    load_ksz(cur, 0, pg0);
+    load_kc(cur, 0, pg0);
+    load_vsz(cur, 0, pg0);
+    load_vc(cur, 0, pg0);
+    if constexpr (EARLY) page_ok = page_in_range(pick_page(pg0, cbk));
+  }
   while (true) {
     m_ref = -INFINITY;
     l_part = 0.f;
