@@ -52,3 +52,46 @@ def test_sequence_longer_than_the_bound_is_flagged():
     spec = spec_of(w, cache.cfg.res_capacity)
     check_decode(out, spec, to_np(inp.q), to_np(inp.k), to_np(inp.v), lengths, pairs=[(1, 0), (1, 1)],
                  scale=default_scale(w.head_dim))
+
+
+@pytest.mark.parametrize("wname,over", [
+    ("ragged-paged", dict(batch=3, num_q_heads=12, num_kv_heads=2)),                     # GQA kernel, n_g = 6
+    ("llama3-8b-gqa-int2", dict(batch=3, num_q_heads=8, num_kv_heads=2, paged=True)),   # GQA kernel, n_g = 4
+    ("llama2-7b-layer", dict(batch=3, num_q_heads=2, num_kv_heads=2, paged=True)),      # block-scaled MHA kernel
+])
+def test_out_of_range_page_skips_its_block(wname, over):
+    """A page-table entry outside [0, num_pages) drops that block from the
+    attention of its sequence; the other blocks and sequences are unchanged."""
+    from oracle import kivi
+    w = W.WORKLOADS[wname].replace(**over)
+    lengths = [600, 1111, 300]
+    print(f"[limits] bad page {wname}", flush=True)
+    inp = W.make_layer(w, device="cpu", seed=21, lengths=lengths)
+    cache = make_cache(w, lengths, 256)
+    cache.prefill(inp.k.cuda(), inp.v.cuda(), lengths, 256)
+    torch.cuda.synchronize()
+    assert cache.read_device_error() == 0
+    G = w.k_group
+    bad = {5: cache.cfg.num_pages, 20: -1}   # quantized blocks of sequence 1
+    assert max(bad) < (lengths[1] - w.residual) // G
+    for j, page in bad.items():
+        cache.page_table[1, j] = page
+    out = cache.decode(inp.q.cuda())
+    torch.cuda.synchronize()
+    got = out.double().cpu().numpy()
+    assert np.all(np.isfinite(got))
+    spec = spec_of(w, cache.cfg.res_capacity)
+    q_np, k_np, v_np = to_np(inp.q), to_np(inp.k), to_np(inp.v)
+    scale = default_scale(w.head_dim)
+    ref = kivi.decode_attention(spec, q_np, k_np, v_np, lengths, scale=scale,
+                                pairs=[(b, h) for b in (0, 2) for h in range(w.num_kv_heads)])
+    ng = w.num_q_heads // w.num_kv_heads
+    keep = np.ones(lengths[1], bool)
+    for j in bad:
+        keep[j * G:(j + 1) * G] = False
+    for h in range(w.num_kv_heads):
+        kh, vh = kivi.pair_cache_fp64(spec, k_np[1, h], v_np[1, h], lengths[1])
+        ref[1, h * ng:(h + 1) * ng] = kivi.attention_fp64(q_np[1, h * ng:(h + 1) * ng], kh[keep], vh[keep], scale)
+    diff = np.abs(got - ref)
+    rel = np.linalg.norm(got - ref) / np.linalg.norm(ref)
+    assert diff.max() <= 2e-3 and rel <= 1e-3, (diff.max(), rel)
