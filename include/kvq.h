@@ -94,6 +94,13 @@
  * index out of range) skip the affected work and OR a KVQ_DEV_* bit into the
  * cache's sticky error word (read it with kvq_read_device_error). No call
  * aborts or throws.
+ *
+ * Streams and graphs. Every call that takes a stream only enqueues kernels on
+ * it: no allocation, memset, copy or synchronisation. Append, flush and decode
+ * calls may therefore be captured in a HIP graph and replayed, provided the
+ * caller passes the workspace and a max_seq_tokens that covers every length
+ * the replays reach (the captured value is fixed). kvq_read_device_error
+ * copies to the host and is not capturable.
  */
 #ifndef KVQ_H
 #define KVQ_H
