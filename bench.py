@@ -14,6 +14,10 @@ Prints one JSON line on stdout; human-readable detail goes to stderr.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--sink P]
 
+The default workload is the largest configuration that fits one GPU: the
+70B-shaped model at 131,072 tokens, a full 80-layer decode step (GQA 64/8,
+d = 128, batch 4, bf16 inputs, INT2 keys and values, G = G_V = 64, R = 128).
+
 With --query-tokens T a step appends T tokens per sequence and runs the
 attention of all T of them, causal within the block (kvq_decode_attention_multi:
 block-wise prefill or checking T drafted tokens).
@@ -193,9 +197,33 @@ def decode_kernel_name(w, T=1) -> str:
     return "decode_generic_kernel"
 
 
-def cpu_baseline(w, inp, lengths, budget_s=15.0, sink=0):
-    """Time the oracle's decode attention on a bounded sample of (sequence, kv head)
-    pairs of the same workload; returns GB/s of the same algorithmic bytes."""
+def host_description():
+    """The host the oracle runs on: logical CPUs, the ones this process may use,
+    and the CPU model."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        affinity = os.cpu_count()
+    return {"host_cpus": os.cpu_count(), "affinity_cpus": affinity, "cpu_model": model}
+
+
+def cpu_baseline(w, inp, lengths, budget_s=15.0, sink=0, quant_budget_s=4.0):
+    """Time the oracle on the host, one thread: its decode attention on a bounded
+    sample of (sequence, kv head) pairs of the same workload (GB/s of the same
+    algorithmic bytes), and its quantizer (formula F + packing) over the blocks
+    of one pair (GB/s of rows read + records written). Also reports, ungated,
+    the fidelity of the quantized cache: the oracle's quantized attention
+    against exact attention on the unquantized inputs, over the sampled pairs."""
+    import numpy as np
     from threadpoolctl import threadpool_limits
 
     from oracle import kivi
@@ -205,30 +233,72 @@ def cpu_baseline(w, inp, lengths, budget_s=15.0, sink=0):
     pairs = [(b, h) for b in range(w.batch) for h in range(w.num_kv_heads)]
     done, nbytes, t_used = 0, 0.0, 0.0
     per_tok = kivi.record_bytes(spec) / w.k_group
+    n_g = w.num_q_heads // w.num_kv_heads
+    diff2 = ref2 = 0.0
+    max_abs = 0.0
     with threadpool_limits(limits=1):
         for b, h in pairs:
-            k = {(b, h): inp.k[b, h].float().cpu().numpy()}
-            v = {(b, h): inp.v[b, h].float().cpu().numpy()}
-
-            class _P:
-                def __init__(s, d):
-                    s.d = d
-
-                def __getitem__(s, key):
-                    return s.d[(key[0], key[1])]
-            t0 = time.perf_counter()
-            kivi.decode_attention(spec, q, _P(k), _P(v), lengths, pairs=[(b, h)])
-            t_used += time.perf_counter() - t0
             S = lengths[b]
+            k = inp.k[b, h, :S].float().cpu().numpy()[None, None]
+            v = inp.v[b, h, :S].float().cpu().numpy()[None, None]
+            qp = q[b:b + 1, h * n_g:(h + 1) * n_g]
+            one = kivi.CacheSpec(1, n_g, 1, w.head_dim, w.k_bits, w.v_bits, w.k_group, w.v_group,
+                                 w.residual, w.residual + w.k_group, w.dtype, sink=sink)
+            t0 = time.perf_counter()
+            got = kivi.decode_attention(one, qp, k, v, [S])
+            t_used += time.perf_counter() - t0
+            exact = kivi.exact_attention(one, qp, k, v, [S])
+            diff2 += float(np.sum((got - exact) ** 2))
+            ref2 += float(np.sum(exact ** 2))
+            max_abs = max(max_abs, float(np.max(np.abs(got - exact))))
             Q = quantized_prefix(max(S - sink, 0), w.residual, w.k_group)
-            nbytes += Q * per_tok + (S - Q) * w.head_dim * 4 + w.num_q_heads // w.num_kv_heads * w.head_dim * 6
+            nbytes += Q * per_tok + (S - Q) * w.head_dim * 4 + n_g * w.head_dim * 6
             done += 1
             if t_used > budget_s:
                 break
-    return {"value": nbytes / t_used / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"numpy fp64 oracle decode attention (quantize+dequantize+attend) on {done} of "
-                      f"{len(pairs)} (sequence, kv head) pairs of one {w.name} step, {t_used:.1f} s, "
-                      f"BLAS limited to 1 thread"}
+        # the quantizer: formula F and packing of one pair's blocks, as many as fit the budget
+        b0, h0 = pairs[0]
+        kq = inp.k[b0, h0].float().cpu().numpy()
+        vq = inp.v[b0, h0].float().cpu().numpy()
+        G = w.k_group
+        nblk = quantized_prefix(lengths[b0], w.residual, G) // G
+        qt, qblk = 0.0, 0
+        for j in range(nblk):
+            t0 = time.perf_counter()
+            kivi.block_to_bytes(kivi.quantize_block(spec, kq[j * G:(j + 1) * G], vq[j * G:(j + 1) * G]))
+            qt += time.perf_counter() - t0
+            qblk += 1
+            if qt > quant_budget_s:
+                break
+    qbytes = qblk * (G * w.head_dim * 2 * 2 + kivi.record_bytes(spec))
+    res = {"value": nbytes / t_used / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+           "sample": f"numpy fp64 oracle decode attention (quantize+dequantize+attend) on {done} of "
+                     f"{len(pairs)} (sequence, kv head) pairs of one {w.name} step, {t_used:.1f} s, "
+                     f"BLAS limited to 1 thread",
+           "blas_threads": 1,
+           "quantize": {"value": qbytes / qt / 1e9, "unit": "GB/s",
+                        "sample": f"oracle formula F + packing of {qblk} blocks of one (sequence, kv head), "
+                                  f"{qt:.1f} s"},
+           "fidelity_vs_unquantized": {"rel_l2": (diff2 / ref2) ** 0.5 if ref2 > 0 else 0.0, "max_abs": max_abs,
+                                       "pairs": done,
+                                       "note": "oracle attention on the quantized cache against exact attention "
+                                               "on the unquantized inputs (ungated: the bits-vs-fidelity trade)"}}
+    res.update(host_description())
+    return res
+
+
+def copy_probe(mb, dev):
+    """Device-to-device copies of a known size, for scaling the HBM traffic
+    counters (a profiling aid: runs after the timed region)."""
+    import torch
+    n = mb << 20
+    src = torch.ones(n, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"[bench] copy probe: 3 device-to-device copies of {n} bytes")
+    del src, dst
 
 
 def bench_layers(w, args, dev):
@@ -240,7 +310,7 @@ def bench_layers(w, args, dev):
     from quantized_kv_cache_append_amd import workloads as W
     from quantized_kv_cache_append_amd.cache import cache_for_workload
 
-    L = w.layers
+    L = args.layers or w.layers
     lengths0 = W.sequence_lengths(w)
     total_steps = args.warmup + 2 * args.steps
     chunk = 8192
@@ -295,6 +365,8 @@ def bench_layers(w, args, dev):
     err = max(c.read_device_error() for c in caches)
     if err:
         raise SystemExit(f"device error word {err} after the timed steps")
+    if args.copy_probe_mb > 0:
+        copy_probe(args.copy_probe_mb, dev)
 
     # algorithmic bytes: every layer sees the same lengths
     lens = list(lengths0)
@@ -327,7 +399,7 @@ def bench_layers(w, args, dev):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": w.dtype,
         "data": "synthetic",
         "config": {"workload": w.name, "layers": L, "batch": w.batch, "num_q_heads": w.num_q_heads,
                    "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim, "seq_len": max(lengths0),
@@ -358,9 +430,9 @@ def bench_layers(w, args, dev):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="llama2-7b-layer")
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="llama-70b-128k-80layer")
     ap.add_argument("--copies", type=int, default=0, help="cache copies to rotate (0: auto, > 3x MALL)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
@@ -369,6 +441,9 @@ def main():
                     help="tokens per sequence per step, attended causally as one block")
     ap.add_argument("--fp8-blocks", type=int, default=0,
                     help="keep the W most recent quantized blocks also as FP8 records, read by decode")
+    ap.add_argument("--layers", type=int, default=0,
+                    help="multi-layer workloads: time this many layers instead of all (profiling runs; "
+                         "the JSON line's config.layers says how many were timed)")
     ap.add_argument("--sink", type=int, default=0,
                     help="keep the first SINK tokens of every sequence in full precision (attention sink)")
     args = ap.parse_args()
@@ -506,13 +581,7 @@ def main():
         f"({achieved / PEAK_HBM_GBPS * 100:.1f}% of 8 TB/s); sources {source_hash()}")
 
     if args.copy_probe_mb > 0:
-        n = args.copy_probe_mb << 20
-        src = torch.ones(n, dtype=torch.uint8, device=dev)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        log(f"[bench] copy probe: 3 device-to-device copies of {n} bytes")
+        copy_probe(args.copy_probe_mb, dev)
 
     kernel = decode_kernel_name(w, T)
     if T > 1:   # the multi-token call's window holds its combine launch too
@@ -535,7 +604,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": w.dtype,
         "data": "synthetic",
         "config": {"workload": w.name, "batch": w.batch, "num_q_heads": w.num_q_heads,
                    "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim, "seq_len": max(lengths0),

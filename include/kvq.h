@@ -30,11 +30,15 @@
  *        section on OSCAR (sink and recent tokens kept in BF16, the history
  *        compressed to INT2).
  *
- * Memory model. The caller owns every buffer (sized with kvq_get_layout and
- * kvq_workspace_size). The library allocates nothing, keeps no global state,
- * borrows the pointers for the duration of a call and enqueues its kernels on
- * the caller's HIP stream (passed as void*; NULL is the default stream). All
- * pointers in kvq_cache and every tensor argument are DEVICE pointers.
+ * Memory model. The caller owns every buffer (sized with kvq_layout_bytes and
+ * kvq_workspace_size). The library allocates nothing and borrows the pointers
+ * for the duration of a call; it enqueues its kernels on the caller's HIP
+ * stream (passed as void*; NULL is the default stream). All pointers in
+ * kvq_cache and every tensor argument are DEVICE pointers. The only state the
+ * library keeps across calls is a host-side table of launch grid sizes per
+ * (device, kernel, LDS bytes), filled on first use under a mutex: calls from
+ * several host threads are safe as long as they do not share a cache or a
+ * workspace.
  *
  * One kvq_cache is one layer. For each (sequence b, kv head h), with a sink of
  * P >= 0 tokens (kvq_config.sink; P = 0: none):
@@ -89,17 +93,19 @@
  * Input values whose group minimum lies outside the fp16 normal range are
  * outside the supported domain (results stay deterministic).
  *
- * Errors. Argument errors are reported synchronously, before any launch.
- * Conditions only the device can see (ring full, flush past max_blocks, page
- * index out of range) skip the affected work and OR a KVQ_DEV_* bit into the
- * cache's sticky error word (read it with kvq_read_device_error). No call
- * aborts or throws.
+ * Errors. Argument errors are reported synchronously, before any launch:
+ * KVQ_ERR_CAPACITY when the request cannot fit the cache as configured (an
+ * append larger than the sink plus the ring, or a max_seq_tokens beyond what
+ * the sink, max_blocks blocks and the ring can hold). Conditions only the
+ * device can see (ring full, flush past max_blocks, page index out of range)
+ * skip the affected work and OR a KVQ_DEV_* bit into the cache's sticky error
+ * word (read it with kvq_get_device_error). No call aborts or throws.
  *
  * Streams and graphs. Every call that takes a stream only enqueues kernels on
  * it: no allocation, memset, copy or synchronisation. Append, flush and decode
  * calls may therefore be captured in a HIP graph and replayed, provided the
  * caller passes the workspace and a max_seq_tokens that covers every length
- * the replays reach (the captured value is fixed). kvq_read_device_error
+ * the replays reach (the captured value is fixed). kvq_get_device_error
  * copies to the host and is not capturable.
  */
 #ifndef KVQ_H
@@ -116,8 +122,9 @@ typedef enum {
   KVQ_OK = 0,
   KVQ_ERR_INVALID_ARG = 1,   /* null pointer, non-positive or inconsistent size */
   KVQ_ERR_UNSUPPORTED = 2,   /* a well-formed configuration with no kernel in this build */
-  KVQ_ERR_WORKSPACE = 3,     /* workspace smaller than kvq_workspace_size() */
-  KVQ_ERR_LAUNCH = 4,        /* the HIP runtime rejected a launch or a copy */
+  KVQ_ERR_CAPACITY = 3,      /* the request exceeds what the cache as configured can hold */
+  KVQ_ERR_WORKSPACE = 4,     /* workspace smaller than kvq_workspace_size() */
+  KVQ_ERR_LAUNCH = 5,        /* the HIP runtime rejected a launch or a copy */
 } kvq_status;
 
 enum { KVQ_F16 = 0, KVQ_BF16 = 1 };
@@ -132,7 +139,7 @@ enum {
 };
 
 typedef struct {
-  int32_t batch;          /* B, sequences in this cache                                   */
+  int32_t batch;          /* B, sequences in this cache: 1 .. 1024                         */
   int32_t num_q_heads;    /* H_q                                                          */
   int32_t num_kv_heads;   /* H_kv; H_q % H_kv == 0; query head h' reads kv head h'/(H_q/H_kv) */
   int32_t head_dim;       /* d: 64 or 128                                                  */
@@ -174,8 +181,13 @@ typedef struct {
 } kvq_cache;
 
 /* Host only. Validates cfg and fills the byte sizes of every cache buffer.
- * Returns KVQ_ERR_INVALID_ARG / KVQ_ERR_UNSUPPORTED for a rejected config. */
-kvq_status kvq_get_layout(const kvq_config* cfg, kvq_layout* out);
+ * [P4] section "Le problème" gives the dense cache as 2*L*H*d*S*bytes (per
+ * layer and sequence: 2*H_kv*d*S*bytes); here each quantized token costs
+ * `record / G` bytes per kv head instead of 2*d*bytes (96 B against 512 B for
+ * INT2, G = 32, d = 128), and only the sink and the ring keep 2*d*bytes per
+ * token. Returns KVQ_ERR_INVALID_ARG / KVQ_ERR_UNSUPPORTED for a rejected
+ * config. */
+kvq_status kvq_layout_bytes(const kvq_config* cfg, kvq_layout* out);
 
 /* Host only. Bytes of the decode workspace for sequences of at most
  * max_seq_tokens tokens (partial softmax states of the sequence splits, and
@@ -191,7 +203,8 @@ kvq_status kvq_workspace_size(const kvq_config* cfg, int32_t max_seq_tokens, siz
  * S_b grows by n_new[b]. A sequence whose ring would overflow (its ring tokens
  * after the call, max(S_b + n_new[b] - P, 0) - Q_b, exceed res_capacity) takes
  * nothing and sets KVQ_DEV_RESIDUAL_FULL; call kvq_flush_residual between
- * large chunks. */
+ * large chunks. n_max > P + res_capacity can never fit and returns
+ * KVQ_ERR_CAPACITY before any launch. */
 kvq_status kvq_append(const kvq_config* cfg, const kvq_cache* cache,
                       const void* k_new, const void* v_new,
                       const int32_t* n_new, int32_t n_max, void* stream);
@@ -219,7 +232,9 @@ kvq_status kvq_append_flush(const kvq_config* cfg, const kvq_cache* cache,
  *   out: [B][H_q][d] fp32 (device);
  *   softmax_scale: multiplies q.k; <= 0 selects 1/sqrt(d);
  *   max_seq_tokens: an upper bound on every S_b (sizes the grid; the exact
- *                   lengths are read on the device);
+ *                   lengths are read on the device); above P + max_blocks*G +
+ *                   res_capacity, which no sequence can reach, it returns
+ *                   KVQ_ERR_CAPACITY;
  *   workspace: device scratch of at least kvq_workspace_size(cfg, max_seq_tokens)
  *              bytes; its contents need no initialisation.
  * A sequence with S_b == 0 gets a zero output. The sink tokens of a sequence
@@ -277,9 +292,10 @@ kvq_status kvq_decode_combine(const kvq_config* cfg, const kvq_cache* cache, flo
                               void* stream);
 
 /* Copies the cache's sticky error word (an OR of KVQ_DEV_* bits; 0 = nothing
- * so far) into *err after the stream's earlier work, waiting for the stream. */
-kvq_status kvq_read_device_error(const kvq_config* cfg, const kvq_cache* cache, void* stream,
-                                 int32_t* err);
+ * so far) into *err after the stream's earlier work, waiting for the stream.
+ * cfg locates the word (it follows the B per-sequence state words). */
+kvq_status kvq_get_device_error(const kvq_config* cfg, const kvq_cache* cache, void* stream,
+                                int32_t* err);
 
 /* Static string naming a status code. */
 const char* kvq_status_string(kvq_status status);

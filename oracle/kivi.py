@@ -249,26 +249,6 @@ def block_to_bytes(sec) -> np.ndarray:
     return np.concatenate(parts)
 
 
-def bytes_to_block(spec: CacheSpec, rec: np.ndarray):
-    """Parse record bytes back into section arrays (inverse of block_to_bytes)."""
-    sizes = record_sections(spec)
-    G, d, gv = spec.k_group, spec.head_dim, spec.v_group
-    out, off = {}, 0
-    shapes = {
-        "k_codes": ((G, d * spec.k_bits // 32), np.uint32),
-        "k_scale": ((d,), np.float16), "k_zero": ((d,), np.float16),
-        "v_codes": ((G * d * spec.v_bits // 32,), np.uint32),
-        "v_scale": ((d // gv, G), np.float16), "v_zero": ((d // gv, G), np.float16),
-    }
-    rec = np.ascontiguousarray(rec, dtype=np.uint8)
-    for name in ("k_codes", "k_scale", "k_zero", "v_codes", "v_scale", "v_zero"):
-        n = sizes[name]
-        shp, dt = shapes[name]
-        out[name] = rec[off:off + n].view(dt).reshape(shp)
-        off += n
-    return out
-
-
 # ---------------------------------------------------------------------------
 # FP8 tier [P1' Minima-KV: recent pages in FP8]. Formula F8, per token row x
 # (d values), every step an fp32 IEEE operation rounded to nearest even:
@@ -520,5 +500,6 @@ def kv_cache_bytes(layers: int, heads: int, head_dim: int, tokens: int, bytes_pe
 
 
 def quantized_bytes_per_token(spec: CacheSpec) -> float:
-    """Bytes one quantized token occupies per kv head (codes + scale/zero)."""
+    """Bytes one quantized token occupies per kv head (codes + scale/zero): the
+    per-token cost that replaces 2 * d * bytes of the closed form above."""
     return record_bytes(spec) / spec.k_group

@@ -14,12 +14,12 @@ import os
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIBRARY_PATH = os.path.join(_PKG, "libkvq.so")
 
-KVQ_OK, KVQ_ERR_INVALID_ARG, KVQ_ERR_UNSUPPORTED, KVQ_ERR_WORKSPACE, KVQ_ERR_LAUNCH = range(5)
+KVQ_OK, KVQ_ERR_INVALID_ARG, KVQ_ERR_UNSUPPORTED, KVQ_ERR_CAPACITY, KVQ_ERR_WORKSPACE, KVQ_ERR_LAUNCH = range(6)
 KVQ_F16, KVQ_BF16 = 0, 1
 KVQ_DEV_RESIDUAL_FULL, KVQ_DEV_BLOCKS_FULL, KVQ_DEV_BAD_PAGE, KVQ_DEV_BAD_COUNT, KVQ_DEV_TOO_LONG = 1, 2, 4, 8, 16
 
-EXPORTED = ("kvq_get_layout", "kvq_workspace_size", "kvq_append", "kvq_append_flush", "kvq_flush_residual",
-            "kvq_decode_attention", "kvq_decode_partials", "kvq_decode_combine", "kvq_read_device_error",
+EXPORTED = ("kvq_layout_bytes", "kvq_workspace_size", "kvq_append", "kvq_append_flush", "kvq_flush_residual",
+            "kvq_decode_attention", "kvq_decode_partials", "kvq_decode_combine", "kvq_get_device_error",
             "kvq_status_string", "kvq_decode_attention_multi", "kvq_workspace_size_multi")
 
 
@@ -64,7 +64,7 @@ def load():
     P, I32, SZ, F = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t, ctypes.c_float
     cfgp, cachep = ctypes.POINTER(kvq_config), ctypes.POINTER(kvq_cache)
     sig = {
-        "kvq_get_layout": [cfgp, ctypes.POINTER(kvq_layout)],
+        "kvq_layout_bytes": [cfgp, ctypes.POINTER(kvq_layout)],
         "kvq_workspace_size": [cfgp, I32, ctypes.POINTER(SZ)],
         "kvq_append": [cfgp, cachep, P, P, P, I32, P],
         "kvq_append_flush": [cfgp, cachep, P, P, P, I32, P],
@@ -72,7 +72,7 @@ def load():
         "kvq_decode_attention": [cfgp, cachep, P, P, F, I32, P, SZ, P],
         "kvq_decode_partials": [cfgp, cachep, P, F, I32, P, SZ, P],
         "kvq_decode_combine": [cfgp, cachep, P, I32, P, SZ, P],
-        "kvq_read_device_error": [cfgp, cachep, P, ctypes.POINTER(I32)],
+        "kvq_get_device_error": [cfgp, cachep, P, ctypes.POINTER(I32)],
         "kvq_status_string": [ctypes.c_int],
         "kvq_decode_attention_multi": [cfgp, cachep, P, I32, P, F, I32, P, SZ, P],
         "kvq_workspace_size_multi": [cfgp, I32, I32, ctypes.POINTER(SZ)],
@@ -96,9 +96,9 @@ def _check(status: int, where: str):
 
 # --- thin wrappers with the C names ---------------------------------------------------
 
-def kvq_get_layout(cfg: kvq_config) -> kvq_layout:
+def kvq_layout_bytes(cfg: kvq_config) -> kvq_layout:
     out = kvq_layout()
-    _check(load().kvq_get_layout(ctypes.byref(cfg), ctypes.byref(out)), "kvq_get_layout")
+    _check(load().kvq_layout_bytes(ctypes.byref(cfg), ctypes.byref(out)), "kvq_layout_bytes")
     return out
 
 
@@ -153,10 +153,10 @@ def kvq_decode_combine(cfg, cache, out_ptr, max_seq_tokens, ws_ptr, ws_bytes, st
                                      int(ws_bytes), stream), "kvq_decode_combine")
 
 
-def kvq_read_device_error(cfg, cache, stream) -> int:
+def kvq_get_device_error(cfg, cache, stream) -> int:
     err = ctypes.c_int32(0)
-    _check(load().kvq_read_device_error(ctypes.byref(cfg), ctypes.byref(cache), stream, ctypes.byref(err)),
-           "kvq_read_device_error")
+    _check(load().kvq_get_device_error(ctypes.byref(cfg), ctypes.byref(cache), stream, ctypes.byref(err)),
+           "kvq_get_device_error")
     return err.value
 
 

@@ -60,7 +60,7 @@ class QuantizedKVCache:
                                 v_group=v_group, residual=residual, res_capacity=res_capacity,
                                 max_blocks=max_blocks, num_pages=num_pages, dtype=_DTYPES[dtype], sink=sink,
                                 fp8_blocks=fp8_blocks)
-        self.layout = B.kvq_get_layout(self.cfg)
+        self.layout = B.kvq_layout_bytes(self.cfg)
         dev = self.device
         self.blocks = torch.zeros(self.layout.blocks, dtype=torch.uint8, device=dev)
         self.page_table = page_table.to(dev).contiguous() if page_table is not None else None
@@ -228,7 +228,7 @@ class QuantizedKVCache:
 
     # --- inspection (tests) --------------------------------------------------------
     def read_device_error(self) -> int:
-        return B.kvq_read_device_error(self.cfg, self.cache, _stream_handle())
+        return B.kvq_get_device_error(self.cfg, self.cache, _stream_handle())
 
     def lengths(self):
         """(Q_b, S_b) per sequence, copied to the host."""

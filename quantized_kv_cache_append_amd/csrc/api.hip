@@ -1,6 +1,7 @@
 // Host side of the C ABI declared in include/kvq.h: argument validation, byte
-// layout arithmetic and kernel launches on the caller's stream. No allocation,
-// no global state.
+// layout arithmetic and kernel launches on the caller's stream. No allocation;
+// the only state kept across calls is the launch-grid table of
+// persistent_grid() (common.h).
 //
 // Sources:
 //   [P4] patricehuetz.fr, "Quantification du KV-Cache : TurboQuant et l'état de
@@ -17,7 +18,10 @@ using kvq::Geom;
 
 namespace {
 
-constexpr int kMaxBatch = 4096;
+// Every decode workgroup keeps a copy of the unit plan (16 + 7B ints) in LDS
+// beside its four waves' buffers (at most 4 x 13 KB); at B = 1024 that is at
+// most 81 KB, inside gfx950's 160 KB per workgroup.
+constexpr int kMaxBatch = 1024;
 constexpr int kMaxSink = 1 << 20;   // sink tokens per sequence
 constexpr int kMaxFp8Blocks = 4096;  // FP8 blocks per (sequence, kv head)
 
@@ -62,11 +66,20 @@ kvq_status validate_cache(const kvq_config* c, const kvq_cache* k) {
 
 kvq_status launched(hipError_t e) { return e == hipSuccess ? KVQ_OK : KVQ_ERR_LAUNCH; }
 
+// The most tokens a sequence can hold: the sink, max_blocks quantized blocks
+// and a full ring.
+long long capacity_tokens(const kvq_config* c) {
+  return (long long)c->sink + (long long)c->max_blocks * c->k_group + c->res_capacity;
+}
+// Rows of one append that can never fit: the sink takes at most P, the ring
+// at most res_capacity.
+bool append_fits(const kvq_config* c, int32_t n_max) { return (long long)n_max <= (long long)c->sink + c->res_capacity; }
+
 }  // namespace
 
 extern "C" {
 
-kvq_status kvq_get_layout(const kvq_config* cfg, kvq_layout* out) {
+kvq_status kvq_layout_bytes(const kvq_config* cfg, kvq_layout* out) {
   const kvq_status st = validate(cfg);
   if (st != KVQ_OK) return st;
   if (out == nullptr) return KVQ_ERR_INVALID_ARG;
@@ -128,6 +141,7 @@ kvq_status kvq_append(const kvq_config* cfg, const kvq_cache* cache, const void*
   if ((st = validate_cache(cfg, cache)) != KVQ_OK) return st;
   if (k_new == nullptr || v_new == nullptr || n_max < 0) return KVQ_ERR_INVALID_ARG;
   if ((reinterpret_cast<uintptr_t>(k_new) | reinterpret_cast<uintptr_t>(v_new)) & 15) return KVQ_ERR_INVALID_ARG;
+  if (!append_fits(cfg, n_max)) return KVQ_ERR_CAPACITY;
   if (n_max == 0) return KVQ_OK;
   return launched(kvq::launch_append(kvq::make_geom(*cfg), *cache, k_new, v_new, n_new, n_max,
                                      static_cast<hipStream_t>(stream)));
@@ -140,6 +154,7 @@ kvq_status kvq_append_flush(const kvq_config* cfg, const kvq_cache* cache, const
   if ((st = validate_cache(cfg, cache)) != KVQ_OK) return st;
   if (k_new == nullptr || v_new == nullptr || n_max < 0) return KVQ_ERR_INVALID_ARG;
   if ((reinterpret_cast<uintptr_t>(k_new) | reinterpret_cast<uintptr_t>(v_new)) & 15) return KVQ_ERR_INVALID_ARG;
+  if (!append_fits(cfg, n_max)) return KVQ_ERR_CAPACITY;
   const hipStream_t s = static_cast<hipStream_t>(stream);
   if (n_max == 0) return launched(kvq::launch_flush(kvq::make_geom(*cfg), *cache, s));
   return launched(kvq::launch_append_flush(kvq::make_geom(*cfg), *cache, k_new, v_new, n_new, n_max, s));
@@ -161,6 +176,7 @@ kvq_status decode_args(const kvq_config* cfg, const kvq_cache* cache, int32_t ma
   if (st != KVQ_OK) return st;
   if ((st = validate_cache(cfg, cache)) != KVQ_OK) return st;
   if (max_seq_tokens < 0 || !std::isfinite(softmax_scale)) return KVQ_ERR_INVALID_ARG;
+  if (max_seq_tokens > capacity_tokens(cfg)) return KVQ_ERR_CAPACITY;
   if ((st = query_geom(cfg, T, g)) != KVQ_OK) return st;
   plan = kvq::plan_decode(g, max_seq_tokens);
   if (workspace == nullptr || workspace_bytes < plan.ws_bytes) return KVQ_ERR_WORKSPACE;
@@ -220,8 +236,8 @@ kvq_status kvq_decode_combine(const kvq_config* cfg, const kvq_cache* cache, flo
   return launched(kvq::launch_decode_combine(g, *cache, out, plan, workspace, static_cast<hipStream_t>(stream)));
 }
 
-kvq_status kvq_read_device_error(const kvq_config* cfg, const kvq_cache* cache, void* stream,
-                                 int32_t* err) {
+kvq_status kvq_get_device_error(const kvq_config* cfg, const kvq_cache* cache, void* stream,
+                                int32_t* err) {
   const kvq_status st = validate(cfg);
   if (st != KVQ_OK) return st;
   if (cache == nullptr || cache->state == nullptr || err == nullptr) return KVQ_ERR_INVALID_ARG;
@@ -240,6 +256,7 @@ const char* kvq_status_string(kvq_status s) {
     case KVQ_OK: return "ok";
     case KVQ_ERR_INVALID_ARG: return "invalid argument";
     case KVQ_ERR_UNSUPPORTED: return "unsupported configuration";
+    case KVQ_ERR_CAPACITY: return "request exceeds the cache's capacity";
     case KVQ_ERR_WORKSPACE: return "workspace too small";
     case KVQ_ERR_LAUNCH: return "kernel launch failed";
   }

@@ -12,6 +12,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "kvq.h"
 
@@ -138,8 +139,10 @@ __device__ __forceinline__ bool last_arrival(int* counter, int total) {
 // Persistent grid of a kernel of 256-thread workgroups: as many workgroups as
 // stay resident at once (from the runtime's occupancy for this kernel and LDS
 // size), rounded up to a multiple of the decode work queues. The answer is
-// remembered per kernel, device and LDS size (the occupancy query is slow next
-// to a launch).
+// remembered per kernel (each instantiation has its own table), device and LDS
+// size, since the occupancy query is slow next to a launch. The table is the
+// library's only state across calls; a mutex guards it, so host threads may
+// launch concurrently.
 template <class K>
 inline int persistent_grid(K kernel, size_t lds_bytes) {
   struct Memo {
@@ -147,17 +150,22 @@ inline int persistent_grid(K kernel, size_t lds_bytes) {
     size_t lds;
     int grid;
   };
+  static std::mutex lock;
   static Memo memo[16] = {};
   static int used = 0;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) dev = 0;
-  for (int i = 0; i < used; ++i)
-    if (memo[i].dev == dev && memo[i].lds == lds_bytes) return memo[i].grid;
+  {
+    std::lock_guard<std::mutex> g(lock);
+    for (int i = 0; i < used; ++i)
+      if (memo[i].dev == dev && memo[i].lds == lds_bytes) return memo[i].grid;
+  }
   int cus = 0, per_cu = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 256, lds_bytes) != hipSuccess || per_cu < 1)
     per_cu = 1;
   const int grid = (cus * per_cu + kQueues - 1) / kQueues * kQueues;
+  std::lock_guard<std::mutex> g(lock);
   if (used < 16) memo[used++] = Memo{dev, lds_bytes, grid};
   return grid;
 }

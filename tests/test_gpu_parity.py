@@ -11,6 +11,7 @@ import numpy as np
 import pytest
 import torch
 
+from quantized_kv_cache_append_amd import binding as B
 from quantized_kv_cache_append_amd import workloads as W
 
 from kvq_harness import check_decode, check_records, default_scale, make_cache, spec_of, to_np
@@ -181,11 +182,19 @@ def test_decode_steps_across_flush(wname, fused):
 def test_ring_overflow_sets_device_error():
     w = W.WORKLOADS["llama2-7b-layer"].replace(batch=1, num_q_heads=1, num_kv_heads=1)
     cache = make_cache(w, [300], 32)   # ring capacity R + G - 1 + 32 = 191
+    # one append of more rows than the ring has slots is refused on the host
     kk = torch.zeros(1, 1, 200, 128, dtype=torch.float16, device="cuda")
-    cache.append(kk, kk)
+    with pytest.raises(B.KVQError) as e:
+        cache.append(kk, kk)
+    assert e.value.status == B.KVQ_ERR_CAPACITY
+    # two appends that fit one by one but not together overflow on the device
+    first = torch.zeros(1, 1, 150, 128, dtype=torch.float16, device="cuda")
+    second = torch.zeros(1, 1, 50, 128, dtype=torch.float16, device="cuda")
+    cache.append(first, first)
+    cache.append(second, second)
     torch.cuda.synchronize()
     assert cache.read_device_error() & 1
-    assert cache.lengths() == ([0], [0])
+    assert cache.lengths() == ([0], [150])
 
 
 def test_fused_append_flush_ragged_counts_match_separate_calls():

@@ -7,6 +7,7 @@ attention within the usual max-abs 2e-3 / rel-L2 1e-3."""
 import pytest
 import torch
 
+from quantized_kv_cache_append_amd import binding as B
 from quantized_kv_cache_append_amd import workloads as W
 
 from kvq_harness import check_decode, check_records, default_scale, make_cache, spec_of, to_np
@@ -123,12 +124,24 @@ def test_sink_multi_token_append_straddles_the_sink():
 
 def test_sink_ring_overflow_counts_tokens_after_the_sink():
     # ring capacity R + G - 1 + 32 = 191: with a sink of 20, 211 rows fit a
-    # fresh sequence, 212 do not
+    # fresh sequence in one append; 212 can never fit and are refused on the host
     w = W.WORKLOADS["llama2-7b-layer"].replace(batch=1, num_q_heads=1, num_kv_heads=1)
-    for n, full in ((211, False), (212, True)):
+    cache = make_cache(w, [400], 32, sink=20)
+    kk = torch.zeros(1, 1, 211, 128, dtype=torch.float16, device="cuda")
+    cache.append(kk, kk)
+    torch.cuda.synchronize()
+    assert cache.read_device_error() == 0 and cache.lengths() == ([0], [211])
+    with pytest.raises(B.KVQError) as e:
+        big = torch.zeros(1, 1, 212, 128, dtype=torch.float16, device="cuda")
+        cache.append(big, big)
+    assert e.value.status == B.KVQ_ERR_CAPACITY
+    # 150 rows leave 130 in the ring after the sink's 20: 61 more fit, 62 overflow on the device
+    for n2, full in ((61, False), (62, True)):
         cache = make_cache(w, [400], 32, sink=20)
-        kk = torch.zeros(1, 1, n, 128, dtype=torch.float16, device="cuda")
-        cache.append(kk, kk)
+        first = torch.zeros(1, 1, 150, 128, dtype=torch.float16, device="cuda")
+        second = torch.zeros(1, 1, n2, 128, dtype=torch.float16, device="cuda")
+        cache.append(first, first)
+        cache.append(second, second)
         torch.cuda.synchronize()
         assert bool(cache.read_device_error() & 1) == full
-        assert cache.lengths() == ([0], [0 if full else n])
+        assert cache.lengths() == ([0], [150 if full else 150 + n2])

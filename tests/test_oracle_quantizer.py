@@ -198,6 +198,9 @@ def test_record_sizes_per_token_match_the_design_table():
     for (kb, vb, G, gv), per_tok in cases:
         spec = kivi.CacheSpec(1, 1, 1, 128, kb, vb, G, gv, 128, 256, "bf16")
         assert kivi.record_bytes(spec) == per_tok * G
+        # the same figure from the layout's parts, per token: d*(b_K + b_V)/8 code bytes,
+        # 2*2*d/G bytes of key scale/zero shared by the block, 2*2*d/G_V of value scale/zero
+        assert kivi.quantized_bytes_per_token(spec) == 128 * (kb + vb) / 8 + 4 * 128 / G + 4 * 128 / gv == per_tok
 
 
 def test_code_bandwidth_divisor_matches_the_page():
