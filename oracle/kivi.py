@@ -210,43 +210,51 @@ def value_code_order(G: int, d: int) -> np.ndarray:
 
 
 def value_code_stream(vcodes: np.ndarray) -> np.ndarray:
-    """[G][d] codes -> 1-D stream in record order (see the record layout)."""
-    G, d = vcodes.shape
-    out = np.empty(G * d, dtype=vcodes.dtype)
-    out[value_code_order(G, d).ravel()] = vcodes.ravel()
+    """[..., G, d] codes -> stream in record order along the last axis, [..., G*d]
+    (see the record layout; leading axes are independent blocks)."""
+    G, d = vcodes.shape[-2:]
+    lead = vcodes.shape[:-2]
+    out = np.empty(lead + (G * d,), dtype=vcodes.dtype)
+    out[..., value_code_order(G, d).ravel()] = vcodes.reshape(lead + (G * d,))
     return out
 
 
 def value_codes_from_stream(stream: np.ndarray, G: int, d: int) -> np.ndarray:
-    return stream[value_code_order(G, d)]
+    """[..., G*d] stream -> [..., G, d] codes."""
+    return stream[..., value_code_order(G, d)]
 
 
 def quantize_block(spec: CacheSpec, kblk: np.ndarray, vblk: np.ndarray):
-    """Quantize one block. kblk, vblk: float32 [G][d] (exact input values).
+    """Quantize one block. kblk, vblk: float32 [G][d] (exact input values), or
+    [n][G][d] for n independent blocks at once (the same steps on each).
 
     Keys: one group per channel over the G tokens [P4 KIVI: keys per channel].
     Values: one group per (token, G_V consecutive channels) [P4 KIVI: values
     per token].
-    Returns a dict of the section arrays.
+    Returns a dict of the section arrays (with the leading block axis, if any).
     """
     G, d, gv = spec.k_group, spec.head_dim, spec.v_group
-    assert kblk.shape == (G, d) and vblk.shape == (G, d)
-    ks, kz, kcodes = quantize_groups(kblk, spec.k_bits, axis=0)          # [d], [d], [G][d]
-    vs, vz, vcodes = quantize_groups(vblk.reshape(G, d // gv, gv), spec.v_bits, axis=2)
-    vcodes = vcodes.reshape(G, d)                                         # [G][d]
+    assert kblk.shape[-2:] == (G, d) and vblk.shape == kblk.shape
+    lead = kblk.shape[:-2]
+    ks, kz, kcodes = quantize_groups(kblk, spec.k_bits, axis=-2)         # [d], [d], [G][d]
+    vs, vz, vcodes = quantize_groups(vblk.reshape(lead + (G, d // gv, gv)), spec.v_bits, axis=-1)
+    vcodes = vcodes.reshape(lead + (G, d))                                # [G][d]
     return {
         "k_codes": pack_lsb_first(kcodes, spec.k_bits),                   # [G][d*bK/32]
         "k_scale": ks, "k_zero": kz,                                      # [d]
         "v_codes": pack_lsb_first(value_code_stream(vcodes), spec.v_bits),
-        "v_scale": np.ascontiguousarray(vs.T),                            # [d/G_V][G]
-        "v_zero": np.ascontiguousarray(vz.T),
+        "v_scale": np.ascontiguousarray(np.swapaxes(vs, -1, -2)),         # [d/G_V][G]
+        "v_zero": np.ascontiguousarray(np.swapaxes(vz, -1, -2)),
     }
 
 
 def block_to_bytes(sec) -> np.ndarray:
-    parts = [np.ascontiguousarray(sec[k]).view(np.uint8).ravel()
+    """Record bytes of a block's sections ([record_bytes]), or of n blocks'
+    ([n][record_bytes])."""
+    lead = sec["k_scale"].shape[:-1]
+    parts = [np.ascontiguousarray(sec[k]).view(np.uint8).reshape(lead + (-1,))
              for k in ("k_codes", "k_scale", "k_zero", "v_codes", "v_scale", "v_zero")]
-    return np.concatenate(parts)
+    return np.concatenate(parts, axis=-1)
 
 
 # ---------------------------------------------------------------------------
@@ -323,13 +331,14 @@ def fp8_window(spec: CacheSpec, S: int):
 
 
 def dequantize_block(spec: CacheSpec, sec):
-    """fp64 [G][d] key and value reconstructions of one block."""
+    """fp64 [G][d] key and value reconstructions of one block (or [n][G][d] of
+    the n blocks of a batched quantize_block)."""
     G, d, gv = spec.k_group, spec.head_dim, spec.v_group
     kcodes = unpack_lsb_first(sec["k_codes"], spec.k_bits)               # [G][d]
-    khat = dequantize(kcodes, sec["k_scale"][None, :], sec["k_zero"][None, :])
+    khat = dequantize(kcodes, sec["k_scale"][..., None, :], sec["k_zero"][..., None, :])
     vcodes = value_codes_from_stream(unpack_lsb_first(sec["v_codes"], spec.v_bits), G, d)  # [G][d]
-    vs = np.repeat(sec["v_scale"].T, gv, axis=1)                          # [G][d]
-    vz = np.repeat(sec["v_zero"].T, gv, axis=1)
+    vs = np.repeat(np.swapaxes(sec["v_scale"], -1, -2), gv, axis=-1)      # [G][d]
+    vz = np.repeat(np.swapaxes(sec["v_zero"], -1, -2), gv, axis=-1)
     vhat = dequantize(vcodes, vs, vz)
     return khat, vhat
 
@@ -364,13 +373,14 @@ def expected_blocks(spec: CacheSpec, K: np.ndarray, V: np.ndarray, S_b: int):
     K, V: float32 [>=S_b][d] input values of that pair. Returns uint8
     [Q/G][record_bytes]; block j holds tokens P + jG .. P + jG + G - 1.
     """
-    G, P = spec.k_group, spec.sink
+    G, P, d = spec.k_group, spec.sink, spec.head_dim
     _, Q, _ = stream_split(spec, S_b)
-    recs = [block_to_bytes(quantize_block(spec, K[P + j * G:P + (j + 1) * G], V[P + j * G:P + (j + 1) * G]))
-            for j in range(Q // G)]
-    if not recs:
+    if Q == 0:
         return np.zeros((0, record_bytes(spec)), np.uint8)
-    return np.stack(recs)
+    # every block at once: block j is row j of the [Q/G][G][d] views
+    kb = np.asarray(K[P:P + Q], F32).reshape(Q // G, G, d)
+    vb = np.asarray(V[P:P + Q], F32).reshape(Q // G, G, d)
+    return block_to_bytes(quantize_block(spec, kb, vb))
 
 
 def ring_slots(Q: int, S: int, capacity: int, sink: int = 0) -> np.ndarray:
@@ -404,12 +414,16 @@ def pair_cache_fp64(spec: CacheSpec, K: np.ndarray, V: np.ndarray, S_b: int):
     ks = [np.asarray(K[:s], np.float64)]
     vs = [np.asarray(V[:s], np.float64)]
     f0 = Q // G - min(Q // G, spec.fp8_blocks)   # blocks from here on are read through FP8
-    for j in range(Q // G):
+    if f0 > 0:   # blocks 0 .. f0-1 through their low-bit records, all at once
+        d = spec.head_dim
+        kb = np.asarray(K[P:P + f0 * G], F32).reshape(f0, G, d)
+        vb = np.asarray(V[P:P + f0 * G], F32).reshape(f0, G, d)
+        kh, vh = dequantize_block(spec, quantize_block(spec, kb, vb))
+        ks.append(kh.reshape(f0 * G, d))
+        vs.append(vh.reshape(f0 * G, d))
+    for j in range(f0, Q // G):
         lo = P + j * G
-        if j >= f0:
-            kh, vh = dequantize_fp8_block(K[lo:lo + G], V[lo:lo + G])
-        else:
-            kh, vh = dequantize_block(spec, quantize_block(spec, K[lo:lo + G], V[lo:lo + G]))
+        kh, vh = dequantize_fp8_block(K[lo:lo + G], V[lo:lo + G])
         ks.append(kh)
         vs.append(vh)
     ks.append(np.asarray(K[P + Q:S_b], np.float64))

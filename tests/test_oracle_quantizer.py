@@ -243,3 +243,20 @@ def test_record_layout_value_codes_second_token_chunk_int4():
     vw = rec[vc_off:vc_off + 128].view(np.uint32)   # 16 tokens x 16 channels x 4 bits
     # position ((1*16 + 3)*1 + 0)*8 + 1 = 153 -> bit 612 -> word 19, bit 4
     assert vw[19] == (15 << 4) and not np.delete(vw, 19).any()
+
+
+@pytest.mark.parametrize("kb,vb,G,gv", [(2, 2, 32, 32), (4, 4, 32, 32), (2, 2, 64, 64), (4, 2, 16, 32)])
+def test_blocks_at_once_equal_blocks_one_by_one(kb, vb, G, gv):
+    # quantize_block over a leading block axis takes the same steps on each block
+    rng = np.random.default_rng(7)
+    spec = kivi.CacheSpec(1, 1, 1, 128, kb, vb, G, gv, 128, 128 + G, "bf16")
+    k = (rng.standard_normal((5, G, 128)) * np.exp(rng.standard_normal(128))).astype(np.float32)
+    v = rng.standard_normal((5, G, 128)).astype(np.float32)
+    k[2] = 1.5   # a constant block: zero scales and codes
+    many = kivi.block_to_bytes(kivi.quantize_block(spec, k, v))
+    one = np.stack([kivi.block_to_bytes(kivi.quantize_block(spec, k[j], v[j])) for j in range(5)])
+    assert many.shape == (5, kivi.record_bytes(spec)) and np.array_equal(many, one)
+    kh, vh = kivi.dequantize_block(spec, kivi.quantize_block(spec, k, v))
+    for j in range(5):
+        kj, vj = kivi.dequantize_block(spec, kivi.quantize_block(spec, k[j], v[j]))
+        assert np.array_equal(kh[j], kj) and np.array_equal(vh[j], vj)
