@@ -67,7 +67,23 @@ of the readings list kept with the design notes):
     tokens of a sequence stay in full precision and are never quantized; the
     quantized blocks and the residual window cover the tokens after them,
     exactly as if the sequence started at token P. The pages give no count, so
-    P is a parameter.
+    P is a parameter;
+  * a Walsh-Hadamard pre-rotation (rotate = 0: none; bit 1 keys, bit 2
+    values) [P4w]: before formula F every key (and/or value) token vector x of
+    d channels is replaced by R(x) = H x / 8, H the d x d Sylvester Hadamard
+    matrix, computed in fp32 by radix-2 butterflies in the order of fwht_f32();
+    attention reads the dequantized vectors back through H y / (d / 8), R's
+    inverse (H H = d I). The page's rotation is orthonormal, H / sqrt(d);
+    splitting that factor into the powers of two 1/8 and 8/d keeps both sides
+    free of extra rounding, and formula F commutes with a power-of-two scale of
+    its group. The residual window and the sink stay in the original
+    coordinates.
+
+  [P4w] the same patricehuetz.fr page, "TurboQuant : les cinq innovations",
+       innovation 1 "Rotation Walsh-Hadamard : normaliser la distribution": a
+       WHT of the key and value vectors before quantization spreads outliers
+       over all dimensions; it is orthogonal and is inverted on the
+       dequantized vectors when attention is computed.
 """
 from __future__ import annotations
 
@@ -97,6 +113,7 @@ class CacheSpec:
     dtype: str            # "f16" or "bf16"
     sink: int = 0         # P: leading tokens kept in full precision (attention sink)
     fp8_blocks: int = 0   # W: most recent quantized blocks also kept (and read) in FP8
+    rotate: int = 0       # Walsh-Hadamard pre-rotation: bit 1 keys, bit 2 values
 
     @property
     def n_g(self) -> int:
@@ -173,6 +190,51 @@ def unpack_lsb_first(words: np.ndarray, bits: int) -> np.ndarray:
 
 
 # ---------------------------------------------------------------------------
+# Walsh-Hadamard pre-rotation [P4w, innovation 1].
+# ---------------------------------------------------------------------------
+ROT_KEYS, ROT_VALUES = 1, 2
+ROT_SHIFT = 3   # the stored side is H x * 2^-3
+
+
+def hadamard(d: int) -> np.ndarray:
+    """The d x d Sylvester Hadamard matrix (d a power of two): H_1 = [1],
+    H_2n = [[H_n, H_n], [H_n, -H_n]]. Symmetric, entries +-1, H H = d I."""
+    h = np.ones((1, 1), dtype=np.int64)
+    while h.shape[0] < d:
+        h = np.block([[h, h], [h, -h]])
+    assert h.shape[0] == d, "d must be a power of two"
+    return h
+
+
+def fwht_f32(x: np.ndarray) -> np.ndarray:
+    """H x along the last axis, in float32: for h = 1, 2, 4, ..., d/2, every
+    pair (i, i + h) with bit h of i clear becomes (x_i + x_{i+h}, x_i - x_{i+h}),
+    each sum rounded to fp32. This order fixes the roundings the stored codes
+    depend on."""
+    y = np.array(x, dtype=F32)
+    d = y.shape[-1]
+    lead = y.shape[:-1]
+    h = 1
+    while h < d:
+        t = y.reshape(lead + (d // (2 * h), 2, h))
+        a, b = t[..., 0, :], t[..., 1, :]
+        y = np.stack([a + b, a - b], axis=-2).reshape(lead + (d,))
+        h *= 2
+    return y
+
+
+def rotate_f32(x: np.ndarray) -> np.ndarray:
+    """R(x) = H x / 8 in float32 (the division by 8 is exact)."""
+    return fwht_f32(x) * F32(2.0 ** -ROT_SHIFT)
+
+
+def unrotate_f64(y: np.ndarray) -> np.ndarray:
+    """R's inverse, H y * 8 / d, in fp64 along the last axis."""
+    d = y.shape[-1]
+    return (np.asarray(y, np.float64) @ hadamard(d).astype(np.float64)) * (2.0 ** ROT_SHIFT / d)
+
+
+# ---------------------------------------------------------------------------
 # One quantized block: G tokens of one (sequence, kv head).
 #
 # Record layout (little-endian bytes, sections in this order):
@@ -236,6 +298,10 @@ def quantize_block(spec: CacheSpec, kblk: np.ndarray, vblk: np.ndarray):
     G, d, gv = spec.k_group, spec.head_dim, spec.v_group
     assert kblk.shape[-2:] == (G, d) and vblk.shape == kblk.shape
     lead = kblk.shape[:-2]
+    if spec.rotate & ROT_KEYS:      # every token's key vector rotated first [P4w]
+        kblk = rotate_f32(kblk)
+    if spec.rotate & ROT_VALUES:
+        vblk = rotate_f32(vblk)
     ks, kz, kcodes = quantize_groups(kblk, spec.k_bits, axis=-2)         # [d], [d], [G][d]
     vs, vz, vcodes = quantize_groups(vblk.reshape(lead + (G, d // gv, gv)), spec.v_bits, axis=-1)
     vcodes = vcodes.reshape(lead + (G, d))                                # [G][d]
@@ -332,7 +398,8 @@ def fp8_window(spec: CacheSpec, S: int):
 
 def dequantize_block(spec: CacheSpec, sec):
     """fp64 [G][d] key and value reconstructions of one block (or [n][G][d] of
-    the n blocks of a batched quantize_block)."""
+    the n blocks of a batched quantize_block), in the rotated coordinates when
+    the spec rotates (pair_cache_fp64 takes them back)."""
     G, d, gv = spec.k_group, spec.head_dim, spec.v_group
     kcodes = unpack_lsb_first(sec["k_codes"], spec.k_bits)               # [G][d]
     khat = dequantize(kcodes, sec["k_scale"][..., None, :], sec["k_zero"][..., None, :])
@@ -406,10 +473,11 @@ def attention_fp64(q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float) ->
 
 def pair_cache_fp64(spec: CacheSpec, K: np.ndarray, V: np.ndarray, S_b: int):
     """The attention inputs of one (sequence, kv head), in token order: the exact
-    sink tokens, the dequantized blocks (the W newest through F8), then the
-    exact residual tokens.
+    sink tokens, the dequantized blocks (the W newest through F8; rotated
+    sides taken back through R's inverse), then the exact residual tokens.
     Returns (Khat, Vhat) [S_b][d]."""
     G, P = spec.k_group, spec.sink
+    assert not (spec.rotate and spec.fp8_blocks), "the FP8 tier stores unrotated rows"
     s, Q, _ = stream_split(spec, S_b)
     ks = [np.asarray(K[:s], np.float64)]
     vs = [np.asarray(V[:s], np.float64)]
@@ -419,6 +487,10 @@ def pair_cache_fp64(spec: CacheSpec, K: np.ndarray, V: np.ndarray, S_b: int):
         kb = np.asarray(K[P:P + f0 * G], F32).reshape(f0, G, d)
         vb = np.asarray(V[P:P + f0 * G], F32).reshape(f0, G, d)
         kh, vh = dequantize_block(spec, quantize_block(spec, kb, vb))
+        if spec.rotate & ROT_KEYS:    # back through R's inverse [P4w]
+            kh = unrotate_f64(kh)
+        if spec.rotate & ROT_VALUES:
+            vh = unrotate_f64(vh)
         ks.append(kh.reshape(f0 * G, d))
         vs.append(vh.reshape(f0 * G, d))
     for j in range(f0, Q // G):
