@@ -232,24 +232,30 @@ __global__ __launch_bounds__(256) void decode_generic_kernel(
 // Merge the partial states of one (sequence, query head) (scores in log2
 // units): with M = max m_i, o = sum_i 2^(m_i - M) o_i / sum_i 2^(m_i - M) l_i.
 // The units of the pair come from the plan the decode kernel left in the
-// workspace. One wave per output row, lane holding D/64 channels: the partials
-// go in batches of kCombineBatch, each batch one round of loads (lane i also
-// fetches m and l of partial i), merged into a running maximum. One wave per
-// workgroup spreads the rows over every compute unit: the rows are few and
-// short, and the cost of this kernel is its dispatch and load latency, not
-// its bandwidth (four waves per workgroup measured 1.4 us slower per step).
-constexpr int kCombineWaves = 1;
+// workspace. One workgroup of WPR waves per output row, lane holding D/64
+// channels: wave w takes batches w, w + WPR, ... of kCombineBatch partials,
+// each batch one round of loads (lane i also fetches m and l of partial i),
+// merged into a running maximum; with WPR > 1 the waves' states are then
+// merged through LDS by wave 0. The kernel is bound by dispatch and load
+// latency, not bandwidth: rows with many partials (long sequences cut into
+// many units) take WPR = 4 so that each wave has one round of loads, rows with
+// few take one wave per workgroup, which spreads them over every compute unit
+// (four rows per workgroup measured 1.4 us slower per step than one).
 constexpr int kCombineBatch = 64;
+// Waves per workgroup of the sink and FP8-tier side launches (one output row,
+// or one round of a row, per wave).
+constexpr int kSideWaves = 1;
 
-template <int D, bool SIDE>
-__global__ __launch_bounds__(64 * kCombineWaves) void combine_kernel(Geom g, const int* __restrict__ plan,
-                                                                     const float* ws,   // (not restrict: the
-                                                                     // compiler barrier below must order its loads)
-                                                                     const float* __restrict__ side_parts,
-                                                                     int nside, float* __restrict__ out) {
+template <int D, bool SIDE, int WPR>
+__global__ __launch_bounds__(64 * WPR) void combine_kernel(Geom g, const int* __restrict__ plan,
+                                                          const float* ws,   // (not restrict: the
+                                                          // compiler barrier below must order its loads)
+                                                          const float* __restrict__ side_parts, int nside,
+                                                          float* __restrict__ out) {
   constexpr int CPL = D / 64;   // channels per lane
   const int lane = threadIdx.x & 63;
-  const int row = blockIdx.x * kCombineWaves + __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int wave = WPR == 1 ? 0 : __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int row = blockIdx.x;
   if (row >= g.B * g.Hq) return;
   const int b = row / g.Hq, hq = row % g.Hq;
   const int h = hq / g.ng, j = hq % g.ng;
@@ -270,7 +276,7 @@ __global__ __launch_bounds__(64 * kCombineWaves) void combine_kernel(Geom g, con
       return src0 + (size_t)pu.slot(i) * stride;
   };
   const int nparts = (SIDE ? nside : 0) + pu.n;
-  for (int i0 = 0; i0 < nparts; i0 += kCombineBatch) {
+  for (int i0 = wave * kCombineBatch; i0 < nparts; i0 += WPR * kCombineBatch) {
     const int cnt = min(kCombineBatch, nparts - i0);
     float v[kCombineBatch][CPL];
 #pragma unroll
@@ -303,6 +309,33 @@ __global__ __launch_bounds__(64 * kCombineWaves) void combine_kernel(Geom g, con
     }
     m = mn;
   }
+  if constexpr (WPR > 1) {
+    __shared__ float s_ml[WPR][2];
+    __shared__ float s_acc[WPR][D];
+    if (lane == 0) {
+      s_ml[wave][0] = m;
+      s_ml[wave][1] = L;
+    }
+#pragma unroll
+    for (int k = 0; k < CPL; ++k) s_acc[wave][CPL * lane + k] = acc[k];
+    __syncthreads();
+    if (wave != 0) return;
+    float M = -INFINITY;
+#pragma unroll
+    for (int x = 0; x < WPR; ++x) M = fmaxf(M, s_ml[x][0]);
+    L = 0.f;
+#pragma unroll
+    for (int k = 0; k < CPL; ++k) acc[k] = 0.f;
+#pragma unroll
+    for (int x = 0; x < WPR; ++x) {
+      const float mx = s_ml[x][0];
+      if (mx == -INFINITY) continue;   // a wave that saw no partial (or only empty ones)
+      const float wx = exp2f(mx - M);
+      L = fmaf(wx, s_ml[x][1], L);
+#pragma unroll
+      for (int k = 0; k < CPL; ++k) acc[k] = fmaf(wx, s_acc[x][CPL * lane + k], acc[k]);
+    }
+  }
   float* dst = out + (size_t)row * D + CPL * lane;
 #pragma unroll
   for (int k = 0; k < CPL; ++k) dst[k] = L > 0.f ? acc[k] / L : 0.f;
@@ -318,7 +351,7 @@ __global__ __launch_bounds__(64 * kCombineWaves) void combine_kernel(Geom g, con
 // the partial layout {o[D], m, l}, the empty state (m = -inf, l = 0) for
 // S_b == 0.
 template <int D, bool BF16>
-__global__ __launch_bounds__(64 * kCombineWaves) void sink_kernel(Geom g, const uint16_t* __restrict__ k_sink,
+__global__ __launch_bounds__(64 * kSideWaves) void sink_kernel(Geom g, const uint16_t* __restrict__ k_sink,
                                                                   const uint16_t* __restrict__ v_sink,
                                                                   const int32_t* __restrict__ state,
                                                                   const uint16_t* __restrict__ q, float qscale,
@@ -326,10 +359,10 @@ __global__ __launch_bounds__(64 * kCombineWaves) void sink_kernel(Geom g, const 
   constexpr int CPL = D / 64;             // channels per lane in the P.V phase
   constexpr int VEC = D / 8;              // 16-byte vectors per row
   constexpr int VW = CPL == 1 ? 1 : CPL / 2;   // words per lane of a value row (d = 64: a half word)
-  __shared__ float lq[kCombineWaves][D];
+  __shared__ float lq[kSideWaves][D];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
-  const int row = blockIdx.x * kCombineWaves + wave;
+  const int row = blockIdx.x * kSideWaves + wave;
   if (row >= g.B * g.Hq) return;
   const int b = row / g.Hq, h = (row % g.Hq) / g.ng;
   // row j of a T-token query block is token S_b - T + j % T: it sees sink rows up to there
@@ -423,16 +456,16 @@ __global__ __launch_bounds__(64 * kCombineWaves) void sink_kernel(Geom g, const 
 // query of a T-token block sees these blocks (they precede the window).
 typedef float f32x2v __attribute__((ext_vector_type(2)));
 template <int D, bool BF16>
-__global__ __launch_bounds__(64 * kCombineWaves) void fp8_kernel(Geom g, const uint8_t* __restrict__ fp8,
+__global__ __launch_bounds__(64 * kSideWaves) void fp8_kernel(Geom g, const uint8_t* __restrict__ fp8,
                                                                  const int32_t* __restrict__ state,
                                                                  const uint16_t* __restrict__ q, float qscale,
                                                                  int rounds, float* __restrict__ out_part) {
   constexpr int CPL = D / 64;   // channels per lane in the P.V phase
   constexpr int VEC = D / 16;   // 16-byte vectors per code row
-  __shared__ float lq[kCombineWaves][D];
+  __shared__ float lq[kSideWaves][D];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
-  const int idx = blockIdx.x * kCombineWaves + wave;   // round * (B * H_q) + row
+  const int idx = blockIdx.x * kSideWaves + wave;   // round * (B * H_q) + row
   if (idx >= g.B * g.Hq * rounds) return;
   const int row = idx % (g.B * g.Hq), round = idx / (g.B * g.Hq);
   const int b = row / g.Hq, h = (row % g.Hq) / g.ng;
@@ -557,8 +590,8 @@ namespace {
 template <int D, bool BF16>
 hipError_t launch_sink(const Geom& g, const kvq_cache& c, const void* q, float scale, const DecodePlan& plan,
                        void* ws, hipStream_t s) {
-  const int grid = (g.B * g.Hq + kCombineWaves - 1) / kCombineWaves;
-  hipLaunchKernelGGL((sink_kernel<D, BF16>), dim3(grid), dim3(64 * kCombineWaves), 0, s, g,
+  const int grid = (g.B * g.Hq + kSideWaves - 1) / kSideWaves;
+  hipLaunchKernelGGL((sink_kernel<D, BF16>), dim3(grid), dim3(64 * kSideWaves), 0, s, g,
                      static_cast<const uint16_t*>(c.k_sink), static_cast<const uint16_t*>(c.v_sink), c.state,
                      static_cast<const uint16_t*>(q), scale * 1.4426950408889634f,
                      reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + plan.side_off));
@@ -567,9 +600,9 @@ hipError_t launch_sink(const Geom& g, const kvq_cache& c, const void* q, float s
 template <int D, bool BF16>
 hipError_t launch_fp8(const Geom& g, const kvq_cache& c, const void* q, float scale, const DecodePlan& plan,
                       void* ws, hipStream_t s) {
-  const int grid = (g.B * g.Hq * plan.fp8_rounds + kCombineWaves - 1) / kCombineWaves;
+  const int grid = (g.B * g.Hq * plan.fp8_rounds + kSideWaves - 1) / kSideWaves;
   const size_t slot = g.P > 0 ? (size_t)g.B * g.Hq * (D + 2) * 4 : 0;   // after the sink's
-  hipLaunchKernelGGL((fp8_kernel<D, BF16>), dim3(grid), dim3(64 * kCombineWaves), 0, s, g,
+  hipLaunchKernelGGL((fp8_kernel<D, BF16>), dim3(grid), dim3(64 * kSideWaves), 0, s, g,
                      static_cast<const uint8_t*>(c.fp8), c.state, static_cast<const uint16_t*>(q),
                      scale * 1.4426950408889634f, plan.fp8_rounds,
                      reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + plan.side_off + slot));
@@ -608,19 +641,31 @@ hipError_t launch_decode_combine(const Geom& g, const kvq_cache& c, float* out, 
   const int* planp = static_cast<const int*>(ws);
   const float* parts = reinterpret_cast<const float*>(static_cast<const uint8_t*>(ws) + plan_bytes(g.B));
   const float* side = reinterpret_cast<const float*>(static_cast<const uint8_t*>(ws) + plan.side_off);
-  const int grid = (g.B * g.Hq + kCombineWaves - 1) / kCombineWaves;
-  const dim3 gd(grid), bd(64 * kCombineWaves);
   const int ns = plan.nside;
-  if (g.d == 128) {
-    if (ns > 0)
-      hipLaunchKernelGGL((combine_kernel<128, true>), gd, bd, 0, s, g, planp, parts, side, ns, out);
-    else
-      hipLaunchKernelGGL((combine_kernel<128, false>), gd, bd, 0, s, g, planp, parts, side, ns, out);
+  // partial states a row can have: its pair's share of the unit bound, plus the side states.
+  // Four waves per row only while all of them fit on the GPU at once (rows * 4
+  // waves within 256 CUs x 32 wave slots): with more rows than that, the extra
+  // waves cost more than the shorter chains save (measured on 3072 rows).
+  const size_t per_row = plan.units_max / ((size_t)g.B * g.Hkv) + (size_t)ns;
+  const dim3 gd(g.B * g.Hq);
+  if (per_row > kCombineBatch && (size_t)g.B * g.Hq * 4 <= 8192) {
+    const dim3 bd(64 * 4);
+    if (g.d == 128) {
+      if (ns > 0) hipLaunchKernelGGL((combine_kernel<128, true, 4>), gd, bd, 0, s, g, planp, parts, side, ns, out);
+      else hipLaunchKernelGGL((combine_kernel<128, false, 4>), gd, bd, 0, s, g, planp, parts, side, ns, out);
+    } else {
+      if (ns > 0) hipLaunchKernelGGL((combine_kernel<64, true, 4>), gd, bd, 0, s, g, planp, parts, side, ns, out);
+      else hipLaunchKernelGGL((combine_kernel<64, false, 4>), gd, bd, 0, s, g, planp, parts, side, ns, out);
+    }
   } else {
-    if (ns > 0)
-      hipLaunchKernelGGL((combine_kernel<64, true>), gd, bd, 0, s, g, planp, parts, side, ns, out);
-    else
-      hipLaunchKernelGGL((combine_kernel<64, false>), gd, bd, 0, s, g, planp, parts, side, ns, out);
+    const dim3 bd(64);
+    if (g.d == 128) {
+      if (ns > 0) hipLaunchKernelGGL((combine_kernel<128, true, 1>), gd, bd, 0, s, g, planp, parts, side, ns, out);
+      else hipLaunchKernelGGL((combine_kernel<128, false, 1>), gd, bd, 0, s, g, planp, parts, side, ns, out);
+    } else {
+      if (ns > 0) hipLaunchKernelGGL((combine_kernel<64, true, 1>), gd, bd, 0, s, g, planp, parts, side, ns, out);
+      else hipLaunchKernelGGL((combine_kernel<64, false, 1>), gd, bd, 0, s, g, planp, parts, side, ns, out);
+    }
   }
   return hipGetLastError();
 }

@@ -102,12 +102,33 @@ __device__ __forceinline__ uint4 unpack_int4_word(uint32_t w) {
 __host__ __device__ constexpr int kperm(int e) { return (e & 4) | ((e & 1) << 1) | ((e >> 1) & 1); }
 
 // --- hi/lo splits -------------------------------------------------------------------
+// Two floats to a bf16 pair, each rounded to nearest even (low half = a). Written
+// as the instruction itself: from the vector-of-bf16 form the compiler converted
+// the low element a second time to get it back as a float.
+__device__ __forceinline__ uint32_t pk_bf16(float a, float b) {
+  uint32_t r;
+  asm("v_cvt_pk_bf16_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+// a times the fp16 in the low (HI = false) or high half of s, rounded once: one
+// mixed-precision FMA with a zero addend instead of a conversion and a multiply.
+template <bool HI>
+__device__ __forceinline__ float mul_f16(float a, uint32_t s) {
+  float x;
+  if constexpr (HI)
+    asm("v_fma_mix_f32 %0, %1, %2, 0 op_sel:[0,1,0] op_sel_hi:[0,1,0]" : "=v"(x) : "v"(a), "v"(s));
+  else
+    asm("v_fma_mix_f32 %0, %1, %2, 0 op_sel_hi:[0,1,0]" : "=v"(x) : "v"(a), "v"(s));
+  return x;
+}
+// x = hi + lo with hi = bf16(x) and lo = bf16(x - hi) (the subtraction is exact):
+// about 16 significant bits per value in two bf16 operands. Six instructions
+// per pair of values.
 __device__ __forceinline__ void split_bf16(float x0, float x1, uint32_t& hi, uint32_t& lo) {
-  const bf16x2v h = {(__bf16)x0, (__bf16)x1};
-  hi = __builtin_bit_cast(uint32_t, h);
-  const float h0 = __uint_as_float(hi << 16), h1 = __uint_as_float(hi & 0xffff0000u);
-  const bf16x2v l = {(__bf16)(x0 - h0), (__bf16)(x1 - h1)};
-  lo = __builtin_bit_cast(uint32_t, l);
+  hi = pk_bf16(x0, x1);
+  const float r0 = x0 - __uint_as_float(hi << 16);
+  const float r1 = x1 - __uint_as_float(hi & 0xffff0000u);
+  lo = pk_bf16(r0, r1);
 }
 __device__ __forceinline__ void split_f16(float x0, float x1, uint32_t& hi, uint32_t& lo) {
   const f16x2v h = {(_Float16)x0, (_Float16)x1};
@@ -187,8 +208,12 @@ struct Cfg {
   static constexpr int REC_VS = REC_VC + G * D * VB / 8;
   static constexpr int REC_VZ = REC_VS + 2 * NGR * G;
   static constexpr int REC = REC_VZ + 2 * NGR * G;
-  // per-wave LDS (bytes)
-  static constexpr int LDS_Q = NG * D * 4;
+  // per-wave LDS (bytes). A query row takes QS floats: 4 more than D, so that the
+  // rows of the group start 4 banks apart and the lanes of one row of the
+  // operand layout, which read the same channels of different heads, do not
+  // collide on a bank.
+  static constexpr int QS = D + 4;
+  static constexpr int LDS_Q = NG * QS * 4;
   static constexpr int LDS_A = KS_SET * NGR * 4 * 2 * NG * 16;
   static constexpr int LDS_O = 2 * NG * D * 4;
   static constexpr int LDS_P = kRingChunk * NG * 4;
@@ -317,7 +342,7 @@ __device__ __forceinline__ void ring_unit(const Geom& g, const WaveLds<C>& L, co
   if constexpr (!C::BF16) {
     // fp16 operands: bring the largest |q'| near 2^14 (an exact power of two)
     float mx = 0.f;
-    for (int idx = lane; idx < NG * D; idx += 64) mx = fmaxf(mx, fabsf(L.qs[idx]));
+    for (int idx = lane; idx < NG * D; idx += 64) mx = fmaxf(mx, fabsf(L.qs[(idx / D) * C::QS + idx % D]));
     mx = wave_max(mx);
     escale = ldexpf(1.0f, mx > 0.f ? 14 - ilogbf(mx) : 0);
   }
@@ -327,8 +352,8 @@ __device__ __forceinline__ void ring_unit(const Geom& g, const WaveLds<C>& L, co
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int c = 32 * gq + 8 * ks + 2 * r;
-      const float x0 = n < NG ? L.qs[n * D + c] * escale : 0.f;
-      const float x1 = n < NG ? L.qs[n * D + c + 1] * escale : 0.f;
+      const float x0 = n < NG ? L.qs[n * C::QS + c] * escale : 0.f;
+      const float x1 = n < NG ? L.qs[n * C::QS + c + 1] * escale : 0.f;
       if constexpr (C::BF16) split_bf16(x0, x1, hi[r], lo[r]);
       else split_f16(x0, x1, hi[r], lo[r]);
     }
@@ -563,8 +588,8 @@ __device__ __forceinline__ void quant_stream(const Geom& g, const WaveLds<C>& L,
   };
   auto store_query = [&](const uint32_t (&w)[QW]) {
 #pragma unroll
-    for (int k = 0; k < QW; ++k)
-      *reinterpret_cast<float2*>(L.qs + 2 * (lane + 64 * k)) =
+    for (int k = 0; k < QW; ++k)   // word lane + 64k holds channels 2*lane, 2*lane+1 of row k
+      *reinterpret_cast<float2*>(L.qs + k * C::QS + 2 * lane) =
           make_float2(in_val<C>(w[k] & 0xffffu) * qscale, in_val<C>(w[k] >> 16) * qscale);
   };
 
@@ -587,7 +612,7 @@ __device__ __forceinline__ void quant_stream(const Geom& g, const WaveLds<C>& L,
     uint4 bhi[4], blo[4];
     float kap = 0.f;
     {
-      const float* qrow = L.qs + chd * D + 32 * gq;
+      const float* qrow = L.qs + chd * C::QS + 32 * gq;
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
         const uint4 sv = ksz[ks], zv = ksz[4 + ks];   // channels 32gq + 8ks + (0..7) as fp16 pairs
@@ -598,9 +623,8 @@ __device__ __forceinline__ void quant_stream(const Geom& g, const WaveLds<C>& L,
         float x[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const float se = (e & 1) ? hi_half_f16(s2[e >> 1]) : lo_half_f16(s2[e >> 1]);
           const float ze = (e & 1) ? hi_half_f16(z2[e >> 1]) : lo_half_f16(z2[e >> 1]);
-          x[e] = qv[e] * se;
+          x[e] = (e & 1) ? mul_f16<true>(qv[e], s2[e >> 1]) : mul_f16<false>(qv[e], s2[e >> 1]);
           kap = fmaf(qv[e], ze, kap);
         }
         uint32_t hi[4], lo[4];
@@ -672,13 +696,17 @@ __device__ __forceinline__ void quant_stream(const Geom& g, const WaveLds<C>& L,
 #pragma unroll
         for (int i = 0; i < 4; ++i) dpv[nt][i] *= a4[i];
     }
+    // exp2(-inf - m) is 0 for a finite m, so masked scores need no test of
+    // their own; m_ref is still -inf only while every score of the head was
+    // masked (a set wholly on out-of-range pages), and then all of them are.
+    const float m_use = m_ref == -INFINITY ? 0.f : m_ref;
     float p[TPB][4];
     float psum = 0.f;
 #pragma unroll
     for (int tt = 0; tt < TPB; ++tt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        p[tt][i] = sc[tt][i] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sc[tt][i] - m_ref);
+        p[tt][i] = __builtin_amdgcn_exp2f(sc[tt][i] - m_use);
         psum += p[tt][i];
       }
     l_part += psum;
@@ -693,14 +721,11 @@ __device__ __forceinline__ void quant_stream(const Geom& g, const WaveLds<C>& L,
 #pragma unroll
         for (int j = 0; j < NGR; ++j) {
           const uint2 sv = vsz[tt][j][0], zv = vsz[tt][j][1];
-          const float s4[4] = {lo_half_f16(sv.x), hi_half_f16(sv.x), lo_half_f16(sv.y), hi_half_f16(sv.y)};
           const float z4[4] = {lo_half_f16(zv.x), hi_half_f16(zv.x), lo_half_f16(zv.y), hi_half_f16(zv.y)};
-          float x[4];
+          const float x[4] = {mul_f16<false>(p[tt][0], sv.x), mul_f16<true>(p[tt][1], sv.x),
+                              mul_f16<false>(p[tt][2], sv.y), mul_f16<true>(p[tt][3], sv.y)};
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            x[i] = p[tt][i] * s4[i];
-            lam[j] = fmaf(p[tt][i], z4[i], lam[j]);
-          }
+          for (int i = 0; i < 4; ++i) lam[j] = fmaf(p[tt][i], z4[i], lam[j]);
           uint32_t hi02, lo02, hi13, lo13;
           split_bf16(x[0], x[2], hi02, lo02);
           split_bf16(x[1], x[3], hi13, lo13);
@@ -818,8 +843,8 @@ __device__ __forceinline__ void load_query(const Geom& g, const WaveLds<C>& L, c
 #pragma unroll
   for (int k = 0; k < QW; ++k) w[k] = src[lane + 64 * k];
 #pragma unroll
-  for (int k = 0; k < QW; ++k)
-    *reinterpret_cast<float2*>(L.qs + 2 * (lane + 64 * k)) =
+  for (int k = 0; k < QW; ++k)   // word lane + 64k holds channels 2*lane, 2*lane+1 of row k
+    *reinterpret_cast<float2*>(L.qs + k * C::QS + 2 * lane) =
         make_float2(in_val<C>(w[k] & 0xffffu) * qscale, in_val<C>(w[k] >> 16) * qscale);
   wave_lds_fence();
 }

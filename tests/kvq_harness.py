@@ -96,3 +96,57 @@ def to_np(t: torch.Tensor) -> np.ndarray:
 
 def default_scale(d: int) -> float:
     return float(np.float32(1.0 / math.sqrt(d)))
+
+
+GUARD_BYTE = 0xA5
+
+
+class Guards:
+    """Guard bands around device buffers: each buffer is replaced by a view into
+    a larger allocation whose first and last `nbytes` hold GUARD_BYTE. check()
+    asserts that no kernel wrote into a band."""
+
+    def __init__(self, nbytes: int = 4096):
+        self.nbytes = nbytes
+        self.bands = []
+
+    def wrap(self, t: torch.Tensor, name: str) -> torch.Tensor:
+        n = t.numel() * t.element_size()
+        big = torch.full((n + 2 * self.nbytes,), GUARD_BYTE, dtype=torch.uint8, device=t.device)
+        view = big[self.nbytes:self.nbytes + n]
+        view.copy_(t.contiguous().view(torch.uint8).reshape(-1))
+        self.bands.append((name, big))
+        return view.view(t.dtype).view(t.shape)
+
+    def check(self):
+        torch.cuda.synchronize()
+        for name, big in self.bands:
+            lo = big[:self.nbytes].cpu().numpy()
+            hi = big[-self.nbytes:].cpu().numpy()
+            assert (lo == GUARD_BYTE).all(), f"write below {name}: bytes {np.nonzero(lo != GUARD_BYTE)[0][:8]}"
+            assert (hi == GUARD_BYTE).all(), f"write past {name}: bytes {np.nonzero(hi != GUARD_BYTE)[0][:8]}"
+
+
+def guard_cache(cache: QuantizedKVCache, guards: Guards) -> QuantizedKVCache:
+    """Move every device buffer of `cache` inside guard bands and re-point its C
+    struct at them."""
+    from quantized_kv_cache_append_amd import binding as B
+    cache.blocks = guards.wrap(cache.blocks, "block store")
+    cache.k_ring = guards.wrap(cache.k_ring, "k_ring")
+    cache.v_ring = guards.wrap(cache.v_ring, "v_ring")
+    cache.state = guards.wrap(cache.state, "state words")
+    if cache.page_table is not None:
+        cache.page_table = guards.wrap(cache.page_table, "page table")
+    if cache.k_sink is not None:
+        cache.k_sink = guards.wrap(cache.k_sink, "k_sink")
+        cache.v_sink = guards.wrap(cache.v_sink, "v_sink")
+    if cache.fp8 is not None:
+        cache.fp8 = guards.wrap(cache.fp8, "fp8 store")
+    cache.cache = B.kvq_cache(
+        blocks=cache.blocks.data_ptr(),
+        block_table=cache.page_table.data_ptr() if cache.page_table is not None else None,
+        k_ring=cache.k_ring.data_ptr(), v_ring=cache.v_ring.data_ptr(), state=cache.state.data_ptr(),
+        k_sink=cache.k_sink.data_ptr() if cache.k_sink is not None else None,
+        v_sink=cache.v_sink.data_ptr() if cache.v_sink is not None else None,
+        fp8=cache.fp8.data_ptr() if cache.fp8 is not None else None)
+    return cache
