@@ -34,11 +34,12 @@
  * kvq_workspace_size). The library allocates nothing and borrows the pointers
  * for the duration of a call; it enqueues its kernels on the caller's HIP
  * stream (passed as void*; NULL is the default stream). All pointers in
- * kvq_cache and every tensor argument are DEVICE pointers. The only state the
+ * kvq_cache and every tensor argument are DEVICE pointers. The state the
  * library keeps across calls is a host-side table of launch grid sizes per
- * (device, kernel, LDS bytes), filled on first use under a mutex: calls from
- * several host threads are safe as long as they do not share a cache or a
- * workspace.
+ * (device, kernel, LDS bytes), filled on first use under a mutex, and the
+ * device array of kvq_decode_attention_noalloc (one per GPU, with its address):
+ * calls from several host threads are safe as long as they do not share a
+ * cache or a workspace (or, for the no-allocation call, a GPU).
  *
  * One kvq_cache is one layer. For each (sequence b, kv head h), with a sink of
  * P >= 0 tokens (kvq_config.sink; P = 0: none):
@@ -290,6 +291,23 @@ kvq_status kvq_decode_partials(const kvq_config* cfg, const kvq_cache* cache,
 kvq_status kvq_decode_combine(const kvq_config* cfg, const kvq_cache* cache, float* out,
                               int32_t max_seq_tokens, void* workspace, size_t workspace_bytes,
                               void* stream);
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc):
+ * kvq_decode_attention with the decode workspace taken from a device array the
+ * library holds per GPU, KVQ_NOALLOC_WORKSPACE_BYTES (64 MiB) on each GPU it
+ * runs on, kept until the process ends. The caller still passes the cache, q
+ * and out. Configurations whose kvq_workspace_size(cfg, max_seq_tokens)
+ * exceeds that size get KVQ_ERR_WORKSPACE before any device call. Every call on
+ * one GPU uses that GPU's array, whose contents need no initialisation and are
+ * left as the last call wrote them: calls that overlap on one GPU (several
+ * streams or threads, or a graph replayed while another call runs) race and
+ * must be ordered by the caller. Arguments, errors and results otherwise as
+ * kvq_decode_attention. No allocation, free or allocating library routine is
+ * called; the first call on a GPU looks the array's address up once. */
+#define KVQ_NOALLOC_WORKSPACE_BYTES ((size_t)64 << 20)
+kvq_status kvq_decode_attention_noalloc(const kvq_config* cfg, const kvq_cache* cache, const void* q, float* out,
+                                        float softmax_scale, int32_t max_seq_tokens, void* stream);
 
 /* Copies the cache's sticky error word (an OR of KVQ_DEV_* bits; 0 = nothing
  * so far) into *err after the stream's earlier work, waiting for the stream.

@@ -20,7 +20,9 @@ KVQ_DEV_RESIDUAL_FULL, KVQ_DEV_BLOCKS_FULL, KVQ_DEV_BAD_PAGE, KVQ_DEV_BAD_COUNT,
 
 EXPORTED = ("kvq_layout_bytes", "kvq_workspace_size", "kvq_append", "kvq_append_flush", "kvq_flush_residual",
             "kvq_decode_attention", "kvq_decode_partials", "kvq_decode_combine", "kvq_get_device_error",
-            "kvq_status_string", "kvq_decode_attention_multi", "kvq_workspace_size_multi")
+            "kvq_status_string", "kvq_decode_attention_multi", "kvq_workspace_size_multi",
+            "kvq_decode_attention_noalloc")
+KVQ_NOALLOC_WORKSPACE_BYTES = 64 << 20
 
 
 class kvq_config(ctypes.Structure):
@@ -76,6 +78,7 @@ def load():
         "kvq_status_string": [ctypes.c_int],
         "kvq_decode_attention_multi": [cfgp, cachep, P, I32, P, F, I32, P, SZ, P],
         "kvq_workspace_size_multi": [cfgp, I32, I32, ctypes.POINTER(SZ)],
+        "kvq_decode_attention_noalloc": [cfgp, cachep, P, P, F, I32, P],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -134,6 +137,12 @@ def kvq_decode_attention(cfg, cache, q_ptr, out_ptr, softmax_scale, max_seq_toke
     _check(load().kvq_decode_attention(ctypes.byref(cfg), ctypes.byref(cache), q_ptr, out_ptr,
                                        float(softmax_scale), int(max_seq_tokens), ws_ptr, int(ws_bytes),
                                        stream), "kvq_decode_attention")
+
+
+def kvq_decode_attention_noalloc(cfg, cache, q_ptr, out_ptr, softmax_scale, max_seq_tokens, stream):
+    _check(load().kvq_decode_attention_noalloc(ctypes.byref(cfg), ctypes.byref(cache), q_ptr, out_ptr,
+                                               float(softmax_scale), int(max_seq_tokens), stream),
+           "kvq_decode_attention_noalloc")
 
 
 def kvq_decode_attention_multi(cfg, cache, q_ptr, T, out_ptr, softmax_scale, max_seq_tokens, ws_ptr, ws_bytes,

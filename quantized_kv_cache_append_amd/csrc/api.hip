@@ -1,7 +1,8 @@
 // Host side of the C ABI declared in include/kvq.h: argument validation, byte
 // layout arithmetic and kernel launches on the caller's stream. No allocation;
-// the only state kept across calls is the launch-grid table of
-// persistent_grid() (common.h).
+// the state kept across calls is the launch-grid table of persistent_grid()
+// (common.h) and, for kvq_decode_attention_noalloc, one device array per GPU
+// (below) with its address.
 //
 // Sources:
 //   [P4] patricehuetz.fr, "Quantification du KV-Cache : TurboQuant et l'état de
@@ -234,6 +235,54 @@ kvq_status kvq_decode_combine(const kvq_config* cfg, const kvq_cache* cache, flo
   const kvq_status st = decode_args(cfg, cache, max_seq_tokens, workspace, workspace_bytes, 0.f, g, plan, scale);
   if (st != KVQ_OK) return st;
   return launched(kvq::launch_decode_combine(g, *cache, out, plan, workspace, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"
+
+// ---- the decode entry point that allocates nothing -----------------------------------
+namespace {
+// The decode workspace of kvq_decode_attention_noalloc: one array per GPU the
+// library runs on, held until the process ends. Host code must not use its name
+// as an address (that is a host-side stand-in): the device address is taken once
+// per device with hipGetSymbolAddress and kept in scratch_ptr.
+constexpr size_t kScratchBytes = KVQ_NOALLOC_WORKSPACE_BYTES;
+__device__ __align__(256) uint8_t scratch[kScratchBytes];
+constexpr int kMaxDevices = 64;
+std::mutex scratch_lock;
+void* scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's scratch array (looked up on the first
+// call on that device, with the device current).
+kvq_status scratch_of_current_device(void** ptr) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return KVQ_ERR_LAUNCH;
+  std::lock_guard<std::mutex> lock(scratch_lock);
+  if (scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return KVQ_ERR_LAUNCH;
+    scratch_ptr[dev] = p;
+  }
+  *ptr = scratch_ptr[dev];
+  return KVQ_OK;
+}
+}  // namespace
+
+extern "C" {
+
+kvq_status kvq_decode_attention_noalloc(const kvq_config* cfg, const kvq_cache* cache, const void* q, float* out,
+                                        float softmax_scale, int32_t max_seq_tokens, void* stream) {
+  kvq_status st = validate(cfg);
+  if (st != KVQ_OK) return st;
+  if ((st = validate_cache(cfg, cache)) != KVQ_OK) return st;
+  if (q == nullptr || out == nullptr || max_seq_tokens < 0 || !std::isfinite(softmax_scale))
+    return KVQ_ERR_INVALID_ARG;
+  if (max_seq_tokens > capacity_tokens(cfg)) return KVQ_ERR_CAPACITY;
+  size_t need = 0;
+  if ((st = kvq_workspace_size(cfg, max_seq_tokens, &need)) != KVQ_OK) return st;
+  if (need > kScratchBytes) return KVQ_ERR_WORKSPACE;   // before any device call
+  void* ws = nullptr;
+  if ((st = scratch_of_current_device(&ws)) != KVQ_OK) return st;
+  return kvq_decode_attention(cfg, cache, q, out, softmax_scale, max_seq_tokens, ws, kScratchBytes, stream);
 }
 
 kvq_status kvq_get_device_error(const kvq_config* cfg, const kvq_cache* cache, void* stream,

@@ -240,3 +240,26 @@ def test_batch_bound_keeps_the_plan_inside_lds(kvq_lib):
                    dtype=1)
         assert kvq_lib.kvq_layout_bytes(ctypes.byref(cfg), ctypes.byref(lay)) == status
     assert (16 + 7 * 1024) * 4 + 4 * 13 * 1024 < 160 * 1024
+
+
+def test_noalloc_decode_rejects_a_workspace_beyond_its_array_before_any_device_call(kvq_lib):
+    # the no-allocation decode holds a fixed array per GPU; a configuration whose
+    # workspace is larger gets KVQ_ERR_WORKSPACE from the host checks alone
+    from quantized_kv_cache_append_amd import binding as B
+    cfg = _cfg(B, batch=1024, num_q_heads=64, num_kv_heads=8, k_group=64, v_group=64, res_capacity=2048 + 191,
+               max_blocks=64, dtype=1)
+    need = B.kvq_workspace_size(cfg, 4096)
+    assert need > B.KVQ_NOALLOC_WORKSPACE_BYTES
+    fake = B.kvq_cache(blocks=0x1000, block_table=None, k_ring=0x2000, v_ring=0x3000, state=0x4000)
+    assert kvq_lib.kvq_decode_attention_noalloc(ctypes.byref(cfg), ctypes.byref(fake), ctypes.c_void_p(0x5000),
+                                                ctypes.c_void_p(0x6000), ctypes.c_float(0.0), 4096,
+                                                None) == B.KVQ_ERR_WORKSPACE
+    # and its other argument errors are the ones of kvq_decode_attention
+    small = _cfg(B)
+    assert kvq_lib.kvq_decode_attention_noalloc(ctypes.byref(small), ctypes.byref(fake), None,
+                                                ctypes.c_void_p(0x6000), ctypes.c_float(0.0), 4096,
+                                                None) == B.KVQ_ERR_INVALID_ARG
+    assert kvq_lib.kvq_decode_attention_noalloc(ctypes.byref(small), ctypes.byref(fake), ctypes.c_void_p(0x5000),
+                                                ctypes.c_void_p(0x6000), ctypes.c_float(0.0), 10 ** 8,
+                                                None) == B.KVQ_ERR_CAPACITY
+    assert B.KVQ_NOALLOC_WORKSPACE_BYTES == 64 << 20
