@@ -25,6 +25,10 @@ block-wise prefill or checking T drafted tokens).
 With --fp8-blocks W the W most recent quantized blocks of every (sequence, kv
 head) are also kept as FP8 records and decode reads them there (FP8 tier).
 
+With --rotate 1|2|3 the key rows, the value rows or both are rotated by a
+Walsh-Hadamard transform before they are quantized (and read back through its
+inverse by decode).
+
 With --sink P the first P tokens of every sequence stay in full precision
 beside the quantized blocks and the ring (attention sink); the decode-partials
 time then covers the sink kernel's launch as well.
@@ -143,7 +147,7 @@ def measured_traffic(workload: str):
         return None
 
 
-def quantize_rate(w, inp, lengths, dev, reps=5):
+def quantize_rate(w, inp, lengths, dev, reps=5, rotate=0):
     """Full-prefix flush: all of every sequence's tokens appended into a ring
     that holds them, then one kvq_flush_residual quantizes and packs every
     complete block past the window (event-timed, median of `reps`). Bytes are
@@ -151,7 +155,7 @@ def quantize_rate(w, inp, lengths, dev, reps=5):
     import torch
     from quantized_kv_cache_append_amd.cache import cache_for_workload
     S = max(lengths)
-    c = cache_for_workload(w, lengths, S, device=dev)
+    c = cache_for_workload(w, lengths, S, device=dev, rotate=rotate)
     lens = torch.tensor(list(lengths), dtype=torch.int32, device=dev)
     k, v = inp.k[:, :, :S].contiguous(), inp.v[:, :, :S].contiguous()
     ts = []
@@ -216,7 +220,7 @@ def host_description():
     return {"host_cpus": os.cpu_count(), "affinity_cpus": affinity, "cpu_model": model}
 
 
-def cpu_baseline(w, inp, lengths, budget_s=15.0, sink=0, quant_budget_s=4.0):
+def cpu_baseline(w, inp, lengths, budget_s=15.0, sink=0, quant_budget_s=4.0, rotate=0):
     """Time the oracle on the host, one thread: its decode attention on a bounded
     sample of (sequence, kv head) pairs of the same workload (GB/s of the same
     algorithmic bytes), and its quantizer (formula F + packing) over the blocks
@@ -228,7 +232,8 @@ def cpu_baseline(w, inp, lengths, budget_s=15.0, sink=0, quant_budget_s=4.0):
 
     from oracle import kivi
     spec = kivi.CacheSpec(w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim, w.k_bits, w.v_bits,
-                          w.k_group, w.v_group, w.residual, w.residual + w.k_group, w.dtype, sink=sink)
+                          w.k_group, w.v_group, w.residual, w.residual + w.k_group, w.dtype, sink=sink,
+                          rotate=rotate)
     q = inp.q.float().cpu().numpy()
     pairs = [(b, h) for b in range(w.batch) for h in range(w.num_kv_heads)]
     done, nbytes, t_used = 0, 0.0, 0.0
@@ -243,7 +248,7 @@ def cpu_baseline(w, inp, lengths, budget_s=15.0, sink=0, quant_budget_s=4.0):
             v = inp.v[b, h, :S].float().cpu().numpy()[None, None]
             qp = q[b:b + 1, h * n_g:(h + 1) * n_g]
             one = kivi.CacheSpec(1, n_g, 1, w.head_dim, w.k_bits, w.v_bits, w.k_group, w.v_group,
-                                 w.residual, w.residual + w.k_group, w.dtype, sink=sink)
+                                 w.residual, w.residual + w.k_group, w.dtype, sink=sink, rotate=rotate)
             t0 = time.perf_counter()
             got = kivi.decode_attention(one, qp, k, v, [S])
             t_used += time.perf_counter() - t0
@@ -319,7 +324,7 @@ def bench_layers(w, args, dev):
     t0 = time.perf_counter()
     for layer in range(L):
         inp = W.make_layer(w, device=dev, layer=layer, lengths=lengths0)
-        c = cache_for_workload(w, lengths0, chunk, extra_tokens=total_steps + 1, device=dev)
+        c = cache_for_workload(w, lengths0, chunk, extra_tokens=total_steps + 1, device=dev, rotate=args.rotate)
         c.prefill(inp.k, inp.v, lengths0, chunk)
         # this layer's decode tokens for the steps (distinct per layer and step)
         toks.append([W.new_tokens(w, inp, 1, device=dev, step=layer * 100003 + s) for s in range(4)])
@@ -404,7 +409,8 @@ def bench_layers(w, args, dev):
         "config": {"workload": w.name, "layers": L, "batch": w.batch, "num_q_heads": w.num_q_heads,
                    "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim, "seq_len": max(lengths0),
                    "input_dtype": w.dtype, "k_bits": w.k_bits, "v_bits": w.v_bits, "k_group": w.k_group,
-                   "v_group": w.v_group, "residual": w.residual, "paged": w.paged, "cache_copies_rotated": 1},
+                   "v_group": w.v_group, "residual": w.residual, "paged": w.paged, "rotate": args.rotate,
+                   "cache_copies_rotated": 1},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBPS, 4),
                      "traffic": None if traffic is None else round(traffic),
@@ -415,12 +421,12 @@ def bench_layers(w, args, dev):
     }
     del caches, ws
     torch.cuda.empty_cache()
-    result["quantize"] = quantize_rate(w, inp0, lengths0, dev)
+    result["quantize"] = quantize_rate(w, inp0, lengths0, dev, rotate=args.rotate)
     result["quantize"]["sample"] += " (one layer)"
     log(f"[bench] quantize (one layer): full-prefix flush {result['quantize']['us_per_flush']:.1f} us, "
         f"{result['quantize']['bytes'] / 1e6:.1f} MB -> {result['quantize']['value']:.0f} GB/s")
     if not args.no_cpu_baseline:
-        cb = cpu_baseline(w, inp0, list(lengths0))
+        cb = cpu_baseline(w, inp0, list(lengths0), rotate=args.rotate)
         cb["sample"] += f"; layer 0 only (a step is {L} such layers)"
         result["cpu_baseline"] = cb
         log(f"[bench] oracle on the host: {cb['value']:.3f} GB/s")
@@ -444,6 +450,8 @@ def main():
     ap.add_argument("--layers", type=int, default=0,
                     help="multi-layer workloads: time this many layers instead of all (profiling runs; "
                          "the JSON line's config.layers says how many were timed)")
+    ap.add_argument("--rotate", type=int, default=0, choices=(0, 1, 2, 3),
+                    help="Walsh-Hadamard pre-rotation of keys (1), values (2) or both (3) before quantization")
     ap.add_argument("--sink", type=int, default=0,
                     help="keep the first SINK tokens of every sequence in full precision (attention sink)")
     args = ap.parse_args()
@@ -480,7 +488,8 @@ def main():
 
     inp = W.make_layer(w, device=dev, lengths=lengths0)
     chunk = 512
-    probe = cache_for_workload(w, lengths0, chunk, extra_tokens=0, device=dev, sink=P, fp8_blocks=W8)
+    probe = cache_for_workload(w, lengths0, chunk, extra_tokens=0, device=dev, sink=P, fp8_blocks=W8,
+                               rotate=args.rotate)
     rec = probe.record_bytes
     per_copy = probe.blocks.numel() + 2 * probe.k_ring.numel() * 2 + \
         (2 * probe.k_sink.numel() * 2 if probe.k_sink is not None else 0) + \
@@ -491,7 +500,8 @@ def main():
     caches = []
     t_fill = 0.0
     for i in range(copies):
-        c = cache_for_workload(w, lengths0, chunk, extra_tokens=steps_per_copy, device=dev, sink=P, fp8_blocks=W8)
+        c = cache_for_workload(w, lengths0, chunk, extra_tokens=steps_per_copy, device=dev, sink=P, fp8_blocks=W8,
+                               rotate=args.rotate)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         c.prefill(inp.k, inp.v, lengths0, chunk)
@@ -610,7 +620,7 @@ def main():
                    "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim, "seq_len": max(lengths0),
                    "input_dtype": w.dtype, "k_bits": w.k_bits, "v_bits": w.v_bits, "k_group": w.k_group,
                    "v_group": w.v_group, "residual": w.residual, "paged": w.paged, "sink": P, "query_tokens": T,
-                   "fp8_blocks": W8,
+                   "fp8_blocks": W8, "rotate": args.rotate,
                    "cache_copies_rotated": copies},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBPS, 4),
@@ -620,13 +630,13 @@ def main():
         "quantize": None,
         "cpu_baseline": None,
     }
-    result["quantize"] = quantize_rate(w, inp, lengths0, dev)
+    result["quantize"] = quantize_rate(w, inp, lengths0, dev, rotate=args.rotate)
     log(f"[bench] quantize: full-prefix flush {result['quantize']['us_per_flush']:.1f} us, "
         f"{result['quantize']['bytes'] / 1e6:.1f} MB -> {result['quantize']['value']:.0f} GB/s")
     if not args.no_cpu_baseline and T > 1:
         log("[bench] the oracle baseline times single-token decode; skipped for --query-tokens > 1")
     elif not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(w, inp, [s + 0 for s in lengths0], sink=P)
+        result["cpu_baseline"] = cpu_baseline(w, inp, [s + 0 for s in lengths0], sink=P, rotate=args.rotate)
         log(f"[bench] oracle on the host: {result['cpu_baseline']['value']:.3f} GB/s")
     print(json.dumps(result), flush=True)
 

@@ -66,6 +66,21 @@
  *   V scale  fp16  [G]
  * Store: [B][H_kv][W] records; block j of a pair lives in slot j mod W.
  *
+ * Walsh-Hadamard pre-rotation (kvq_config.rotate; [P4], "TurboQuant : les cinq
+ * innovations", innovation 1: a WHT of the key and value vectors before
+ * quantization spreads outliers over every dimension and is inverted on the
+ * dequantized vectors). With KVQ_ROTATE_KEYS (KVQ_ROTATE_VALUES) every key
+ * (value) token row x of a flushed block is replaced, before formula F, by
+ * R(x) = H x / 8: H the d x d Sylvester Hadamard matrix (H_1 = [1], H_2n =
+ * [[H_n, H_n], [H_n, -H_n]]), applied in fp32 as radix-2 butterflies -- for h =
+ * 1, 2, ..., d/2, each pair (i, i + h) with bit h of i clear becomes
+ * (x_i + x_{i+h}, x_i - x_{i+h}) -- then multiplied by 1/8 (exact). Records
+ * then hold the rotated rows' codes, scales and zero-points; the ring and the
+ * sink keep the original rows. Attention reads a dequantized rotated row y
+ * back as H y * 8 / d (H H = d I): decode rotates the query instead for the
+ * quantized keys, and applies H * 8 / d once per output row to the quantized
+ * tokens' share of the value sum. Not with the FP8 tier (KVQ_ERR_UNSUPPORTED).
+ *
  * Record of one block (little-endian, sections in this order, no padding):
  *   K codes  uint32 [G][d*k_bits/32]   token-major; word w of token t holds
  *                                       channels w*32/k_bits.. , LSB first
@@ -129,6 +144,7 @@ typedef enum {
 } kvq_status;
 
 enum { KVQ_F16 = 0, KVQ_BF16 = 1 };
+enum { KVQ_ROTATE_KEYS = 1, KVQ_ROTATE_VALUES = 2 };
 
 /* Bits of the device-side sticky error word. */
 enum {
@@ -155,6 +171,7 @@ typedef struct {
   int32_t dtype;          /* KVQ_F16 or KVQ_BF16: K, V, q and the ring                     */
   int32_t sink;           /* P >= 0: leading tokens of every sequence kept in full precision */
   int32_t fp8_blocks;     /* W >= 0: most recent quantized blocks also kept, and read, in FP8 */
+  int32_t rotate;         /* Walsh-Hadamard pre-rotation: 0 none, | KVQ_ROTATE_KEYS, | KVQ_ROTATE_VALUES */
 } kvq_config;
 
 typedef struct {

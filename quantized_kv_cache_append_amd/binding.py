@@ -16,6 +16,7 @@ LIBRARY_PATH = os.path.join(_PKG, "libkvq.so")
 
 KVQ_OK, KVQ_ERR_INVALID_ARG, KVQ_ERR_UNSUPPORTED, KVQ_ERR_CAPACITY, KVQ_ERR_WORKSPACE, KVQ_ERR_LAUNCH = range(6)
 KVQ_F16, KVQ_BF16 = 0, 1
+KVQ_ROTATE_KEYS, KVQ_ROTATE_VALUES = 1, 2
 KVQ_DEV_RESIDUAL_FULL, KVQ_DEV_BLOCKS_FULL, KVQ_DEV_BAD_PAGE, KVQ_DEV_BAD_COUNT, KVQ_DEV_TOO_LONG = 1, 2, 4, 8, 16
 
 EXPORTED = ("kvq_layout_bytes", "kvq_workspace_size", "kvq_append", "kvq_append_flush", "kvq_flush_residual",
@@ -28,7 +29,7 @@ KVQ_NOALLOC_WORKSPACE_BYTES = 64 << 20
 class kvq_config(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "batch", "num_q_heads", "num_kv_heads", "head_dim", "k_bits", "v_bits", "k_group", "v_group",
-        "residual", "res_capacity", "max_blocks", "num_pages", "dtype", "sink", "fp8_blocks")]
+        "residual", "res_capacity", "max_blocks", "num_pages", "dtype", "sink", "fp8_blocks", "rotate")]
 
 
 class kvq_layout(ctypes.Structure):

@@ -32,13 +32,15 @@ class QuantizedKVCache:
     sink); the quantized blocks and the ring then hold the tokens after them.
     `fp8_blocks` > 0 keeps the most recent `fp8_blocks` quantized blocks of
     every (sequence, kv head) also as FP8 records, which decode reads instead.
+    `rotate` (binding.KVQ_ROTATE_KEYS | KVQ_ROTATE_VALUES) rotates key and/or
+    value rows by a Walsh-Hadamard transform before they are quantized.
     """
 
     def __init__(self, batch: int, num_q_heads: int, num_kv_heads: int, head_dim: int, *,
                  k_bits: int, v_bits: int, k_group: int, v_group: int, residual: int,
                  dtype=torch.float16, max_tokens: int | None = None, res_capacity: int | None = None,
                  page_table: torch.Tensor | None = None, num_pages: int = 0, sink: int = 0, fp8_blocks: int = 0,
-                 device="cuda"):
+                 rotate: int = 0, device="cuda"):
         if dtype not in _DTYPES:
             raise TypeError(f"dtype must be float16 or bfloat16, got {dtype}")
         self.device = torch.device(device)
@@ -59,7 +61,7 @@ class QuantizedKVCache:
                                 head_dim=head_dim, k_bits=k_bits, v_bits=v_bits, k_group=k_group,
                                 v_group=v_group, residual=residual, res_capacity=res_capacity,
                                 max_blocks=max_blocks, num_pages=num_pages, dtype=_DTYPES[dtype], sink=sink,
-                                fp8_blocks=fp8_blocks)
+                                fp8_blocks=fp8_blocks, rotate=rotate)
         self.layout = B.kvq_layout_bytes(self.cfg)
         dev = self.device
         self.blocks = torch.zeros(self.layout.blocks, dtype=torch.uint8, device=dev)
@@ -253,7 +255,7 @@ class QuantizedKVCache:
 
 
 def cache_for_workload(w, lengths, chunk: int, extra_tokens: int = 0, device="cuda", seed: int = 0, sink: int = 0,
-                       fp8_blocks: int = 0):
+                       fp8_blocks: int = 0, rotate: int = 0):
     """An empty cache for a `workloads.Workload`, sized for `lengths` plus
     `extra_tokens` of decode growth, whose ring takes `chunk` tokens per append
     on top of R + G - 1, with a sink of `sink` tokens. Paged workloads get a
@@ -262,7 +264,7 @@ def cache_for_workload(w, lengths, chunk: int, extra_tokens: int = 0, device="cu
     res_capacity = w.residual + w.k_group - 1 + max(chunk, 1)
     common = dict(k_bits=w.k_bits, v_bits=w.v_bits, k_group=w.k_group, v_group=w.v_group,
                   residual=w.residual, dtype=w.torch_dtype, res_capacity=res_capacity, sink=sink,
-                  fp8_blocks=fp8_blocks, device=device)
+                  fp8_blocks=fp8_blocks, rotate=rotate, device=device)
     if w.paged:
         table, num_pages = W.random_page_table(w, lengths, extra_tokens=extra_tokens, seed=seed)
         return QuantizedKVCache(w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim,

@@ -46,6 +46,8 @@ kvq_status validate(const kvq_config* c) {
   if (c->sink > kMaxSink) return KVQ_ERR_UNSUPPORTED;
   if (c->fp8_blocks > kMaxFp8Blocks) return KVQ_ERR_UNSUPPORTED;
   if ((long long)c->k_group * c->v_bits < 32) return KVQ_ERR_UNSUPPORTED;
+  if (c->rotate & ~(KVQ_ROTATE_KEYS | KVQ_ROTATE_VALUES)) return KVQ_ERR_INVALID_ARG;
+  if (c->rotate != 0 && c->fp8_blocks > 0) return KVQ_ERR_UNSUPPORTED;   // the FP8 tier stores unrotated rows
   return KVQ_OK;
 }
 

@@ -36,18 +36,46 @@ namespace {
 constexpr int kAppendTokensPerWG = 64;
 constexpr int kThreads = 256;
 
-// LDS of the block routine: raw tile [G][d] x 2 (16-bit), codes [G][d] x 2 (8-bit).
-__host__ __device__ inline size_t block_lds_bytes(int G, int d) { return (size_t)6 * G * d; }
+// LDS of the block routine: raw tile [G][d] x 2 (16-bit), codes [G][d] x 2
+// (8-bit); with the pre-rotation the tiles are fp32 instead.
+__host__ __device__ inline size_t block_lds_bytes(int G, int d, bool rot = false) {
+  return (size_t)(rot ? 10 : 6) * G * d;
+}
 
-// Quantize tokens blk*G .. blk*G+G-1 of ring `pair` into record `rec`.
+// Walsh-Hadamard pre-rotation of every row of an fp32 tile [G][d] in LDS
+// (patricehuetz.fr, "TurboQuant : les cinq innovations", innovation 1): for
+// h = 1, 2, ..., d/2 each pair (i, i + h) of a row with bit h of i clear becomes
+// (x_i + x_{i+h}, x_i - x_{i+h}), rounded to fp32; the last stage also takes the
+// factor 1/8 (exact). All threads of the workgroup call it; ends with a barrier.
+__device__ void rotate_rows(float* f, int G, int d) {
+  const int half = d / 2;
+  for (int h = 1; h < d; h <<= 1) {
+    const bool last = 2 * h == d;
+    for (int idx = threadIdx.x; idx < G * half; idx += kThreads) {
+      const int t = idx / half, j = idx % half;
+      float* row = f + t * d;
+      const int i = (j / h) * 2 * h + j % h;
+      const float a = row[i], b = row[i + h];
+      const float s = __fadd_rn(a, b), r = __fsub_rn(a, b);
+      row[i] = last ? __fmul_rn(s, 0.125f) : s;
+      row[i + h] = last ? __fmul_rn(r, 0.125f) : r;
+    }
+    __syncthreads();
+  }
+}
+
+// Quantize tokens blk*G .. blk*G+G-1 of ring `pair` into record `rec`; with ROT
+// the rows of the sides g.rot names are rotated first (rotate_rows).
 // Called by all kThreads threads of the workgroup; ends with a barrier.
-template <bool BF16>
+template <bool BF16, bool ROT = false>
 __device__ void quantize_block(const Geom& g, uint8_t* __restrict__ rec, const uint16_t* __restrict__ k_ring,
                                const uint16_t* __restrict__ v_ring, int pair, int blk, uint8_t* smem) {
   const int G = g.G, d = g.d, tid = threadIdx.x;
-  uint16_t* s_k = reinterpret_cast<uint16_t*>(smem);   // [G][d]
+  uint16_t* s_k = reinterpret_cast<uint16_t*>(smem);   // [G][d] (without rotation)
   uint16_t* s_v = s_k + G * d;                         // [G][d]
-  uint8_t* s_kc = reinterpret_cast<uint8_t*>(s_v + G * d);   // [G][d] key codes
+  float* f_k = reinterpret_cast<float*>(smem);         // [G][d] (with rotation)
+  float* f_v = f_k + G * d;
+  uint8_t* s_kc = ROT ? reinterpret_cast<uint8_t*>(f_v + G * d) : reinterpret_cast<uint8_t*>(s_v + G * d);   // [G][d]
   uint8_t* s_vc = s_kc + G * d;                              // [d][G] value codes
 
   const int vec_per_tok = d / 8;
@@ -55,10 +83,30 @@ __device__ void quantize_block(const Geom& g, uint8_t* __restrict__ rec, const u
     const int t = idx / vec_per_tok, v = idx % vec_per_tok;
     const int slot = (blk * G + t) % g.C;
     const size_t src = ((size_t)pair * g.C + slot) * d + (size_t)v * 8;
-    *reinterpret_cast<uint4*>(&s_k[t * d + v * 8]) = *reinterpret_cast<const uint4*>(k_ring + src);
-    *reinterpret_cast<uint4*>(&s_v[t * d + v * 8]) = *reinterpret_cast<const uint4*>(v_ring + src);
+    const uint4 kw = *reinterpret_cast<const uint4*>(k_ring + src);
+    const uint4 vw = *reinterpret_cast<const uint4*>(v_ring + src);
+    if constexpr (ROT) {
+      const uint32_t kk[4] = {kw.x, kw.y, kw.z, kw.w}, vv[4] = {vw.x, vw.y, vw.z, vw.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        f_k[t * d + v * 8 + 2 * e] = in_to_f32<BF16>(kk[e] & 0xffffu);
+        f_k[t * d + v * 8 + 2 * e + 1] = in_to_f32<BF16>(kk[e] >> 16);
+        f_v[t * d + v * 8 + 2 * e] = in_to_f32<BF16>(vv[e] & 0xffffu);
+        f_v[t * d + v * 8 + 2 * e + 1] = in_to_f32<BF16>(vv[e] >> 16);
+      }
+    } else {
+      *reinterpret_cast<uint4*>(&s_k[t * d + v * 8]) = kw;
+      *reinterpret_cast<uint4*>(&s_v[t * d + v * 8]) = vw;
+    }
   }
   __syncthreads();
+  if constexpr (ROT) {
+    if (g.rot & KVQ_ROTATE_KEYS) rotate_rows(f_k, G, d);
+    if (g.rot & KVQ_ROTATE_VALUES) rotate_rows(f_v, G, d);
+  }
+  // element (t, c) of the key / value tile, as fp32
+  auto kx = [&](int t, int c) -> float { return ROT ? f_k[t * d + c] : in_to_f32<BF16>(s_k[t * d + c]); };
+  auto vx = [&](int t, int c) -> float { return ROT ? f_v[t * d + c] : in_to_f32<BF16>(s_v[t * d + c]); };
 
   uint16_t* ks = reinterpret_cast<uint16_t*>(rec + g.rec_ks);
   uint16_t* kz = reinterpret_cast<uint16_t*>(rec + g.rec_kz);
@@ -67,25 +115,25 @@ __device__ void quantize_block(const Geom& g, uint8_t* __restrict__ rec, const u
 
   // keys: one group per channel over the G tokens
   for (int c = tid; c < d; c += kThreads) {
-    float mn = in_to_f32<BF16>(s_k[c]), mx = mn;
+    float mn = kx(0, c), mx = mn;
     for (int t = 1; t < G; ++t) {
-      const float x = in_to_f32<BF16>(s_k[t * d + c]);
+      const float x = kx(t, c);
       mn = fminf(mn, x);
       mx = fmaxf(mx, x);
     }
     const GroupParams p = group_params(mn, mx, g.kb);
     ks[c] = p.s16;
     kz[c] = p.z16;
-    for (int t = 0; t < G; ++t) s_kc[t * d + c] = (uint8_t)group_code(in_to_f32<BF16>(s_k[t * d + c]), p, g.kb);
+    for (int t = 0; t < G; ++t) s_kc[t * d + c] = (uint8_t)group_code(kx(t, c), p, g.kb);
   }
   // values: one group per (token, G_V consecutive channels)
   const int ngr = d / g.GV;
   for (int idx = tid; idx < G * ngr; idx += kThreads) {
     const int t = idx / ngr, j = idx % ngr;
-    const uint16_t* row = &s_v[t * d + j * g.GV];
-    float mn = in_to_f32<BF16>(row[0]), mx = mn;
+    const int c0 = j * g.GV;
+    float mn = vx(t, c0), mx = mn;
     for (int c = 1; c < g.GV; ++c) {
-      const float x = in_to_f32<BF16>(row[c]);
+      const float x = vx(t, c0 + c);
       mn = fminf(mn, x);
       mx = fmaxf(mx, x);
     }
@@ -93,7 +141,7 @@ __device__ void quantize_block(const Geom& g, uint8_t* __restrict__ rec, const u
     vs[j * G + t] = p.s16;
     vz[j * G + t] = p.z16;
     for (int c = 0; c < g.GV; ++c)
-      s_vc[(j * g.GV + c) * G + t] = (uint8_t)group_code(in_to_f32<BF16>(row[c]), p, g.vb);
+      s_vc[(c0 + c) * G + t] = (uint8_t)group_code(vx(t, c0 + c), p, g.vb);
   }
   __syncthreads();
 
@@ -273,17 +321,19 @@ __device__ inline void write_fp8_rows(const Geom& g, uint8_t* __restrict__ rec8,
 // workgroup (the wave routine: one per wave; the workgroup routine: one).
 // fp8() writes the block's FP8 record (every wave of a workgroup worker
 // takes a share of its tokens).
-template <bool BF16>
+// The workgroup routine; ROT: with the Walsh-Hadamard pre-rotation of the sides
+// g.rot names (every rotated configuration takes this routine).
+template <bool BF16, bool ROT = false>
 struct WgBlock {
   static constexpr int kWorkers = 1;
   __device__ static void fp8(const Geom& g, uint8_t* rec8, const uint16_t* kr, const uint16_t* vr, int pair,
                              int blk) {
     write_fp8_rows<BF16>(g, rec8, kr, vr, pair, blk, (int)(threadIdx.x >> 6), kThreads / 64);
   }
-  static size_t lds(const Geom& g) { return block_lds_bytes(g.G, g.d); }
+  static size_t lds(const Geom& g) { return block_lds_bytes(g.G, g.d, ROT); }
   __device__ static void run(const Geom& g, uint8_t* rec, const uint16_t* kr, const uint16_t* vr, int pair,
                              int blk, uint8_t* smem) {
-    quantize_block<BF16>(g, rec, kr, vr, pair, blk, smem);
+    quantize_block<BF16, ROT>(g, rec, kr, vr, pair, blk, smem);
   }
 };
 template <class Q>
@@ -484,6 +534,9 @@ const QuantEntry* find_wave(const Geom& g) {
 }  // namespace
 
 hipError_t launch_flush(const Geom& g, const kvq_cache& c, hipStream_t s) {
+  if (g.rot != 0)
+    return g.dtype == KVQ_BF16 ? launch_flush_p<WgBlock<true, true>>(g, c, s)
+                               : launch_flush_p<WgBlock<false, true>>(g, c, s);
   if (const QuantEntry* e = find_wave(g)) return e->flush(g, c, s);
   return g.dtype == KVQ_BF16 ? launch_flush_p<WgBlock<true>>(g, c, s) : launch_flush_p<WgBlock<false>>(g, c, s);
 }
@@ -495,6 +548,9 @@ hipError_t launch_append_flush(const Geom& g, const kvq_cache& c, const void* k_
     hipError_t e = launch_append(g, c, k_new, v_new, n_new, n_max, s);
     return e != hipSuccess ? e : launch_flush(g, c, s);
   }
+  if (g.rot != 0)
+    return g.dtype == KVQ_BF16 ? launch_append_flush_p<WgBlock<true, true>>(g, c, k_new, v_new, n_new, n_max, s)
+                               : launch_append_flush_p<WgBlock<false, true>>(g, c, k_new, v_new, n_new, n_max, s);
   if (const QuantEntry* e = find_wave(g)) return e->append_flush(g, c, k_new, v_new, n_new, n_max, s);
   return g.dtype == KVQ_BF16 ? launch_append_flush_p<WgBlock<true>>(g, c, k_new, v_new, n_new, n_max, s)
                              : launch_append_flush_p<WgBlock<false>>(g, c, k_new, v_new, n_new, n_max, s);

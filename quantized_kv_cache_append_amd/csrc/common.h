@@ -32,6 +32,7 @@ struct Geom {
   int T;         // queries per (sequence, query head): the T newest tokens, causal; Hq and ng count them
   int W;         // FP8 tier: most recent quantized blocks also kept (and read) as FP8 records
   int rec8;      // bytes of one FP8 record: K codes [G][d], K scales [G], V codes [G][d], V scales [G]
+  int rot;       // Walsh-Hadamard pre-rotation: KVQ_ROTATE_KEYS | KVQ_ROTATE_VALUES bits
 };
 
 // Query rows per kv head one launch serves (n_g times T).
@@ -58,6 +59,7 @@ inline Geom make_geom(const kvq_config& c) {
   g.T = 1;
   g.W = c.fp8_blocks;
   g.rec8 = 2 * g.G * g.d + 4 * g.G;
+  g.rot = c.rotate;
   return g;
 }
 
@@ -112,6 +114,49 @@ __device__ __forceinline__ float wave_sum(float v) {
   for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
   return v;
 }
+// ---- Walsh-Hadamard transform of one row held by a wave ------------------------
+// H x * scale (H the Sylvester Hadamard matrix) for a row of 128 channels held as
+// lane l: (x[2l], x[2l+1]), in the butterfly order of the flush's pre-rotation
+// (h = 1, 2, ..., 64; the pair (c, c + h) becomes (x_c + x_{c+h}, x_c - x_{c+h})).
+// Stage h = 1 is inside the lane, stage h = 2m pairs lane l with lane l ^ m.
+__device__ __forceinline__ void wht_row_pairs(float& x0, float& x1, float scale) {
+  const int lane = threadIdx.x & 63;
+  const float a = x0 + x1, b = x0 - x1;
+  x0 = a;
+  x1 = b;
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) {
+    const float p0 = __shfl_xor(x0, m, 64), p1 = __shfl_xor(x1, m, 64);
+    const bool upper = (lane & m) != 0;   // this lane holds the (c + h) side
+    x0 = upper ? p0 - x0 : x0 + p0;
+    x1 = upper ? p1 - x1 : x1 + p1;
+  }
+  x0 *= scale;
+  x1 *= scale;
+}
+// The same for a row of 64 * CPL channels held as lane l: x[k] = channel l + 64k
+// (stages h = 1 .. 32 across lanes, h = 64 inside the lane).
+template <int CPL>
+__device__ __forceinline__ void wht_row_strided(float (&x)[CPL], float scale) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) {
+    const bool upper = (lane & m) != 0;
+#pragma unroll
+    for (int k = 0; k < CPL; ++k) {
+      const float p = __shfl_xor(x[k], m, 64);
+      x[k] = upper ? p - x[k] : x[k] + p;
+    }
+  }
+  if constexpr (CPL == 2) {
+    const float a = x[0] + x[1], b = x[0] - x[1];
+    x[0] = a;
+    x[1] = b;
+  }
+#pragma unroll
+  for (int k = 0; k < CPL; ++k) x[k] *= scale;
+}
+
 // Orders this wave's LDS writes before its later LDS reads of other lanes'
 // data: waits for the wave's outstanding LDS operations only (global loads in
 // flight stay in flight) and keeps the compiler from moving memory accesses

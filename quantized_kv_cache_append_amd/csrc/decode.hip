@@ -100,6 +100,12 @@ __global__ __launch_bounds__(256) void decode_generic_kernel(
 
     if (!un.ring) {
       // ---- quantized blocks of this unit ----
+      // (rotated keys: the query is rotated the same way, H q' * 8 / D)
+      if (g.rot & KVQ_ROTATE_KEYS) {
+#pragma unroll
+        for (int j = 0; j < kNgMax; ++j)
+          if (j < ng) wht_row_strided<CPL>(qv[j], 8.0f / D);
+      }
       const int blk0 = un.begin, blk1 = un.end;
       const int kP = 32 / g.kb;
       const uint32_t kmask = (1u << g.kb) - 1, vmask = (1u << g.vb) - 1;
@@ -246,7 +252,11 @@ constexpr int kCombineBatch = 64;
 // or one round of a row, per wave).
 constexpr int kSideWaves = 1;
 
-template <int D, bool SIDE, int WPR>
+// ROTV (values pre-rotated): the quantized units' partials (after the side
+// states and the pair's ring units) sum in the rotated coordinates, kept apart
+// and taken back through H y * 8 / D once per row: o = (sum_plain + H sum_rot
+// * 8 / D) / L.
+template <int D, bool SIDE, int WPR, bool ROTV>
 __global__ __launch_bounds__(64 * WPR) void combine_kernel(Geom g, const int* __restrict__ plan,
                                                           const float* ws,   // (not restrict: the
                                                           // compiler barrier below must order its loads)
@@ -263,9 +273,10 @@ __global__ __launch_bounds__(64 * WPR) void combine_kernel(Geom g, const int* __
   const size_t stride = (size_t)g.ng * (D + 2);
   const float* src0 = ws + (size_t)j * (D + 2);
 
-  float m = -INFINITY, L = 0.f, acc[CPL];
+  float m = -INFINITY, L = 0.f, acc[CPL], accq[CPL];
 #pragma unroll
-  for (int k = 0; k < CPL; ++k) acc[k] = 0.f;
+  for (int k = 0; k < CPL; ++k) acc[k] = accq[k] = 0.f;
+  const int q0 = (SIDE ? nside : 0) + pu.cnt[0];   // partials from q0 on are quantized units
   // partial i: the side states (sink, FP8 tier rounds) first, then the pair's units
   const size_t side_stride = (size_t)g.B * g.Hq * (D + 2);
   const float* side0 = side_parts + (size_t)row * (D + 2);
@@ -300,24 +311,36 @@ __global__ __launch_bounds__(64 * WPR) void combine_kernel(Geom g, const int* __
     const float w = mi == -INFINITY ? 0.f : exp2f(mi - mn);   // weight of partial i0 + lane
     L = L * a + wave_sum(w * li);
 #pragma unroll
-    for (int k = 0; k < CPL; ++k) acc[k] *= a;
+    for (int k = 0; k < CPL; ++k) {
+      acc[k] *= a;
+      if constexpr (ROTV) accq[k] *= a;
+    }
 #pragma unroll
     for (int u = 0; u < kCombineBatch; ++u) {
       const float wu = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), u));   // 0 past cnt
+      if (ROTV && i0 + u >= q0) {
 #pragma unroll
-      for (int k = 0; k < CPL; ++k) acc[k] = wu == 0.f ? acc[k] : fmaf(wu, v[u][k], acc[k]);   // (empty partials: o unset)
+        for (int k = 0; k < CPL; ++k) accq[k] = wu == 0.f ? accq[k] : fmaf(wu, v[u][k], accq[k]);
+      } else {
+#pragma unroll
+        for (int k = 0; k < CPL; ++k) acc[k] = wu == 0.f ? acc[k] : fmaf(wu, v[u][k], acc[k]);   // (empty partials: o unset)
+      }
     }
     m = mn;
   }
   if constexpr (WPR > 1) {
     __shared__ float s_ml[WPR][2];
     __shared__ float s_acc[WPR][D];
+    __shared__ float s_accq[ROTV ? WPR : 1][D];
     if (lane == 0) {
       s_ml[wave][0] = m;
       s_ml[wave][1] = L;
     }
 #pragma unroll
-    for (int k = 0; k < CPL; ++k) s_acc[wave][CPL * lane + k] = acc[k];
+    for (int k = 0; k < CPL; ++k) {
+      s_acc[wave][CPL * lane + k] = acc[k];
+      if constexpr (ROTV) s_accq[wave][CPL * lane + k] = accq[k];
+    }
     __syncthreads();
     if (wave != 0) return;
     float M = -INFINITY;
@@ -325,7 +348,7 @@ __global__ __launch_bounds__(64 * WPR) void combine_kernel(Geom g, const int* __
     for (int x = 0; x < WPR; ++x) M = fmaxf(M, s_ml[x][0]);
     L = 0.f;
 #pragma unroll
-    for (int k = 0; k < CPL; ++k) acc[k] = 0.f;
+    for (int k = 0; k < CPL; ++k) acc[k] = accq[k] = 0.f;
 #pragma unroll
     for (int x = 0; x < WPR; ++x) {
       const float mx = s_ml[x][0];
@@ -333,8 +356,17 @@ __global__ __launch_bounds__(64 * WPR) void combine_kernel(Geom g, const int* __
       const float wx = exp2f(mx - M);
       L = fmaf(wx, s_ml[x][1], L);
 #pragma unroll
-      for (int k = 0; k < CPL; ++k) acc[k] = fmaf(wx, s_acc[x][CPL * lane + k], acc[k]);
+      for (int k = 0; k < CPL; ++k) {
+        acc[k] = fmaf(wx, s_acc[x][CPL * lane + k], acc[k]);
+        if constexpr (ROTV) accq[k] = fmaf(wx, s_accq[x][CPL * lane + k], accq[k]);
+      }
     }
+  }
+  if constexpr (ROTV) {   // the quantized share back from the rotated coordinates
+    if constexpr (CPL == 2) wht_row_pairs(accq[0], accq[1], 8.0f / D);
+    else wht_row_strided<CPL>(accq, 8.0f / D);
+#pragma unroll
+    for (int k = 0; k < CPL; ++k) acc[k] += accq[k];
   }
   float* dst = out + (size_t)row * D + CPL * lane;
 #pragma unroll
@@ -569,7 +601,9 @@ hipError_t launch_generic(const Geom& g, const kvq_cache& c, const void* q, floa
 DecodePlan plan_decode(const Geom& g, int max_seq_tokens) {
   DecodePlan p{};
   int nb_set = 1, rc = kRingAll, us = 0;
-  p.fast = fast_supported(g, &nb_set, &rc, &us);
+  // the pre-rotation runs on the GQA matrix-core kernel and the generic kernel
+  // (the one-query-head kernels merge a wave's ring and quantized units)
+  p.fast = fast_supported(g, &nb_set, &rc, &us) && !(g.rot != 0 && g.ng == 1);
   p.nb_set = p.fast ? nb_set : 1;
   p.ring_chunk = p.fast ? rc : kRingAll;
   p.unit_sets = p.fast ? us : 0;
@@ -635,6 +669,22 @@ hipError_t launch_decode_partials(const Geom& g, const kvq_cache& c, const void*
               : launch_generic<64, false>(g, c, q, scale, plan, ws, s);
 }
 
+namespace {
+template <int D, bool SIDE>
+hipError_t launch_combine(bool wide, bool rotv, const Geom& g, const int* planp, const float* parts,
+                          const float* side, int ns, float* out, hipStream_t s) {
+  const dim3 gd(g.B * g.Hq);
+  if (wide) {
+    if (rotv) hipLaunchKernelGGL((combine_kernel<D, SIDE, 4, true>), gd, dim3(256), 0, s, g, planp, parts, side, ns, out);
+    else hipLaunchKernelGGL((combine_kernel<D, SIDE, 4, false>), gd, dim3(256), 0, s, g, planp, parts, side, ns, out);
+  } else {
+    if (rotv) hipLaunchKernelGGL((combine_kernel<D, SIDE, 1, true>), gd, dim3(64), 0, s, g, planp, parts, side, ns, out);
+    else hipLaunchKernelGGL((combine_kernel<D, SIDE, 1, false>), gd, dim3(64), 0, s, g, planp, parts, side, ns, out);
+  }
+  return hipGetLastError();
+}
+}  // namespace
+
 hipError_t launch_decode_combine(const Geom& g, const kvq_cache& c, float* out, const DecodePlan& plan, void* ws,
                                  hipStream_t s) {
   (void)c;
@@ -647,27 +697,14 @@ hipError_t launch_decode_combine(const Geom& g, const kvq_cache& c, float* out, 
   // waves within 256 CUs x 32 wave slots): with more rows than that, the extra
   // waves cost more than the shorter chains save (measured on 3072 rows).
   const size_t per_row = plan.units_max / ((size_t)g.B * g.Hkv) + (size_t)ns;
-  const dim3 gd(g.B * g.Hq);
-  if (per_row > kCombineBatch && (size_t)g.B * g.Hq * 4 <= 8192) {
-    const dim3 bd(64 * 4);
-    if (g.d == 128) {
-      if (ns > 0) hipLaunchKernelGGL((combine_kernel<128, true, 4>), gd, bd, 0, s, g, planp, parts, side, ns, out);
-      else hipLaunchKernelGGL((combine_kernel<128, false, 4>), gd, bd, 0, s, g, planp, parts, side, ns, out);
-    } else {
-      if (ns > 0) hipLaunchKernelGGL((combine_kernel<64, true, 4>), gd, bd, 0, s, g, planp, parts, side, ns, out);
-      else hipLaunchKernelGGL((combine_kernel<64, false, 4>), gd, bd, 0, s, g, planp, parts, side, ns, out);
-    }
-  } else {
-    const dim3 bd(64);
-    if (g.d == 128) {
-      if (ns > 0) hipLaunchKernelGGL((combine_kernel<128, true, 1>), gd, bd, 0, s, g, planp, parts, side, ns, out);
-      else hipLaunchKernelGGL((combine_kernel<128, false, 1>), gd, bd, 0, s, g, planp, parts, side, ns, out);
-    } else {
-      if (ns > 0) hipLaunchKernelGGL((combine_kernel<64, true, 1>), gd, bd, 0, s, g, planp, parts, side, ns, out);
-      else hipLaunchKernelGGL((combine_kernel<64, false, 1>), gd, bd, 0, s, g, planp, parts, side, ns, out);
-    }
+  const bool wide = per_row > kCombineBatch && (size_t)g.B * g.Hq * 4 <= 8192;
+  const bool rotv = (g.rot & KVQ_ROTATE_VALUES) != 0;
+  if (g.d == 128) {
+    if (ns > 0) return launch_combine<128, true>(wide, rotv, g, planp, parts, side, ns, out, s);
+    return launch_combine<128, false>(wide, rotv, g, planp, parts, side, ns, out, s);
   }
-  return hipGetLastError();
+  if (ns > 0) return launch_combine<64, true>(wide, rotv, g, planp, parts, side, ns, out, s);
+  return launch_combine<64, false>(wide, rotv, g, planp, parts, side, ns, out, s);
 }
 
 }  // namespace kvq

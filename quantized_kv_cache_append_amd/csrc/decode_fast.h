@@ -586,11 +586,16 @@ __device__ __forceinline__ void quant_stream(const Geom& g, const WaveLds<C>& L,
 #pragma unroll
     for (int k = 0; k < QW; ++k) w[k] = src[lane + 64 * k];
   };
+  // (with rotated keys the quantized blocks hold R(k) = H k / 8: their scores
+  // take the query rotated the same way, H q' * 8 / D, since R(k) . H q' 8 / D = k . q')
+  const bool rot_q = (g.rot & KVQ_ROTATE_KEYS) != 0;
   auto store_query = [&](const uint32_t (&w)[QW]) {
 #pragma unroll
-    for (int k = 0; k < QW; ++k)   // word lane + 64k holds channels 2*lane, 2*lane+1 of row k
-      *reinterpret_cast<float2*>(L.qs + k * C::QS + 2 * lane) =
-          make_float2(in_val<C>(w[k] & 0xffffu) * qscale, in_val<C>(w[k] >> 16) * qscale);
+    for (int k = 0; k < QW; ++k) {   // word lane + 64k holds channels 2*lane, 2*lane+1 of row k
+      float x0 = in_val<C>(w[k] & 0xffffu) * qscale, x1 = in_val<C>(w[k] >> 16) * qscale;
+      if (rot_q) wht_row_pairs(x0, x1, 8.0f / D);
+      *reinterpret_cast<float2*>(L.qs + k * C::QS + 2 * lane) = make_float2(x0, x1);
+    }
   };
 
   // running state of the current unit: per lane for its column's head

@@ -15,17 +15,17 @@ ATOL = 2e-3     # max-abs error against the fp64 oracle on the same dequantized 
 RTOL_L2 = 1e-3  # relative L2 error over the whole output
 
 
-def spec_of(w: W.Workload, res_capacity: int, sink: int = 0, fp8_blocks: int = 0) -> kivi.CacheSpec:
+def spec_of(w: W.Workload, res_capacity: int, sink: int = 0, fp8_blocks: int = 0, rotate: int = 0) -> kivi.CacheSpec:
     return kivi.CacheSpec(batch=w.batch, num_q_heads=w.num_q_heads, num_kv_heads=w.num_kv_heads,
                           head_dim=w.head_dim, k_bits=w.k_bits, v_bits=w.v_bits, k_group=w.k_group,
                           v_group=w.v_group, residual=w.residual, res_capacity=res_capacity, dtype=w.dtype,
-                          sink=sink, fp8_blocks=fp8_blocks)
+                          sink=sink, fp8_blocks=fp8_blocks, rotate=rotate)
 
 
 def make_cache(w: W.Workload, lengths, chunk: int, extra_tokens: int = 0, device="cuda", seed: int = 0,
-               sink: int = 0, fp8_blocks: int = 0):
+               sink: int = 0, fp8_blocks: int = 0, rotate: int = 0):
     return cache_for_workload(w, lengths, chunk, extra_tokens=extra_tokens, device=device, seed=seed, sink=sink,
-                              fp8_blocks=fp8_blocks)
+                              fp8_blocks=fp8_blocks, rotate=rotate)
 
 
 def errors(got: np.ndarray, ref: np.ndarray):

@@ -263,3 +263,19 @@ def test_noalloc_decode_rejects_a_workspace_beyond_its_array_before_any_device_c
                                                 ctypes.c_void_p(0x6000), ctypes.c_float(0.0), 10 ** 8,
                                                 None) == B.KVQ_ERR_CAPACITY
     assert B.KVQ_NOALLOC_WORKSPACE_BYTES == 64 << 20
+
+
+def test_rotation_field_is_validated(kvq_lib):
+    from quantized_kv_cache_append_amd import binding as B
+    lay = B.kvq_layout()
+    for rot, status in ((0, B.KVQ_OK), (1, B.KVQ_OK), (2, B.KVQ_OK), (3, B.KVQ_OK), (4, B.KVQ_ERR_INVALID_ARG),
+                        (-1, B.KVQ_ERR_INVALID_ARG)):
+        assert kvq_lib.kvq_layout_bytes(ctypes.byref(_cfg(B, rotate=rot)), ctypes.byref(lay)) == status, rot
+    # the FP8 tier keeps unrotated rows: not together with a rotation
+    assert kvq_lib.kvq_layout_bytes(ctypes.byref(_cfg(B, rotate=1, fp8_blocks=2)),
+                                    ctypes.byref(lay)) == B.KVQ_ERR_UNSUPPORTED
+    # the stored layout does not change with the rotation
+    a, b = B.kvq_layout(), B.kvq_layout()
+    kvq_lib.kvq_layout_bytes(ctypes.byref(_cfg(B)), ctypes.byref(a))
+    kvq_lib.kvq_layout_bytes(ctypes.byref(_cfg(B, rotate=3)), ctypes.byref(b))
+    assert (a.record, a.blocks, a.ring) == (b.record, b.blocks, b.ring)
