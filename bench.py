@@ -38,6 +38,11 @@ resident (27 GB for 80 layers, so no copies are rotated) and times the full
 decode step: for each layer in turn, append+flush, decode partials and combine,
 all on one stream; `roofline` is then the per-layer decode-partials launch.
 
+The timed steps are launched one by one on one stream (--graph 1 replays them
+as HIP graphs instead, a whole step per graph: no faster here, since the
+launches already queue back to back); the per-launch kernel timings are taken
+on further steps with events around the decode-partials launch.
+
 `value` is the step's algorithmic bytes over its time (effective GB/s of the
 whole step); `roofline` is the decode-partials kernel's algorithmic bytes over
 its own event-timed duration, against the 8 TB/s HBM peak; `traffic` is the
@@ -354,10 +359,23 @@ def bench_layers(w, args, dev):
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
+    run = step
+    if args.graph:
+        # one HIP graph per token set: the whole step (3 launches per layer) in
+        # one submission; every call takes the fixed max_seq_tokens and workspace
+        graphs = []
+        for k in range(4):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                step(k)
+            graphs.append(g)
+        torch.cuda.synchronize()
+        run = lambda i: graphs[i % 4].replay()   # noqa: E731
+        log(f"[bench] step captured as a HIP graph of {3 * L} launches")
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     start.record()
     for j in range(args.steps):
-        step(args.warmup + j)
+        run(args.warmup + j)
     end.record()
     torch.cuda.synchronize()
     ms_step = start.elapsed_time(end) / args.steps
@@ -406,7 +424,8 @@ def bench_layers(w, args, dev):
         "vs_baseline": None,
         "dtype": w.dtype,
         "data": "synthetic",
-        "config": {"workload": w.name, "layers": L, "batch": w.batch, "num_q_heads": w.num_q_heads,
+        "config": {"workload": w.name, "layers": L, "hip_graph": bool(args.graph), "batch": w.batch,
+                   "num_q_heads": w.num_q_heads,
                    "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim, "seq_len": max(lengths0),
                    "input_dtype": w.dtype, "k_bits": w.k_bits, "v_bits": w.v_bits, "k_group": w.k_group,
                    "v_group": w.v_group, "residual": w.residual, "paged": w.paged, "rotate": args.rotate,
@@ -452,6 +471,9 @@ def main():
                          "the JSON line's config.layers says how many were timed)")
     ap.add_argument("--rotate", type=int, default=0, choices=(0, 1, 2, 3),
                     help="Walsh-Hadamard pre-rotation of keys (1), values (2) or both (3) before quantization")
+    ap.add_argument("--graph", type=int, default=0, choices=(0, 1),
+                    help="replay the timed steps as HIP graphs (1) or launch them one by one (0); the graphs "
+                         "measured no faster on this path (the launches already queue back to back)")
     ap.add_argument("--sink", type=int, default=0,
                     help="keep the first SINK tokens of every sequence in full precision (attention sink)")
     args = ap.parse_args()
@@ -543,12 +565,27 @@ def main():
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
+    run = step
+    if args.graph:
+        # one HIP graph per (cache copy, token set) pair of the step sequence
+        period = math.lcm(copies, pool)
+        graphs = {}
+        for j in range(args.steps):
+            k = (args.warmup + j) % period
+            if k not in graphs:
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g):
+                    step(k)
+                graphs[k] = g
+        torch.cuda.synchronize()
+        run = lambda i: graphs[i % period].replay()   # noqa: E731
+        log(f"[bench] steps captured as {len(graphs)} HIP graphs")
     # the K timed steps: one event pair around all of them (events between the
     # launches would add their own gaps to the step)
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     start.record()
     for j in range(args.steps):
-        step(args.warmup + j)
+        run(args.warmup + j)
     end.record()
     torch.cuda.synchronize()
     ms_total = start.elapsed_time(end)
@@ -620,7 +657,7 @@ def main():
                    "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim, "seq_len": max(lengths0),
                    "input_dtype": w.dtype, "k_bits": w.k_bits, "v_bits": w.v_bits, "k_group": w.k_group,
                    "v_group": w.v_group, "residual": w.residual, "paged": w.paged, "sink": P, "query_tokens": T,
-                   "fp8_blocks": W8, "rotate": args.rotate,
+                   "fp8_blocks": W8, "rotate": args.rotate, "hip_graph": bool(args.graph),
                    "cache_copies_rotated": copies},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBPS, 4),

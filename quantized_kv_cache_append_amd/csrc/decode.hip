@@ -240,7 +240,8 @@ __global__ __launch_bounds__(256) void decode_generic_kernel(
 // The units of the pair come from the plan the decode kernel left in the
 // workspace. One workgroup of WPR waves per output row, lane holding D/64
 // channels: wave w takes batches w, w + WPR, ... of kCombineBatch partials,
-// each batch one round of loads (lane i also fetches m and l of partial i),
+// each batch one round of loads (lane i also fetches m and l of partial i;
+// a batch of fewer partials issues only the loads it needs),
 // merged into a running maximum; with WPR > 1 the waves' states are then
 // merged through LDS by wave 0. The kernel is bound by dispatch and load
 // latency, not bandwidth: rows with many partials (long sequences cut into
@@ -248,6 +249,7 @@ __global__ __launch_bounds__(256) void decode_generic_kernel(
 // few take one wave per workgroup, which spreads them over every compute unit
 // (four rows per workgroup measured 1.4 us slower per step than one).
 constexpr int kCombineBatch = 64;
+constexpr int kLoadStep = 8;   // granularity of a short batch's loads
 // Waves per workgroup of the sink and FP8-tier side launches (one output row,
 // or one round of a row, per wave).
 constexpr int kSideWaves = 1;
@@ -289,17 +291,23 @@ __global__ __launch_bounds__(64 * WPR) void combine_kernel(Geom g, const int* __
   const int nparts = (SIDE ? nside : 0) + pu.n;
   for (int i0 = wave * kCombineBatch; i0 < nparts; i0 += WPR * kCombineBatch) {
     const int cnt = min(kCombineBatch, nparts - i0);
+    const int lim = __builtin_amdgcn_readfirstlane((cnt + kLoadStep - 1) / kLoadStep * kLoadStep);
     float v[kCombineBatch][CPL];
 #pragma unroll
     for (int u = 0; u < kCombineBatch; ++u) {
-      const float* src = part(i0 + (u < cnt ? u : 0)) + CPL * lane;
-      if constexpr (CPL == 2) {
-        const float2 x = *reinterpret_cast<const float2*>(src);
-        v[u][0] = x.x;
-        v[u][1] = x.y;
+      if (u < lim) {   // (loads of a short batch stop at the next multiple of kLoadStep)
+        const float* src = part(i0 + (u < cnt ? u : 0)) + CPL * lane;
+        if constexpr (CPL == 2) {
+          const float2 x = *reinterpret_cast<const float2*>(src);
+          v[u][0] = x.x;
+          v[u][1] = x.y;
+        } else {
+#pragma unroll
+          for (int k = 0; k < CPL; ++k) v[u][k] = src[k];
+        }
       } else {
 #pragma unroll
-        for (int k = 0; k < CPL; ++k) v[u][k] = src[k];
+        for (int k = 0; k < CPL; ++k) v[u][k] = 0.f;
       }
     }
     const float2 ml = *reinterpret_cast<const float2*>(part(i0 + min(lane, cnt - 1)) + D);

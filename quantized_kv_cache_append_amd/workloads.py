@@ -130,7 +130,9 @@ class LayerInputs:
 
 
 def channel_scales(w: Workload, device, layer: int = 0, seed: int = 0) -> torch.Tensor:
-    """Per (sequence, kv head, channel) key multiplier: lognormal and/or hot channels."""
+    """Key multiplier [B][H_kv][d]: e^Z with Z ~ N(0,1) per (kv head, channel),
+    shared by the sequences (lognormal model), times 20 on the hot channels,
+    drawn per (sequence, kv head) (or fixed)."""
     B, H, d = w.batch, w.num_kv_heads, w.head_dim
     g = _gen(device, w.name, seed, layer, "kscale")
     scale = torch.ones(B, H, d, device=device, dtype=torch.float32)
