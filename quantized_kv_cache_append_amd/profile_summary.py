@@ -11,6 +11,12 @@ under profiles/ (and read back by bench.py).
       then WRITE_SIZE, in KiB per dispatch). Each counter is scaled by what it
       reads for a plain device-to-device copy of COPY_MIB MiB in the same run
       (bench.py --copy-probe-mb), so that the figure is in true bytes.
+
+  python -m quantized_kv_cache_append_amd.profile_summary counters OUT --command CMD DIR [DIR ...]
+      SQ/GRBM counters of the decode-partials kernel from --pmc runs (one
+      directory per pass): the median per dispatch of each counter (summed
+      over the GPU's instances), instructions per wave, and the share of the
+      kernel's cycles each SIMD spent issuing VALU and MFMA work.
 """
 from __future__ import annotations
 
@@ -98,6 +104,47 @@ def traffic(fetch_dir, write_dir, copy_mib, workload, out, command, source_hash)
     print("\n".join(lines))
 
 
+# gfx950: 8 XCDs, 256 compute units of 4 SIMDs
+XCDS, SIMDS = 8, 1024
+
+
+def counters(dirs, out, command):
+    med = {}
+    kernel = None
+    for d in dirs:
+        rows = _csv(d, "counter_collection.csv")
+        names = sorted({r["Counter_Name"] for r in rows})
+        for cn in names:
+            per = {k: v for k, v in _per_dispatch(rows, cn).items() if DECODE.search(k[1])}
+            if per:
+                med[cn] = statistics.median(per.values())
+                kernel = kernel or _short(next(iter(per))[1])
+    lines = [f"# rocprofv3 --pmc counters of the decode-partials kernel ({kernel}); passes of: {command}",
+             "# median per dispatch, each counter summed over its instances (SQ per shader engine,",
+             "# GRBM per XCD)"]
+    for cn in sorted(med):
+        lines.append(f"{cn}: {med[cn]:.0f}")
+    waves = med.get("SQ_WAVES")
+    if waves:
+        for cn, label in (("SQ_INSTS_VALU", "valu_insts_per_wave"), ("SQ_INSTS_MFMA", "mfma_insts_per_wave"),
+                          ("SQ_INSTS_LDS", "lds_insts_per_wave")):
+            if cn in med:
+                lines.append(f"{label}: {med[cn] / waves:.0f}")
+    gui = med.get("GRBM_GUI_ACTIVE")
+    if gui:
+        cyc = gui / XCDS   # the kernel's cycles (each XCD counts its own busy clocks)
+        lines.append(f"kernel_cycles_per_xcd: {cyc:.0f}")
+        if "SQ_ACTIVE_INST_VALU" in med:   # quad-cycles, summed over the SIMDs
+            lines.append(f"valu_issue_share_per_simd: {med['SQ_ACTIVE_INST_VALU'] * 4 / SIMDS / cyc:.3f}")
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in med:   # cycles, summed over the SIMDs
+            lines.append(f"mfma_busy_share_per_simd: {med['SQ_VALU_MFMA_BUSY_CYCLES'] / SIMDS / cyc:.3f}")
+    if "SQ_WAIT_INST_ANY" in med and "SQ_WAVE_CYCLES" in med:   # both in quad-cycles per wave, summed
+        lines.append(f"wave_time_waiting_on_counters: {med['SQ_WAIT_INST_ANY'] / med['SQ_WAVE_CYCLES']:.3f}")
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -112,9 +159,15 @@ def main(argv=None):
     b.add_argument("workload")
     b.add_argument("out")
     b.add_argument("--command", required=True)
+    c = sub.add_parser("counters")
+    c.add_argument("out")
+    c.add_argument("dirs", nargs="+")
+    c.add_argument("--command", required=True)
     args = ap.parse_args(argv)
     if args.cmd == "stats":
         stats(args.dir, args.out, args.command)
+    elif args.cmd == "counters":
+        counters(args.dirs, args.out, args.command)
     else:
         root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
         sys.path.insert(0, root)
