@@ -1,7 +1,9 @@
-"""Limits of the decode path through the C ABI: a batch of several hundred
-ragged sequences (the unit plan takes 64 sequences per pass; empty sequences
-among them), and a sequence longer than the caller's max_seq_tokens (flagged
-on the device, its work capped to what the workspace was sized for)."""
+"""Limits of the path through the C ABI: a batch of several hundred ragged
+sequences (the unit plan takes 64 sequences per pass; empty sequences among
+them), a sequence longer than the caller's max_seq_tokens (flagged on the
+device, its work capped to what the workspace was sized for), out-of-range
+page-table entries met by decode and by the bulk flush, and a bulk flush that
+needs more blocks than the store holds."""
 import numpy as np
 import pytest
 import torch
@@ -95,3 +97,69 @@ def test_out_of_range_page_skips_its_block(wname, over):
     diff = np.abs(got - ref)
     rel = np.linalg.norm(got - ref) / np.linalg.norm(ref)
     assert diff.max() <= 2e-3 and rel <= 1e-3, (diff.max(), rel)
+
+
+def test_bulk_flush_past_max_blocks_is_flagged():
+    """A flush that needs more blocks than the store has quantizes the blocks
+    that fit, caps Q_b there and flags KVQ_DEV_BLOCKS_FULL; sequences that fit
+    are flushed in full."""
+    from oracle import kivi
+    from quantized_kv_cache_append_amd import binding as B
+    from quantized_kv_cache_append_amd.cache import QuantizedKVCache
+    w = W.WORKLOADS["llama3-8b-gqa-int2"].replace(batch=3, num_q_heads=8, num_kv_heads=2)
+    lengths = [1500, 300, 700]
+    G, R = w.k_group, w.residual
+    print("[limits] flush past max_blocks", flush=True)
+    inp = W.make_layer(w, device="cpu", seed=23, lengths=lengths)
+    cache = QuantizedKVCache(w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim, k_bits=w.k_bits, v_bits=w.v_bits,
+                             k_group=G, v_group=w.v_group, residual=R, dtype=w.torch_dtype, max_tokens=16 * G,
+                             res_capacity=2048)
+    S = max(lengths)
+    counts = torch.tensor(lengths, dtype=torch.int32, device="cuda")
+    cache.append(inp.k[:, :, :S].contiguous().cuda(), inp.v[:, :, :S].contiguous().cuda(), counts)
+    cache.flush()
+    torch.cuda.synchronize()
+    assert cache.read_device_error() == B.KVQ_DEV_BLOCKS_FULL
+    Qs, Ss = cache.lengths()
+    want_Q = [min(16, (s - R) // G) * G for s in lengths]
+    assert Qs == want_Q and Ss == lengths, (Qs, Ss)
+    spec = spec_of(w, cache.cfg.res_capacity)
+    k_np, v_np = to_np(inp.k), to_np(inp.v)
+    for b, s in enumerate(lengths):
+        for h in range(w.num_kv_heads):
+            exp = kivi.expected_blocks(spec, k_np[b, h], v_np[b, h], s)
+            for j in range(want_Q[b] // G):
+                assert np.array_equal(cache.record(b, h, j).cpu().numpy(), exp[j]), (b, h, j)
+
+
+def test_bulk_flush_skips_an_out_of_range_page():
+    """A page-table entry outside [0, num_pages) met by the bulk flush: that
+    block is skipped (KVQ_DEV_BAD_PAGE), every other block of every pair is
+    written bit for bit and the lengths advance as usual."""
+    from oracle import kivi
+    from quantized_kv_cache_append_amd import binding as B
+    w = W.WORKLOADS["ragged-paged"].replace(batch=3, num_q_heads=12, num_kv_heads=2)
+    lengths = [600, 1111, 300]
+    G = w.k_group
+    print("[limits] flush over a bad page", flush=True)
+    inp = W.make_layer(w, device="cpu", seed=29, lengths=lengths)
+    cache = make_cache(w, lengths, 256)
+    cache.page_table[1, 5] = cache.cfg.num_pages
+    cache.prefill(inp.k.cuda(), inp.v.cuda(), lengths, 256)
+    torch.cuda.synchronize()
+    assert cache.read_device_error() == B.KVQ_DEV_BAD_PAGE
+    spec = spec_of(w, cache.cfg.res_capacity)
+    Qs, Ss = cache.lengths()
+    k_np, v_np = to_np(inp.k), to_np(inp.v)
+    checked = 0
+    for b, s in enumerate(lengths):
+        _, Q, _ = kivi.stream_split(spec, s)
+        assert Qs[b] == Q and Ss[b] == s
+        for h in range(w.num_kv_heads):
+            exp = kivi.expected_blocks(spec, k_np[b, h], v_np[b, h], s)
+            for j in range(Q // G):
+                if (b, j) == (1, 5):
+                    continue
+                assert np.array_equal(cache.record(b, h, j).cpu().numpy(), exp[j]), (b, h, j)
+                checked += 1
+    assert checked > 100
