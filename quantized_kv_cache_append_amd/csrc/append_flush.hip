@@ -47,22 +47,62 @@ __host__ __device__ inline size_t block_lds_bytes(int G, int d, bool rot = false
 // (patricehuetz.fr, "TurboQuant : les cinq innovations", innovation 1): for
 // h = 1, 2, ..., d/2 each pair (i, i + h) of a row with bit h of i clear becomes
 // (x_i + x_{i+h}, x_i - x_{i+h}), rounded to fp32; the last stage also takes the
-// factor 1/8 (exact). All threads of the workgroup call it; ends with a barrier.
-__device__ void rotate_rows(float* f, int G, int d) {
-  const int half = d / 2;
-  for (int h = 1; h < d; h <<= 1) {
-    const bool last = 2 * h == d;
-    for (int idx = threadIdx.x; idx < G * half; idx += kThreads) {
-      const int t = idx / half, j = idx % half;
-      float* row = f + t * d;
-      const int i = (j / h) * 2 * h + j % h;
-      const float a = row[i], b = row[i + h];
-      const float s = __fadd_rn(a, b), r = __fsub_rn(a, b);
-      row[i] = last ? __fmul_rn(s, 0.125f) : s;
-      row[i + h] = last ? __fmul_rn(r, 0.125f) : r;
-    }
-    __syncthreads();
+// factor 1/8 (exact). Four threads per row, each holding CPT = d/4 consecutive
+// channels in registers: the stages h < CPT run inside a thread, h = CPT and
+// 2 CPT between the threads (partners lane ^ 1, lane ^ 2), so the tile is read
+// and written once. All threads of the workgroup call it; ends with a barrier.
+// One butterfly stage between the threads of a row: the partner (lane ^ M,
+// through a quad permutation) holds the channels M * CPT away.
+template <int CPT, int M>
+__device__ __forceinline__ void rotate_cross(float (&x)[CPT], int q) {
+  const bool upper = (q & M) != 0;
+#pragma unroll
+  for (int e = 0; e < CPT; ++e) {
+    const float o = __int_as_float(
+        __builtin_amdgcn_update_dpp(0, __float_as_int(x[e]), M == 1 ? 0xB1 : 0x4E, 0xF, 0xF, false));
+    const float r = upper ? __fsub_rn(o, x[e]) : __fadd_rn(x[e], o);
+    x[e] = M == 2 ? __fmul_rn(r, 0.125f) : r;
   }
+}
+template <int CPT>
+__device__ __forceinline__ void rotate_rows_reg(float* f, int G) {
+  constexpr int d = 4 * CPT;
+  const int q = threadIdx.x & 3;
+  for (int t0 = 0; t0 < G; t0 += kThreads / 4) {
+    const int t = t0 + (int)(threadIdx.x >> 2);
+    const bool live = t < G;   // the same for the four threads of a row
+    float* row = f + (size_t)(live ? t : 0) * d + q * CPT;
+    float x[CPT];
+#pragma unroll
+    for (int e = 0; e < CPT; e += 4) {
+      const float4 v = *reinterpret_cast<const float4*>(row + e);
+      x[e] = v.x;
+      x[e + 1] = v.y;
+      x[e + 2] = v.z;
+      x[e + 3] = v.w;
+    }
+#pragma unroll
+    for (int h = 1; h < CPT; h <<= 1)
+#pragma unroll
+      for (int j = 0; j < CPT / 2; ++j) {
+        const int i = (j / h) * 2 * h + j % h;
+        const float a = x[i], b = x[i + h];
+        x[i] = __fadd_rn(a, b);
+        x[i + h] = __fsub_rn(a, b);
+      }
+    rotate_cross<CPT, 1>(x, q);   // h = CPT: partner lane ^ 1
+    rotate_cross<CPT, 2>(x, q);   // h = 2 CPT (the last stage): partner lane ^ 2
+    if (live) {
+#pragma unroll
+      for (int e = 0; e < CPT; e += 4) *reinterpret_cast<float4*>(row + e) = make_float4(x[e], x[e + 1], x[e + 2], x[e + 3]);
+    }
+  }
+  __syncthreads();
+}
+__device__ __forceinline__ void rotate_rows(float* f, int G, int d) {
+  __syncthreads();   // (the tile's writes before any thread reads another's)
+  if (d == 128) rotate_rows_reg<32>(f, G);
+  else rotate_rows_reg<16>(f, G);
 }
 
 // Quantize tokens blk*G .. blk*G+G-1 of ring `pair` into record `rec`; with ROT
