@@ -63,3 +63,21 @@ def test_kernel_names_follow_the_dispatch_table():
     assert b.decode_kernel_name(W.WORKLOADS["llama2-7b-layer"], T=4) == "decode_fast_kernel"
     assert b.decode_kernel_name(W.WORKLOADS["llama3-8b-gqa-int2"]) == "decode_fast_kernel"
     assert b.decode_kernel_name(W.WORKLOADS["tiny"]) == "decode_generic_kernel"
+
+
+def test_more_than_one_gpu_is_refused_with_a_message():
+    # the bench measures one GPU; --gpus N > 1 exits before touching torch or a GPU
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr and r.stdout == ""
+
+
+def test_the_default_workload_is_the_80_layer_70b_step():
+    b = _bench()
+    import inspect
+    src = inspect.getsource(b.main)
+    assert re.search(r'"--workload", default="llama-70b-128k-80layer"', src)
+    assert W.WORKLOADS["llama-70b-128k-80layer"].layers == 80
