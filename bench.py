@@ -193,14 +193,17 @@ FAST_CONFIGS = {(4, 4, 4, 32, 32, "bf16"), (4, 2, 2, 32, 32, "bf16"), (8, 2, 2, 
                 (8, 2, 2, 32, 32, "bf16"), (8, 4, 4, 32, 32, "bf16")}
 
 
-def decode_kernel_name(w, T=1) -> str:
-    """The decode-partials kernel a workload's configuration runs (T query tokens per sequence)."""
+def decode_kernel_name(w, T=1, rotate=0) -> str:
+    """The decode-partials kernel a workload's configuration runs (T query tokens
+    per sequence; a rotated cache skips the multi-head vector kernel)."""
     rows = w.n_g * T
     if w.head_dim != 128:
         return "decode_generic_kernel"
     if rows == 1:
         mx = (w.k_bits, w.v_bits, w.k_group, w.v_group) == (2, 2, 32, 32)
-        return "decode_mx_kernel" if mx else "decode_mha_kernel"
+        if mx:
+            return "decode_mx_kernel"
+        return "decode_generic_kernel" if rotate else "decode_mha_kernel"
     if (rows, w.k_bits, w.v_bits, w.k_group, w.v_group, w.dtype) in FAST_CONFIGS:
         return "decode_fast_kernel"
     return "decode_generic_kernel"
@@ -433,7 +436,7 @@ def bench_layers(w, args, dev):
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBPS, 4),
                      "traffic": None if traffic is None else round(traffic),
-                     "kernel": decode_kernel_name(w), "us_per_launch": round(part_avg_ms * 1e3, 2),
+                     "kernel": decode_kernel_name(w, 1, args.rotate), "us_per_launch": round(part_avg_ms * 1e3, 2),
                      "bytes_per_launch": int(avg_part_bytes), "launches_per_step": L},
         "quantize": None,
         "cpu_baseline": None,
@@ -630,7 +633,7 @@ def main():
     if args.copy_probe_mb > 0:
         copy_probe(args.copy_probe_mb, dev)
 
-    kernel = decode_kernel_name(w, T)
+    kernel = decode_kernel_name(w, T, args.rotate)
     if T > 1:   # the multi-token call's window holds its combine launch too
         kernel += "+combine_kernel"
         log(f"[bench] {T} query tokens per sequence per step (causal block); the decode time covers {kernel}")

@@ -609,9 +609,9 @@ hipError_t launch_generic(const Geom& g, const kvq_cache& c, const void* q, floa
 DecodePlan plan_decode(const Geom& g, int max_seq_tokens) {
   DecodePlan p{};
   int nb_set = 1, rc = kRingAll, us = 0;
-  // the pre-rotation runs on the GQA matrix-core kernel and the generic kernel
-  // (the one-query-head kernels merge a wave's ring and quantized units)
-  p.fast = fast_supported(g, &nb_set, &rc, &us) && !(g.rot != 0 && g.ng == 1);
+  // (a rotated cache takes the kernels that rotate the query: the GQA
+  // matrix-core and block-scaled ones; the others run the generic kernel)
+  p.fast = fast_supported(g, &nb_set, &rc, &us);
   p.nb_set = p.fast ? nb_set : 1;
   p.ring_chunk = p.fast ? rc : kRingAll;
   p.unit_sets = p.fast ? us : 0;

@@ -21,25 +21,26 @@ struct FastEntry {
   int nb_set;      // blocks per set
   int ring_chunk;  // ring tokens per ring unit
   int unit_sets;   // fixed sets per quantized unit (0: sized from the lengths)
+  bool rot_ok;     // takes caches with pre-rotated keys and/or values
   LaunchFn launch;
 };
 
 template <int NG, int KB, int VB, int G, int GV, bool BF16, bool PAGED>
 FastEntry mfma_entry() {
   using C = fast::Cfg<NG, KB, VB, G, GV, BF16, PAGED>;
-  return FastEntry{NG, KB, VB, G, GV, BF16 ? KVQ_BF16 : KVQ_F16, PAGED, C::NB, fast::kRingChunk, 0,
+  return FastEntry{NG, KB, VB, G, GV, BF16 ? KVQ_BF16 : KVQ_F16, PAGED, C::NB, fast::kRingChunk, 0, true,
                    &fast::launch_fast<C>};
 }
 template <bool BF16, bool PAGED>
 FastEntry mx_entry() {
   using C = mx::Cfg<BF16, PAGED>;
   return FastEntry{1, C::KB, C::VB, C::G, C::GV, BF16 ? KVQ_BF16 : KVQ_F16, PAGED, mx::kSetBlk, mx::kRingTok,
-                   mx::kUnitSets, &mx::launch_mx<C>};
+                   mx::kUnitSets, true, &mx::launch_mx<C>};
 }
 template <int KB, int VB, int G, int GV, bool BF16, bool PAGED>
 FastEntry mha_entry() {
   using C = mha::Cfg<KB, VB, G, GV, BF16, PAGED>;
-  return FastEntry{1, KB, VB, G, GV, BF16 ? KVQ_BF16 : KVQ_F16, PAGED, C::NBS, mha::kRingTok, 0,
+  return FastEntry{1, KB, VB, G, GV, BF16 ? KVQ_BF16 : KVQ_F16, PAGED, C::NBS, mha::kRingTok, 0, false,
                    &mha::launch_mha<C>};
 }
 
@@ -79,7 +80,7 @@ const FastEntry* find(const Geom& g) {
   for (int i = 0; i < kEntries; ++i) {
     const FastEntry& e = t[i];
     if (e.ng == g.ng && e.kb == g.kb && e.vb == g.vb && e.G == g.G && e.GV == g.GV && e.dtype == g.dtype &&
-        e.paged == (g.num_pages > 0))
+        e.paged == (g.num_pages > 0) && (g.rot == 0 || e.rot_ok))
       return &e;
   }
   return nullptr;

@@ -225,11 +225,15 @@ __device__ __forceinline__ void quant_stream(const Geom& g, float* __restrict__ 
   float m_run, l_lane, lam_lane;
   v4f acc[8];
 
+  const bool rot_q = (g.rot & KVQ_ROTATE_KEYS) != 0;
   auto compute_set = [&](const SetBuf& cb, mha::Span cur, bool new_query) {
     const int blk0 = cur.begin;
     if (new_query) {   // a new pair's first set: its query into LDS
-      *reinterpret_cast<float2*>(lq + 2 * lane) =
-          make_float2(in_val<C>(cb.qw & 0xffffu) * qscale, in_val<C>(cb.qw >> 16) * qscale);
+      float x0 = in_val<C>(cb.qw & 0xffffu) * qscale, x1 = in_val<C>(cb.qw >> 16) * qscale;
+      // (rotated keys: the blocks hold R(k) = H k / 8, so the query is rotated
+      // the same way, H q' * 8 / D, and the scores are unchanged)
+      if (rot_q) wht_row_pairs(x0, x1, 8.0f / D);
+      *reinterpret_cast<float2*>(lq + 2 * lane) = make_float2(x0, x1);
       wave_lds_fence();
     }
     // ---- q~ digit rows of block gq, channels 8n .. 8n + 7, and kappa of block gq ----

@@ -2,10 +2,11 @@
 cinq innovations", innovation 1): records of rotated key and/or value rows
 bit for bit against the oracle (the flush's fp32 butterflies follow the oracle's
 order), and decode attention within max-abs 2e-3 / relative L2 1e-3 of the fp64
-oracle on the same dequantized cache, for every decode path: the GQA
-matrix-core kernel (dense and paged, G = 32 and the 70B shape's G = 64), the
-generic kernel (one query head per kv head, and d = 64); steps across flushes
-of the fused append+flush, a sink, and a multi-token query."""
+oracle on the same dequantized cache, for every decode path that takes
+rotated caches: the GQA matrix-core kernel (dense and paged, G = 32 and the
+70B shape's G = 64), the block-scaled multi-head kernel (fp16 and bf16 INT2)
+and the generic kernel (multi-head INT4, and d = 64); steps across flushes of
+the fused append+flush, a sink, and a multi-token query."""
 import numpy as np
 import pytest
 import torch
@@ -25,6 +26,9 @@ CASES = {
     "70b-g64-both": ("llama-70b-128k-80layer", dict(batch=2, num_q_heads=16, num_kv_heads=2, layers=1),
                      [2100, 500], 3),
     "mha-fp16-both": ("llama2-7b-layer", dict(batch=2, num_q_heads=4, num_kv_heads=4), [1000, 300], 3),
+    "mha-bf16-keys": ("llama2-7b-layer", dict(batch=2, num_q_heads=4, num_kv_heads=4, dtype="bf16"), [1000, 300], 1),
+    "mha-int4-both": ("llama2-7b-layer", dict(batch=2, num_q_heads=4, num_kv_heads=4, k_bits=4, v_bits=4),
+                      [800, 260], 3),
     "paged-ng6-both": ("ragged-paged", dict(batch=3, num_q_heads=12, num_kv_heads=2), [37, 300, 1111], 3),
     "tiny-d64-both": ("tiny", dict(batch=2), [512, 200], 3),
 }
