@@ -195,15 +195,14 @@ FAST_CONFIGS = {(4, 4, 4, 32, 32, "bf16"), (4, 2, 2, 32, 32, "bf16"), (8, 2, 2, 
 
 def decode_kernel_name(w, T=1, rotate=0) -> str:
     """The decode-partials kernel a workload's configuration runs (T query tokens
-    per sequence; a rotated cache skips the multi-head vector kernel)."""
+    per sequence; the same with a rotated cache)."""
+    del rotate
     rows = w.n_g * T
     if w.head_dim != 128:
         return "decode_generic_kernel"
     if rows == 1:
         mx = (w.k_bits, w.v_bits, w.k_group, w.v_group) == (2, 2, 32, 32)
-        if mx:
-            return "decode_mx_kernel"
-        return "decode_generic_kernel" if rotate else "decode_mha_kernel"
+        return "decode_mx_kernel" if mx else "decode_mha_kernel"
     if (rows, w.k_bits, w.v_bits, w.k_group, w.v_group, w.dtype) in FAST_CONFIGS:
         return "decode_fast_kernel"
     return "decode_generic_kernel"

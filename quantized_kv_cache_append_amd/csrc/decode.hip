@@ -609,8 +609,7 @@ hipError_t launch_generic(const Geom& g, const kvq_cache& c, const void* q, floa
 DecodePlan plan_decode(const Geom& g, int max_seq_tokens) {
   DecodePlan p{};
   int nb_set = 1, rc = kRingAll, us = 0;
-  // (a rotated cache takes the kernels that rotate the query: the GQA
-  // matrix-core and block-scaled ones; the others run the generic kernel)
+  // (every specialised kernel rotates the query for a rotated cache)
   p.fast = fast_supported(g, &nb_set, &rc, &us);
   p.nb_set = p.fast ? nb_set : 1;
   p.ring_chunk = p.fast ? rc : kRingAll;

@@ -40,7 +40,7 @@ FastEntry mx_entry() {
 template <int KB, int VB, int G, int GV, bool BF16, bool PAGED>
 FastEntry mha_entry() {
   using C = mha::Cfg<KB, VB, G, GV, BF16, PAGED>;
-  return FastEntry{1, KB, VB, G, GV, BF16 ? KVQ_BF16 : KVQ_F16, PAGED, C::NBS, mha::kRingTok, 0, false,
+  return FastEntry{1, KB, VB, G, GV, BF16 ? KVQ_BF16 : KVQ_F16, PAGED, C::NBS, mha::kRingTok, 0, true,
                    &mha::launch_mha<C>};
 }
 

@@ -342,14 +342,18 @@ __device__ __forceinline__ void quant_stream(const Geom& g, const WaveLds<C>& L,
     lam_grp[k] = (bi < NBS && off >= 2 * NGR * G) ? ((off - 2 * NGR * G) / 2) / G : -1;
   }
 
+  const bool rot_q = (g.rot & KVQ_ROTATE_KEYS) != 0;
   auto run_set = [&](Span cur, int si, Span nsp, int nsi) {
     const int blk0 = cur.begin + si * NBS;
     // the next set's loads go out first and stay in flight through this set
     SetBuf nb;
     load_set(nb, nsp, nsi);
     if (si == 0) {   // a unit's first set: its query (prefetched with the set) into LDS
-      *reinterpret_cast<float2*>(L.q + 2 * lane) =
-          make_float2(in_val<C>(cb.qw & 0xffffu) * qscale, in_val<C>(cb.qw >> 16) * qscale);
+      float x0 = in_val<C>(cb.qw & 0xffffu) * qscale, x1 = in_val<C>(cb.qw >> 16) * qscale;
+      // (rotated keys: the blocks hold R(k) = H k / 8, so the query is rotated
+      // the same way, H q' * 8 / D, and the scores are unchanged)
+      if (rot_q) wht_row_pairs(x0, x1, 8.0f / D);
+      *reinterpret_cast<float2*>(L.q + 2 * lane) = make_float2(x0, x1);
       wave_lds_fence();
     }
     // ---- q~ = q' * s_K and kappa partials from the key scale/zero chunks ----

@@ -4,9 +4,9 @@ bit for bit against the oracle (the flush's fp32 butterflies follow the oracle's
 order), and decode attention within max-abs 2e-3 / relative L2 1e-3 of the fp64
 oracle on the same dequantized cache, for every decode path that takes
 rotated caches: the GQA matrix-core kernel (dense and paged, G = 32 and the
-70B shape's G = 64), the block-scaled multi-head kernel (fp16 and bf16 INT2)
-and the generic kernel (multi-head INT4, and d = 64); steps across flushes of
-the fused append+flush, a sink, and a multi-token query."""
+70B shape's G = 64), the block-scaled multi-head kernel (fp16 and bf16 INT2),
+the multi-head vector kernel (INT4) and the generic kernel (d = 64); steps
+across flushes of the fused append+flush, a sink, and a multi-token query."""
 import numpy as np
 import pytest
 import torch
