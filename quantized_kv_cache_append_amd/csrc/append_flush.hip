@@ -377,7 +377,7 @@ struct WgBlock {
     quantize_block<BF16, ROT>(g, rec, kr, vr, pair, blk, smem);
   }
 };
-template <class Q>
+template <class Q, bool ROT = false>
 struct WaveBlock {
   static constexpr int kWorkers = kThreads / 64;
   __device__ static void fp8(const Geom& g, uint8_t* rec8, const uint16_t* kr, const uint16_t* vr, int pair,
@@ -387,7 +387,7 @@ struct WaveBlock {
   __host__ __device__ static size_t lds(const Geom&) { return 0; }
   __device__ static void run(const Geom& g, uint8_t* rec, const uint16_t* kr, const uint16_t* vr, int pair,
                              int blk, uint8_t*) {
-    qwave::quantize_block<Q>(g, rec, kr, vr, pair, blk);
+    qwave::quantize_block<Q, ROT>(g, rec, kr, vr, pair, blk);
   }
 };
 
@@ -625,13 +625,16 @@ using AppendFlushFn = hipError_t (*)(const Geom&, const kvq_cache&, const void*,
                                      hipStream_t);
 struct QuantEntry {
   int G, kb, vb, GV, dtype;
-  FlushFn flush;
-  AppendFlushFn append_flush;
+  FlushFn flush, flush_rot;                      // plain and pre-rotated rows
+  AppendFlushFn append_flush, append_flush_rot;
 };
 template <bool BF16, int G, int KB, int VB, int GV>
 QuantEntry wave_entry() {
-  using P = WaveBlock<qwave::Cfg<BF16, G, KB, VB, GV>>;
-  return QuantEntry{G, KB, VB, GV, BF16 ? KVQ_BF16 : KVQ_F16, &launch_flush_p<P>, &launch_append_flush_p<P>};
+  using Q = qwave::Cfg<BF16, G, KB, VB, GV>;
+  using P = WaveBlock<Q>;
+  using PR = WaveBlock<Q, true>;
+  return QuantEntry{G, KB, VB, GV, BF16 ? KVQ_BF16 : KVQ_F16, &launch_flush_p<P>, &launch_flush_p<PR>,
+                    &launch_append_flush_p<P>, &launch_append_flush_p<PR>};
 }
 // head_dim 128: the key/value bits and groups of the workloads, fp16 and bf16
 #define KVQ_WAVE(G, KB, VB, GV) wave_entry<false, G, KB, VB, GV>(), wave_entry<true, G, KB, VB, GV>()
@@ -649,10 +652,13 @@ const QuantEntry* find_wave(const Geom& g) {
 }  // namespace
 
 hipError_t launch_flush(const Geom& g, const kvq_cache& c, hipStream_t s) {
-  if (g.rot != 0)
+  const QuantEntry* e = find_wave(g);
+  if (g.rot != 0) {
+    if (e) return e->flush_rot(g, c, s);
     return g.dtype == KVQ_BF16 ? launch_flush_p<WgBlock<true, true>>(g, c, s)
                                : launch_flush_p<WgBlock<false, true>>(g, c, s);
-  if (const QuantEntry* e = find_wave(g)) return e->flush(g, c, s);
+  }
+  if (e) return e->flush(g, c, s);
   return g.dtype == KVQ_BF16 ? launch_flush_p<WgBlock<true>>(g, c, s) : launch_flush_p<WgBlock<false>>(g, c, s);
 }
 
@@ -663,10 +669,13 @@ hipError_t launch_append_flush(const Geom& g, const kvq_cache& c, const void* k_
     hipError_t e = launch_append(g, c, k_new, v_new, n_new, n_max, s);
     return e != hipSuccess ? e : launch_flush(g, c, s);
   }
-  if (g.rot != 0)
+  const QuantEntry* e = find_wave(g);
+  if (g.rot != 0) {
+    if (e) return e->append_flush_rot(g, c, k_new, v_new, n_new, n_max, s);
     return g.dtype == KVQ_BF16 ? launch_append_flush_p<WgBlock<true, true>>(g, c, k_new, v_new, n_new, n_max, s)
                                : launch_append_flush_p<WgBlock<false, true>>(g, c, k_new, v_new, n_new, n_max, s);
-  if (const QuantEntry* e = find_wave(g)) return e->append_flush(g, c, k_new, v_new, n_new, n_max, s);
+  }
+  if (e) return e->append_flush(g, c, k_new, v_new, n_new, n_max, s);
   return g.dtype == KVQ_BF16 ? launch_append_flush_p<WgBlock<true>>(g, c, k_new, v_new, n_new, n_max, s)
                              : launch_append_flush_p<WgBlock<false>>(g, c, k_new, v_new, n_new, n_max, s);
 }

@@ -81,9 +81,43 @@ __device__ __forceinline__ uint32_t or8(uint32_t x) {
   return x;
 }
 
+// Walsh-Hadamard pre-rotation of a value row held as SL consecutive channels
+// per lane (lane l: channels (l / G) SL ..; the row's other channels in lanes
+// l ^ G, l ^ 2G, ...), in the order of the stored-side definition: stages
+// h = 1, 2, ..., 64, each (a, b) -> (a + b, a - b) rounded to fp32, the stages
+// below SL inside the lane, the others with the partner lane; then x 1/8.
+template <int SL, int G>
+__device__ __forceinline__ void rotate_value_row(float (&x)[SL]) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int h = 1; h < SL; h <<= 1)
+#pragma unroll
+    for (int j = 0; j < SL / 2; ++j) {
+      const int i = (j / h) * 2 * h + j % h;
+      const float a = x[i], b = x[i + h];
+      x[i] = a + b;
+      x[i + h] = a - b;
+    }
+#pragma unroll
+  for (int m = 1; m * SL < 128; m <<= 1) {   // stage h = m SL: the partner is lane ^ m G
+    const bool upper = ((lane / G) & m) != 0;
+#pragma unroll
+    for (int k = 0; k < SL; ++k) {
+      const float p = __shfl_xor(x[k], m * G, 64);
+      x[k] = upper ? p - x[k] : x[k] + p;
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < SL; ++k) x[k] *= 0.125f;
+}
+
 // Quantize tokens blk*G .. blk*G+G-1 of ring `pair` into record `rec`. Called
-// by all 64 lanes of one wave; the ring rows must be visible to the wave.
-template <class Q>
+// by all 64 lanes of one wave; the ring rows must be visible to the wave. With
+// ROT the rows of the sides g.rot names are rotated first, in registers: a key
+// row is spread over the wave (wht_row_pairs), a value row over 128 / SL lanes
+// (at G = 64 the rotated rows exceed the register file by 32 values per lane,
+// which the compiler spills: still 6.6x the workgroup routine's rate).
+template <class Q, bool ROT = false>
 __device__ __forceinline__ void quantize_block(const Geom& g, uint8_t* __restrict__ rec,
                                                const uint16_t* __restrict__ k_ring,
                                                const uint16_t* __restrict__ v_ring, int pair, int blk) {
@@ -104,19 +138,42 @@ __device__ __forceinline__ void quantize_block(const Geom& g, uint8_t* __restric
   for (int t = 0; t < G; ++t) kd[t] = reinterpret_cast<const uint32_t*>(k_ring + row(t))[lane];
   const int vt = lane % G, cbase = (lane / G) * Q::SL;
   uint4 vd[Q::SLV];
-  {
+  auto load_values = [&]() {
     const uint4* src = reinterpret_cast<const uint4*>(v_ring + row(vt) + cbase);
 #pragma unroll
     for (int k = 0; k < Q::SLV; ++k) vd[k] = src[k];
+  };
+  // (rotated: the value rows are loaded once the keys are done, so that the
+  // rotated key rows and value slice are never live together)
+  if constexpr (!ROT) load_values();
+
+  // rotated key rows (fp32): channels 2 lane, 2 lane + 1 of each token
+  float kr0[ROT ? G : 1], kr1[ROT ? G : 1];
+  if constexpr (ROT) {
+    const bool rk = (g.rot & KVQ_ROTATE_KEYS) != 0;
+#pragma unroll
+    for (int t = 0; t < G; ++t) {
+      kr0[t] = in_to_f32<Q::BF16>(kd[t] & 0xffffu);
+      kr1[t] = in_to_f32<Q::BF16>(kd[t] >> 16);
+      if (rk) wht_row_pairs(kr0[t], kr1[t], 0.125f);
+    }
   }
+  auto key0 = [&](int t) -> float {
+    if constexpr (ROT) return kr0[t];
+    else return in_to_f32<Q::BF16>(kd[t] & 0xffffu);
+  };
+  auto key1 = [&](int t) -> float {
+    if constexpr (ROT) return kr1[t];
+    else return in_to_f32<Q::BF16>(kd[t] >> 16);
+  };
 
   // ---- keys: one group per channel over the G tokens ----
   {
-    float mn0 = in_to_f32<Q::BF16>(kd[0] & 0xffffu), mx0 = mn0;
-    float mn1 = in_to_f32<Q::BF16>(kd[0] >> 16), mx1 = mn1;
+    float mn0 = key0(0), mx0 = mn0;
+    float mn1 = key1(0), mx1 = mn1;
 #pragma unroll
     for (int t = 1; t < G; ++t) {
-      const float x0 = in_to_f32<Q::BF16>(kd[t] & 0xffffu), x1 = in_to_f32<Q::BF16>(kd[t] >> 16);
+      const float x0 = key0(t), x1 = key1(t);
       mn0 = fminf(mn0, x0);
       mx0 = fmaxf(mx0, x0);
       mn1 = fminf(mn1, x1);
@@ -135,8 +192,8 @@ __device__ __forceinline__ void quantize_block(const Geom& g, uint8_t* __restric
 #pragma unroll
       for (int k = 0; k < Q::KLPW; ++k) {
         const int t = t0 + k;
-        const uint32_t c0 = group_code(in_to_f32<Q::BF16>(kd[t] & 0xffffu), p0, KB);
-        const uint32_t c1 = group_code(in_to_f32<Q::BF16>(kd[t] >> 16), p1, KB);
+        const uint32_t c0 = group_code(key0(t), p0, KB);
+        const uint32_t c1 = group_code(key1(t), p1, KB);
         uint32_t w = (c0 << sh) | (c1 << (sh + KB));
         w = KB == 2 ? or8(w) : or4(w);
         mine = sub == k ? w : mine;
@@ -147,12 +204,23 @@ __device__ __forceinline__ void quantize_block(const Geom& g, uint8_t* __restric
   }
 
   // ---- values: one group per (token, GV channels) ----
+  if constexpr (ROT) load_values();
   {
     uint16_t* vs = reinterpret_cast<uint16_t*>(rec + g.rec_vs);
     uint16_t* vz = reinterpret_cast<uint16_t*>(rec + g.rec_vz);
-    auto vval = [&](int c) -> float {   // channel cbase + c of token vt
+    auto vraw = [&](int c) -> float {   // channel cbase + c of token vt
       const uint32_t w = reinterpret_cast<const uint32_t*>(&vd[c / 8])[(c % 8) / 2];
       return in_to_f32<Q::BF16>((c & 1) ? (w >> 16) : (w & 0xffffu));
+    };
+    float vr[ROT ? Q::SL : 1];   // the rotated row slice (fp32)
+    if constexpr (ROT) {
+#pragma unroll
+      for (int c = 0; c < Q::SL; ++c) vr[c] = vraw(c);
+      if (g.rot & KVQ_ROTATE_VALUES) rotate_value_row<Q::SL, G>(vr);
+    }
+    auto vval = [&](int c) -> float {
+      if constexpr (ROT) return vr[c];
+      else return vraw(c);
     };
     GroupParams p[Q::SL / GV];
 #pragma unroll
