@@ -536,6 +536,15 @@ __global__ __launch_bounds__(kThreads) void append_flush_kernel(Geom g, const ui
   const int pair = blockIdx.x;
   const int b = pair / g.Hkv, h = pair % g.Hkv;
   __shared__ int s_Q, s_S, s_n, s_ok, s_nfl, s_nok, s_bad;
+  // the first kThreads 16-byte vectors of the new rows are loaded before the
+  // lengths (a decode step's whole append): the two round trips overlap
+  const int vec_per_tok = g.d / 8;
+  uint4 pk = make_uint4(0, 0, 0, 0), pv = pk;
+  if ((int)threadIdx.x < n_max * vec_per_tok) {
+    const size_t src = (size_t)pair * n_max * g.d + (size_t)threadIdx.x * 8;
+    pk = *reinterpret_cast<const uint4*>(k_new + src);
+    pv = *reinterpret_cast<const uint4*>(v_new + src);
+  }
   if (threadIdx.x == 0) {
     const int Q = state[4 * b + kStateQ];
     const int S = state[4 * b + kStateS];
@@ -553,10 +562,30 @@ __global__ __launch_bounds__(kThreads) void append_flush_kernel(Geom g, const ui
     s_bad = 0;
   }
   __syncthreads();
-  if (s_ok == 1) {
+  if (s_ok == 1) {   // rows [0, ns) to sink rows S.., the others to ring position S - P + i
     const int ns = append_split(g, s_S, s_n).n_sink;
-    copy_to_sink(g, k_new, v_new, n_max, k_sink, v_sink, pair, s_S, 0, ns);
-    copy_to_ring(g, k_new, v_new, n_max, k_ring, v_ring, pair, s_S - g.P, ns, s_n);
+    for (int idx = threadIdx.x; idx < s_n * vec_per_tok; idx += kThreads) {
+      const int i = idx / vec_per_tok, v = idx % vec_per_tok;
+      uint4 kw = pk, vw = pv;
+      if (idx >= kThreads) {
+        const size_t src = ((size_t)pair * n_max + i) * g.d + (size_t)v * 8;
+        kw = *reinterpret_cast<const uint4*>(k_new + src);
+        vw = *reinterpret_cast<const uint4*>(v_new + src);
+      }
+      size_t dst;
+      uint16_t *kd, *vd;
+      if (i < ns) {
+        dst = ((size_t)pair * g.P + s_S + i) * g.d + (size_t)v * 8;
+        kd = k_sink;
+        vd = v_sink;
+      } else {
+        dst = ((size_t)pair * g.C + (s_S - g.P + i) % g.C) * g.d + (size_t)v * 8;
+        kd = k_ring;
+        vd = v_ring;
+      }
+      *reinterpret_cast<uint4*>(kd + dst) = kw;
+      *reinterpret_cast<uint4*>(vd + dst) = vw;
+    }
   }
   // the block routine reads the ring through plain loads: make this
   // workgroup's ring writes visible to all of its threads first
