@@ -14,23 +14,26 @@ from kvq_harness import check_decode, check_records, default_scale, make_cache, 
 pytestmark = pytest.mark.gpu
 
 CASES = {
-    "mha-int2": ("llama2-7b-layer", dict(batch=3, num_q_heads=4, num_kv_heads=4), [300, 95, 1000]),
-    "paged-ng6": ("ragged-paged", dict(batch=3, num_q_heads=12, num_kv_heads=2), [37, 300, 1111]),
+    # name: (workload, overrides, lengths, rotate)
+    "mha-int2": ("llama2-7b-layer", dict(batch=3, num_q_heads=4, num_kv_heads=4), [300, 95, 1000], 0),
+    "paged-ng6": ("ragged-paged", dict(batch=3, num_q_heads=12, num_kv_heads=2), [37, 300, 1111], 0),
+    "70b-rotated": ("llama-70b-128k-80layer", dict(batch=2, num_q_heads=16, num_kv_heads=2, layers=1),
+                    [1000, 160], 3),
 }
 
 
 @pytest.mark.parametrize("name", list(CASES))
 def test_graph_replays_match_eager_steps(name):
-    wname, over, lengths = CASES[name]
+    wname, over, lengths, rot = CASES[name]
     w = W.WORKLOADS[wname].replace(**over)
     steps = 40                       # every sequence crosses at least one flush
     full = [s + steps for s in lengths]
     cap = max(full)
     print(f"[graph case {name}] lengths={lengths} steps={steps}", flush=True)
     inp = W.make_layer(w, device="cpu", seed=31, lengths=full)
-    A = make_cache(w, lengths, 256, extra_tokens=steps)    # replayed graph
-    E = make_cache(w, lengths, 256, extra_tokens=steps)    # eager twin
-    warm = make_cache(w, lengths, 256, extra_tokens=steps)
+    A = make_cache(w, lengths, 256, extra_tokens=steps, rotate=rot)    # replayed graph
+    E = make_cache(w, lengths, 256, extra_tokens=steps, rotate=rot)    # eager twin
+    warm = make_cache(w, lengths, 256, extra_tokens=steps, rotate=rot)
     for c in (A, E, warm):
         c.prefill(inp.k.cuda(), inp.v.cuda(), lengths, 256)
     kv_shape = (w.batch, w.num_kv_heads, 1, w.head_dim)
@@ -50,7 +53,7 @@ def test_graph_replays_match_eager_steps(name):
         A.decode(q, out=out_a, max_seq_tokens=cap, workspace=ws_a)
     torch.cuda.synchronize()
 
-    spec = spec_of(w, A.cfg.res_capacity)
+    spec = spec_of(w, A.cfg.res_capacity, rotate=rot)
     k_np, v_np = to_np(inp.k), to_np(inp.v)
     for st in range(steps):
         idx = [s + st for s in lengths]
