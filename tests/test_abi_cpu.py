@@ -279,3 +279,20 @@ def test_rotation_field_is_validated(kvq_lib):
     kvq_lib.kvq_layout_bytes(ctypes.byref(_cfg(B)), ctypes.byref(a))
     kvq_lib.kvq_layout_bytes(ctypes.byref(_cfg(B, rotate=3)), ctypes.byref(b))
     assert (a.record, a.blocks, a.ring) == (b.record, b.blocks, b.ring)
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    # no fallback: without the HIP library the binding raises instead of computing anything
+    import subprocess
+    import sys
+    code = ("import sys; sys.path.insert(0, %r)\n"
+            "from quantized_kv_cache_append_amd import binding as B\n"
+            "B.LIBRARY_PATH = %r\n"
+            "try:\n"
+            "    B.load()\n"
+            "except Exception as e:\n"
+            "    print('raised', type(e).__name__)\n"
+            "else:\n"
+            "    print('loaded')\n") % (ROOT, str(tmp_path / "libkvq_absent.so"))
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=120)
+    assert r.stdout.startswith("raised"), r.stdout + r.stderr
