@@ -646,6 +646,10 @@ __device__ __forceinline__ void quant_stream(const Geom& g, const WaveLds<C>& L,
     load_ksz(nsp, nsi, pgn);
 
     // ---- scores: D[token][column] for every tile of every block of the set ----
+    // (the wave issuing its score MFMAs goes first: the other wave of the
+    // SIMD fills the matrix-core cycles with its vector work; measured 3%
+    // faster on the INT4 layer, neutral elsewhere)
+    __builtin_amdgcn_s_setprio(1);
     float sc[TPB][4];
 #pragma unroll
     for (int tt = 0; tt < TPB; ++tt)
@@ -668,6 +672,7 @@ __device__ __forceinline__ void quant_stream(const Geom& g, const WaveLds<C>& L,
         for (int i = 0; i < 4; ++i) sc[tt][i] = mine ? acc[i] : sc[tt][i];
       }
     }
+    __builtin_amdgcn_s_setprio(0);
     load_kc(nsp, nsi, pgn);
     if (!my_blk) {
 #pragma unroll
