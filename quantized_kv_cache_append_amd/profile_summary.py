@@ -138,8 +138,14 @@ def counters(dirs, out, command):
             lines.append(f"valu_issue_share_per_simd: {med['SQ_ACTIVE_INST_VALU'] * 4 / SIMDS / cyc:.3f}")
         if "SQ_VALU_MFMA_BUSY_CYCLES" in med:   # cycles, summed over the SIMDs
             lines.append(f"mfma_busy_share_per_simd: {med['SQ_VALU_MFMA_BUSY_CYCLES'] / SIMDS / cyc:.3f}")
-    if "SQ_WAIT_INST_ANY" in med and "SQ_WAVE_CYCLES" in med:   # both in quad-cycles per wave, summed
-        lines.append(f"wave_time_waiting_on_counters: {med['SQ_WAIT_INST_ANY'] / med['SQ_WAVE_CYCLES']:.3f}")
+    # shares of the waves' lifetime (all three in quad-cycles per wave, summed):
+    # issuing an instruction, ready but waiting to be issued, and stopped at a
+    # dependency (a wait counter, a barrier)
+    if "SQ_WAVE_CYCLES" in med:
+        for cn, label in (("SQ_ACTIVE_INST_ANY", "wave_time_issuing"), ("SQ_WAIT_INST_ANY", "wave_time_waiting_for_issue"),
+                          ("SQ_WAIT_ANY", "wave_time_waiting_on_dependencies")):
+            if cn in med:
+                lines.append(f"{label}: {med[cn] / med['SQ_WAVE_CYCLES']:.3f}")
     with open(out, "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
