@@ -294,11 +294,17 @@ __global__ __launch_bounds__(64 * WPR) void combine_kernel(Geom g, const int* __
   for (int i0 = wave * kCombineBatch; i0 < nparts; i0 += WPR * kCombineBatch) {
     const int cnt = min(kCombineBatch, nparts - i0);
     const int lim = __builtin_amdgcn_readfirstlane((cnt + kLoadStep - 1) / kLoadStep * kLoadStep);
+    // lane u locates partial i0 + u once (in parallel); load u takes its address
+    // from lane u (two lane reads instead of a scalar slot search per load)
+    const float* mine = part(i0 + min(lane, cnt - 1));
+    const uint64_t mine_bits = reinterpret_cast<uint64_t>(mine);
     float v[kCombineBatch][CPL];
 #pragma unroll
     for (int u = 0; u < kCombineBatch; ++u) {
       if (u < lim) {   // (loads of a short batch stop at the next multiple of kLoadStep)
-        const float* src = part(i0 + (u < cnt ? u : 0)) + CPL * lane;
+        const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)mine_bits, u < cnt ? u : 0);
+        const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(mine_bits >> 32), u < cnt ? u : 0);
+        const float* src = reinterpret_cast<const float*>(((uint64_t)hi << 32) | lo) + CPL * lane;
         if constexpr (CPL == 2) {
           const float2 x = *reinterpret_cast<const float2*>(src);
           v[u][0] = x.x;
@@ -312,7 +318,7 @@ __global__ __launch_bounds__(64 * WPR) void combine_kernel(Geom g, const int* __
         for (int k = 0; k < CPL; ++k) v[u][k] = 0.f;
       }
     }
-    const float2 ml = *reinterpret_cast<const float2*>(part(i0 + min(lane, cnt - 1)) + D);
+    const float2 ml = *reinterpret_cast<const float2*>(mine + D);
     asm volatile("" ::: "memory");   // the whole batch is in flight before the first wait
     const float mi = lane < cnt ? ml.x : -INFINITY, li = lane < cnt ? ml.y : 0.f;
     const float mn = fmaxf(m, wave_max(mi));
