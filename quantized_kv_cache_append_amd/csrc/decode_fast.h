@@ -208,6 +208,16 @@ struct Cfg {
   static constexpr int REC_VS = REC_VC + G * D * VB / 8;
   static constexpr int REC_VZ = REC_VS + 2 * NGR * G;
   static constexpr int REC = REC_VZ + 2 * NGR * G;
+  // the scale/zero sections of a record (scales then zero-points, contiguous)
+  static constexpr int KSEC = REC_VC - REC_KS;                       // 4 D bytes
+  static constexpr int VSEC = REC - REC_VS;                          // 4 NGR G bytes
+  // a set's sections are loaded once, a contiguous share per lane, and staged
+  // in LDS; each lane then reads the scales of its own column and channels
+  static constexpr int KSZ_LANE = NB * KSEC / 64;
+  static constexpr int VSZ_LANE = NB * VSEC / 64;
+  // waves per SIMD: the 6-head group (32-token sets, the fewest registers and
+  // LDS) runs three, which keeps more of its loads in flight; the others two
+  static constexpr int WAVES_PER_SIMD = NG == 6 ? 3 : 2;
   // per-wave LDS (bytes). A query row takes QS floats: 4 more than D, so that the
   // rows of the group start 4 banks apart and the lanes of one row of the
   // operand layout, which read the same channels of different heads, do not
@@ -221,11 +231,16 @@ struct Cfg {
   static constexpr int LDS_ALPHA = 16 * 4;
   static constexpr int LDS_LAM = NG * NGR * 4;
   static constexpr int LDS_ZERO = 16;
-  static constexpr int LDS_WAVE = LDS_Q + LDS_BUF + LDS_ALPHA + LDS_LAM + LDS_ZERO;
+  static constexpr int LDS_KS = NB * KSEC;
+  static constexpr int LDS_VS = NB * VSEC;
+  static constexpr int LDS_WAVE = LDS_Q + LDS_BUF + LDS_KS + LDS_VS + LDS_ALPHA + LDS_LAM + LDS_ZERO;
   static_assert(NG == 1 || NG == 2 || NG == 4 || NG == 6 || NG == 8, "column reductions exist for these groups");
   static_assert(NB >= 2, "query group must fit two blocks in 16 columns");
   static_assert(G % 16 == 0 && SET_TOK % 32 == 0, "sets must be whole P.V k-steps");
   static_assert(GV >= 16 && D % GV == 0, "value groups must cover whole 16-channel tiles");
+  static_assert(KSEC == 4 * D && REC_KZ == REC_KS + 2 * D && REC_VZ == REC_VS + VSEC / 2, "sections contiguous");
+  static_assert((KSZ_LANE == 8 || KSZ_LANE == 16 || KSZ_LANE == 32) && KSEC % KSZ_LANE == 0, "key share");
+  static_assert((VSZ_LANE == 8 || VSZ_LANE == 16 || VSZ_LANE == 32) && VSEC % VSZ_LANE == 0, "value share");
 };
 
 // Pointer to block `blk` of (b, h); nullptr if a paged entry is out of range.
@@ -264,6 +279,18 @@ __device__ __forceinline__ Chunk<NBYTES> load_chunk(const uint8_t* p) {
     c.b = *reinterpret_cast<const uint4*>(p + 16);
   }
   return c;
+}
+
+template <int NBYTES>
+__device__ __forceinline__ void store_chunk(uint8_t* p, const Chunk<NBYTES>& c) {
+  if constexpr (NBYTES == 8) {
+    *reinterpret_cast<uint2*>(p) = c.v;
+  } else if constexpr (NBYTES == 16) {
+    *reinterpret_cast<uint4*>(p) = c.v;
+  } else {
+    *reinterpret_cast<uint4*>(p) = c.a;
+    *reinterpret_cast<uint4*>(p + 16) = c.b;
+  }
 }
 
 // Key-code A operand of k-step ks from a lane's chunk of one token row
@@ -317,6 +344,8 @@ template <class C>
 struct WaveLds {
   float* qs;        // [NG][D] query scaled to log2 units
   uint8_t* buf;     // P.V A operands / item outputs / ring probabilities
+  uint8_t* ks;      // [NB][KSEC] key scale / zero sections of the set being computed
+  uint8_t* vs;      // [NB][VSEC] value scale / zero sections
   float* alpha;     // [16] per P.V row
   float* lam;       // [NG][NGR]
   uint4* zero16;
@@ -502,9 +531,13 @@ __device__ __forceinline__ void quant_stream(const Geom& g, const WaveLds<C>& L,
   const bool col_used = n < C::NCOL;
 
   // ---- register buffers for one set, refilled right after their last use ----
-  uint4 ksz[8];                 // K scale (4 x 16 B) and zero (4 x 16 B), channels 32gq..+31, column block
+  // (The scale / zero sections are loaded once per set, a contiguous share per
+  // lane, and staged in LDS at the top of the set: a per-lane copy of the
+  // sections its column needs would hold them 8 to 16 times over, about 60
+  // registers that the waves need for loads in flight.)
+  Chunk<C::KSZ_LANE> ksz;       // this lane's share of the set's key scale / zero sections
   Chunk<C::KLANE> kc[NB][TPB];  // key code rows
-  uint2 vsz[TPB][NGR][2];       // V scale / zero of the lane's 4 tokens per tile and group
+  Chunk<C::VSZ_LANE> vsz;       // this lane's share of the value scale / zero sections
   Chunk<C::VLANE> vc[KS_SET];   // value code chunks
 
   // The paged store reads a set's page numbers once, ahead of its record
@@ -542,12 +575,8 @@ __device__ __forceinline__ void quant_stream(const Geom& g, const WaveLds<C>& L,
 
   // loaders for set si of span sp, whose pages are pg
   auto load_ksz = [&](Span sp, int si, const int (&pg)[NB]) {
-    const uint8_t* p = set_rec(sp, si, cbk, pg) + C::REC_KS + 64 * gq;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      ksz[k] = *reinterpret_cast<const uint4*>(p + 16 * k);
-      ksz[4 + k] = *reinterpret_cast<const uint4*>(p + (C::REC_KZ - C::REC_KS) + 16 * k);
-    }
+    const int byte = lane * C::KSZ_LANE;   // of the set's NB sections
+    ksz = load_chunk<C::KSZ_LANE>(set_rec(sp, si, byte / C::KSEC, pg) + C::REC_KS + byte % C::KSEC);
   };
   auto load_kc = [&](Span sp, int si, const int (&pg)[NB]) {
     const int off = C::REC_KC + n * C::KROW + gq * C::KLANE;
@@ -559,15 +588,8 @@ __device__ __forceinline__ void quant_stream(const Geom& g, const WaveLds<C>& L,
     }
   };
   auto load_vsz = [&](Span sp, int si, const int (&pg)[NB]) {
-    const uint8_t* p = set_rec(sp, si, cbk, pg) + C::REC_VS + 8 * gq;
-#pragma unroll
-    for (int tt = 0; tt < TPB; ++tt)
-#pragma unroll
-      for (int j = 0; j < NGR; ++j) {
-        const int off = (j * C::G + 16 * tt) * 2;
-        vsz[tt][j][0] = *reinterpret_cast<const uint2*>(p + off);
-        vsz[tt][j][1] = *reinterpret_cast<const uint2*>(p + (C::REC_VZ - C::REC_VS) + off);
-      }
+    const int byte = lane * C::VSZ_LANE;
+    vsz = load_chunk<C::VSZ_LANE>(set_rec(sp, si, byte / C::VSEC, pg) + C::REC_VS + byte % C::VSEC);
   };
   auto load_vc = [&](Span sp, int si, const int (&pg)[NB]) {
 #pragma unroll
@@ -613,14 +635,23 @@ __device__ __forceinline__ void quant_stream(const Geom& g, const WaveLds<C>& L,
     bool my_blk = col_used && my_b < cur.end && page_ok;
     if constexpr (C::PAGED && !EARLY)
       my_blk = my_blk && page_in_range(table[(size_t)cur.b * g.max_blocks + min(my_b, cur.end - 1)]);
+    // ---- the set's scale / zero sections into LDS; the next set's are loaded at once ----
+    store_chunk<C::KSZ_LANE>(L.ks + lane * C::KSZ_LANE, ksz);
+    store_chunk<C::VSZ_LANE>(L.vs + lane * C::VSZ_LANE, vsz);
+    load_ksz(nsp, nsi, pgn);
+    load_vsz(nsp, nsi, pgn);
+    wave_lds_fence();
     // ---- B operand: q~ = q' * s_K (hi/lo) and kappa = q' . z_K for the column ----
     uint4 bhi[4], blo[4];
     float kap = 0.f;
     {
       const float* qrow = L.qs + chd * C::QS + 32 * gq;
+      const uint8_t* ksec = L.ks + cbk * C::KSEC + 2 * 32 * gq;   // channels 32gq.. of the column's block
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
-        const uint4 sv = ksz[ks], zv = ksz[4 + ks];   // channels 32gq + 8ks + (0..7) as fp16 pairs
+        // channels 32gq + 8ks + (0..7) as fp16 pairs
+        const uint4 sv = *reinterpret_cast<const uint4*>(ksec + 16 * ks);
+        const uint4 zv = *reinterpret_cast<const uint4*>(ksec + 2 * D + 16 * ks);
         const float4 qa = *reinterpret_cast<const float4*>(qrow + 8 * ks);
         const float4 qb = *reinterpret_cast<const float4*>(qrow + 8 * ks + 4);
         const float qv[8] = {qa.x, qa.y, qa.z, qa.w, qb.x, qb.y, qb.z, qb.w};
@@ -643,7 +674,6 @@ __device__ __forceinline__ void quant_stream(const Geom& g, const WaveLds<C>& L,
       }
       kap = reduce_rows(kap, OpAdd{});
     }
-    load_ksz(nsp, nsi, pgn);
 
     // ---- scores: D[token][column] for every tile of every block of the set ----
     // (the wave issuing its score MFMAs goes first: the other wave of the
@@ -730,7 +760,10 @@ __device__ __forceinline__ void quant_stream(const Geom& g, const WaveLds<C>& L,
         const int ks = T >> 5, gp = (T >> 3) & 3, kvb = (T >> 2) & 1;
 #pragma unroll
         for (int j = 0; j < NGR; ++j) {
-          const uint2 sv = vsz[tt][j][0], zv = vsz[tt][j][1];
+          // value group j of the lane's 4 tokens
+          const uint8_t* vsec = L.vs + cbk * C::VSEC + 2 * (j * C::G + 16 * tt + 4 * gq);
+          const uint2 sv = *reinterpret_cast<const uint2*>(vsec);
+          const uint2 zv = *reinterpret_cast<const uint2*>(vsec + C::VSEC / 2);
           const float z4[4] = {lo_half_f16(zv.x), hi_half_f16(zv.x), lo_half_f16(zv.y), hi_half_f16(zv.y)};
           const float x[4] = {mul_f16<false>(p[tt][0], sv.x), mul_f16<true>(p[tt][1], sv.x),
                               mul_f16<false>(p[tt][2], sv.y), mul_f16<true>(p[tt][3], sv.y)};
@@ -745,7 +778,6 @@ __device__ __forceinline__ void quant_stream(const Geom& g, const WaveLds<C>& L,
         }
       }
     }
-    load_vsz(nsp, nsi, pgn);
     wave_lds_fence();
 
     // ---- P.V: D[head hi|lo][channel] += p~ . code ----
@@ -860,7 +892,7 @@ __device__ __forceinline__ void load_query(const Geom& g, const WaveLds<C>& L, c
 }
 
 // ------------------------------------------------------------------------------------
-// The kernel: persistent waves (2 per SIMD). The units are dealt to kQueues
+// The kernel: persistent waves (C::WAVES_PER_SIMD per SIMD). The units are dealt to kQueues
 // queues (unit u to queue u % kQueues) served by the workgroups with
 // blockIdx.x % kQueues == queue -- with the usual round-robin placement of
 // workgroups that is one queue per XCD, so the counters, each on its own cache
@@ -870,7 +902,7 @@ __device__ __forceinline__ void load_query(const Geom& g, const WaveLds<C>& L, c
 // share the unit plan in LDS and nothing else.
 // ------------------------------------------------------------------------------------
 template <class C>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void decode_fast_kernel(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(C::WAVES_PER_SIMD, C::WAVES_PER_SIMD))) void decode_fast_kernel(
     Geom g, const uint8_t* __restrict__ blocks, const int32_t* __restrict__ table,
     const uint16_t* __restrict__ k_ring, const uint16_t* __restrict__ v_ring, int32_t* __restrict__ state,
     const uint16_t* __restrict__ q, float qscale, int max_blk, int* __restrict__ ws_plan, float* __restrict__ ws) {
@@ -884,7 +916,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   WaveLds<C> L;
   L.qs = reinterpret_cast<float*>(wl);
   L.buf = wl + C::LDS_Q;
-  L.alpha = reinterpret_cast<float*>(L.buf + C::LDS_BUF);
+  L.ks = L.buf + C::LDS_BUF;
+  L.vs = L.ks + C::LDS_KS;
+  L.alpha = reinterpret_cast<float*>(L.vs + C::LDS_VS);
   L.lam = L.alpha + 16;
   L.zero16 = reinterpret_cast<uint4*>(L.lam + NG * C::NGR);
 
