@@ -20,8 +20,8 @@ using kvq::Geom;
 namespace {
 
 // Every decode workgroup keeps a copy of the unit plan (16 + 7B ints) in LDS
-// beside its four waves' buffers (at most 4 x 13 KB); at B = 1024 that is at
-// most 81 KB, inside gfx950's 160 KB per workgroup.
+// beside its four waves' buffers (at most 4 x 15 KB); at B = 1024 that is at
+// most 89 KB, inside gfx950's 160 KB per workgroup.
 constexpr int kMaxBatch = 1024;
 constexpr int kMaxSink = 1 << 20;   // sink tokens per sequence
 constexpr int kMaxFp8Blocks = 4096;  // FP8 blocks per (sequence, kv head)
