@@ -628,7 +628,14 @@ __device__ __forceinline__ void quant_stream(const Geom& g, const WaveLds<C>& L,
   // One set si of span cur; prefetches set nsi of span nsp into each register
   // buffer right after its last use (always a valid set, so the loads are never
   // under a branch and stay in flight across the loop).
+  // Issue priority: the waves that share a SIMD do not progress alike (the
+  // older one wins arbitration between equals), so each wave's base priority
+  // alternates with its set count -- whichever of them is on an odd set goes
+  // first -- and the score phase (below) sits two levels above both. A/B on one
+  // box: Llama-3 GQA INT4 272 -> 263.5 us, paged 265 -> 260 us, 70B unchanged.
+  int sets_done = 0;
   auto run_set = [&](Span cur, int si, Span nsp, int nsi) {
+    const bool odd = (sets_done++ & 1) != 0;
     int pgn[NB];   // pages of the prefetched set, read before its first record load
     set_pages(nsp, nsi, pgn);
     const int my_b = cur.begin + si * NB + cbk;
@@ -679,7 +686,8 @@ __device__ __forceinline__ void quant_stream(const Geom& g, const WaveLds<C>& L,
     // (the wave issuing its score MFMAs goes first: the other wave of the
     // SIMD fills the matrix-core cycles with its vector work; measured 3%
     // faster on the INT4 layer, neutral elsewhere)
-    __builtin_amdgcn_s_setprio(1);
+    if (odd) __builtin_amdgcn_s_setprio(3);
+    else __builtin_amdgcn_s_setprio(2);
     float sc[TPB][4];
 #pragma unroll
     for (int tt = 0; tt < TPB; ++tt)
@@ -702,7 +710,8 @@ __device__ __forceinline__ void quant_stream(const Geom& g, const WaveLds<C>& L,
         for (int i = 0; i < 4; ++i) sc[tt][i] = mine ? acc[i] : sc[tt][i];
       }
     }
-    __builtin_amdgcn_s_setprio(0);
+    if (odd) __builtin_amdgcn_s_setprio(1);
+    else __builtin_amdgcn_s_setprio(0);
     load_kc(nsp, nsi, pgn);
     if (!my_blk) {
 #pragma unroll
